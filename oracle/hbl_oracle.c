@@ -1,0 +1,379 @@
+/*
+ * hbl_oracle.c -- plain, slow, obviously-correct CPU oracle for the H-BitLinear
+ * forward pass (BitNet v2).  TEST INFRASTRUCTURE ONLY: the tests, the smoke
+ * check and the benchmark's CPU-baseline leg may call it; the product path
+ * (the HIP library) never does, and shares no code, header or table with it.
+ *
+ * Sources (web pages about BitNet v2; their display equations were lost in
+ * extraction, so each step below states which passage it follows and, where
+ * the page is silent, which reading it takes):
+ *   [XZY]  "新智元: 微软 BitNet v2" repost (0755model.com), sections
+ *          "BitNet v2：原生4位激活" and "H-BitLinear模块"
+ *   [CSDN] "[论文品鉴] 1-bit LLM" (blog.csdn.net), sections "掩码存储" and "量化函数"
+ *   [XDNF] "【AI论文】BitNet v2：针对1位LLM的原生4位激活和哈达玛变换" (xdnf.cn)
+ *   [SXAI] "AI极简主义革命：BitNet v2如何用4位激活重塑大模型部署与能效", §2.3.2
+ *
+ * Every function is a direct statement of a definition:
+ *   O1  alpha   = mean |W| over the whole tensor            (per-tensor absmean, [XZY] H-BitLinear)
+ *   O2  W_q     = clamp(rint(W / (alpha+eps)), -1, 1)          (ternary; zero band |w| <= alpha/2, [CSDN] 量化函数)
+ *   O3  pack    2-bit two's complement, 4 per byte; in each aligned group of
+ *               16 k, byte (k%4) holds field ((k%16)/4)  (the library's format)
+ *   O4  x       = fp32(X)  (bf16 -> fp32 is exact)
+ *   O5  r       = RMSNorm / LayerNorm / identity of x, in fp64  ([XZY] layer formula uses LN; architecture uses RMSNorm)
+ *   O6  z       = H_K r, H_K[i][j] = (-1)^popcount(i&j) / sqrt(K)  (normalised Sylvester, dense, fp64)
+ *   O7  scale   INT8: gamma = max|z|, s = 127/(gamma+eps), d = gamma/127
+ *               INT4: beta = mean|z|, s = sqrt7/(beta+eps), d = beta/sqrt7 (default)
+ *                     or gamma = max|z|, s = 7/(gamma+eps), d = gamma/7     (alternative)
+ *   O8  q       = clamp(rint(fp32(z*s)), lo, hi)   INT8 [-128,127], INT4 [-8,7]; INT4 packs 2/byte
+ *   O9  acc     = sum_k q[m][k] * W_q[n][k]   (int64 triple loop, stored as int32)
+ *   O10 y       = fp32(fp32(acc * d[m]) * alpha)
+ *
+ * Rounding is round-half-to-even (rint under the default FP environment)
+ * everywhere.  No step is fused, blocked or reordered beyond these definitions.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fopenmp -fPIC -shared hbl_oracle.c -o libhbl_oracle.so -lm
+ * (no -ffast-math, no contraction: every fp32 operation rounds exactly as written.)
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define HBO_OK 0
+#define HBO_ERR 1
+
+/* fp32 nearest to sqrt(7) (2.6457512...), bit pattern 0x402953FD.  Used by the
+ * INT4 absmean quantiser; stated as a bit pattern so that no library sqrt
+ * rounding enters the definition. */
+static float hbo_sqrt7_f32(void) {
+    union { uint32_t u; float f; } v;
+    v.u = 0x402953FDu;
+    return v.f;
+}
+
+int hbo_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void hbo_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* ---------------------------------------------------------------- O4 ---- */
+/* bf16 -> fp32: the bf16 bit pattern is the top half of the fp32 pattern. */
+void hbo_bf16_to_f32(const uint16_t* x, int64_t n, float* out) {
+    for (int64_t i = 0; i < n; i++) {
+        union { uint32_t u; float f; } v;
+        v.u = ((uint32_t)x[i]) << 16;
+        out[i] = v.f;
+    }
+}
+
+/* fp32 -> bf16, round to nearest even (used only for a bf16 output variant). */
+void hbo_f32_to_bf16(const float* x, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; i++) {
+        union { uint32_t u; float f; } v;
+        v.f = x[i];
+        uint32_t lsb = (v.u >> 16) & 1u;
+        out[i] = (uint16_t)((v.u + 0x7FFFu + lsb) >> 16);
+    }
+}
+
+/* ---------------------------------------------------------- O1, O2 ------ */
+/* alpha = (sum |W| in fp64, sequential) / count, rounded to fp32.
+ * Per-tensor absmean [XZY, H-BitLinear module]. */
+float hbo_weight_alpha(const float* W, int64_t count) {
+    double s = 0.0;
+    for (int64_t i = 0; i < count; i++) s += fabs((double)W[i]);
+    if (count <= 0) return 0.0f;
+    return (float)(s / (double)count);
+}
+
+/* Ternarise one tensor of `count` latent weights with the given alpha.
+ * t = fp32(W / fp32(alpha + eps)); W_q = clamp(rint(t), -1, 1).
+ * With round-half-even, |t| = 0.5 maps to 0, so the zero band -D <= w <= D of
+ * the threshold form ([CSDN] 量化函数) is inclusive with D = (alpha+eps)/2.
+ * alpha + eps == 0 (an all-zero tensor with eps = 0) gives all zeros. */
+void hbo_ternarize(const float* W, int64_t count, float alpha, float eps, int8_t* Wq) {
+    float den = alpha + eps;
+    for (int64_t i = 0; i < count; i++) {
+        if (den == 0.0f) { Wq[i] = 0; continue; }
+        float t = W[i] / den;
+        float r = rintf(t);
+        if (r > 1.0f) r = 1.0f;
+        if (r < -1.0f) r = -1.0f;
+        Wq[i] = (int8_t)r;
+    }
+}
+
+/* ---------------------------------------------------------------- O3 ---- */
+/* 2-bit packing of a [N][K] ternary matrix into bytes [N][K/4].  The pages
+ * give no 2-bit layout (they describe 5-trits-per-byte and bitmask+sign
+ * storage, [CSDN] 掩码存储), so this one is the library's own definition:
+ *   code:     2-bit two's complement, 0 -> 00, +1 -> 01, -1 -> 11 (10 unused)
+ *   position: K is cut into aligned groups of 16; the group g of row n owns
+ *             bytes 4g..4g+3 of that row; element k goes to byte 4*(k/16) + k%4,
+ *             bits 2*((k%16)/4) and 2*((k%16)/4)+1.
+ * So byte b of a group holds the four elements whose index is b mod 4, in
+ * increasing k from the lowest bit pair.  Requires K % 16 == 0. */
+static int64_t hbo_tern_byte(int64_t k) { return 4 * (k / 16) + (k % 4); }
+static int hbo_tern_shift(int64_t k) { return (int)(2 * ((k % 16) / 4)); }
+
+int hbo_pack_ternary(const int8_t* Wq, int64_t N, int64_t K, uint8_t* Wp) {
+    if (K % 16) return HBO_ERR;
+    memset(Wp, 0, (size_t)(N * (K / 4)));
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++) {
+            int v = Wq[n * K + k];
+            uint8_t code = (v == 0) ? 0u : (v == 1 ? 1u : 3u);
+            Wp[n * (K / 4) + hbo_tern_byte(k)] |= (uint8_t)(code << hbo_tern_shift(k));
+        }
+    return HBO_OK;
+}
+
+/* Inverse of hbo_pack_ternary; the unused code 10 decodes to 2 so that a
+ * corrupted byte is visible. */
+int hbo_unpack_ternary(const uint8_t* Wp, int64_t N, int64_t K, int8_t* Wq) {
+    if (K % 16) return HBO_ERR;
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++) {
+            int code = (Wp[n * (K / 4) + hbo_tern_byte(k)] >> hbo_tern_shift(k)) & 3;
+            Wq[n * K + k] = (int8_t)(code == 0 ? 0 : (code == 1 ? 1 : (code == 3 ? -1 : 2)));
+        }
+    return HBO_OK;
+}
+
+/* O1-O3 in one call: alpha from the whole tensor, then ternarise and pack. */
+int hbo_quantize_weights(const float* W, int64_t N, int64_t K, float eps,
+                         int8_t* Wq, uint8_t* Wp, float* alpha_out) {
+    if (N <= 0 || K <= 0 || K % 16) return HBO_ERR;
+    float alpha = hbo_weight_alpha(W, N * K);
+    hbo_ternarize(W, N * K, alpha, eps, Wq);
+    *alpha_out = alpha;
+    return hbo_pack_ternary(Wq, N, K, Wp);
+}
+
+/* ---------------------------------------------------------------- O5 ---- */
+/* norm: 0 = RMSNorm, 1 = LayerNorm, 2 = none.  fp64 throughout.
+ * RMS:  r_k = x_k / sqrt(sum x^2 / K + eps) * g_k
+ * LN:   r_k = (x_k - mu) / sqrt(sum (x - mu)^2 / K + eps) * g_k
+ * gain == NULL means g = 1.  There is no bias ([XZY] "BitNet v2：原生4位激活"). */
+void hbo_norm_row(const float* x, int64_t K, const float* gain, int norm, float eps, double* r) {
+    if (norm == 2) {
+        for (int64_t k = 0; k < K; k++) r[k] = (double)x[k] * (gain ? (double)gain[k] : 1.0);
+        return;
+    }
+    double mu = 0.0;
+    if (norm == 1) {
+        for (int64_t k = 0; k < K; k++) mu += (double)x[k];
+        mu /= (double)K;
+    }
+    double ss = 0.0;
+    for (int64_t k = 0; k < K; k++) {
+        double c = (double)x[k] - mu;
+        ss += c * c;
+    }
+    double den = sqrt(ss / (double)K + (double)eps);
+    for (int64_t k = 0; k < K; k++) {
+        double v = ((double)x[k] - mu) / den;
+        r[k] = v * (gain ? (double)gain[k] : 1.0);
+    }
+}
+
+/* ---------------------------------------------------------------- O6 ---- */
+/* Dense normalised Sylvester Hadamard, natural order:
+ * z_i = sum_j (-1)^popcount(i & j) r_j / sqrt(K), K a power of two.
+ * The +-1 entries and orthogonal rows are the properties the pages state
+ * ([XZY] H-BitLinear module, Hadamard paragraph); the O(K log K) fast
+ * transform the pages mention computes this same product, which is why the
+ * oracle keeps the dense O(K^2) form.  The matrix is never materialised. */
+void hbo_hadamard_row(const double* r, int64_t K, double* z) {
+    double inv = 1.0 / sqrt((double)K);
+    for (int64_t i = 0; i < K; i++) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < K; j++) {
+            int odd = __builtin_popcountll((unsigned long long)(i & j)) & 1;
+            acc += (odd ? -1.0 : 1.0) * r[j];
+        }
+        z[i] = acc * inv;
+    }
+}
+
+/* ------------------------------------------------------------ O7, O8 ---- */
+/* Per-token activation scale.  bits = 8: absmax.  bits = 4: a4_mode 0 =
+ * absmean with sqrt7, a4_mode 1 = absmax with 7.  Outputs the quantiser
+ * multiplier s and the dequantisation factor d.  A zero statistic gives
+ * s = d = 0 (all codes 0). */
+int hbo_act_scale(const float* z, int64_t K, int bits, int a4_mode, float eps, float* s_out, float* d_out) {
+    float stat, num;
+    if (bits == 8 || (bits == 4 && a4_mode == 1)) {
+        float g = 0.0f;
+        for (int64_t k = 0; k < K; k++) {
+            float a = fabsf(z[k]);
+            if (a > g) g = a;
+        }
+        stat = g;
+        num = (bits == 8) ? 127.0f : 7.0f;
+    } else if (bits == 4 && a4_mode == 0) {
+        double s = 0.0;
+        for (int64_t k = 0; k < K; k++) s += fabs((double)z[k]);
+        stat = (float)(s / (double)K);
+        num = hbo_sqrt7_f32();
+    } else {
+        return HBO_ERR;
+    }
+    if (stat == 0.0f) { *s_out = 0.0f; *d_out = 0.0f; return HBO_OK; }
+    float den = stat + eps;
+    *s_out = num / den;
+    *d_out = stat / num;
+    return HBO_OK;
+}
+
+/* q_k = clamp(rint(fp32(z_k * s)), lo, hi): one fp32 multiply, then
+ * round-half-even, then clip to the signed range of the bit width. */
+int hbo_act_codes(const float* z, int64_t K, int bits, float s, int8_t* q) {
+    float lo, hi;
+    if (bits == 8) { lo = -128.0f; hi = 127.0f; }
+    else if (bits == 4) { lo = -8.0f; hi = 7.0f; }
+    else return HBO_ERR;
+    for (int64_t k = 0; k < K; k++) {
+        float t = z[k] * s;   /* a single rounded fp32 product */
+        float r = rintf(t);
+        if (r > hi) r = hi;
+        if (r < lo) r = lo;
+        q[k] = (int8_t)r;
+    }
+    return HBO_OK;
+}
+
+/* INT4 packing of [M][K] codes into bytes [M][K/2]: low nibble = even k,
+ * high nibble = odd k, each 4-bit two's complement.  Requires K % 2 == 0. */
+int hbo_pack_int4(const int8_t* q, int64_t M, int64_t K, uint8_t* p) {
+    if (K % 2) return HBO_ERR;
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t k2 = 0; k2 < K / 2; k2++) {
+            uint8_t lo = (uint8_t)(q[m * K + 2 * k2] & 0xF);
+            uint8_t hi = (uint8_t)(q[m * K + 2 * k2 + 1] & 0xF);
+            p[m * (K / 2) + k2] = (uint8_t)(lo | (hi << 4));
+        }
+    return HBO_OK;
+}
+
+int hbo_unpack_int4(const uint8_t* p, int64_t M, int64_t K, int8_t* q) {
+    if (K % 2) return HBO_ERR;
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t k = 0; k < K; k++) {
+            int nib = (p[m * (K / 2) + k / 2] >> (4 * (k % 2))) & 0xF;
+            q[m * K + k] = (int8_t)(nib >= 8 ? nib - 16 : nib);
+        }
+    return HBO_OK;
+}
+
+/* O4-O8 for a batch of rows.  X is fp32 [M][K] (bf16 callers convert with
+ * hbo_bf16_to_f32 first, which is exact).  hadamard = 1: H-BitLinear,
+ * hadamard = 0: plain BitLinear (same steps without O6).
+ * Outputs (all caller-allocated, host memory):
+ *   z_out [M][K] fp32 (nullable), q [M][K] int8 codes, s_out/d_out [M].
+ * Rows are independent; OpenMP splits them over threads. */
+int hbo_quantize_activations(const float* X, int64_t M, int64_t K, const float* gain,
+                             int norm, float norm_eps, int hadamard, int bits, int a4_mode,
+                             float quant_eps, float* z_out, int8_t* q, float* s_out, float* d_out) {
+    if (M < 0 || K <= 0) return HBO_ERR;
+    if (hadamard && (K & (K - 1))) return HBO_ERR;
+    if (!(bits == 8 || bits == 4)) return HBO_ERR;
+    int err = 0;
+#pragma omp parallel
+    {
+        double* r = (double*)malloc(sizeof(double) * (size_t)K);
+        double* zd = (double*)malloc(sizeof(double) * (size_t)K);
+        float* zf = (float*)malloc(sizeof(float) * (size_t)K);
+        if (!r || !zd || !zf) {
+#pragma omp atomic write
+            err = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t m = 0; m < M; m++) {
+                hbo_norm_row(X + m * K, K, gain, norm, norm_eps, r);
+                if (hadamard) {
+                    hbo_hadamard_row(r, K, zd);
+                    for (int64_t k = 0; k < K; k++) zf[k] = (float)zd[k];
+                } else {
+                    for (int64_t k = 0; k < K; k++) zf[k] = (float)r[k];
+                }
+                if (z_out) memcpy(z_out + m * K, zf, sizeof(float) * (size_t)K);
+                hbo_act_scale(zf, K, bits, a4_mode, quant_eps, &s_out[m], &d_out[m]);
+                hbo_act_codes(zf, K, bits, s_out[m], q + m * K);
+            }
+        }
+        free(r); free(zd); free(zf);
+    }
+    return err ? HBO_ERR : HBO_OK;
+}
+
+/* ---------------------------------------------------------------- O9 ---- */
+/* acc[m][n] = sum_k q[m][k] * Wq[n][k], int64 accumulation, stored as int32.
+ * Returns HBO_ERR if any |acc| >= 2^31 (cannot happen for K <= 2^16 with
+ * INT8 codes and ternary weights). */
+int hbo_int_gemm(const int8_t* q, const int8_t* Wq, int64_t M, int64_t N, int64_t K, int32_t* acc) {
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++) {
+            int64_t s = 0;
+            for (int64_t k = 0; k < K; k++) s += (int64_t)q[m * K + k] * (int64_t)Wq[n * K + k];
+            if (s >= 2147483648LL || s < -2147483648LL) {
+#pragma omp atomic write
+                err = 1;
+            }
+            acc[m * N + n] = (int32_t)s;
+        }
+    return err ? HBO_ERR : HBO_OK;
+}
+
+/* --------------------------------------------------------------- O10 ---- */
+/* y[m][n] = fp32(fp32(float(acc) * d[m]) * alpha): two rounded fp32 products,
+ * no bias. */
+void hbo_rescale(const int32_t* acc, const float* d, float alpha, int64_t M, int64_t N, float* y) {
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++) {
+            float t = (float)acc[m * N + n] * d[m];
+            y[m * N + n] = t * alpha;
+        }
+}
+
+/* O4-O10: the whole forward for M rows of fp32 input and a ternary weight
+ * matrix already quantised (Wq [N][K] int8, alpha).  Per-row intermediates
+ * are returned when the pointers are non-NULL. */
+int hbo_forward(const float* X, int64_t M, int64_t K, const float* gain, int norm, float norm_eps,
+                int hadamard, int bits, int a4_mode, float quant_eps,
+                const int8_t* Wq, float alpha, int64_t N,
+                float* y, int32_t* acc_out, int8_t* q_out, float* d_out, float* z_out) {
+    if (M < 0 || N <= 0 || K <= 0) return HBO_ERR;
+    int8_t* q = q_out ? q_out : (int8_t*)malloc((size_t)(M * K > 0 ? M * K : 1));
+    float* s = (float*)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1));
+    float* d = d_out ? d_out : (float*)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1));
+    int32_t* acc = acc_out ? acc_out : (int32_t*)malloc(sizeof(int32_t) * (size_t)(M * N > 0 ? M * N : 1));
+    int rc = HBO_ERR;
+    if (q && s && d && acc) {
+        rc = hbo_quantize_activations(X, M, K, gain, norm, norm_eps, hadamard, bits, a4_mode,
+                                      quant_eps, z_out, q, s, d);
+        if (rc == HBO_OK) rc = hbo_int_gemm(q, Wq, M, N, K, acc);
+        if (rc == HBO_OK) hbo_rescale(acc, d, alpha, M, N, y);
+    }
+    if (!q_out) free(q);
+    free(s);
+    if (!d_out) free(d);
+    if (!acc_out) free(acc);
+    return rc;
+}

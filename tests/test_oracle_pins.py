@@ -1,0 +1,341 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks one oracle step against something other than the oracle:
+values the pages print (tests/golden), hand-derived cases, closed forms,
+library routines (scipy's Sylvester Hadamard, torch's norms, numpy's integer
+matmul), invariants, and brute force on tiny inputs.  Together they are chosen
+so that a dropped term, a wrong sign or index, a transposed operand, a wrong
+rounding mode or a misplaced epsilon in the oracle fails at least one test.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+import oracle
+import workloads
+
+
+# ------------------------------------------------------------------ Hadamard
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024])
+def test_hadamard_equals_scipy_sylvester(n):
+    """O6 against scipy.linalg.hadamard (Sylvester construction, natural order)."""
+    rng = np.random.default_rng(n)
+    R = rng.standard_normal((3, n))
+    H = scipy.linalg.hadamard(n).astype(np.float64) / math.sqrt(n)
+    Z = oracle.hadamard_rows(R)
+    ref = R @ H.T
+    assert np.max(np.abs(Z - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_hadamard_small_explicit(golden):
+    g = golden("hadamard_sylvester.txt")
+    for key, n in (("H2", 2), ("H4", 4)):
+        H = np.array(g[key], np.float64)
+        Hor = oracle.hadamard_rows(np.eye(n)).T      # columns = H e_j
+        assert np.allclose(Hor * math.sqrt(n), H, atol=1e-14)
+    assert oracle.hadamard_rows(np.array([[5.0]]))[0, 0] == 5.0
+
+
+@pytest.mark.parametrize("n", [8, 64, 256])
+def test_hadamard_orthonormal_symmetric(n):
+    H = oracle.hadamard_rows(np.eye(n))              # row i = H e_i = column i (H symmetric)
+    assert np.allclose(H, H.T, atol=1e-14)
+    assert np.allclose(H @ H.T, np.eye(n), atol=1e-12)
+    assert np.all(np.isclose(np.abs(H) * math.sqrt(n), 1.0, atol=1e-13))
+
+
+def test_hadamard_recursive_block_structure():
+    """H_2n r = [H_n(a+b), H_n(a-b)] / sqrt(2) for r = [a, b] (natural order)."""
+    rng = np.random.default_rng(7)
+    for n in (16, 128, 512):
+        r = rng.standard_normal(2 * n)
+        a, b = r[:n], r[n:]
+        z = oracle.hadamard_rows(r[None])[0]
+        top = oracle.hadamard_rows((a + b)[None])[0] / math.sqrt(2)
+        bot = oracle.hadamard_rows((a - b)[None])[0] / math.sqrt(2)
+        assert np.allclose(z, np.concatenate([top, bot]), atol=1e-12)
+
+
+def test_hadamard_involution_norm_ones():
+    rng = np.random.default_rng(3)
+    n = 2048
+    r = rng.standard_normal((2, n))
+    z = oracle.hadamard_rows(r)
+    assert np.allclose(oracle.hadamard_rows(z), r, atol=1e-11)           # H H = I
+    assert np.allclose(np.linalg.norm(z, axis=1), np.linalg.norm(r, axis=1), rtol=1e-13)
+    ones = oracle.hadamard_rows(np.ones((1, n)))[0]                       # H 1 = sqrt(n) e_0
+    e0 = np.zeros(n)
+    e0[0] = math.sqrt(n)
+    assert np.allclose(ones, e0, atol=1e-10)
+
+
+# ---------------------------------------------------------------------- norm
+def test_rmsnorm_matches_torch():
+    rng = np.random.default_rng(11)
+    X = (rng.standard_normal((5, 96)) * 3).astype(np.float32)
+    g = (rng.standard_normal(96) + 1).astype(np.float32)
+    for eps in (0.0, 1e-5, 0.25):
+        for gain in (None, g):
+            r = oracle.norm_rows(X, gain=gain, norm=oracle.NORM_RMS, eps=eps)
+            w = None if gain is None else torch.from_numpy(gain.astype(np.float64))
+            ref = torch.nn.functional.rms_norm(torch.from_numpy(X.astype(np.float64)), (96,), weight=w, eps=eps)
+            assert np.allclose(r, ref.numpy(), rtol=1e-13, atol=1e-13)
+
+
+def test_layernorm_matches_torch():
+    rng = np.random.default_rng(12)
+    X = (rng.standard_normal((5, 64)) * 2 + 1.5).astype(np.float32)
+    g = (rng.standard_normal(64) + 1).astype(np.float32)
+    for eps in (0.0, 1e-5):
+        for gain in (None, g):
+            r = oracle.norm_rows(X, gain=gain, norm=oracle.NORM_LN, eps=eps)
+            w = None if gain is None else torch.from_numpy(gain.astype(np.float64))
+            ref = torch.nn.functional.layer_norm(torch.from_numpy(X.astype(np.float64)), (64,), weight=w,
+                                                 bias=None, eps=eps)
+            assert np.allclose(r, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_norm_hand_and_none():
+    r = oracle.norm_rows(np.array([[3.0, 4.0]], np.float32), norm=oracle.NORM_RMS, eps=0.0)[0]
+    rms = math.sqrt((9 + 16) / 2)
+    assert np.allclose(r, [3 / rms, 4 / rms], rtol=1e-15)
+    x = np.array([[1.0, -2.0, 3.0, 0.5]], np.float32)
+    g = np.array([2.0, 0.5, -1.0, 4.0], np.float32)
+    assert np.array_equal(oracle.norm_rows(x, gain=g, norm=oracle.NORM_NONE)[0], [2.0, -1.0, -3.0, 2.0])
+
+
+# ------------------------------------------------------------------ weights
+def test_ternary_page_example(golden):
+    """The bitmask-storage example of the CSDN blog, section 掩码存储."""
+    g = golden("ternary_page_example.txt")
+    W = np.array(g["latent"], np.float32)
+    alpha = oracle.weight_alpha(W)
+    assert alpha == np.float32(g["alpha"])
+    q = oracle.ternarize(W, alpha, 0.0)
+    assert q.tolist() == g["ternary"]
+    bitmask = (q != 0).astype(int).tolist()
+    signs = [1 if v > 0 else 0 for v in q if v != 0]
+    assert bitmask == g["bitmask"] and signs == g["signs"]
+    assert len(bitmask) + len(signs) == g["bits"]
+
+
+def test_ternary_hand_cases(golden):
+    g = golden("ternary_hand.txt")
+    for key in ("tie", "mean", "eps"):
+        W = np.array(g[key + "_latent"], np.float32)
+        alpha = oracle.weight_alpha(W)
+        assert oracle.ternarize(W, alpha, g[key + "_eps"]).tolist() == g[key + "_ternary"], key
+    W = np.array(g["eps_latent"], np.float32)
+    assert oracle.ternarize(W, oracle.weight_alpha(W), 0.0).tolist() == g["eps0_ternary"]
+    assert oracle.weight_alpha(np.array(g["alpha_tensor"], np.float32)) == np.float32(g["alpha_value"])
+
+
+def test_ternary_threshold_rule():
+    """q = 0 exactly when |W| <= (alpha+eps)/2 (inclusive zero band), sign kept otherwise."""
+    rng = np.random.default_rng(5)
+    W = (rng.standard_normal(20000) * 0.02).astype(np.float32)
+    alpha = oracle.weight_alpha(W)
+    q = oracle.ternarize(W, alpha, 0.0)
+    t = np.abs(W.astype(np.float64)) / float(alpha)
+    clear = np.abs(t - 0.5) > 1e-6
+    assert np.array_equal((q == 0)[clear], (t <= 0.5)[clear])
+    nz = q != 0
+    assert np.array_equal(np.sign(q[nz]), np.sign(W[nz]).astype(np.int8))
+    assert set(np.unique(q).tolist()) <= {-1, 0, 1}
+    assert 0.2 < np.mean(q == 0) < 0.45       # Gaussian: P(|w| <= 0.5*mean|w|) ~ 0.31
+
+
+def test_ternary_scale_invariance():
+    rng = np.random.default_rng(6)
+    W = rng.standard_normal((4, 64)).astype(np.float32)
+    q0 = oracle.quantize_weights(W, eps=0.0)[0]
+    for e in (-3, 5):
+        Ws = (W * np.float32(2.0 ** e)).astype(np.float32)
+        assert np.array_equal(oracle.quantize_weights(Ws, eps=0.0)[0], q0)
+
+
+def test_pack_ternary_golden(golden):
+    g = golden("pack_ternary_k16.txt")
+    q = np.array([g["ternary"]], np.int8)
+    p = oracle.pack_ternary(q)
+    assert p[0].tolist() == g["bytes"]
+    assert np.array_equal(oracle.unpack_ternary(p, 16), q)
+
+
+def test_pack_ternary_roundtrip_and_positions():
+    rng = np.random.default_rng(8)
+    q = rng.integers(-1, 2, size=(37, 128)).astype(np.int8)
+    p = oracle.pack_ternary(q)
+    assert p.shape == (37, 32)
+    assert np.array_equal(oracle.unpack_ternary(p, 128), q)
+    # a single +1 at k lands in byte 4*(k//16) + k%4 at bit pair (k%16)//4
+    for k in range(128):
+        one = np.zeros((1, 128), np.int8)
+        one[0, k] = 1
+        pk = oracle.pack_ternary(one)[0]
+        expect = np.zeros(32, np.uint8)
+        expect[4 * (k // 16) + k % 4] = 1 << (2 * ((k % 16) // 4))
+        assert np.array_equal(pk, expect), k
+    # the code 10 never appears
+    bits = np.unpackbits(p.reshape(-1, 1), axis=1, bitorder="little").reshape(-1, 4, 2)
+    assert not np.any((bits[:, :, 0] == 0) & (bits[:, :, 1] == 1))
+
+
+def test_quantize_weights_composition():
+    rng = np.random.default_rng(9)
+    W = workloads.w_latent(rng, 48, 64)
+    Wq, Wp, alpha = oracle.quantize_weights(W, eps=1e-5)
+    assert alpha == oracle.weight_alpha(W)
+    assert abs(float(alpha) - float(np.mean(np.abs(W.astype(np.float64))))) <= 1e-7 * float(alpha)
+    assert np.array_equal(Wq, oracle.ternarize(W, alpha, 1e-5))
+    assert np.array_equal(oracle.unpack_ternary(Wp, 64), Wq)
+    with pytest.raises(ValueError):
+        oracle.quantize_weights(W[:, :40])      # K % 16 != 0
+
+
+# -------------------------------------------------------------- activations
+def test_int8_hand_cases(golden):
+    g = golden("act_quant_hand.txt")
+    for key in ("i8_a", "i8_b", "i8_c", "i8_d"):
+        z = np.array(g[key + "_z"], np.float32)
+        s, d = oracle.act_scale(z, 8, eps=g[key + "_eps"])
+        assert oracle.act_codes(z, 8, s).tolist() == g[key + "_codes"], key
+        gamma = np.max(np.abs(z))
+        assert d == np.float32(gamma / np.float32(127.0))
+    s, _ = oracle.act_scale(np.array(g["i8_a_z"], np.float32), 8, eps=0.0)
+    assert s == np.float32(g["i8_a_s"])
+
+
+def test_int4_hand_cases(golden):
+    g = golden("act_quant_hand.txt")
+    sqrt7 = np.float32(math.sqrt(7.0))
+    for key in ("i4_a", "i4_b", "i4_c", "i4_d"):
+        z = np.array(g[key + "_z"], np.float32)
+        s, d = oracle.act_scale(z, 4, a4_mode=oracle.A4_ABSMEAN, eps=0.0)
+        assert oracle.act_codes(z, 4, s).tolist() == g[key + "_codes"], key
+        beta = np.float32(np.mean(np.abs(z.astype(np.float64))))
+        assert s == np.float32(sqrt7 / beta) and d == np.float32(beta / sqrt7)
+    z = np.array(g["i4m_z"], np.float32)
+    s, d = oracle.act_scale(z, 4, a4_mode=oracle.A4_ABSMAX, eps=0.0)
+    assert s == np.float32(1.75) and d == np.float32(np.float32(4.0) / np.float32(7.0))
+    assert oracle.act_codes(z, 4, s).tolist() == g["i4m_codes"]
+
+
+def test_int4_pack_golden(golden):
+    g = golden("act_quant_hand.txt")
+    q = np.array([g["pack4_codes"]], np.int8)
+    p = oracle.pack_int4(q)
+    assert p[0].tolist() == g["pack4_bytes"]
+    assert np.array_equal(oracle.unpack_int4(p, 4), q)
+    rng = np.random.default_rng(2)
+    q = rng.integers(-8, 8, size=(9, 64)).astype(np.int8)
+    assert np.array_equal(oracle.unpack_int4(oracle.pack_int4(q), 64), q)
+
+
+def test_act_quant_invariants():
+    rng = np.random.default_rng(13)
+    for _ in range(20):
+        z = (rng.standard_normal(256) * rng.uniform(0.01, 100)).astype(np.float32)
+        s, _ = oracle.act_scale(z, 8, eps=0.0)
+        q = oracle.act_codes(z, 8, s)
+        am = np.argmax(np.abs(z))
+        assert abs(int(q[am])) == 127 and np.sign(q[am]) == np.sign(z[am])
+        assert q.min() >= -127 and q.max() <= 127
+        assert np.array_equal(oracle.act_codes(-z, 8, s), -q)                    # odd symmetry
+        z2 = (z * np.float32(8.0)).astype(np.float32)
+        assert np.array_equal(oracle.act_codes(z2, 8, oracle.act_scale(z2, 8, eps=0.0)[0]), q)
+        s4, _ = oracle.act_scale(z, 4, eps=0.0)
+        q4 = oracle.act_codes(z, 4, s4)
+        assert q4.min() >= -8 and q4.max() <= 7
+        z4 = (z * np.float32(0.25)).astype(np.float32)
+        assert np.array_equal(oracle.act_codes(z4, 4, oracle.act_scale(z4, 4, eps=0.0)[0]), q4)
+    s, d = oracle.act_scale(np.zeros(64, np.float32), 8, eps=1e-5)          # all-zero row
+    assert s == 0 and d == 0
+    assert not oracle.act_codes(np.zeros(64, np.float32), 8, s).any()
+
+
+# --------------------------------------------------------------- int GEMM
+def test_int_gemm_matches_numpy():
+    rng = np.random.default_rng(21)
+    q = rng.integers(-128, 128, size=(7, 96)).astype(np.int8)
+    w = rng.integers(-1, 2, size=(11, 96)).astype(np.int8)
+    acc = oracle.int_gemm(q, w)
+    ref = q.astype(np.int64) @ w.astype(np.int64).T
+    assert acc.shape == (7, 11) and np.array_equal(acc, ref)
+
+
+def test_int_gemm_brute_force_tiny():
+    """Every ternary row of length 4 against every INT4 code in each position."""
+    import itertools
+    rows = np.array(list(itertools.product([-1, 0, 1], repeat=4)), np.int8)      # 81 x 4
+    codes = np.array(list(itertools.product(range(-8, 8), repeat=2)), np.int8)   # 256 x 2
+    q = np.concatenate([codes, codes[::-1]], axis=1)                             # 256 x 4
+    acc = oracle.int_gemm(q, rows)
+    for m in range(0, 256, 17):
+        for n in range(81):
+            assert acc[m, n] == sum(int(q[m, k]) * int(rows[n, k]) for k in range(4))
+
+
+def test_int_gemm_identity_and_ones():
+    rng = np.random.default_rng(22)
+    q = rng.integers(-128, 128, size=(5, 16)).astype(np.int8)
+    assert np.array_equal(oracle.int_gemm(q, np.eye(16, dtype=np.int8)), q.astype(np.int32))
+    assert np.array_equal(oracle.int_gemm(q, np.ones((3, 16), np.int8))[:, 0], q.astype(np.int64).sum(1))
+
+
+def test_rescale_hand():
+    y = oracle.rescale(np.array([[3, -5, 0]], np.int32), np.array([0.5], np.float32), 0.25)
+    assert y.tolist() == [[0.375, -0.625, 0.0]]
+
+
+# --------------------------------------------------------------- end to end
+@pytest.mark.parametrize("K", [256, 1024, 4096])
+def test_forward_closed_form_hadamard_column(K):
+    """x = c * (column j of the unnormalised Sylvester H): RMSNorm gives the +-1
+    column, the normalised H maps it to sqrt(K) e_j, so INT8 codes are 127 e_j
+    and y[n] = sqrt(K) * alpha * W_q[n, j] (up to the two fp32 roundings)."""
+    rng = np.random.default_rng(K)
+    N = 24
+    W = workloads.w_latent(rng, N, K)
+    Wq, _, alpha = oracle.quantize_weights(W, eps=1e-5)
+    Hs = scipy.linalg.hadamard(K)
+    for j in (0, 1, K // 2 + 3, K - 1):
+        x = (Hs[:, j] * 2.5).astype(np.float32)[None, :]
+        out = oracle.forward(x, Wq, alpha, bits=8, quant_eps=0.0, norm_eps=0.0)
+        e = np.zeros(K, np.int8)
+        e[j] = 127
+        assert np.array_equal(out["q"][0], e)
+        zref = np.zeros(K)
+        zref[j] = math.sqrt(K)
+        assert np.allclose(out["z"][0], zref, rtol=1e-6, atol=1e-5)
+        assert np.array_equal(out["acc"][0], 127 * Wq[:, j].astype(np.int32))
+        assert np.allclose(out["y"][0], math.sqrt(K) * float(alpha) * Wq[:, j], rtol=2e-7, atol=0)
+        # INT4 absmean on the same row: beta = 1/sqrt(K), the spike clips at 7
+        out4 = oracle.forward(x, Wq, alpha, bits=4, quant_eps=0.0, norm_eps=0.0)
+        e4 = np.zeros(K, np.int8)
+        e4[j] = 7
+        assert np.array_equal(out4["q"][0], e4)
+
+
+def test_forward_plain_bitlinear_and_bf16():
+    """hadamard=0 skips O6; bf16 inputs convert exactly (0x3F80 = 1.0, 0xC000 = -2, 0x3F81 = 1+2^-7)."""
+    assert oracle.bf16_to_f32(np.array([0x3F80, 0xC000, 0x3F81], np.uint16)).tolist() == [1.0, -2.0, 1.0078125]
+    rng = np.random.default_rng(31)
+    X = rng.standard_normal((3, 64)).astype(np.float32)
+    qa = oracle.quantize_activations(X, bits=8, hadamard=False)
+    r = oracle.norm_rows(X).astype(np.float32)
+    assert np.array_equal(qa["z"], r)
+    Xb = workloads.f32_to_bf16_bits(X)
+    qb = oracle.quantize_activations(Xb, bits=8, hadamard=True)
+    qf = oracle.quantize_activations(workloads.bf16_bits_to_f32(Xb), bits=8, hadamard=True)
+    assert np.array_equal(qb["q"], qf["q"]) and np.array_equal(qb["z"], qf["z"])
+
+
+def test_forward_rejects_bad_shapes():
+    with pytest.raises(ValueError):
+        oracle.quantize_activations(np.zeros((2, 96), np.float32), bits=8, hadamard=True)   # not a power of two
+    with pytest.raises(ValueError):
+        oracle.quantize_activations(np.zeros((2, 64), np.float32), bits=5)
