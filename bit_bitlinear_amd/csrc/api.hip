@@ -1,0 +1,185 @@
+// api.hip -- the C ABI of libhbl.so: host-side validation, workspace carving
+// and kernel dispatch.  Every argument is checked before anything is queued,
+// so invalid calls return an error without touching the GPU.
+#include <hip/hip_runtime.h>
+
+#include "hbl.h"
+#include "hbl_device.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+hbl_status hip_fail(hipError_t e) {
+    g_last_hip_error = (int32_t)e;
+    return HBL_ERR_HIP;
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+bool dtype_ok(int32_t d) { return d == HBL_F32 || d == HBL_BF16; }
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+constexpr int64_t kMaxGemmM = int64_t(1) << 23;
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+
+hbl_status check_weight_shape(int64_t N, int64_t K) {
+    if (N < 1 || K < 16) return HBL_ERR_SHAPE;
+    if (K % 16) return HBL_ERR_ALIGN;
+    if (N > (int64_t(1) << 40) / K) return HBL_ERR_SHAPE;
+    return HBL_OK;
+}
+
+hbl_status check_config(const hbl_config* cfg) {
+    if (!cfg) return HBL_ERR_NULL;
+    if (cfg->act_bits != 8 && cfg->act_bits != 4) return HBL_ERR_BITS;
+    if (cfg->hadamard != 0 && cfg->hadamard != 1) return HBL_ERR_BITS;
+    if (cfg->norm != HBL_NORM_RMS && cfg->norm != HBL_NORM_LN && cfg->norm != HBL_NORM_NONE) return HBL_ERR_BITS;
+    if (cfg->act_bits == 4 && cfg->a4_mode != HBL_A4_ABSMEAN_SQRT7 && cfg->a4_mode != HBL_A4_ABSMAX_7)
+        return HBL_ERR_BITS;
+    if (!(cfg->norm_eps >= 0.f) || !(cfg->quant_eps >= 0.f)) return HBL_ERR_SHAPE;
+    return HBL_OK;
+}
+
+hbl_status check_act_shape(int64_t M, int64_t K) {
+    if (M < 0 || M > kMaxRows) return HBL_ERR_SHAPE;
+    if (K < HBL_MIN_K || K > HBL_MAX_K) return HBL_ERR_SHAPE;
+    if (!is_pow2(K)) return HBL_ERR_NOT_POW2;
+    return HBL_OK;
+}
+
+hbl_status check_gemm_shape(int64_t M, int64_t K, int64_t N) {
+    if (M < 0 || M > kMaxGemmM) return HBL_ERR_SHAPE;
+    if (K < 64 || K > HBL_MAX_K) return HBL_ERR_SHAPE;
+    if (K % 64) return HBL_ERR_ALIGN;
+    if (N < 16 || N > kMaxRows) return HBL_ERR_SHAPE;
+    if (N % 16) return HBL_ERR_ALIGN;
+    return HBL_OK;
+}
+
+size_t codes_bytes(int64_t M, int64_t K, int32_t bits) { return (size_t)M * (size_t)K * (size_t)bits / 8; }
+
+}  // namespace
+
+extern "C" {
+
+const char* hbl_status_string(hbl_status s) {
+    switch (s) {
+        case HBL_OK: return "ok";
+        case HBL_ERR_NULL: return "a required pointer is NULL";
+        case HBL_ERR_SHAPE: return "a size is out of range";
+        case HBL_ERR_NOT_POW2: return "K must be a power of two";
+        case HBL_ERR_ALIGN: return "misaligned size or pointer (K, N multiples of 16; pointers 16-byte aligned)";
+        case HBL_ERR_DTYPE: return "unknown dtype";
+        case HBL_ERR_BITS: return "unsupported act_bits, a4_mode, norm or hadamard flag";
+        case HBL_ERR_WORKSPACE: return "workspace too small";
+        case HBL_ERR_UNSUPPORTED: return "request not supported by this build";
+        case HBL_ERR_HIP: return "HIP error (see hbl_last_hip_error)";
+    }
+    return "unknown status";
+}
+
+int32_t hbl_last_hip_error(void) { return g_last_hip_error; }
+
+hbl_status hbl_packed_weight_bytes(int64_t N, int64_t K, size_t* bytes) {
+    if (!bytes) return HBL_ERR_NULL;
+    hbl_status st = check_weight_shape(N, K);
+    if (st != HBL_OK) return st;
+    *bytes = (size_t)N * (size_t)(K / 4);
+    return HBL_OK;
+}
+
+hbl_status hbl_weight_workspace_bytes(int64_t N, int64_t K, size_t* bytes) {
+    if (!bytes) return HBL_ERR_NULL;
+    hbl_status st = check_weight_shape(N, K);
+    if (st != HBL_OK) return st;
+    *bytes = (size_t)hbl::weight_partial_count(N * K) * sizeof(double);
+    return HBL_OK;
+}
+
+hbl_status hbl_quantize_weights(const void* W, int32_t w_dtype, int64_t N, int64_t K, float eps, uint8_t* W_packed,
+                                float* alpha, void* ws, size_t ws_bytes, void* stream) {
+    if (!W || !W_packed || !alpha || !ws) return HBL_ERR_NULL;
+    if (!dtype_ok(w_dtype)) return HBL_ERR_DTYPE;
+    hbl_status st = check_weight_shape(N, K);
+    if (st != HBL_OK) return st;
+    if (!(eps >= 0.f)) return HBL_ERR_SHAPE;
+    if (!aligned16(W) || !aligned16(W_packed) || !aligned(alpha, 4) || !aligned(ws, 8)) return HBL_ERR_ALIGN;
+    const int n_partial = hbl::weight_partial_count(N * K);
+    if (ws_bytes < (size_t)n_partial * sizeof(double)) return HBL_ERR_WORKSPACE;
+    hipError_t e = hbl::launch_weight_quant(W, w_dtype, N, K, eps, W_packed, alpha, (double*)ws, n_partial,
+                                            (hipStream_t)stream);
+    return e == hipSuccess ? HBL_OK : hip_fail(e);
+}
+
+hbl_status hbl_workspace_bytes(int64_t M, int64_t K, const hbl_config* cfg, size_t* bytes) {
+    if (!bytes) return HBL_ERR_NULL;
+    hbl_status st = check_config(cfg);
+    if (st != HBL_OK) return st;
+    if (M < 0 || M > kMaxRows || K < 1 || K > HBL_MAX_K) return HBL_ERR_SHAPE;
+    *bytes = round_up(codes_bytes(M, K, cfg->act_bits), 256) + round_up((size_t)M * sizeof(float), 256);
+    return HBL_OK;
+}
+
+hbl_status hbl_quantize_activations(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
+                                    const hbl_config* cfg, void* codes, float* xscale, float* z_debug,
+                                    float* s_debug, void* stream) {
+    hbl_status st = check_config(cfg);
+    if (st != HBL_OK) return st;
+    if (!dtype_ok(x_dtype)) return HBL_ERR_DTYPE;
+    st = check_act_shape(M, K);
+    if (st != HBL_OK) return st;
+    if (M == 0) return HBL_OK;
+    if (!X || !codes || !xscale) return HBL_ERR_NULL;
+    if (!aligned16(X) || !aligned16(codes) || !aligned(xscale, 4) || !aligned16(z_debug) || !aligned(s_debug, 4) ||
+        !aligned(gain, 4))
+        return HBL_ERR_ALIGN;
+    hipError_t e = hbl::launch_act_quant(X, x_dtype, M, K, gain, *cfg, codes, xscale, z_debug, s_debug,
+                                         (hipStream_t)stream);
+    return e == hipSuccess ? HBL_OK : hip_fail(e);
+}
+
+hbl_status hbl_gemm(const void* codes, const float* xscale, int32_t act_bits, int64_t M, int64_t K,
+                    const uint8_t* W_packed, const float* alpha, int64_t N, void* Y, int32_t y_dtype, void* stream) {
+    if (act_bits != 8 && act_bits != 4) return HBL_ERR_BITS;
+    if (!dtype_ok(y_dtype)) return HBL_ERR_DTYPE;
+    hbl_status st = check_gemm_shape(M, K, N);
+    if (st != HBL_OK) return st;
+    if (M == 0) return HBL_OK;
+    if (!codes || !xscale || !W_packed || !alpha || !Y) return HBL_ERR_NULL;
+    if (!aligned16(codes) || !aligned(xscale, 4) || !aligned16(W_packed) || !aligned(alpha, 4) || !aligned16(Y))
+        return HBL_ERR_ALIGN;
+    hipError_t e = hbl::launch_gemm(codes, xscale, act_bits, M, K, W_packed, alpha, N, Y, y_dtype,
+                                    (hipStream_t)stream);
+    return e == hipSuccess ? HBL_OK : hip_fail(e);
+}
+
+hbl_status hbl_forward(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
+                       const uint8_t* W_packed, const float* alpha, int64_t N, const hbl_config* cfg, void* Y,
+                       int32_t y_dtype, void* ws, size_t ws_bytes, void* stream) {
+    hbl_status st = check_config(cfg);
+    if (st != HBL_OK) return st;
+    if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return HBL_ERR_DTYPE;
+    st = check_act_shape(M, K);
+    if (st != HBL_OK) return st;
+    st = check_gemm_shape(M, K, N);
+    if (st != HBL_OK) return st;
+    if (M == 0) return HBL_OK;
+    if (!X || !W_packed || !alpha || !Y || !ws) return HBL_ERR_NULL;
+    if (!aligned16(X) || !aligned16(W_packed) || !aligned(alpha, 4) || !aligned16(Y) || !aligned16(ws) ||
+        !aligned(gain, 4))
+        return HBL_ERR_ALIGN;
+    const size_t cb = round_up(codes_bytes(M, K, cfg->act_bits), 256);
+    const size_t need = cb + round_up((size_t)M * sizeof(float), 256);
+    if (ws_bytes < need) return HBL_ERR_WORKSPACE;
+    void* codes = ws;
+    float* xscale = (float*)((uint8_t*)ws + cb);
+    hipError_t e = hbl::launch_act_quant(X, x_dtype, M, K, gain, *cfg, codes, xscale, nullptr, nullptr,
+                                         (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    e = hbl::launch_gemm(codes, xscale, cfg->act_bits, M, K, W_packed, alpha, N, Y, y_dtype, (hipStream_t)stream);
+    return e == hipSuccess ? HBL_OK : hip_fail(e);
+}
+
+}  // extern "C"

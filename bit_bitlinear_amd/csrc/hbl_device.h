@@ -1,0 +1,102 @@
+// hbl_device.h -- device-side helpers shared by the gfx950 kernels of libhbl.
+// Internal header: not part of the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hbl.h"
+
+#define HBL_DEVINL __device__ __forceinline__
+
+namespace hbl {
+
+constexpr int kWave = 64;
+
+// fp32 nearest to sqrt(7): bit pattern 0x402953FD (2.64575124f).
+HBL_DEVINL float sqrt7_f32() { return __uint_as_float(0x402953FDu); }
+
+HBL_DEVINL float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+HBL_DEVINL float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+HBL_DEVINL uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---- wave / block reductions (fixed butterfly order: deterministic) ----
+HBL_DEVINL float wave_sum_f32(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+HBL_DEVINL float wave_max_f32(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+HBL_DEVINL double wave_sum_f64(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// Block-wide reductions for NT threads (NT a multiple of 64).  `scratch` must
+// hold NT/64 values of the reduced type; the result is returned to every
+// thread.  Two barriers.
+template <int NT>
+HBL_DEVINL float block_sum_f32(float v, float* scratch) {
+    v = wave_sum_f32(v);
+    if constexpr (NT == kWave) return v;
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+    __syncthreads();
+    float r = 0.f;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; i++) r += scratch[i];
+    __syncthreads();
+    return r;
+}
+template <int NT>
+HBL_DEVINL float block_max_f32(float v, float* scratch) {
+    v = wave_max_f32(v);
+    if constexpr (NT == kWave) return v;
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+    __syncthreads();
+    float r = 0.f;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; i++) r = fmaxf(r, scratch[i]);
+    __syncthreads();
+    return r;
+}
+template <int NT>
+HBL_DEVINL double block_sum_f64(double v, double* scratch) {
+    v = wave_sum_f64(v);
+    if constexpr (NT == kWave) return v;
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+    __syncthreads();
+    double r = 0.0;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; i++) r += scratch[i];
+    __syncthreads();
+    return r;
+}
+
+}  // namespace hbl
+
+// ---- launchers implemented in the kernel translation units ----
+namespace hbl {
+hipError_t launch_weight_quant(const void* W, int w_dtype, int64_t N, int64_t K, float eps, uint8_t* W_packed,
+                               float* alpha, double* partial, int n_partial, hipStream_t s);
+int weight_partial_count(int64_t count);
+
+hipError_t launch_act_quant(const void* X, int x_dtype, int64_t M, int64_t K, const float* gain,
+                            const hbl_config& cfg, void* codes, float* xscale, float* z_debug, float* s_debug,
+                            hipStream_t s);
+
+hipError_t launch_gemm(const void* codes, const float* xscale, int act_bits, int64_t M, int64_t K,
+                       const uint8_t* W_packed, const float* alpha, int64_t N, void* Y, int y_dtype,
+                       hipStream_t s);
+}  // namespace hbl

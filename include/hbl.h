@@ -1,0 +1,171 @@
+/*
+ * hbl.h -- C ABI of libhbl.so, the H-BitLinear forward pass (BitNet v2) on
+ * AMD MI355X (gfx950).
+ *
+ * The layer replaces a standard linear layer y[M][N] = x[M][K] W[N][K]^T
+ * (no bias).  Each token row of x is normalised, rotated by an online
+ * Hadamard transform, quantised per token to INT8 or INT4, and multiplied
+ * against per-tensor absmean-ternarised weights with integer accumulation,
+ * then rescaled to float.  Pages followed (their display equations were lost
+ * in extraction; the readings are stated per call):
+ *   - "新智元: 微软 BitNet v2" repost, section "H-BitLinear模块": the online
+ *     Hadamard before activation quantisation, computed by a fast O(n log n)
+ *     transform; the per-tensor absmean ternary weight quantiser; the
+ *     separate 8-bit and 4-bit activation strategies; the layer formula with
+ *     a normalisation LN(.) in front.
+ *   - same page, section "BitNet v2：原生4位激活": RMSNorm, no bias, H-BitLinear
+ *     only at the attention output Wo and the FFN down projection Wdown; plain
+ *     BitLinear (no Hadamard) elsewhere.
+ *   - CSDN blog "[论文品鉴] 1-bit LLM", section "量化函数": the threshold form of
+ *     the ternariser (inclusive zero band).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers, owned by the caller, row-major
+ *     and contiguous.  The library never allocates, frees or synchronises.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is queued on it and the call returns before the GPU finishes.
+ *   - Every argument is validated on the host before anything is queued; an
+ *     invalid argument returns an error code and queues nothing.  No call
+ *     aborts or throws.  HBL_ERR_HIP reports a failed launch; the HIP error
+ *     code is then available from hbl_last_hip_error() on the same thread.
+ *   - Calls on one stream are ordered; calls that share output or workspace
+ *     buffers on different streams race.
+ *   - NaN or Inf inputs are outside the contract.
+ */
+#ifndef HBL_H
+#define HBL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HBL_OK = 0,
+    HBL_ERR_NULL = 1,        /* a required pointer is NULL */
+    HBL_ERR_SHAPE = 2,       /* a size is out of range (M < 0, N or K <= 0, too large) */
+    HBL_ERR_NOT_POW2 = 3,    /* hadamard = 1 needs K a power of two */
+    HBL_ERR_ALIGN = 4,       /* K % 16 or N % 16 != 0, or a pointer not 16-byte aligned */
+    HBL_ERR_DTYPE = 5,       /* unknown hbl_dtype */
+    HBL_ERR_BITS = 6,        /* act_bits not 4 or 8, or unknown a4_mode / norm */
+    HBL_ERR_WORKSPACE = 7,   /* workspace smaller than the *_workspace_bytes query */
+    HBL_ERR_UNSUPPORTED = 8, /* valid request this build does not implement */
+    HBL_ERR_HIP = 9          /* a HIP call failed; see hbl_last_hip_error() */
+} hbl_status;
+
+typedef enum { HBL_F32 = 0, HBL_BF16 = 1 } hbl_dtype;
+
+typedef enum { HBL_NORM_RMS = 0, HBL_NORM_LN = 1, HBL_NORM_NONE = 2 } hbl_norm;
+
+/* INT4 per-token scale.  The pages announce two different strategies for
+ * 8-bit and 4-bit activations but the formulas were lost; the default reads
+ * the 4-bit one as absmean with sqrt(7) (beta = mean|z|, codes =
+ * clip(rint(z*sqrt7/(beta+eps)), -8, 7), dequant beta/sqrt7), with absmax/7 as
+ * the alternative.  sqrt7 is the fp32 constant 0x402953FD. */
+typedef enum { HBL_A4_ABSMEAN_SQRT7 = 0, HBL_A4_ABSMAX_7 = 1 } hbl_a4_mode;
+
+typedef struct {
+    int32_t act_bits;  /* 8: INT8 absmax codes [M][K] int8; 4: INT4 codes packed [M][K/2] */
+    int32_t hadamard;  /* 1: H-BitLinear (online Hadamard), 0: plain BitLinear */
+    int32_t norm;      /* hbl_norm; applied before the Hadamard */
+    int32_t a4_mode;   /* hbl_a4_mode; ignored when act_bits == 8 */
+    float norm_eps;    /* added to the mean square (variance) inside the sqrt */
+    float quant_eps;   /* added to the per-token statistic in the quantiser divisor */
+} hbl_config;
+
+/* Limits of this build. */
+#define HBL_MAX_K 32768
+#define HBL_MIN_K 256
+
+/*
+ * Weight format (library definition; the pages give none for 2-bit storage).
+ *   W_packed: uint8 [N][K/4].  Each ternary value is 2-bit two's complement
+ *   (0 -> 00, +1 -> 01, -1 -> 11; 10 never written).  K is cut into aligned
+ *   groups of 16; group g of row n owns bytes 4g..4g+3 of that row, and
+ *   element k sits in byte 4*(k/16) + k%4 at bits 2*((k%16)/4)..+1.
+ *   alpha: one fp32 in device memory, the per-tensor absmean mean|W|.
+ * INT8 activation codes: int8 [M][K].  INT4 codes: uint8 [M][K/2], low nibble
+ * = even k, high nibble = odd k, 4-bit two's complement.  xscale: fp32 [M],
+ * the per-token dequantisation factor (gamma/127, beta/sqrt7 or gamma/7).
+ */
+
+/* Bytes of W_packed for an N x K weight (N*K/4).  Errors: NULL, SHAPE, ALIGN. */
+hbl_status hbl_packed_weight_bytes(int64_t N, int64_t K, size_t* bytes);
+
+/* Device workspace needed by hbl_quantize_weights (partial sums). */
+hbl_status hbl_weight_workspace_bytes(int64_t N, int64_t K, size_t* bytes);
+
+/*
+ * Per-tensor absmean ternarisation and packing of latent weights W [N][K]
+ * (fp32 or bf16):  alpha = mean|W| over all N*K entries (fp64 sum, rounded
+ * to fp32);  W_q = clip(rint(W / (alpha + eps)), -1, 1) with round half to
+ * even, so the zero band |W| <= (alpha+eps)/2 is inclusive;  dequant factor
+ * is alpha.  Writes W_packed (hbl_packed_weight_bytes) and alpha (1 float,
+ * device).  ws must hold hbl_weight_workspace_bytes.  An all-zero W gives
+ * alpha = 0 and all-zero codes.  Constraints: N >= 1, K >= 16, K % 16 == 0,
+ * N*K < 2^40.
+ */
+hbl_status hbl_quantize_weights(const void* W, int32_t w_dtype, int64_t N, int64_t K, float eps,
+                                uint8_t* W_packed, float* alpha, void* ws, size_t ws_bytes, void* stream);
+
+/* Device workspace needed by hbl_forward (activation codes + per-token scale). */
+hbl_status hbl_workspace_bytes(int64_t M, int64_t K, const hbl_config* cfg, size_t* bytes);
+
+/*
+ * Activation half of the layer, per token row m of X [M][K] (fp32 or bf16):
+ *   r = norm(x) * gain   (RMS: x/sqrt(mean x^2 + norm_eps); LN: (x-mean)/
+ *                          sqrt(var + norm_eps); NONE: x; gain NULL = 1)
+ *   z = H_K r             when cfg->hadamard (normalised Sylvester Hadamard,
+ *                          natural order, H[i][j] = (-1)^popcount(i&j)/sqrt(K),
+ *                          computed by an in-register/LDS fast transform)
+ *   s, d from z           INT8: gamma = max|z|, s = 127/(gamma+eps), d = gamma/127
+ *                          INT4: see hbl_a4_mode.  A zero statistic gives s = d = 0.
+ *   q = clip(rint(z*s))   INT8 [-128,127] -> codes int8 [M][K]
+ *                          INT4 [-8,7]     -> codes uint8 [M][K/2] (packed)
+ *   xscale[m] = d
+ * z_debug (nullable): fp32 [M][K] copy of z; s_debug (nullable): fp32 [M]
+ * quantiser multiplier s.  Both exist for parity checks.
+ * gain (nullable): fp32 [K].
+ * Constraints: K a power of two in [256, 32768] (both modes); 0 <= M < 2^31
+ * (M == 0 queues nothing); X, codes and z_debug 16-byte aligned.
+ */
+hbl_status hbl_quantize_activations(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
+                                    const hbl_config* cfg, void* codes, float* xscale, float* z_debug,
+                                    float* s_debug, void* stream);
+
+/*
+ * Integer half of the layer: acc[m][n] = sum_k q[m][k] * W_q[n][k] in int32
+ * (exact: |acc| <= 128*K < 2^31), then Y[m][n] = fp32(fp32(acc * xscale[m]) *
+ * alpha), stored as fp32 or bf16 (round to nearest even).  With xscale = 1 and
+ * alpha = 1 the fp32 output equals acc exactly (|acc| < 2^24).  INT8 x ternary
+ * products run on the gfx950 i8 matrix cores (MFMA).  Constraints: K in
+ * [64, 32768], K % 64 == 0; N >= 16, N % 16 == 0; 0 <= M <= 2^23 (M == 0
+ * queues nothing); codes, W_packed and Y 16-byte aligned.
+ */
+hbl_status hbl_gemm(const void* codes, const float* xscale, int32_t act_bits, int64_t M, int64_t K,
+                    const uint8_t* W_packed, const float* alpha, int64_t N, void* Y, int32_t y_dtype,
+                    void* stream);
+
+/*
+ * The whole H-BitLinear (or plain BitLinear) forward: hbl_quantize_activations
+ * into the workspace, then hbl_gemm.  Y [M][N] fp32 or bf16.  ws (16-byte
+ * aligned) must hold hbl_workspace_bytes(M, K, cfg): the codes followed by
+ * xscale.  Constraints: those of both stages.
+ */
+hbl_status hbl_forward(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
+                       const uint8_t* W_packed, const float* alpha, int64_t N, const hbl_config* cfg,
+                       void* Y, int32_t y_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* hbl_status_string(hbl_status status);
+
+/* The hipError_t of the last HBL_ERR_HIP returned on this thread (0 if none). */
+int32_t hbl_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HBL_H */

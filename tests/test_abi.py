@@ -1,0 +1,112 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/hbl.h declares, and rejects invalid arguments on the host before
+anything is queued (these calls need no GPU)."""
+import ctypes
+
+import pytest
+
+import bit_bitlinear_amd as hbl
+
+# Fake, never-dereferenced device addresses (validation must reject first).
+A16 = ctypes.c_void_p(0x10000)
+A16b = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10004)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return hbl.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = hbl.declared_symbols()
+    assert len(names) == 9
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(hbl.HblLibraryError):
+        hbl.load_library(str(tmp_path / "libhbl.so"))
+
+
+def test_status_strings(lib):
+    for s in range(10):
+        assert hbl.hbl_status_string(s)
+    assert hbl.hbl_status_string(12345) == "unknown status"
+    assert hbl.hbl_last_hip_error() == 0
+
+
+def test_size_queries():
+    assert hbl.hbl_packed_weight_bytes(256, 256) == 256 * 64
+    assert hbl.hbl_packed_weight_bytes(4096, 16384) == 4096 * 4096
+    assert hbl.hbl_weight_workspace_bytes(2048, 2048) >= 8
+    ws8 = hbl.hbl_workspace_bytes(4096, 2048, hbl.Config(act_bits=8))
+    ws4 = hbl.hbl_workspace_bytes(4096, 2048, hbl.Config(act_bits=4))
+    assert ws8 >= 4096 * 2048 + 4096 * 4 and ws4 >= 4096 * 1024 + 4096 * 4 and ws4 < ws8
+    assert hbl.hbl_workspace_bytes(0, 2048, hbl.Config()) == 0
+    with pytest.raises(hbl.HblError) as e:
+        hbl.hbl_packed_weight_bytes(16, 40)
+    assert e.value.status == 4
+    with pytest.raises(hbl.HblError):
+        hbl.hbl_workspace_bytes(8, 256, hbl.Config(act_bits=5))
+
+
+def _act(lib, X=A16, dt=0, M=8, K=256, gain=None, cfg=None, codes=A16b, xs=A16b, z=None, s=None):
+    c = (cfg or hbl.Config()).c()
+    return lib.hbl_quantize_activations(X, dt, M, K, gain, ctypes.byref(c), codes, xs, z, s, None)
+
+
+def test_quantize_activations_validation(lib):
+    assert _act(lib, K=300) == 3                                   # not a power of two
+    assert _act(lib, K=128) == 2 and _act(lib, K=65536) == 2       # outside [256, 32768]
+    assert _act(lib, M=-1) == 2
+    assert _act(lib, dt=7) == 5
+    assert _act(lib, cfg=hbl.Config(act_bits=5)) == 6
+    assert _act(lib, cfg=hbl.Config(act_bits=4, a4_mode=9)) == 6
+    assert _act(lib, cfg=hbl.Config(norm=7)) == 6
+    assert _act(lib, cfg=hbl.Config(norm_eps=-1.0)) == 2
+    assert _act(lib, X=None) == 1 and _act(lib, codes=None) == 1 and _act(lib, xs=None) == 1
+    assert _act(lib, X=MIS) == 4 and _act(lib, z=MIS) == 4
+    assert _act(lib, M=0, X=None) == 0                              # empty input: nothing queued
+    c = hbl.Config().c()
+    assert lib.hbl_quantize_activations(A16, 0, 8, 256, None, None, A16b, A16b, None, None, None) == 1
+    del c
+
+
+def _gemm(lib, codes=A16, xs=A16, bits=8, M=128, K=1024, W=A16b, alpha=A16b, N=256, Y=A16b, ydt=0):
+    return lib.hbl_gemm(codes, xs, bits, M, K, W, alpha, N, Y, ydt, None)
+
+
+def test_gemm_validation(lib):
+    assert _gemm(lib, bits=2) == 6
+    assert _gemm(lib, ydt=3) == 5
+    assert _gemm(lib, K=1000) == 4 and _gemm(lib, N=100) == 4
+    assert _gemm(lib, K=32) == 2 and _gemm(lib, K=65536) == 2 and _gemm(lib, N=0) == 2 and _gemm(lib, M=-3) == 2
+    assert _gemm(lib, M=(1 << 23) + 1) == 2
+    assert _gemm(lib, codes=None) == 1 and _gemm(lib, alpha=None) == 1 and _gemm(lib, Y=None) == 1
+    assert _gemm(lib, Y=MIS) == 4 and _gemm(lib, W=MIS) == 4
+    assert _gemm(lib, M=0, codes=None) == 0
+
+
+def test_quantize_weights_validation(lib):
+    q = lib.hbl_quantize_weights
+    assert q(A16, 0, 64, 40, 1e-5, A16b, A16b, A16b, 1 << 20, None) == 4          # K % 16
+    assert q(A16, 0, 0, 64, 1e-5, A16b, A16b, A16b, 1 << 20, None) == 2           # N = 0
+    assert q(A16, 2, 64, 64, 1e-5, A16b, A16b, A16b, 1 << 20, None) == 5          # dtype
+    assert q(None, 0, 64, 64, 1e-5, A16b, A16b, A16b, 1 << 20, None) == 1
+    assert q(A16, 0, 64, 64, -1.0, A16b, A16b, A16b, 1 << 20, None) == 2          # negative eps
+    assert q(MIS, 0, 64, 64, 1e-5, A16b, A16b, A16b, 1 << 20, None) == 4
+    assert q(A16, 0, 64, 64, 1e-5, A16b, A16b, A16b, 0, None) == 7                # workspace
+
+
+def test_forward_validation(lib):
+    cfg = hbl.Config(act_bits=8).c()
+    f = lib.hbl_forward
+    need = hbl.hbl_workspace_bytes(64, 1024, hbl.Config(act_bits=8))
+    assert f(A16, 0, 64, 1024, None, A16b, A16b, 256, ctypes.byref(cfg), A16b, 0, A16b, need - 1, None) == 7
+    assert f(A16, 0, 64, 1000, None, A16b, A16b, 256, ctypes.byref(cfg), A16b, 0, A16b, need, None) == 3
+    assert f(A16, 0, 64, 1024, None, A16b, A16b, 250, ctypes.byref(cfg), A16b, 0, A16b, need, None) == 4
+    assert f(A16, 0, 64, 1024, None, None, A16b, 256, ctypes.byref(cfg), A16b, 0, A16b, need, None) == 1
+    assert f(A16, 0, 64, 1024, None, A16b, A16b, 256, None, A16b, 0, A16b, need, None) == 1
+    assert f(A16, 0, 0, 1024, None, A16b, A16b, 256, ctypes.byref(cfg), A16b, 0, A16b, 0, None) == 0

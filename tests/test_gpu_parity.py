@@ -1,0 +1,274 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Small cases compare every element; the full-size layer workloads compare a
+sample of 64 rows (first, last, evenly spaced) that the oracle can compute,
+in the same launch configuration the benchmark times (hbl_quantize_weights,
+then hbl_forward).  Tolerances: see tests/parity.py.
+"""
+import numpy as np
+import pytest
+
+import bit_bitlinear_amd as hbl
+import oracle
+import workloads
+from parity import (check_codes_end_to_end, check_codes_given_inputs, check_y, check_z, to_dev, to_host,
+                    unpack_codes, y_to_f32)
+
+pytestmark = pytest.mark.gpu
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _announce(msg):
+    print("[case] " + msg, flush=True)
+
+
+# ================================================================= weights ==
+@pytest.mark.parametrize("N,K,dt", [(256, 256, "f32"), (48, 80, "f32"), (2048, 2048, "f32"), (96, 4096, "bf16"),
+                                    (4096, 16384, "bf16")])
+def test_quantize_weights_parity(N, K, dt):
+    _announce("weights N=%d K=%d %s" % (N, K, dt))
+    rng = np.random.default_rng(N * 7 + K)
+    W = workloads.w_latent(rng, N, K)
+    if dt == "bf16":
+        W = workloads.f32_to_bf16_bits(W)
+    Wp, alpha = hbl.hbl_quantize_weights(to_dev(W), eps=1e-5)
+    _sync()
+    Wp, a_gpu = to_host(Wp), to_host(alpha)[0]
+    a_ref = oracle.weight_alpha(W)
+    assert abs(float(a_gpu) - float(a_ref)) <= 1e-6 * float(a_ref)
+    # bit-exact packing given the GPU's alpha
+    Wq = oracle.ternarize(W, a_gpu, 1e-5)
+    assert np.array_equal(Wp, oracle.pack_ternary(Wq))
+
+
+def test_quantize_weights_hand_cases(golden):
+    g = golden("ternary_hand.txt")
+    for key in ("tie", "mean", "eps"):
+        W = np.tile(np.array(g[key + "_latent"], np.float32), 4)[None, :]      # mean|W| unchanged by tiling
+        Wp, alpha = hbl.hbl_quantize_weights(to_dev(W), eps=g[key + "_eps"])
+        _sync()
+        q = oracle.unpack_ternary(to_host(Wp), 16)[0]
+        assert q.tolist() == g[key + "_ternary"] * 4, key
+    gp = golden("pack_ternary_k16.txt")
+    W = np.array([gp["ternary"]], np.float32) * np.float32(0.75)   # alpha = 0.75*mean|t|; |W|/alpha >= 1.45 or 0
+    Wp, _ = hbl.hbl_quantize_weights(to_dev(W), eps=0.0)
+    _sync()
+    assert to_host(Wp)[0].tolist() == gp["bytes"]
+    Wz = np.zeros((16, 64), np.float32)
+    Wp, alpha = hbl.hbl_quantize_weights(to_dev(Wz), eps=0.0)
+    _sync()
+    assert to_host(alpha)[0] == 0.0 and not to_host(Wp).any()
+
+
+# ============================================================= activations ==
+ACT_CASES = [
+    # (K, x_dtype, bits, hadamard, norm, a4_mode, gain, M)
+    (256, "f32", 8, True, hbl.HBL_NORM_RMS, 0, False, 8),
+    (256, "bf16", 4, True, hbl.HBL_NORM_RMS, 0, False, 37),
+    (512, "f32", 4, True, hbl.HBL_NORM_LN, 1, True, 5),
+    (1024, "bf16", 8, False, hbl.HBL_NORM_RMS, 0, True, 9),
+    (2048, "bf16", 8, True, hbl.HBL_NORM_RMS, 0, False, 33),
+    (2048, "f32", 4, True, hbl.HBL_NORM_NONE, 0, False, 7),
+    (4096, "bf16", 4, False, hbl.HBL_NORM_RMS, 0, False, 11),
+    (8192, "f32", 4, True, hbl.HBL_NORM_RMS, 0, False, 16),
+    (16384, "bf16", 4, True, hbl.HBL_NORM_RMS, 0, False, 6),
+    (16384, "bf16", 8, True, hbl.HBL_NORM_LN, 0, True, 3),
+    (32768, "f32", 8, True, hbl.HBL_NORM_RMS, 0, False, 2),
+    (32768, "bf16", 4, True, hbl.HBL_NORM_RMS, 1, False, 2),
+]
+
+
+@pytest.mark.parametrize("K,dt,bits,had,norm,a4,use_gain,M", ACT_CASES)
+def test_quantize_activations_parity(K, dt, bits, had, norm, a4, use_gain, M):
+    _announce("act K=%d %s a%d H=%d norm=%d a4=%d gain=%d M=%d" % (K, dt, bits, had, norm, a4, use_gain, M))
+    rng = np.random.default_rng(K + bits + M)
+    X, _ = workloads.x_outlier_gaussian(rng, M, K, 4, 30.0)
+    if M > 2:
+        X[1] = 0.0                                   # an all-zero row
+    gain = (rng.standard_normal(K).astype(np.float32) * 0.5 + 1.0) if use_gain else None
+    Xh = workloads.f32_to_bf16_bits(X) if dt == "bf16" else X
+    cfg = hbl.Config(act_bits=bits, hadamard=had, norm=norm, a4_mode=a4)
+    codes, xs, z, s = hbl.hbl_quantize_activations(to_dev(Xh), cfg, gain=None if gain is None else to_dev(gain),
+                                                   z_debug=True, s_debug=True)
+    _sync()
+    q_gpu = unpack_codes(to_host(codes), K, bits)
+    z_gpu, d_gpu, s_gpu = to_host(z), to_host(xs), to_host(s)
+    ref = oracle.quantize_activations(Xh, bits=bits, hadamard=had, gain=gain, norm=norm, a4_mode=a4)
+    check_z(z_gpu, ref["z"], "z")
+    check_codes_given_inputs(z_gpu, s_gpu, d_gpu, q_gpu, bits, a4, 1e-5, "codes")
+    n_boundary = check_codes_end_to_end(q_gpu, ref["z"], ref["s"], ref["q"], "end-to-end codes")
+    assert n_boundary <= max(2, q_gpu.size // 10000)
+    if M > 2:
+        assert not q_gpu[1].any() and d_gpu[1] == 0.0
+
+
+def test_quantize_activations_deterministic():
+    rng = np.random.default_rng(5)
+    X, _ = workloads.x_laplace_mixture(rng, 64, 4096)
+    Xd = to_dev(workloads.f32_to_bf16_bits(X))
+    outs = []
+    for _ in range(2):
+        c, xs, z, _ = hbl.hbl_quantize_activations(Xd, hbl.Config(act_bits=4), z_debug=True)
+        _sync()
+        outs.append((to_host(c), to_host(xs), to_host(z)))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+
+
+# ===================================================================== GEMM ==
+def _random_codes(rng, M, K, bits):
+    q = rng.integers(-128 if bits == 8 else -8, 128 if bits == 8 else 8, size=(M, K)).astype(np.int8)
+    packed = q if bits == 8 else oracle.pack_int4(q)
+    return q, packed
+
+
+GEMM_CASES = [
+    # (M, K, N, bits) -- prefill tiles are 128 x 128, decode (M <= 64) tiles 16 columns
+    (300, 2048, 272, 8), (300, 2048, 272, 4), (129, 256, 16, 8), (128, 1024, 128, 4), (257, 64, 400, 8),
+    (1, 8192, 4096, 4), (7, 8192, 512, 8), (16, 4096, 1024, 4), (17, 2048, 256, 4), (33, 1024, 64, 8),
+    (64, 8192, 1024, 4), (65, 512, 192, 4),
+]
+
+
+@pytest.mark.parametrize("M,K,N,bits", GEMM_CASES)
+def test_gemm_int32_accumulators_exact(M, K, N, bits):
+    """xscale = 1 and alpha = 1 make the fp32 output the int32 accumulator itself."""
+    _announce("gemm M=%d K=%d N=%d a%d" % (M, K, N, bits))
+    import torch
+    rng = np.random.default_rng(M * 131 + K + N + bits)
+    q, packed = _random_codes(rng, M, K, bits)
+    Wq = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    Wp = oracle.pack_ternary(Wq)
+    ones = torch.ones(M, dtype=torch.float32, device="cuda:0")
+    one = torch.ones(1, dtype=torch.float32, device="cuda:0")
+    Y = hbl.hbl_gemm(to_dev(packed), ones, bits, K, to_dev(Wp), one, N)
+    _sync()
+    acc = oracle.int_gemm(q, Wq)
+    assert np.array_equal(to_host(Y), acc.astype(np.float32))
+
+
+@pytest.mark.parametrize("M,bits,ydt", [(200, 8, "f32"), (200, 4, "bf16"), (5, 4, "f32"), (40, 8, "bf16")])
+def test_gemm_rescale_epilogue_exact(M, bits, ydt):
+    import torch
+    K, N = 1024, 256
+    rng = np.random.default_rng(M + bits)
+    q, packed = _random_codes(rng, M, K, bits)
+    Wq = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    d = (rng.random(M).astype(np.float32) * np.float32(0.01)).astype(np.float32)
+    alpha = np.array([0.0173], np.float32)
+    Y = hbl.hbl_gemm(to_dev(packed), to_dev(d), bits, K, to_dev(oracle.pack_ternary(Wq)), to_dev(alpha), N,
+                     y_dtype=torch.float32 if ydt == "f32" else torch.bfloat16)
+    _sync()
+    y_ref = oracle.rescale(oracle.int_gemm(q, Wq), d, alpha[0])
+    if ydt == "f32":
+        assert np.array_equal(to_host(Y), y_ref)
+    else:
+        assert np.array_equal(to_host(Y), oracle.f32_to_bf16(y_ref))
+
+
+# ================================================================= forward ==
+def _run_layer(layer, rows, seed=0):
+    """Quantise weights and run hbl_forward on the full layer (as the bench
+    does), plus the stage entry points for z/s; return host arrays for `rows`."""
+    import torch
+    X, W, _ = workloads.make_inputs(layer, seed)
+    Xd, Wd = to_dev(X), to_dev(W)
+    cfg = hbl.Config(act_bits=layer.act_bits, hadamard=layer.hadamard)
+    Wp, alpha = hbl.hbl_quantize_weights(Wd, eps=1e-5)
+    ydt = torch.float32 if layer.y_dtype == "f32" else torch.bfloat16
+    Y = hbl.hbl_forward(Xd, Wp, alpha, layer.N, cfg, y_dtype=ydt)
+    codes, xs, z, s = hbl.hbl_quantize_activations(Xd, cfg, z_debug=True, s_debug=True)
+    ridx = torch.from_numpy(rows).to("cuda:0")
+    out = {
+        "Y": to_host(Y.index_select(0, ridx)),
+        "codes": to_host(codes.index_select(0, ridx)),
+        "xs": to_host(xs.index_select(0, ridx)),
+        "z": to_host(z.index_select(0, ridx)),
+        "s": to_host(s.index_select(0, ridx)),
+        "Wp": to_host(Wp),
+        "alpha": to_host(alpha)[0],
+    }
+    # the stage entry points and hbl_forward must agree bit for bit
+    Y2 = hbl.hbl_gemm(codes, xs, layer.act_bits, layer.K, Wp, alpha, layer.N, y_dtype=ydt)
+    _sync()
+    assert np.array_equal(to_host(Y2.index_select(0, ridx)), out["Y"])
+    del Xd, Wd, Y, Y2, codes, z
+    torch.cuda.empty_cache()
+    Xs = X[rows]
+    return Xs, W, out
+
+
+def _check_layer(layer, rows):
+    _announce("layer %s rows=%d" % (layer.desc, len(rows)))
+    Xs, W, g = _run_layer(layer, rows)
+    K, bits = layer.K, layer.act_bits
+    a_ref = oracle.weight_alpha(W)
+    assert abs(float(g["alpha"]) - float(a_ref)) <= 1e-6 * float(a_ref)
+    Wq = oracle.ternarize(W, g["alpha"], 1e-5)
+    assert np.array_equal(g["Wp"], oracle.pack_ternary(Wq))
+    ref = oracle.quantize_activations(Xs, bits=bits, hadamard=layer.hadamard)
+    q_gpu = unpack_codes(g["codes"], K, bits)
+    check_z(g["z"], ref["z"], layer.name + " z")
+    check_codes_given_inputs(g["z"], g["s"], g["xs"], q_gpu, bits, 0, 1e-5, layer.name + " codes")
+    nb = check_codes_end_to_end(q_gpu, ref["z"], ref["s"], ref["q"], layer.name + " end-to-end codes")
+    # int32 accumulators: the oracle's GEMM on the GPU's own codes and weights, then the
+    # oracle's rescale with the GPU's own scales reproduces the fp32 output exactly
+    acc = oracle.int_gemm(q_gpu, Wq)
+    y_exact = oracle.rescale(acc, g["xs"], g["alpha"])
+    if layer.y_dtype == "f32":
+        assert np.array_equal(g["Y"], y_exact)
+    else:
+        assert np.array_equal(g["Y"], oracle.f32_to_bf16(y_exact))
+    # end to end against the oracle's own pipeline.  Rows where a code flipped at a
+    # rounding boundary (allowed above) are compared with the oracle's arithmetic on
+    # those codes; every other row with the oracle's own codes.
+    flipped = np.any(q_gpu != ref["q"], axis=1)
+    q_cmp = np.where(flipped[:, None], q_gpu, ref["q"])
+    y_ref = oracle.rescale(oracle.int_gemm(q_cmp, Wq), ref["d"], a_ref)
+    check_y(y_to_f32(g["Y"]), y_ref, layer.name + " y", bf16_out=layer.y_dtype == "bf16")
+    print("[parity] %s: %d boundary code flips in %d of %d rows" % (layer.name, nb, int(flipped.sum()), len(rows)))
+    return nb
+
+
+def test_forward_small_layer_all_rows():
+    layer = workloads.SMALL
+    _check_layer(layer, np.arange(layer.M))
+
+
+def test_forward_wo_1p3b_sampled():
+    layer = workloads.WO_1P3B
+    _check_layer(layer, workloads.sample_rows(layer.M))
+
+
+def test_forward_wdown_7b_sampled():
+    layer = workloads.WDOWN_7B
+    _check_layer(layer, workloads.sample_rows(layer.M, 48))
+
+
+@pytest.mark.parametrize("layer", workloads.DECODE, ids=lambda l: l.name)
+def test_forward_decode_all_rows(layer):
+    _check_layer(layer, np.arange(layer.M))
+
+
+@pytest.mark.parametrize("layer", workloads.CHAIN_3B, ids=lambda l: l.name)
+def test_forward_chain_3b_sampled(layer):
+    _check_layer(layer, workloads.sample_rows(layer.M, 32))
+
+
+def test_forward_deterministic_and_empty():
+    import torch
+    layer = workloads.WO_1P3B
+    X, W, _ = workloads.make_inputs(layer, 3, M=300)
+    Xd = to_dev(X)
+    Wp, alpha = hbl.hbl_quantize_weights(to_dev(W))
+    cfg = hbl.Config(act_bits=8)
+    y1 = to_host(hbl.hbl_forward(Xd, Wp, alpha, layer.N, cfg))
+    y2 = to_host(hbl.hbl_forward(Xd, Wp, alpha, layer.N, cfg))
+    assert np.array_equal(y1, y2)
+    Y0 = hbl.hbl_forward(Xd[:0], Wp, alpha, layer.N, cfg)
+    _sync()
+    assert Y0.shape == (0, layer.N)
