@@ -1,0 +1,239 @@
+"""Benchmark of the H-BitLinear forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layer NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+per-tensor absmean ternarisation of the latent weights (hbl_quantize_weights)
+and the layer forward (hbl_forward: norm + Hadamard + per-token quantisation,
+then the integer GEMM with the rescale epilogue).  The default layer is the
+attention output projection Wo of a 1.3B-like model: 4096 tokens, K = N = 2048,
+bf16 activations, INT8 codes, bf16 output.  Inputs are seeded synthetic arrays
+already resident in HBM; the timed steps rotate over enough distinct buffer
+sets (> 512 MiB) that the 256 MB last-level cache cannot hold them.
+
+Prints one JSON line.  Besides the throughput it reports, for the kernel that
+takes the most time per step, the algorithmic work per launch divided by its
+average launch time (HIP events on the launch stream) against the MI355X peak,
+and the CPU oracle timed on a bounded row sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_I8_TOPS = 5000.0          # MI355X dense INT8 MFMA, TOP/s
+ROTATE_BYTES = 576 << 20       # > 2 x 256 MB last-level cache
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=40)
+    p.add_argument("--layer", default="wo_1.3b")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--kernel-iters", type=int, default=200)
+    return p.parse_args()
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (the H-BitLinear forward is measured on one "
+              "MI355X's share); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_bitlinear_amd as hbl
+    import workloads
+
+    layer = workloads.by_name(args.layer)
+    M, K, N, bits = layer.M, layer.K, layer.N, layer.act_bits
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hbl.load_library()
+
+    # ---------------------------------------------------------------- inputs
+    X, W, _ = workloads.make_inputs(layer, seed=0)
+    if layer.x_dtype == "bf16":
+        Xd = torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        Xd = torch.from_numpy(X).to(dev)
+    Wd = torch.from_numpy(W).to(dev)
+    ydt = torch.bfloat16 if layer.y_dtype == "bf16" else torch.float32
+    cfg = hbl.Config(act_bits=bits, hadamard=layer.hadamard)
+    ws_bytes = hbl.hbl_workspace_bytes(M, K, cfg)
+    wws_bytes = hbl.hbl_weight_workspace_bytes(N, K)
+    y_bytes = M * N * (2 if ydt == torch.bfloat16 else 4)
+    set_bytes = Xd.numel() * Xd.element_size() + Wd.numel() * 4 + N * K // 4 + ws_bytes + y_bytes
+    R = max(2, -(-ROTATE_BYTES // set_bytes))
+    sets = []
+    for r in range(R):
+        s = {
+            "X": Xd if r == 0 else Xd.clone(),
+            "W": Wd if r == 0 else Wd.clone(),
+            "Wp": torch.empty((N, K // 4), dtype=torch.uint8, device=dev),
+            "alpha": torch.empty(1, dtype=torch.float32, device=dev),
+            "wws": torch.empty(wws_bytes, dtype=torch.uint8, device=dev),
+            "ws": torch.empty(ws_bytes, dtype=torch.uint8, device=dev),
+            "Y": torch.empty((M, N), dtype=ydt, device=dev),
+            "codes": torch.empty((M, K if bits == 8 else K // 2), dtype=torch.int8 if bits == 8 else torch.uint8,
+                                 device=dev),
+            "xs": torch.empty(M, dtype=torch.float32, device=dev),
+        }
+        sets.append(s)
+    torch.cuda.synchronize()
+
+    def step(s):
+        hbl.hbl_quantize_weights(s["W"], 1e-5, W_packed=s["Wp"], alpha=s["alpha"], ws=s["wws"])
+        hbl.hbl_forward(s["X"], s["Wp"], s["alpha"], N, cfg, Y=s["Y"], ws=s["ws"])
+
+    # ---------------------------------------------------------------- steps
+    for i in range(args.warmup):
+        step(sets[i % R])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % R])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    tokens_per_s = M * args.steps / wall
+
+    # ------------------------------------------------------ per-kernel timing
+    stream = torch.cuda.current_stream()
+
+    def time_launches(fn, iters):
+        for i in range(min(10, iters)):
+            fn(sets[i % R])
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(iters):
+            fn(sets[i % R])
+        ev1.record(stream)
+        ev1.synchronize()
+        return ev0.elapsed_time(ev1) / iters * 1e3   # microseconds per launch
+
+    it = args.kernel_iters
+    t_wq = time_launches(lambda s: hbl.hbl_quantize_weights(s["W"], 1e-5, W_packed=s["Wp"], alpha=s["alpha"],
+                                                            ws=s["wws"]), it)
+    t_act = time_launches(lambda s: hbl.hbl_quantize_activations(s["X"], cfg, codes=s["codes"], xscale=s["xs"]), it)
+    t_gemm = time_launches(lambda s: hbl.hbl_gemm(s["codes"], s["xs"], bits, K, s["Wp"], s["alpha"], N, Y=s["Y"]), it)
+
+    x_bytes = M * K * (2 if layer.x_dtype == "bf16" else 4)
+    code_bytes = M * K * bits // 8
+    kernels = {
+        "weight_ternarise": {"us": t_wq, "bound": "hbm", "unit": "GB/s",
+                             "work": N * K * 4 + N * K // 4 + 4,
+                             "work_desc": "read latent W once (fp32) + write 2-bit W + alpha"},
+        "norm_fwht_quant": {"us": t_act, "bound": "hbm", "unit": "GB/s",
+                            "work": x_bytes + code_bytes + 4 * M,
+                            "work_desc": "read X + write codes + write xscale"},
+        "gemm_i8_mfma" if M > 64 else "gemv_decode": {
+            "us": t_gemm, "bound": "mfma" if M > 64 else "hbm", "unit": "TFLOP/s" if M > 64 else "GB/s",
+            "work": 2 * M * N * K if M > 64 else code_bytes + 4 * M + N * K // 4 + M * N * 2,
+            "work_desc": "2*M*N*K integer ops" if M > 64 else "read codes + xscale + 2-bit W, write Y"},
+    }
+    for k, v in kernels.items():
+        per_s = v["work"] / (v["us"] * 1e-6)
+        v["achieved"] = per_s / 1e12 if v["unit"] == "TFLOP/s" else per_s / 1e9
+        v["peak"] = PEAK_I8_TOPS if v["unit"] == "TFLOP/s" else PEAK_HBM_GBS
+        v["frac"] = v["achieved"] / v["peak"]
+    dom_name = max(kernels, key=lambda k: kernels[k]["us"])
+    dom = kernels[dom_name]
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (dom_name, layer.name))
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            t = json.load(f)
+        if t.get("source_hash") == source_hash(t.get("sources", [])):
+            traffic = t.get("bytes_per_launch")
+
+    roofline = {"kernel": dom_name, "bound": dom["bound"], "achieved": round(dom["achieved"], 2),
+                "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4), "traffic": traffic,
+                "work_per_launch": dom["work"], "work_desc": dom["work_desc"], "us_per_launch": round(dom["us"], 3)}
+
+    # ----------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(layer, X, W)
+
+    out = {
+        "metric": "H-BitLinear tokens/s + TOPS (a4/a8 x ternary W) and % of HBM/MFMA roofline",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic (seeded; outlier-channel activations, N(0,0.02) latent weights)",
+        "config": {"workload": layer.desc, "M": M, "K": K, "N": N, "act_bits": bits,
+                   "hadamard": layer.hadamard, "x_dtype": layer.x_dtype, "y_dtype": layer.y_dtype,
+                   "step": "hbl_quantize_weights + hbl_forward", "rotating_sets": R},
+        "tops": round(2.0 * M * N * K * args.steps / wall / 1e12, 2),
+        "forward_us": round(t_act + t_gemm, 3),
+        "forward_only_tokens_per_s": round(M / ((t_act + t_gemm) * 1e-6), 1),
+        "roofline": roofline,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(layer, X, W):
+    """The oracle as it stands, timed on the host cores on a bounded sample of
+    the same workload: weight quantisation of the full W once, then the
+    forward of the first S rows; tokens/s scales the row time to all M rows."""
+    import numpy as np
+
+    import oracle
+
+    Xs = X
+    t0 = time.perf_counter()
+    Wq, _, alpha = oracle.quantize_weights(W)
+    t_wq = time.perf_counter() - t0
+    # calibrate on 16 rows, then size the sample for about 2 s of wall time
+    t0 = time.perf_counter()
+    oracle.forward(Xs[:16], Wq, alpha, bits=layer.act_bits, hadamard=layer.hadamard)
+    per_row = (time.perf_counter() - t0) / 16
+    S = int(min(layer.M, max(64, round(2.0 / max(per_row, 1e-6)))))
+    S = max(16, S - S % 16)
+    t0 = time.perf_counter()
+    oracle.forward(Xs[:S], Wq, alpha, bits=layer.act_bits, hadamard=layer.hadamard)
+    t_rows = time.perf_counter() - t0
+    t_step = t_wq + t_rows * layer.M / S
+    cores = oracle.num_threads()
+    return {"value": round(layer.M / t_step, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "full weight ternarisation once (%.3f s) + forward of the first %d of %d rows (%.3f s), "
+                      "scaled to all rows; %d OpenMP threads" % (t_wq, S, layer.M, t_rows, cores),
+            "cpu_seconds": round((t_wq + t_rows) * cores, 1)}
+
+
+if __name__ == "__main__":
+    main()
