@@ -51,8 +51,8 @@ hbl_status check_act_shape(int64_t M, int64_t K) {
 
 hbl_status check_gemm_shape(int64_t M, int64_t K, int64_t N) {
     if (M < 0 || M > kMaxGemmM) return HBL_ERR_SHAPE;
-    if (K < 64 || K > HBL_MAX_K) return HBL_ERR_SHAPE;
-    if (K % 64) return HBL_ERR_ALIGN;
+    if (K < 128 || K > HBL_MAX_K) return HBL_ERR_SHAPE;
+    if (K % 128) return HBL_ERR_ALIGN;
     if (N < 16 || N > kMaxRows) return HBL_ERR_SHAPE;
     if (N % 16) return HBL_ERR_ALIGN;
     return HBL_OK;

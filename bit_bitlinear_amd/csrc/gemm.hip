@@ -48,6 +48,20 @@ HBL_DEVINL v4i unpack_a4(uint32_t x0, uint32_t x1) {
     return r;
 }
 
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): loads whose offset falls
+// outside return zeros, so tile edges need no branches (branch-free loads
+// also let the compiler keep several loads in flight with exact vmcnt waits).
+HBL_DEVINL __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int64_t lim = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)lim, 0x00020000);
+}
+HBL_DEVINL uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 template <int BITS>
 struct Shift {
     static constexpr int value = BITS == 8 ? 6 : 10;
@@ -60,75 +74,111 @@ HBL_DEVINL void store_y<float>(float* p, float v) { *p = v; }
 template <>
 HBL_DEVINL void store_y<uint16_t>(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16_bits(v); }
 
+// Buffer stores: an offset outside the resource is dropped by the hardware.
+template <typename YT>
+HBL_DEVINL void buf_store_y(__amdgpu_buffer_rsrc_t r, uint32_t off, float v);
+template <>
+HBL_DEVINL void buf_store_y<float>(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, 0);
+}
+template <>
+HBL_DEVINL void buf_store_y<uint16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_bits(v), r, (int)off, 0, 0);
+}
+constexpr uint32_t kDropOffset = 0x80000000u;  // beyond every resource: store dropped
+
 HBL_DEVINL float rescale(int acc, float d, float alpha) {
     const float t = (float)acc * d;  // two separately rounded fp32 products
     return t * alpha;
 }
 
 // ============================================================ prefill GEMM ==
-// Block tile 128 x 128, K step 64, 4 waves in a 2 x 2 grid, each wave 64 x 64
-// = 2 x 2 MFMA 32x32x32 tiles.  Packed A and W tiles are staged in LDS (double
-// buffered) and unpacked in registers right before the MFMA.
-constexpr int kBM = 128, kBN = 128, kBK = 64, kGemmThreads = 256;
+// Block tile 128 x 128, K step 128, 4 waves in a 2 x 2 grid, each wave 64 x 64
+// = 2 x 2 MFMA 32x32x32 tiles (acc in 64 AGPR/VGPRs).  Packed A and W tiles go
+// global -> registers -> LDS (double buffered); three register buffers keep
+// the global loads two K steps ahead of their use, so L2 latency hides behind
+// the MFMA work of the two steps in between.  Operands are unpacked in
+// registers right before the MFMA.
+//
+// Tile order: blocks are dealt to the 8 XCDs round robin (block b -> XCD b%8);
+// the kernel maps block b to tile (b%8)*T8 + b/8, so every XCD works on a
+// contiguous band of M tiles and its L2 holds that band of A plus all of W.
+constexpr int kBM = 128, kBN = 128, kBK = 128, kGemmThreads = 256, kPF = 3;
 
 template <int BITS>
 struct ATile {
     static constexpr int row_bytes = BITS == 8 ? kBK : kBK / 2;  // bytes of one row per K step
-    static constexpr int stride = row_bytes + 16;                // padded LDS row
+    static constexpr int stride = row_bytes + 16;                // padded LDS row (9 or 5 x 16 B)
     static constexpr int chunks = kBM * row_bytes / 16;          // 16-byte chunks per tile
+    static constexpr int per_thread = chunks / kGemmThreads;
+    static constexpr int cpr = row_bytes / 16;                   // chunks per row
 };
-constexpr int kBStride = 20;  // 16 bytes of packed W per row and K step, padded to 5 dwords
+constexpr int kBRow = kBK / 4;        // 32 bytes of packed W per row and K step
+constexpr int kBStride = kBRow + 4;   // 9 dwords: conflict-free 4-byte fragment reads
+constexpr int kBPerThread = kBN * kBRow / 16 / kGemmThreads;  // 16-byte chunks per thread (1)
+
+template <int BITS>
+struct Regs {
+    uint4 a[ATile<BITS>::per_thread];
+    uint4 b[kBPerThread];
+};
 
 template <int BITS, typename YT>
-__global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(const uint8_t* __restrict__ A,
-                                                                 const float* __restrict__ xscale, int64_t M,
-                                                                 int64_t K, const uint8_t* __restrict__ Wp,
-                                                                 const float* __restrict__ alpha_p, int64_t N,
-                                                                 YT* __restrict__ Y) {
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_mfma_kernel(const uint8_t* __restrict__ A,
+                                                                    const float* __restrict__ xscale, int64_t M,
+                                                                    int64_t K, const uint8_t* __restrict__ Wp,
+                                                                    const float* __restrict__ alpha_p, int64_t N,
+                                                                    YT* __restrict__ Y, int tiles_n, int tiles_total) {
     using AT = ATile<BITS>;
     __shared__ __attribute__((aligned(16))) uint8_t As[2][kBM * AT::stride];
     __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kBN * kBStride];
+    __shared__ float xs_tile[kBM];  // per-token scales of this tile's rows (0 past M)
+
+    // XCD-aware tile order (see above); falls back to linear order when the
+    // tile count is not a multiple of 8.
+    const int b = blockIdx.x;
+    const int tile = (tiles_total % 8 == 0) ? (b % 8) * (tiles_total / 8) + b / 8 : b;
+    const int64_t m0 = (int64_t)(tile / tiles_n) * kBM;
+    const int64_t n0 = (int64_t)(tile % tiles_n) * kBN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * kBM;
-    const int64_t n0 = (int64_t)blockIdx.x * kBN;
     const int64_t a_ld = K * BITS / 8;  // bytes per activation row
     const int64_t w_ld = K / 4;         // bytes per weight row
     const int KT = (int)(K / kBK);
 
-    constexpr int A_PER_THREAD = (AT::chunks + kGemmThreads - 1) / kGemmThreads;
-    constexpr int A_CPR = AT::row_bytes / 16;  // chunks per row
-    uint4 a_reg[A_PER_THREAD];
-    uint4 b_reg;
-
-    auto load_tile = [&](int kt) {
+    // rows past M (columns past N) lie outside these resources and load as zeros
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A + m0 * a_ld, (M - m0) * a_ld);
+    const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(Wp + n0 * w_ld, (N - n0) * w_ld);
+    auto load_tile = [&](Regs<BITS>& r, int kt) {
 #pragma unroll
-        for (int r = 0; r < A_PER_THREAD; r++) {
-            const int q = tid + r * kGemmThreads;
-            const int row = q / A_CPR, c16 = q % A_CPR;
-            const int64_t m = m0 + row;
-            a_reg[r] = m < M ? *reinterpret_cast<const uint4*>(A + m * a_ld + (int64_t)kt * AT::row_bytes + c16 * 16)
-                             : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < AT::per_thread; i++) {
+            const int q = tid + i * kGemmThreads;
+            const int row = q / AT::cpr, c16 = q % AT::cpr;
+            r.a[i] = buf_load16(a_rsrc, (uint32_t)(row * a_ld + kt * AT::row_bytes + c16 * 16));
         }
-        if (tid < kBN) {
-            const int64_t n = n0 + tid;
-            b_reg = n < N ? *reinterpret_cast<const uint4*>(Wp + n * w_ld + (int64_t)kt * (kBK / 4))
-                          : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kBPerThread; i++) {
+            const int q = tid + i * kGemmThreads;
+            const int row = q / (kBRow / 16), c16 = q % (kBRow / 16);
+            r.b[i] = buf_load16(w_rsrc, (uint32_t)(row * w_ld + kt * kBRow + c16 * 16));
         }
     };
-    auto store_tile = [&](int st) {
+    auto store_tile = [&](const Regs<BITS>& r, int st) {
 #pragma unroll
-        for (int r = 0; r < A_PER_THREAD; r++) {
-            const int q = tid + r * kGemmThreads;
-            const int row = q / A_CPR, c16 = q % A_CPR;
-            *reinterpret_cast<uint4*>(&As[st][row * AT::stride + c16 * 16]) = a_reg[r];
+        for (int i = 0; i < AT::per_thread; i++) {
+            const int q = tid + i * kGemmThreads;
+            const int row = q / AT::cpr, c16 = q % AT::cpr;
+            *reinterpret_cast<uint4*>(&As[st][row * AT::stride + c16 * 16]) = r.a[i];
         }
-        if (tid < kBN) {
-            uint32_t* d = reinterpret_cast<uint32_t*>(&Bs[st][tid * kBStride]);
-            d[0] = b_reg.x; d[1] = b_reg.y; d[2] = b_reg.z; d[3] = b_reg.w;
+#pragma unroll
+        for (int i = 0; i < kBPerThread; i++) {
+            const int q = tid + i * kGemmThreads;
+            const int row = q / (kBRow / 16), c16 = q % (kBRow / 16);
+            uint32_t* d = reinterpret_cast<uint32_t*>(&Bs[st][row * kBStride + c16 * 16]);
+            d[0] = r.b[i].x; d[1] = r.b[i].y; d[2] = r.b[i].z; d[3] = r.b[i].w;
         }
     };
 
@@ -140,59 +190,103 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_mfma_kernel(const uint8_t* 
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0;
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
     const int lr = lane & 31;  // row (A) / column (W) inside a 32-wide MFMA tile
     const int lg = lane >> 5;  // which 16-k half of the 32-k MFMA step
-    for (int kt = 0; kt < KT; kt++) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) load_tile(kt + 1);
+    // Fragments of one 32-k step: two A operands (rows) and two W operands (columns).
+    struct Frag {
+        v4i a[2];
+        uint32_t w[2];
+    };
+    auto read_frag = [&](Frag& f, int st, int s) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int row = wm * 64 + i * 32 + lr;
+            if constexpr (BITS == 8) {
+                const uint4 q = *reinterpret_cast<const uint4*>(&As[st][row * AT::stride + s * 32 + lg * 16]);
+                f.a[i][0] = (int)q.x; f.a[i][1] = (int)q.y; f.a[i][2] = (int)q.z; f.a[i][3] = (int)q.w;
+            } else {
+                const uint2 q = *reinterpret_cast<const uint2*>(&As[st][row * AT::stride + s * 16 + lg * 8]);
+                f.a[i][0] = (int)q.x; f.a[i][1] = (int)q.y;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int col = wn * 64 + j * 32 + lr;
+            f.w[j] = *reinterpret_cast<const uint32_t*>(&Bs[st][col * kBStride + s * 8 + lg * 4]);
+        }
+    };
+    // Software pipeline over the 32-k steps of a stage: the LDS reads of step
+    // s+1 are issued before the MFMAs of step s, so their latency hides under
+    // the four MFMAs (4 x 32 cycles) instead of stalling the next step.
+    auto compute = [&](int st) {
+        Frag f[2];
+        read_frag(f[0], st, 0);
 #pragma unroll
         for (int s = 0; s < kBK / 32; s++) {
-            v4i a[2], b[2];
+            Frag& cur = f[s & 1];
+            if (s + 1 < kBK / 32) read_frag(f[(s + 1) & 1], st, s + 1);
+            v4i a[2], bw[2];
 #pragma unroll
             for (int i = 0; i < 2; i++) {
-                const int row = wm * 64 + i * 32 + lr;
-                if constexpr (BITS == 8) {
-                    const uint4 q = *reinterpret_cast<const uint4*>(&As[cur][row * AT::stride + s * 32 + lg * 16]);
-                    a[i][0] = (int)q.x; a[i][1] = (int)q.y; a[i][2] = (int)q.z; a[i][3] = (int)q.w;
-                } else {
-                    const uint2 q = *reinterpret_cast<const uint2*>(&As[cur][row * AT::stride + s * 16 + lg * 8]);
-                    a[i] = unpack_a4(q.x, q.y);
-                }
+                if constexpr (BITS == 8) a[i] = cur.a[i];
+                else a[i] = unpack_a4((uint32_t)cur.a[i][0], (uint32_t)cur.a[i][1]);
             }
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const int col = wn * 64 + j * 32 + lr;
-                const uint32_t y = *reinterpret_cast<const uint32_t*>(&Bs[cur][col * kBStride + s * 8 + lg * 4]);
-                b[j] = unpack_w(y);
-            }
+            for (int j = 0; j < 2; j++) bw[j] = unpack_w(cur.w[j]);
 #pragma unroll
             for (int i = 0; i < 2; i++)
 #pragma unroll
                 for (int j = 0; j < 2; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bw[j], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < KT) store_tile(cur ^ 1);
-        __syncthreads();
+    };
+
+    if (tid < kBM) {
+        const __amdgpu_buffer_rsrc_t xs_rsrc = make_rsrc(xscale + m0, (M - m0) * 4);
+        xs_tile[tid] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xs_rsrc, tid * 4, 0, 0));
     }
 
-    // ---- epilogue: lane holds column lr, rows 8*(r/4) + 4*lg + r%4 of each 32x32 tile
+    // prologue: tiles 0..kPF-1 in flight, tile 0 in LDS stage 0
+    Regs<BITS> R[kPF];
+#pragma unroll
+    for (int u = 0; u < kPF; u++) load_tile(R[u], min(u, KT - 1));
+    store_tile(R[0], 0);
+    __syncthreads();
+
+    // Loads and LDS stores are unconditional (past the last tile they re-load
+    // tile KT-1 and fill the idle LDS stage), so the compiler sees the same
+    // number of loads in flight on every path and waits only for the oldest.
+    for (int kt0 = 0; kt0 < KT; kt0 += kPF) {
+#pragma unroll
+        for (int u = 0; u < kPF; u++) {
+            const int kt = kt0 + u;
+            // R[(u+1)%kPF] holds tile kt+1; R[u] held tile kt (already in LDS)
+            store_tile(R[(u + 1) % kPF], (kt + 1) & 1);
+            load_tile(R[u], min(kt + kPF, KT - 1));
+            if (kt < KT) compute(kt & 1);
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue: lane holds column lr, rows 8*(r/4) + 4*lg + r%4 of each 32x32 tile.
+    // Y is written through a buffer resource over this tile's rows: rows past M
+    // fall outside it, columns past N get an out-of-range offset; both stores
+    // are dropped, so there are no per-element branches.
     const float alpha = *alpha_p;
+    const int rows_here = (int)min<int64_t>(kBM, M - m0);
+    const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(Y + m0 * N, (int64_t)rows_here * N * (int64_t)sizeof(YT));
 #pragma unroll
     for (int i = 0; i < 2; i++) {
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            const int64_t n = n0 + wn * 64 + j * 32 + lr;
+            const int nl = wn * 64 + j * 32 + lr;
+            const bool col_ok = n0 + nl < N;
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-                if (m < M && n < N) {
-                    const int v = acc[i][j][r] >> Shift<BITS>::value;
-                    store_y<YT>(Y + m * N + n, rescale(v, xscale[m], alpha));
-                }
+                const int ml = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+                const int v = acc[i][j][r] >> Shift<BITS>::value;
+                const uint32_t off = col_ok ? (uint32_t)((ml * N + n0 + nl) * (int64_t)sizeof(YT)) : kDropOffset;
+                buf_store_y<YT>(y_rsrc, off, rescale(v, xs_tile[ml], alpha));
             }
         }
     }
@@ -307,9 +401,11 @@ hipError_t launch_typed(const uint8_t* A, const float* xscale, int64_t M, int64_
                                alpha, N, Y);
         return hipGetLastError();
     }
-    const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
-    hipLaunchKernelGGL((gemm_mfma_kernel<BITS, YT>), grid, dim3(kGemmThreads), 0, s, A, xscale, M, K, Wp, alpha, N,
-                       Y);
+    if (K % kBK != 0) return hipErrorInvalidValue;  // the C ABI only admits K % 128 == 0 for M > 64
+    const int tiles_n = (int)((N + kBN - 1) / kBN);
+    const int tiles_total = tiles_n * (int)((M + kBM - 1) / kBM);
+    hipLaunchKernelGGL((gemm_mfma_kernel<BITS, YT>), dim3(tiles_total), dim3(kGemmThreads), 0, s, A, xscale, M, K, Wp,
+                       alpha, N, Y, tiles_n, tiles_total);
     return hipGetLastError();
 }
 

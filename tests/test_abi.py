@@ -82,7 +82,7 @@ def test_gemm_validation(lib):
     assert _gemm(lib, bits=2) == 6
     assert _gemm(lib, ydt=3) == 5
     assert _gemm(lib, K=1000) == 4 and _gemm(lib, N=100) == 4
-    assert _gemm(lib, K=32) == 2 and _gemm(lib, K=65536) == 2 and _gemm(lib, N=0) == 2 and _gemm(lib, M=-3) == 2
+    assert _gemm(lib, K=64) == 2 and _gemm(lib, K=192) == 4 and _gemm(lib, K=65536) == 2 and _gemm(lib, N=0) == 2 and _gemm(lib, M=-3) == 2
     assert _gemm(lib, M=(1 << 23) + 1) == 2
     assert _gemm(lib, codes=None) == 1 and _gemm(lib, alpha=None) == 1 and _gemm(lib, Y=None) == 1
     assert _gemm(lib, Y=MIS) == 4 and _gemm(lib, W=MIS) == 4

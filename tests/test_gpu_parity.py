@@ -128,9 +128,9 @@ def _random_codes(rng, M, K, bits):
 
 GEMM_CASES = [
     # (M, K, N, bits) -- prefill tiles are 128 x 128, decode (M <= 64) tiles 16 columns
-    (300, 2048, 272, 8), (300, 2048, 272, 4), (129, 256, 16, 8), (128, 1024, 128, 4), (257, 64, 400, 8),
+    (300, 2048, 272, 8), (300, 2048, 272, 4), (129, 256, 16, 8), (128, 1024, 128, 4), (257, 128, 400, 8), (1024, 4096, 1024, 8), (520, 16384, 384, 4),
     (1, 8192, 4096, 4), (7, 8192, 512, 8), (16, 4096, 1024, 4), (17, 2048, 256, 4), (33, 1024, 64, 8),
-    (64, 8192, 1024, 4), (65, 512, 192, 4),
+    (64, 8192, 1024, 4), (65, 512, 192, 4), (64, 128, 32, 8),
 ]
 
 
