@@ -293,12 +293,20 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_mfma_kernel(const uint8_
 }
 
 // ============================================================ decode GEMM ==
-// M <= 64 tokens.  The weights dominate the traffic, so the kernel streams W
-// once: one block per 16 output columns, its 4 waves split K (wave w takes the
-// 64-wide K steps w, w+4, ...), each K step is one MFMA 16x16x64 per 16-row
-// token tile.  The partial accumulators of the 4 waves are summed in LDS
-// (int32, exact) before the rescale.
-constexpr int kDecThreads = 256, kDecBN = 16, kDecUnroll = 4;
+// M <= 64 tokens: the packed weights (N*K/4 bytes) are the traffic, so the
+// kernel is written to stream them at HBM rate.  One block of 8 waves per 16
+// output columns; the waves split K.  A "super-step" covers 256 k: lane
+// (n = lane%16, g = lane/16) loads one 16-byte vector of weight row n = 64
+// trits k in [256*ss + 64*g, +64), so each instruction reads 16 rows x 64
+// contiguous bytes.  Every wave issues all its weight vectors first (up to 16,
+// 32 KiB per block in flight for K = 8192), then the activation codes in
+// batches of at most 32 16-byte vectors per lane (they come from L2: every
+// block reads the same codes).  MFMA 16x16x64 step d of a super-step takes,
+// for lane group g, the 16-k chunk 256*ss + 64*g + 16*d; the activation
+// operand uses the same chunk, so a lane's codes for one super-step are
+// contiguous (32 bytes INT4, 64 bytes INT8).  The waves' int32 partial sums
+// are added in LDS (exact) before the rescale.
+constexpr int kDecWaves = 8, kDecThreads = kDecWaves * 64, kDecBN = 16, kDecMaxSS = 16, kDecSB = 4;
 
 template <int BITS, int MT, typename YT>
 __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const uint8_t* __restrict__ A,
@@ -306,65 +314,75 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const uint8_t*
                                                                   int64_t K, const uint8_t* __restrict__ Wp,
                                                                   const float* __restrict__ alpha_p, int64_t N,
                                                                   YT* __restrict__ Y) {
-    __shared__ int red[4][MT][4][64];
+    constexpr int kAVec = (BITS == 8 ? 64 : 32) / 16;              // 16-byte A vectors per super-step and tile
+    constexpr int TG = (MT * kDecSB * kAVec <= 32) ? MT : 32 / (kDecSB * kAVec);  // token tiles per A batch
+    __shared__ int red[kDecWaves][MT][4][64];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int l16 = lane & 15;  // token row (A) / weight column (W) inside the tile
-    const int lg = lane >> 4;   // which 16-k quarter of the 64-k step
-    const int64_t n = (int64_t)blockIdx.x * kDecBN + l16;
+    const int l16 = lane & 15;  // weight column (W) / token row (A) inside the 16-wide tile
+    const int g = lane >> 4;    // lane group: 64-k quarter of each super-step
+    const int64_t n0 = (int64_t)blockIdx.x * kDecBN;
     const int64_t a_ld = K * BITS / 8;
     const int64_t w_ld = K / 4;
-    const int KS = (int)(K / 64);
+    const int SS = (int)(K / 256);  // super-steps in K
+    const int per_wave = (SS + kDecWaves - 1) / kDecWaves;
+    const int ss0 = wave * per_wave;
+    const int cnt = max(0, min(SS, ss0 + per_wave) - ss0);
+
+    const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(Wp + n0 * w_ld, (N - n0) * w_ld);
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A, M * a_ld);  // rows past M load as zeros
+    const uint32_t w_lane = (uint32_t)(l16 * w_ld + g * 16);
+
+    uint4 wv[kDecMaxSS];
+#pragma unroll
+    for (int u = 0; u < kDecMaxSS; u++)
+        if (u < cnt) wv[u] = buf_load16(w_rsrc, w_lane + (uint32_t)(ss0 + u) * 64);
 
     v4i acc[MT];
 #pragma unroll
     for (int t = 0; t < MT; t++) acc[t] = v4i{0, 0, 0, 0};
 
-    const uint8_t* wrow = Wp + n * w_ld + lg * 4;  // 16 trits = 4 bytes per lane per K step
-    int ks = wave;
-    for (; ks + 4 * (kDecUnroll - 1) < KS; ks += 4 * kDecUnroll) {
-        uint32_t wv[kDecUnroll];
 #pragma unroll
-        for (int u = 0; u < kDecUnroll; u++) wv[u] = *reinterpret_cast<const uint32_t*>(wrow + (ks + 4 * u) * 16);
+    for (int sb = 0; sb < kDecMaxSS; sb += kDecSB) {
+        if (sb < cnt) {
 #pragma unroll
-        for (int u = 0; u < kDecUnroll; u++) {
-            const v4i b = unpack_w(wv[u]);
-            const int64_t k0 = (int64_t)(ks + 4 * u) * 64 + lg * 16;
+            for (int tg = 0; tg < MT; tg += TG) {
+                uint4 aq[kDecSB][TG][kAVec];
 #pragma unroll
-            for (int t = 0; t < MT; t++) {
-                const int64_t m = t * 16 + l16;
-                v4i a = v4i{0, 0, 0, 0};
-                if (m < M) {
-                    if constexpr (BITS == 8) {
-                        const uint4 q = *reinterpret_cast<const uint4*>(A + m * a_ld + k0);
-                        a[0] = (int)q.x; a[1] = (int)q.y; a[2] = (int)q.z; a[3] = (int)q.w;
-                    } else {
-                        const uint2 q = *reinterpret_cast<const uint2*>(A + m * a_ld + k0 / 2);
-                        a = unpack_a4(q.x, q.y);
+                for (int u = 0; u < kDecSB; u++) {
+                    const uint32_t k_byte = (uint32_t)(ss0 + sb + u) * (256 * BITS / 8) + g * (kAVec * 16);
+#pragma unroll
+                    for (int t = 0; t < TG; t++) {
+                        const uint32_t a_lane = (uint32_t)(((tg + t) * 16 + l16) * a_ld) + k_byte;
+#pragma unroll
+                        for (int v = 0; v < kAVec; v++)
+                            aq[u][t][v] = (sb + u < cnt) ? buf_load16(a_rsrc, a_lane + v * 16) : make_uint4(0, 0, 0, 0);
                     }
                 }
-                acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[t], 0, 0, 0);
-            }
-        }
-    }
-    for (; ks < KS; ks += 4) {
-        const v4i b = unpack_w(*reinterpret_cast<const uint32_t*>(wrow + ks * 16));
-        const int64_t k0 = (int64_t)ks * 64 + lg * 16;
 #pragma unroll
-        for (int t = 0; t < MT; t++) {
-            const int64_t m = t * 16 + l16;
-            v4i a = v4i{0, 0, 0, 0};
-            if (m < M) {
-                if constexpr (BITS == 8) {
-                    const uint4 q = *reinterpret_cast<const uint4*>(A + m * a_ld + k0);
-                    a[0] = (int)q.x; a[1] = (int)q.y; a[2] = (int)q.z; a[3] = (int)q.w;
-                } else {
-                    const uint2 q = *reinterpret_cast<const uint2*>(A + m * a_ld + k0 / 2);
-                    a = unpack_a4(q.x, q.y);
+                for (int u = 0; u < kDecSB; u++) {
+                    if (sb + u < cnt) {
+                        const uint32_t wd[4] = {wv[sb + u].x, wv[sb + u].y, wv[sb + u].z, wv[sb + u].w};
+#pragma unroll
+                        for (int d = 0; d < 4; d++) {
+                            const v4i b = unpack_w(wd[d]);
+#pragma unroll
+                            for (int t = 0; t < TG; t++) {
+                                v4i a;
+                                if constexpr (BITS == 8) {
+                                    const uint4 q = aq[u][t][d];
+                                    a = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+                                } else {
+                                    const uint4 q = aq[u][t][d >> 1];
+                                    a = (d & 1) ? unpack_a4(q.z, q.w) : unpack_a4(q.x, q.y);
+                                }
+                                acc[tg + t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[tg + t], 0, 0, 0);
+                            }
+                        }
+                    }
                 }
             }
-            acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[t], 0, 0, 0);
         }
     }
 
@@ -373,13 +391,16 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const uint8_t*
 #pragma unroll
         for (int r = 0; r < 4; r++) red[wave][t][r][lane] = acc[t][r];
     __syncthreads();
-    // wave w finishes token tiles t = w, w+4, ... (output: column l16, rows 4*lg + r)
+    // wave w finishes token tiles t = w, w+8, ... (output: column l16, rows 4*g + r)
     const float alpha = *alpha_p;
-    for (int t = wave; t < MT; t += 4) {
+    const int64_t n = n0 + l16;
+    for (int t = wave; t < MT; t += kDecWaves) {
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-            const int sum = red[0][t][r][lane] + red[1][t][r][lane] + red[2][t][r][lane] + red[3][t][r][lane];
-            const int64_t m = t * 16 + 4 * lg + r;
+            int sum = 0;
+#pragma unroll
+            for (int w = 0; w < kDecWaves; w++) sum += red[w][t][r][lane];
+            const int64_t m = t * 16 + 4 * g + r;
             if (m < M && n < N) store_y<YT>(Y + m * N + n, rescale(sum >> Shift<BITS>::value, xscale[m], alpha));
         }
     }
@@ -388,7 +409,7 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const uint8_t*
 template <int BITS, typename YT>
 hipError_t launch_typed(const uint8_t* A, const float* xscale, int64_t M, int64_t K, const uint8_t* Wp,
                         const float* alpha, int64_t N, YT* Y, hipStream_t s) {
-    if (M <= 64) {
+    if (M <= 64 && K % 256 == 0 && K / 256 <= kDecWaves * kDecMaxSS) {
         const dim3 grid((unsigned)((N + kDecBN - 1) / kDecBN));
         if (M <= 16)
             hipLaunchKernelGGL((gemm_decode_kernel<BITS, 1, YT>), grid, dim3(kDecThreads), 0, s, A, xscale, M, K, Wp,
