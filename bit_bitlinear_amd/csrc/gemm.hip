@@ -93,53 +93,62 @@ HBL_DEVINL float rescale(int acc, float d, float alpha) {
 }
 
 // ============================================================ prefill GEMM ==
-// Block tile 128 x 128, K step 128, 4 waves in a 2 x 2 grid, each wave 64 x 64
-// = 2 x 2 MFMA 32x32x32 tiles (acc in 64 AGPR/VGPRs).  Packed A and W tiles go
-// global -> registers -> LDS (double buffered); three register buffers keep
-// the global loads two K steps ahead of their use, so L2 latency hides behind
-// the MFMA work of the two steps in between.  Operands are unpacked in
-// registers right before the MFMA.
+// Block tile (64*TA) x (64*TB), K step 128, 4 waves in a 2 x 2 grid, each wave
+// (32*TA) x (32*TB) = TA x TB MFMA 32x32x32 tiles.  LDS bandwidth is the
+// binding resource of this kernel (the i8 MFMA itself sustains 4.2 POP/s even
+// at one wave per SIMD with VALU work interleaved), and the fragment bytes a
+// wave reads from LDS per MFMA are A/TB + W/TA (1 KiB and 256 B per 32x32
+// fragment for INT8; 512 B and 256 B for INT4), so the default wave tile is
+// 2 x 4 for large problems (>= 512 such tiles); small ones use 2 x 2 so that
+// every CU still gets at least two blocks.  Both are built for two waves per
+// SIMD (<= 256 registers).  Packed A and W tiles go global -> registers ->
+// LDS (double buffered); kPF register buffers keep the global loads kPF-1 K
+// steps ahead of their use.  Operands are unpacked in registers right before
+// the MFMA.
 //
 // Tile order: blocks are dealt to the 8 XCDs round robin (block b -> XCD b%8);
 // the kernel maps block b to tile (b%8)*T8 + b/8, so every XCD works on a
 // contiguous band of M tiles and its L2 holds that band of A plus all of W.
-constexpr int kBM = 128, kBN = 128, kBK = 128, kGemmThreads = 256, kPF = 3;
+constexpr int kBK = 128, kGemmThreads = 256, kPF = 2;
 
-template <int BITS>
+template <int BITS, int BM>
 struct ATile {
     static constexpr int row_bytes = BITS == 8 ? kBK : kBK / 2;  // bytes of one row per K step
-    static constexpr int stride = row_bytes + 16;                // padded LDS row (9 or 5 x 16 B)
-    static constexpr int chunks = kBM * row_bytes / 16;          // 16-byte chunks per tile
+    // padded LDS row: 144 B (INT8: 8 consecutive rows of 16-byte reads hit
+    // disjoint banks) or 72 B (INT4: 16 consecutive rows of 8-byte reads do)
+    static constexpr int stride = BITS == 8 ? row_bytes + 16 : row_bytes + 8;
+    static constexpr int chunks = BM * row_bytes / 16;           // 16-byte chunks per tile
     static constexpr int per_thread = chunks / kGemmThreads;
     static constexpr int cpr = row_bytes / 16;                   // chunks per row
 };
 constexpr int kBRow = kBK / 4;        // 32 bytes of packed W per row and K step
 constexpr int kBStride = kBRow + 4;   // 9 dwords: conflict-free 4-byte fragment reads
-constexpr int kBPerThread = kBN * kBRow / 16 / kGemmThreads;  // 16-byte chunks per thread (1)
 
-template <int BITS>
+template <int BITS, int BM, int BN>
 struct Regs {
-    uint4 a[ATile<BITS>::per_thread];
-    uint4 b[kBPerThread];
+    uint4 a[ATile<BITS, BM>::per_thread];
+    uint4 b[BN * kBRow / 16 / kGemmThreads];
 };
 
-template <int BITS, typename YT>
+template <int BITS, typename YT, int TA, int TB>
 __global__ __launch_bounds__(kGemmThreads, 2) void gemm_mfma_kernel(const uint8_t* __restrict__ A,
                                                                     const float* __restrict__ xscale, int64_t M,
                                                                     int64_t K, const uint8_t* __restrict__ Wp,
                                                                     const float* __restrict__ alpha_p, int64_t N,
                                                                     YT* __restrict__ Y, int tiles_n, int tiles_total) {
-    using AT = ATile<BITS>;
-    __shared__ __attribute__((aligned(16))) uint8_t As[2][kBM * AT::stride];
-    __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kBN * kBStride];
-    __shared__ float xs_tile[kBM];  // per-token scales of this tile's rows (0 past M)
+    constexpr int BM = 64 * TA, BN = 64 * TB;
+    using AT = ATile<BITS, BM>;
+    constexpr int kBPerThread = BN * kBRow / 16 / kGemmThreads;
+    __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * AT::stride];
+    __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * kBStride];
+    __shared__ float xs_tile[BM];  // per-token scales of this tile's rows (0 past M)
 
     // XCD-aware tile order (see above); falls back to linear order when the
     // tile count is not a multiple of 8.
     const int b = blockIdx.x;
     const int tile = (tiles_total % 8 == 0) ? (b % 8) * (tiles_total / 8) + b / 8 : b;
-    const int64_t m0 = (int64_t)(tile / tiles_n) * kBM;
-    const int64_t n0 = (int64_t)(tile % tiles_n) * kBN;
+    const int64_t m0 = (int64_t)(tile / tiles_n) * BM;
+    const int64_t n0 = (int64_t)(tile % tiles_n) * BN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -152,7 +161,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_mfma_kernel(const uint8_
     // rows past M (columns past N) lie outside these resources and load as zeros
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A + m0 * a_ld, (M - m0) * a_ld);
     const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(Wp + n0 * w_ld, (N - n0) * w_ld);
-    auto load_tile = [&](Regs<BITS>& r, int kt) {
+    auto load_tile = [&](Regs<BITS, BM, BN>& r, int kt) {
 #pragma unroll
         for (int i = 0; i < AT::per_thread; i++) {
             const int q = tid + i * kGemmThreads;
@@ -166,12 +175,18 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_mfma_kernel(const uint8_
             r.b[i] = buf_load16(w_rsrc, (uint32_t)(row * w_ld + kt * kBRow + c16 * 16));
         }
     };
-    auto store_tile = [&](const Regs<BITS>& r, int st) {
+    auto store_tile = [&](const Regs<BITS, BM, BN>& r, int st) {
 #pragma unroll
         for (int i = 0; i < AT::per_thread; i++) {
             const int q = tid + i * kGemmThreads;
             const int row = q / AT::cpr, c16 = q % AT::cpr;
-            *reinterpret_cast<uint4*>(&As[st][row * AT::stride + c16 * 16]) = r.a[i];
+            uint8_t* dst = &As[st][row * AT::stride + c16 * 16];
+            if constexpr (AT::stride % 16 == 0) {
+                *reinterpret_cast<uint4*>(dst) = r.a[i];
+            } else {
+                reinterpret_cast<uint2*>(dst)[0] = make_uint2(r.a[i].x, r.a[i].y);
+                reinterpret_cast<uint2*>(dst)[1] = make_uint2(r.a[i].z, r.a[i].w);
+            }
         }
 #pragma unroll
         for (int i = 0; i < kBPerThread; i++) {
@@ -182,25 +197,25 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_mfma_kernel(const uint8_
         }
     };
 
-    v16i acc[2][2];
+    v16i acc[TA][TB];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < TA; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < TB; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0;
 
     const int lr = lane & 31;  // row (A) / column (W) inside a 32-wide MFMA tile
     const int lg = lane >> 5;  // which 16-k half of the 32-k MFMA step
-    // Fragments of one 32-k step: two A operands (rows) and two W operands (columns).
+    // Fragments of one 32-k step: TA A operands (rows) and TB W words (columns).
     struct Frag {
-        v4i a[2];
-        uint32_t w[2];
+        v4i a[TA];
+        uint32_t w[TB];
     };
     auto read_frag = [&](Frag& f, int st, int s) {
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const int row = wm * 64 + i * 32 + lr;
+        for (int i = 0; i < TA; i++) {
+            const int row = wm * 32 * TA + i * 32 + lr;
             if constexpr (BITS == 8) {
                 const uint4 q = *reinterpret_cast<const uint4*>(&As[st][row * AT::stride + s * 32 + lg * 16]);
                 f.a[i][0] = (int)q.x; f.a[i][1] = (int)q.y; f.a[i][2] = (int)q.z; f.a[i][3] = (int)q.w;
@@ -210,14 +225,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_mfma_kernel(const uint8_
             }
         }
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int col = wn * 64 + j * 32 + lr;
+        for (int j = 0; j < TB; j++) {
+            const int col = wn * 32 * TB + j * 32 + lr;
             f.w[j] = *reinterpret_cast<const uint32_t*>(&Bs[st][col * kBStride + s * 8 + lg * 4]);
         }
     };
     // Software pipeline over the 32-k steps of a stage: the LDS reads of step
-    // s+1 are issued before the MFMAs of step s, so their latency hides under
-    // the four MFMAs (4 x 32 cycles) instead of stalling the next step.
+    // s+1 are issued before the MFMAs of step s.
     auto compute = [&](int st) {
         Frag f[2];
         read_frag(f[0], st, 0);
@@ -225,29 +239,28 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_mfma_kernel(const uint8_
         for (int s = 0; s < kBK / 32; s++) {
             Frag& cur = f[s & 1];
             if (s + 1 < kBK / 32) read_frag(f[(s + 1) & 1], st, s + 1);
-            v4i a[2], bw[2];
+            v4i bw[TB];
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
-                if constexpr (BITS == 8) a[i] = cur.a[i];
-                else a[i] = unpack_a4((uint32_t)cur.a[i][0], (uint32_t)cur.a[i][1]);
+            for (int j = 0; j < TB; j++) bw[j] = unpack_w(cur.w[j]);
+#pragma unroll
+            for (int i = 0; i < TA; i++) {
+                v4i a;
+                if constexpr (BITS == 8) a = cur.a[i];
+                else a = unpack_a4((uint32_t)cur.a[i][0], (uint32_t)cur.a[i][1]);
+#pragma unroll
+                for (int j = 0; j < TB; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bw[j], acc[i][j], 0, 0, 0);
             }
-#pragma unroll
-            for (int j = 0; j < 2; j++) bw[j] = unpack_w(cur.w[j]);
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int j = 0; j < 2; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bw[j], acc[i][j], 0, 0, 0);
         }
     };
 
-    if (tid < kBM) {
+    for (int r = tid; r < BM; r += kGemmThreads) {
         const __amdgpu_buffer_rsrc_t xs_rsrc = make_rsrc(xscale + m0, (M - m0) * 4);
-        xs_tile[tid] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xs_rsrc, tid * 4, 0, 0));
+        xs_tile[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xs_rsrc, r * 4, 0, 0));
     }
 
     // prologue: tiles 0..kPF-1 in flight, tile 0 in LDS stage 0
-    Regs<BITS> R[kPF];
+    Regs<BITS, BM, BN> R[kPF];
 #pragma unroll
     for (int u = 0; u < kPF; u++) load_tile(R[u], min(u, KT - 1));
     store_tile(R[0], 0);
@@ -273,17 +286,17 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_mfma_kernel(const uint8_
     // fall outside it, columns past N get an out-of-range offset; both stores
     // are dropped, so there are no per-element branches.
     const float alpha = *alpha_p;
-    const int rows_here = (int)min<int64_t>(kBM, M - m0);
+    const int rows_here = (int)min<int64_t>(BM, M - m0);
     const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(Y + m0 * N, (int64_t)rows_here * N * (int64_t)sizeof(YT));
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
+    for (int i = 0; i < TA; i++) {
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int nl = wn * 64 + j * 32 + lr;
+        for (int j = 0; j < TB; j++) {
+            const int nl = wn * 32 * TB + j * 32 + lr;
             const bool col_ok = n0 + nl < N;
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int ml = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+                const int ml = wm * 32 * TA + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
                 const int v = acc[i][j][r] >> Shift<BITS>::value;
                 const uint32_t off = col_ok ? (uint32_t)((ml * N + n0 + nl) * (int64_t)sizeof(YT)) : kDropOffset;
                 buf_store_y<YT>(y_rsrc, off, rescale(v, xs_tile[ml], alpha));
@@ -422,11 +435,19 @@ hipError_t launch_typed(const uint8_t* A, const float* xscale, int64_t M, int64_
                                alpha, N, Y);
         return hipGetLastError();
     }
-    if (K % kBK != 0) return hipErrorInvalidValue;  // the C ABI only admits K % 128 == 0 for M > 64
-    const int tiles_n = (int)((N + kBN - 1) / kBN);
-    const int tiles_total = tiles_n * (int)((M + kBM - 1) / kBM);
-    hipLaunchKernelGGL((gemm_mfma_kernel<BITS, YT>), dim3(tiles_total), dim3(kGemmThreads), 0, s, A, xscale, M, K, Wp,
-                       alpha, N, Y, tiles_n, tiles_total);
+    if (K % kBK != 0) return hipErrorInvalidValue;  // the C ABI only admits K % 128 == 0
+    const int64_t big_tiles = ((M + 127) / 128) * ((N + 255) / 256);
+    if (big_tiles >= 512) {
+        const int tiles_n = (int)((N + 255) / 256);
+        const int tiles_total = (int)big_tiles;
+        hipLaunchKernelGGL((gemm_mfma_kernel<BITS, YT, 2, 4>), dim3(tiles_total), dim3(kGemmThreads), 0, s, A, xscale,
+                           M, K, Wp, alpha, N, Y, tiles_n, tiles_total);
+    } else {
+        const int tiles_n = (int)((N + 127) / 128);
+        const int tiles_total = tiles_n * (int)((M + 127) / 128);
+        hipLaunchKernelGGL((gemm_mfma_kernel<BITS, YT, 2, 2>), dim3(tiles_total), dim3(kGemmThreads), 0, s, A, xscale,
+                           M, K, Wp, alpha, N, Y, tiles_n, tiles_total);
+    }
     return hipGetLastError();
 }
 

@@ -127,10 +127,12 @@ def _random_codes(rng, M, K, bits):
 
 
 GEMM_CASES = [
-    # (M, K, N, bits) -- prefill tiles are 128 x 128, decode (M <= 64) tiles 16 columns
+    # (M, K, N, bits) -- prefill tiles 128 x 128 or 128 x 256, decode (M <= 64) tiles 16 columns
     (300, 2048, 272, 8), (300, 2048, 272, 4), (129, 256, 16, 8), (128, 1024, 128, 4), (257, 128, 400, 8), (1024, 4096, 1024, 8), (520, 16384, 384, 4),
     (1, 8192, 4096, 4), (7, 8192, 512, 8), (16, 4096, 1024, 4), (17, 2048, 256, 4), (33, 1024, 64, 8),
     (64, 8192, 1024, 4), (65, 512, 192, 4), (64, 128, 32, 8),
+    # >= 512 tiles of 128 x 256: the large-tile kernel, ragged in M and N
+    (4100, 256, 4000, 4), (4100, 384, 4000, 8),
 ]
 
 
