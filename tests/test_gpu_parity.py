@@ -79,6 +79,12 @@ ACT_CASES = [
     (16384, "bf16", 8, True, hbl.HBL_NORM_LN, 0, True, 3),
     (32768, "f32", 8, True, hbl.HBL_NORM_RMS, 0, False, 2),
     (32768, "bf16", 4, True, hbl.HBL_NORM_RMS, 1, False, 2),
+    # LayerNorm without a gain (Hadamard path folds the mean into element 0), plain LN, NONE with a gain
+    (2048, "bf16", 4, True, hbl.HBL_NORM_LN, 0, False, 9),
+    (16384, "f32", 8, True, hbl.HBL_NORM_LN, 0, False, 3),
+    (4096, "f32", 8, False, hbl.HBL_NORM_LN, 0, False, 5),
+    (1024, "bf16", 8, True, hbl.HBL_NORM_NONE, 0, True, 4),
+    (256, "f32", 8, False, hbl.HBL_NORM_RMS, 0, False, 3),
 ]
 
 
@@ -87,6 +93,8 @@ def test_quantize_activations_parity(K, dt, bits, had, norm, a4, use_gain, M):
     _announce("act K=%d %s a%d H=%d norm=%d a4=%d gain=%d M=%d" % (K, dt, bits, had, norm, a4, use_gain, M))
     rng = np.random.default_rng(K + bits + M)
     X, _ = workloads.x_outlier_gaussian(rng, M, K, 4, 30.0)
+    if norm == hbl.HBL_NORM_LN:
+        X = (X + np.float32(3.0)).astype(np.float32)  # nonzero mean
     if M > 2:
         X[1] = 0.0                                   # an all-zero row
     gain = (rng.standard_normal(K).astype(np.float32) * 0.5 + 1.0) if use_gain else None
