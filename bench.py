@@ -41,7 +41,22 @@ def parse():
     p.add_argument("--layer", default="wo_1.3b")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-iters", type=int, default=200)
+    p.add_argument("--counter-run", action="store_true",
+                   help="for rocprofv3 --pmc passes: a 256 MiB device copy (the counters' known-size reference), "
+                        "then each kernel of the layer 3 times; prints no JSON")
     return p.parse_args()
+
+
+def read_kv(path):
+    """Parse a 'key = value' text file (lines starting with # are comments)."""
+    out = {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#") and "=" in line:
+                k, v = line.split("=", 1)
+                out[k.strip()] = v.strip()
+    return out
 
 
 def source_hash(files):
@@ -106,6 +121,20 @@ def main():
     def step(s):
         hbl.hbl_quantize_weights(s["W"], 1e-5, W_packed=s["Wp"], alpha=s["alpha"], ws=s["wws"])
         hbl.hbl_forward(s["X"], s["Wp"], s["alpha"], N, cfg, Y=s["Y"], ws=s["ws"])
+
+    if args.counter_run:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        s0 = sets[0]
+        for _ in range(3):
+            hbl.hbl_quantize_weights(s0["W"], 1e-5, W_packed=s0["Wp"], alpha=s0["alpha"], ws=s0["wws"])
+            hbl.hbl_quantize_activations(s0["X"], cfg, codes=s0["codes"], xscale=s0["xs"])
+            hbl.hbl_gemm(s0["codes"], s0["xs"], bits, K, s0["Wp"], s0["alpha"], N, Y=s0["Y"])
+        torch.cuda.synchronize()
+        print("counter run done: %s" % layer.desc)
+        return
 
     # ---------------------------------------------------------------- steps
     # Eager warmup (also initialises every kernel), then the timed work is
@@ -180,13 +209,14 @@ def main():
     dom_name = max(kernels, key=lambda k: kernels[k]["us"])
     dom = kernels[dom_name]
 
+    # HBM bytes per launch from committed counter passes, only while the
+    # kernel's sources are unchanged since the counters were taken
     traffic = None
-    tfile = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (dom_name, layer.name))
+    tfile = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (dom_name, layer.name))
     if os.path.exists(tfile):
-        with open(tfile) as f:
-            t = json.load(f)
-        if t.get("source_hash") == source_hash(t.get("sources", [])):
-            traffic = t.get("bytes_per_launch")
+        t = read_kv(tfile)
+        if t.get("source_hash") == source_hash(t.get("sources", "").split()):
+            traffic = int(t["bytes_per_launch"])
 
     roofline = {"kernel": dom_name, "bound": dom["bound"], "achieved": round(dom["achieved"], 2),
                 "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4), "traffic": traffic,
