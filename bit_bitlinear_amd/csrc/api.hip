@@ -22,6 +22,7 @@ bool dtype_ok(int32_t d) { return d == HBL_F32 || d == HBL_BF16; }
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr int64_t kMaxGemmM = int64_t(1) << 23;
+constexpr int64_t kMaxGemmN = int64_t(1) << 20;  // keeps a 128-row output tile's byte offsets in 32 bits
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 
 hbl_status check_weight_shape(int64_t N, int64_t K) {
@@ -53,7 +54,7 @@ hbl_status check_gemm_shape(int64_t M, int64_t K, int64_t N) {
     if (M < 0 || M > kMaxGemmM) return HBL_ERR_SHAPE;
     if (K < 128 || K > HBL_MAX_K) return HBL_ERR_SHAPE;
     if (K % 128) return HBL_ERR_ALIGN;
-    if (N < 16 || N > kMaxRows) return HBL_ERR_SHAPE;
+    if (N < 16 || N > kMaxGemmN) return HBL_ERR_SHAPE;
     if (N % 16) return HBL_ERR_ALIGN;
     return HBL_OK;
 }

@@ -49,6 +49,8 @@ HBL_DEVINL v4i unpack_a4(uint32_t x0, uint32_t x1) {
 }
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 // Raw buffer resource over [base, base + bytes): loads whose offset falls
 // outside return zeros, so tile edges need no branches (branch-free loads
@@ -75,16 +77,6 @@ template <>
 HBL_DEVINL void store_y<uint16_t>(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16_bits(v); }
 
 // Buffer stores: an offset outside the resource is dropped by the hardware.
-template <typename YT>
-HBL_DEVINL void buf_store_y(__amdgpu_buffer_rsrc_t r, uint32_t off, float v);
-template <>
-HBL_DEVINL void buf_store_y<float>(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, 0);
-}
-template <>
-HBL_DEVINL void buf_store_y<uint16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
-    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16_bits(v), r, (int)off, 0, 0);
-}
 constexpr uint32_t kDropOffset = 0x80000000u;  // beyond every resource: store dropped
 
 HBL_DEVINL float rescale(int acc, float d, float alpha) {
@@ -109,7 +101,13 @@ HBL_DEVINL float rescale(int acc, float d, float alpha) {
 // Tile order: blocks are dealt to the 8 XCDs round robin (block b -> XCD b%8);
 // the kernel maps block b to tile (b%8)*T8 + b/8, so every XCD works on a
 // contiguous band of M tiles and its L2 holds that band of A plus all of W.
-constexpr int kBK = 128, kGemmThreads = 256, kPF = 2;
+#ifndef HBL_GEMM_BK
+#define HBL_GEMM_BK 128
+#endif
+#ifndef HBL_GEMM_PF
+#define HBL_GEMM_PF 2
+#endif
+constexpr int kBK = HBL_GEMM_BK, kGemmThreads = 256, kPF = HBL_GEMM_PF;
 
 template <int BITS, int BM>
 struct ATile {
@@ -141,7 +139,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_mfma_kernel(const uint8_
     constexpr int kBPerThread = BN * kBRow / 16 / kGemmThreads;
     __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * AT::stride];
     __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * kBStride];
-    __shared__ float xs_tile[BM];  // per-token scales of this tile's rows (0 past M)
+    __shared__ __attribute__((aligned(16))) float xs_tile[BM];  // per-token scales of this tile's rows (0 past M)
 
     // XCD-aware tile order (see above); falls back to linear order when the
     // tile count is not a multiple of 8.
@@ -283,23 +281,41 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_mfma_kernel(const uint8_
 
     // ---- epilogue: lane holds column lr, rows 8*(r/4) + 4*lg + r%4 of each 32x32 tile.
     // Y is written through a buffer resource over this tile's rows: rows past M
-    // fall outside it, columns past N get an out-of-range offset; both stores
-    // are dropped, so there are no per-element branches.
+    // fall outside it, columns past N start from an out-of-range offset; both
+    // stores are dropped, so there are no per-element branches.  A lane's
+    // offset is its base offset plus a row step that is uniform across the
+    // wave; the four scales of rows 8q + 4lg .. +3 are one 16-byte LDS read.
     const float alpha = *alpha_p;
     const int rows_here = (int)min<int64_t>(BM, M - m0);
-    const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(Y + m0 * N, (int64_t)rows_here * N * (int64_t)sizeof(YT));
+    const uint32_t row_bytes = (uint32_t)(N * (int64_t)sizeof(YT));  // <= 4 MiB (N <= 2^20)
+    const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(Y + m0 * N, (int64_t)rows_here * row_bytes);
+    const int row0 = wm * 32 * TA + 4 * lg;
 #pragma unroll
-    for (int i = 0; i < TA; i++) {
+    for (int j = 0; j < TB; j++) {
+        const int64_t n = n0 + wn * 32 * TB + j * 32 + lr;
+        const uint32_t lane_off = n < N ? (uint32_t)row0 * row_bytes + (uint32_t)(n * (int64_t)sizeof(YT)) : kDropOffset;
 #pragma unroll
-        for (int j = 0; j < TB; j++) {
-            const int nl = wn * 32 * TB + j * 32 + lr;
-            const bool col_ok = n0 + nl < N;
+        for (int i = 0; i < TA; i++) {
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int ml = wm * 32 * TA + i * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-                const int v = acc[i][j][r] >> Shift<BITS>::value;
-                const uint32_t off = col_ok ? (uint32_t)((ml * N + n0 + nl) * (int64_t)sizeof(YT)) : kDropOffset;
-                buf_store_y<YT>(y_rsrc, off, rescale(v, xs_tile[ml], alpha));
+            for (int q = 0; q < 4; q++) {
+                const float4 xs4 = *reinterpret_cast<const float4*>(&xs_tile[row0 + i * 32 + 8 * q]);
+                const float xsr[4] = {xs4.x, xs4.y, xs4.z, xs4.w};
+                float y[4];
+#pragma unroll
+                for (int r = 0; r < 4; r++) y[r] = rescale(acc[i][j][4 * q + r] >> Shift<BITS>::value, xsr[r], alpha);
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const uint32_t off = lane_off + (uint32_t)(i * 32 + 8 * q + r) * row_bytes;
+                    if constexpr (sizeof(YT) == 4) {
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y[r]), y_rsrc, (int)off, 0, 0);
+                    } else if (r % 2 == 0) {
+                        // hardware round-to-nearest-even pair conversion (same result as f32_to_bf16_bits)
+                        const v2bf h = __builtin_convertvector((v2f){y[r], y[r + 1]}, v2bf);
+                        const uint32_t hp = __builtin_bit_cast(uint32_t, h);
+                        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(hp & 0xFFFFu), y_rsrc, (int)off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(hp >> 16), y_rsrc, (int)(off + row_bytes), 0, 0);
+                    }
+                }
             }
         }
     }

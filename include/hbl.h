@@ -141,7 +141,7 @@ hbl_status hbl_quantize_activations(const void* X, int32_t x_dtype, int64_t M, i
  * alpha), stored as fp32 or bf16 (round to nearest even).  With xscale = 1 and
  * alpha = 1 the fp32 output equals acc exactly (|acc| < 2^24).  INT8 x ternary
  * products run on the gfx950 i8 matrix cores (MFMA).  Constraints: K in
- * [128, 32768], K % 128 == 0; N >= 16, N % 16 == 0; 0 <= M <= 2^23 (M == 0
+ * [128, 32768], K % 128 == 0; N in [16, 2^20], N % 16 == 0; 0 <= M <= 2^23 (M == 0
  * queues nothing); codes, W_packed and Y 16-byte aligned.
  */
 hbl_status hbl_gemm(const void* codes, const float* xscale, int32_t act_bits, int64_t M, int64_t K,

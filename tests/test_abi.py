@@ -83,7 +83,7 @@ def test_gemm_validation(lib):
     assert _gemm(lib, ydt=3) == 5
     assert _gemm(lib, K=1000) == 4 and _gemm(lib, N=100) == 4
     assert _gemm(lib, K=64) == 2 and _gemm(lib, K=192) == 4 and _gemm(lib, K=65536) == 2 and _gemm(lib, N=0) == 2 and _gemm(lib, M=-3) == 2
-    assert _gemm(lib, M=(1 << 23) + 1) == 2
+    assert _gemm(lib, M=(1 << 23) + 1) == 2 and _gemm(lib, N=(1 << 20) + 16) == 2
     assert _gemm(lib, codes=None) == 1 and _gemm(lib, alpha=None) == 1 and _gemm(lib, Y=None) == 1
     assert _gemm(lib, Y=MIS) == 4 and _gemm(lib, W=MIS) == 4
     assert _gemm(lib, M=0, codes=None) == 0
