@@ -48,21 +48,8 @@ HBL_DEVINL v4i unpack_a4(uint32_t x0, uint32_t x1) {
     return r;
 }
 
-typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-
-// Raw buffer resource over [base, base + bytes): loads whose offset falls
-// outside return zeros, so tile edges need no branches (branch-free loads
-// also let the compiler keep several loads in flight with exact vmcnt waits).
-HBL_DEVINL __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    const int64_t lim = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)lim, 0x00020000);
-}
-HBL_DEVINL uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
 
 template <int BITS>
 struct Shift {
@@ -101,26 +88,24 @@ HBL_DEVINL float rescale(int acc, float d, float alpha) {
 // Tile order: blocks are dealt to the 8 XCDs round robin (block b -> XCD b%8);
 // the kernel maps block b to tile (b%8)*T8 + b/8, so every XCD works on a
 // contiguous band of M tiles and its L2 holds that band of A plus all of W.
-#ifndef HBL_GEMM_BK
-#define HBL_GEMM_BK 128
-#endif
-#ifndef HBL_GEMM_PF
-#define HBL_GEMM_PF 2
-#endif
-constexpr int kBK = HBL_GEMM_BK, kGemmThreads = 256, kPF = HBL_GEMM_PF;
+constexpr int kBK = 128, kGemmThreads = 256, kPF = 2;
 
+// k order inside a K step: 32-k MFMA step s of lane group g (lanes 32g..32g+31)
+// takes the 16-k group 4g + s of the step, for both operands.  A lane's
+// weight words for the whole step are then 16 contiguous bytes (one LDS read)
+// and its INT4 codes 32 contiguous bytes.
 template <int BITS, int BM>
 struct ATile {
     static constexpr int row_bytes = BITS == 8 ? kBK : kBK / 2;  // bytes of one row per K step
-    // padded LDS row: 144 B (INT8: 8 consecutive rows of 16-byte reads hit
-    // disjoint banks) or 72 B (INT4: 16 consecutive rows of 8-byte reads do)
-    static constexpr int stride = BITS == 8 ? row_bytes + 16 : row_bytes + 8;
+    // padded LDS row (144 B INT8, 80 B INT4): 16 consecutive rows of 16-byte
+    // reads at one column hit disjoint banks
+    static constexpr int stride = row_bytes + 16;
     static constexpr int chunks = BM * row_bytes / 16;           // 16-byte chunks per tile
     static constexpr int per_thread = chunks / kGemmThreads;
     static constexpr int cpr = row_bytes / 16;                   // chunks per row
 };
 constexpr int kBRow = kBK / 4;        // 32 bytes of packed W per row and K step
-constexpr int kBStride = kBRow + 4;   // 9 dwords: conflict-free 4-byte fragment reads
+constexpr int kBStride = kBRow + 16;  // 48 B: 16 consecutive columns of 16-byte reads hit disjoint banks
 
 template <int BITS, int BM, int BN>
 struct Regs {
@@ -178,20 +163,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_mfma_kernel(const uint8_
         for (int i = 0; i < AT::per_thread; i++) {
             const int q = tid + i * kGemmThreads;
             const int row = q / AT::cpr, c16 = q % AT::cpr;
-            uint8_t* dst = &As[st][row * AT::stride + c16 * 16];
-            if constexpr (AT::stride % 16 == 0) {
-                *reinterpret_cast<uint4*>(dst) = r.a[i];
-            } else {
-                reinterpret_cast<uint2*>(dst)[0] = make_uint2(r.a[i].x, r.a[i].y);
-                reinterpret_cast<uint2*>(dst)[1] = make_uint2(r.a[i].z, r.a[i].w);
-            }
+            *reinterpret_cast<uint4*>(&As[st][row * AT::stride + c16 * 16]) = r.a[i];
         }
 #pragma unroll
         for (int i = 0; i < kBPerThread; i++) {
             const int q = tid + i * kGemmThreads;
             const int row = q / (kBRow / 16), c16 = q % (kBRow / 16);
-            uint32_t* d = reinterpret_cast<uint32_t*>(&Bs[st][row * kBStride + c16 * 16]);
-            d[0] = r.b[i].x; d[1] = r.b[i].y; d[2] = r.b[i].z; d[3] = r.b[i].w;
+            *reinterpret_cast<uint4*>(&Bs[st][row * kBStride + c16 * 16]) = r.b[i];
         }
     };
 
@@ -205,46 +183,49 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_mfma_kernel(const uint8_
 
     const int lr = lane & 31;  // row (A) / column (W) inside a 32-wide MFMA tile
     const int lg = lane >> 5;  // which 16-k half of the 32-k MFMA step
-    // Fragments of one 32-k step: TA A operands (rows) and TB W words (columns).
-    struct Frag {
+    // Per K step a lane reads, for each of its TB columns, the four weight
+    // words of its k groups (one 16-byte read), and for each of its TA rows
+    // 16 bytes per MFMA step (INT8) or 32 bytes for all four (INT4).
+    struct AFrag {
         v4i a[TA];
-        uint32_t w[TB];
     };
-    auto read_frag = [&](Frag& f, int st, int s) {
+    auto read_a = [&](AFrag& f, int st, int s) {
 #pragma unroll
         for (int i = 0; i < TA; i++) {
             const int row = wm * 32 * TA + i * 32 + lr;
-            if constexpr (BITS == 8) {
-                const uint4 q = *reinterpret_cast<const uint4*>(&As[st][row * AT::stride + s * 32 + lg * 16]);
-                f.a[i][0] = (int)q.x; f.a[i][1] = (int)q.y; f.a[i][2] = (int)q.z; f.a[i][3] = (int)q.w;
-            } else {
-                const uint2 q = *reinterpret_cast<const uint2*>(&As[st][row * AT::stride + s * 16 + lg * 8]);
-                f.a[i][0] = (int)q.x; f.a[i][1] = (int)q.y;
-            }
+            const uint4 q = *reinterpret_cast<const uint4*>(&As[st][row * AT::stride + (BITS == 8 ? (4 * lg + s) * 16 : lg * 32 + s * 16)]);
+            f.a[i][0] = (int)q.x; f.a[i][1] = (int)q.y; f.a[i][2] = (int)q.z; f.a[i][3] = (int)q.w;
         }
+    };
+    // Software pipeline: the A reads of step s+1 (INT8) or of the second
+    // half (INT4) are issued before the MFMAs that precede them.
+    auto compute = [&](int st) {
+        uint4 wq[TB];
 #pragma unroll
         for (int j = 0; j < TB; j++) {
             const int col = wn * 32 * TB + j * 32 + lr;
-            f.w[j] = *reinterpret_cast<const uint32_t*>(&Bs[st][col * kBStride + s * 8 + lg * 4]);
+            wq[j] = *reinterpret_cast<const uint4*>(&Bs[st][col * kBStride + lg * 16]);
         }
-    };
-    // Software pipeline over the 32-k steps of a stage: the LDS reads of step
-    // s+1 are issued before the MFMAs of step s.
-    auto compute = [&](int st) {
-        Frag f[2];
-        read_frag(f[0], st, 0);
+        constexpr int kReads = BITS == 8 ? kBK / 32 : kBK / 64;  // A reads per K step
+        AFrag f[2];
+        read_a(f[0], st, 0);
 #pragma unroll
         for (int s = 0; s < kBK / 32; s++) {
-            Frag& cur = f[s & 1];
-            if (s + 1 < kBK / 32) read_frag(f[(s + 1) & 1], st, s + 1);
+            const int rd = BITS == 8 ? s : s / 2;
+            if ((BITS == 8 || s % 2 == 0) && rd + 1 < kReads) read_a(f[(rd + 1) & 1], st, rd + 1);
+            const AFrag& cur = f[rd & 1];
             v4i bw[TB];
 #pragma unroll
-            for (int j = 0; j < TB; j++) bw[j] = unpack_w(cur.w[j]);
+            for (int j = 0; j < TB; j++) {
+                const uint32_t w = s == 0 ? wq[j].x : s == 1 ? wq[j].y : s == 2 ? wq[j].z : wq[j].w;
+                bw[j] = unpack_w(w);
+            }
 #pragma unroll
             for (int i = 0; i < TA; i++) {
                 v4i a;
                 if constexpr (BITS == 8) a = cur.a[i];
-                else a = unpack_a4((uint32_t)cur.a[i][0], (uint32_t)cur.a[i][1]);
+                else a = (s & 1) ? unpack_a4((uint32_t)cur.a[i][2], (uint32_t)cur.a[i][3])
+                                 : unpack_a4((uint32_t)cur.a[i][0], (uint32_t)cur.a[i][1]);
 #pragma unroll
                 for (int j = 0; j < TB; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bw[j], acc[i][j], 0, 0, 0);

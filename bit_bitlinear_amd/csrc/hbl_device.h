@@ -24,6 +24,22 @@ HBL_DEVINL uint32_t f32_to_bf16_bits(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// ---- raw buffer resources ----
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): loads whose offset falls
+// outside return zeros and stores there are dropped, so tile edges need no
+// branches (branch-free loads also let the compiler keep several loads in
+// flight with exact vmcnt waits).  Ranges are clamped to 2^31 - 16 bytes.
+HBL_DEVINL __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int64_t lim = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)lim, 0x00020000);
+}
+HBL_DEVINL uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // ---- wave / block reductions (fixed butterfly order: deterministic) ----
 HBL_DEVINL float wave_sum_f32(float v) {
 #pragma unroll
