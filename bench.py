@@ -244,7 +244,7 @@ def main():
                    "hadamard": layer.hadamard, "x_dtype": layer.x_dtype, "y_dtype": layer.y_dtype,
                    "step": "hbl_quantize_weights + hbl_forward", "rotating_sets": R,
                    "timing": "HIP graph replay of captured launches"},
-        "tops": round(2.0 * M * N * K * args.steps / wall / 1e12, 2),
+        "tops": round(2.0 * M * N * K * timed_steps / wall / 1e12, 2),
         "forward_us": round(t_act + t_gemm, 3),
         "forward_only_tokens_per_s": round(M / ((t_act + t_gemm) * 1e-6), 1),
         "roofline": roofline,

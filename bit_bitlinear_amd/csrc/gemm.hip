@@ -416,9 +416,138 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const uint8_t*
     }
 }
 
+// ======================================================= small-M GEMV ==
+// M <= 4 tokens, K a power of two in [1024, 16384]: a matrix-vector product
+// on the vector ALU (v_dot4_i32_i8), so that the weight stream is read with
+// fully coalesced 16-byte loads like a plain copy.  One block of 256 threads
+// per 16 output columns; the block's 16 weight rows are contiguous in memory
+// (16 * K/4 bytes).  Vector v of that slice (64 trits) is row v / CPR, chunk
+// v % CPR, with CPR = K/64 chunks per row; thread t takes v = t + 256 j, so
+// it always sees chunk c = t % CPR (one set of activation codes, kept in
+// registers) of rows t / CPR + j * (256 / CPR).  Each instruction of a wave
+// reads 1 KiB of consecutive bytes.  Partial dot products are summed over the
+// CPR threads of a row: DPP adds inside each 16-lane row, then LDS.
+constexpr int kGvThreads = 256, kGvRows = 16, kGvMaxM = 4;
+
+// Sum over the 16 lanes of a DPP row (every lane of the row gets the sum):
+// swap neighbours, swap pairs, rotate the row by 4, rotate it by 8.
+HBL_DEVINL int row16_sum(int x) {
+    x += __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    x += __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    x += __builtin_amdgcn_mov_dpp(x, 0x124, 0xF, 0xF, false);  // row_ror:4
+    x += __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror:8
+    return x;
+}
+
+template <int BITS, int LCPR, int MS, typename YT>
+__global__ __launch_bounds__(kGvThreads) void gemv_small_kernel(const uint8_t* __restrict__ A,
+                                                                const float* __restrict__ xscale, int M,
+                                                                const uint8_t* __restrict__ Wp,
+                                                                const float* __restrict__ alpha_p, int64_t N,
+                                                                YT* __restrict__ Y) {
+    constexpr int CPR = 1 << LCPR;                 // 64-trit chunks per weight row
+    constexpr int K = 64 * CPR;
+    constexpr int V = kGvRows * CPR / kGvThreads;  // weight vectors per thread
+    constexpr int RS = kGvThreads / CPR;           // row stride between a thread's vectors
+    constexpr int ABytes = 64 * BITS / 8;          // code bytes per chunk and token
+    static_assert(V >= 1 && RS * V == kGvRows, "K outside [1024, 16384]");
+    __shared__ int part[V][MS][kGvThreads / 16];
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int c = tid & (CPR - 1);
+    const int64_t n0 = (int64_t)blockIdx.x * kGvRows;
+    // Codes first (a few KiB, from L2), then the weight stream: the weight
+    // vectors are consumed in the order they were issued, so the dot products
+    // of vector j overlap the arrival of vectors j+1, j+2, ...
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A, (int64_t)M * (K * BITS / 8));  // tokens past M: zeros
+    uint4 a[MS][ABytes / 16];
+#pragma unroll
+    for (int m = 0; m < MS; m++)
+#pragma unroll
+        for (int q = 0; q < ABytes / 16; q++)
+            a[m][q] = buf_load16(a_rsrc, (uint32_t)(m * (K * BITS / 8) + c * ABytes + q * 16));
+    const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(Wp + n0 * (K / 4), (int64_t)kGvRows * (K / 4));
+    uint4 w[V];
+#pragma unroll
+    for (int j = 0; j < V; j++) w[j] = buf_load16(w_rsrc, (uint32_t)((tid + j * kGvThreads) * 16));
+
+    // activation operands of the chunk's four 16-k groups, as int8 dwords
+    v4i av[MS][4];
+#pragma unroll
+    for (int m = 0; m < MS; m++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            if constexpr (BITS == 8) {
+                const uint4 q = a[m][i];
+                av[m][i] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+            } else {
+                const uint4 q = a[m][i / 2];
+                av[m][i] = (i & 1) ? unpack_a4(q.z, q.w) : unpack_a4(q.x, q.y);
+            }
+        }
+    int acc[V][MS];
+#pragma unroll
+    for (int j = 0; j < V; j++) {
+#pragma unroll
+        for (int m = 0; m < MS; m++) acc[j][m] = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {  // 16-k group i of the chunk
+            const uint32_t word = i == 0 ? w[j].x : i == 1 ? w[j].y : i == 2 ? w[j].z : w[j].w;
+            const v4i b = unpack_w(word);
+#pragma unroll
+            for (int m = 0; m < MS; m++) {
+                int t = acc[j][m];
+#pragma unroll
+                for (int d = 0; d < 4; d++) t = __builtin_amdgcn_sdot4(b[d], av[m][i][d], t, false);
+                acc[j][m] = t;
+            }
+        }
+    }
+    // Sum over the CPR threads of a row group: DPP adds over each 16-lane row
+    // of the wave (exact integer adds), then the row sums through LDS.
+    const float alpha = *alpha_p;
+#pragma unroll
+    for (int j = 0; j < V; j++)
+#pragma unroll
+        for (int m = 0; m < MS; m++) {
+            const int t = row16_sum(acc[j][m]);
+            if ((lane & 15) == 0) part[j][m][tid >> 4] = t;
+        }
+    __syncthreads();
+    // output (row r, token m): row group r % RS, which owns the 16-lane rows
+    // (r % RS) * CPR/16 .. +CPR/16-1, vector j = r / RS
+    if (tid < kGvRows * MS) {
+        const int r = tid / MS, m = tid % MS;
+        const int gr = r % RS, j = r / RS;
+        int sum = 0;
+#pragma unroll
+        for (int x = 0; x < CPR / 16; x++) sum += part[j][m][gr * (CPR / 16) + x];
+        if (m < M) store_y<YT>(Y + m * N + n0 + r, rescale(sum >> Shift<BITS>::value, xscale[m], alpha));
+    }
+}
+
+template <int BITS, int MS, typename YT>
+hipError_t launch_gemv_small(const uint8_t* A, const float* xscale, int64_t M, int64_t K, const uint8_t* Wp,
+                             const float* alpha, int64_t N, YT* Y, hipStream_t s) {
+    const dim3 grid((unsigned)(N / kGvRows));
+    switch (K) {
+        case 1024: hipLaunchKernelGGL((gemv_small_kernel<BITS, 4, MS, YT>), grid, dim3(kGvThreads), 0, s, A, xscale, (int)M, Wp, alpha, N, Y); break;
+        case 2048: hipLaunchKernelGGL((gemv_small_kernel<BITS, 5, MS, YT>), grid, dim3(kGvThreads), 0, s, A, xscale, (int)M, Wp, alpha, N, Y); break;
+        case 4096: hipLaunchKernelGGL((gemv_small_kernel<BITS, 6, MS, YT>), grid, dim3(kGvThreads), 0, s, A, xscale, (int)M, Wp, alpha, N, Y); break;
+        case 8192: hipLaunchKernelGGL((gemv_small_kernel<BITS, 7, MS, YT>), grid, dim3(kGvThreads), 0, s, A, xscale, (int)M, Wp, alpha, N, Y); break;
+        default: hipLaunchKernelGGL((gemv_small_kernel<BITS, 8, MS, YT>), grid, dim3(kGvThreads), 0, s, A, xscale, (int)M, Wp, alpha, N, Y); break;
+    }
+    return hipGetLastError();
+}
+
 template <int BITS, typename YT>
 hipError_t launch_typed(const uint8_t* A, const float* xscale, int64_t M, int64_t K, const uint8_t* Wp,
                         const float* alpha, int64_t N, YT* Y, hipStream_t s) {
+    if (M <= kGvMaxM && K >= 1024 && K <= 16384 && (K & (K - 1)) == 0) {
+        if (M == 1) return launch_gemv_small<BITS, 1, YT>(A, xscale, M, K, Wp, alpha, N, Y, s);
+        if (M == 2) return launch_gemv_small<BITS, 2, YT>(A, xscale, M, K, Wp, alpha, N, Y, s);
+        return launch_gemv_small<BITS, 4, YT>(A, xscale, M, K, Wp, alpha, N, Y, s);
+    }
     if (M <= 64 && K % 256 == 0 && K / 256 <= kDecWaves * kDecMaxSS) {
         const dim3 grid((unsigned)((N + kDecBN - 1) / kDecBN));
         if (M <= 16)

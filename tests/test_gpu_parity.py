@@ -139,6 +139,9 @@ GEMM_CASES = [
     (300, 2048, 272, 8), (300, 2048, 272, 4), (129, 256, 16, 8), (128, 1024, 128, 4), (257, 128, 400, 8), (1024, 4096, 1024, 8), (520, 16384, 384, 4),
     (1, 8192, 4096, 4), (7, 8192, 512, 8), (16, 4096, 1024, 4), (17, 2048, 256, 4), (33, 1024, 64, 8),
     (64, 8192, 1024, 4), (65, 512, 192, 4), (64, 128, 32, 8),
+    # M <= 4 with K a power of two in [1024, 16384]: the vector-ALU GEMV, every K and M
+    (1, 1024, 48, 8), (2, 2048, 64, 4), (3, 4096, 32, 8), (4, 8192, 16, 8), (4, 16384, 80, 4), (1, 16384, 4096, 8),
+    (2, 1024, 32, 4), (3, 8192, 64, 4), (1, 4096, 1024, 4), (2, 512, 64, 8), (3, 32768, 32, 4),
     # >= 512 tiles of 128 x 256: the large-tile kernel, ragged in M and N
     (4100, 256, 4000, 4), (4100, 384, 4000, 8),
 ]
@@ -161,7 +164,8 @@ def test_gemm_int32_accumulators_exact(M, K, N, bits):
     assert np.array_equal(to_host(Y), acc.astype(np.float32))
 
 
-@pytest.mark.parametrize("M,bits,ydt", [(200, 8, "f32"), (200, 4, "bf16"), (5, 4, "f32"), (40, 8, "bf16")])
+@pytest.mark.parametrize("M,bits,ydt", [(200, 8, "f32"), (200, 4, "bf16"), (5, 4, "f32"), (40, 8, "bf16"),
+                                        (1, 8, "f32"), (3, 4, "bf16")])
 def test_gemm_rescale_epilogue_exact(M, bits, ydt):
     import torch
     K, N = 1024, 256
