@@ -174,6 +174,11 @@ hbl_status hbl_forward(const void* X, int32_t x_dtype, int64_t M, int64_t K, con
     const size_t cb = round_up(codes_bytes(M, K, cfg->act_bits), 256);
     const size_t need = cb + round_up((size_t)M * sizeof(float), 256);
     if (ws_bytes < need) return HBL_ERR_WORKSPACE;
+    if (hbl::forward_small_eligible(M, K)) {
+        const hipError_t e = hbl::launch_forward_small(X, x_dtype, M, K, gain, *cfg, W_packed, alpha, N, Y, y_dtype,
+                                                       (hipStream_t)stream);
+        return e == hipSuccess ? HBL_OK : hip_fail(e);
+    }
     void* codes = ws;
     float* xscale = (float*)((uint8_t*)ws + cb);
     hipError_t e = hbl::launch_act_quant(X, x_dtype, M, K, gain, *cfg, codes, xscale, nullptr, nullptr,

@@ -7,69 +7,19 @@
 // and runs on MFMA.  The epilogue applies y = fp32(fp32(acc * xscale[m]) * alpha)
 // (no bias: section "BitNet v2：原生4位激活").
 //
-// Operand unpack (in registers, per wave):
-//   * weights: one 32-bit word holds an aligned group of 16 trits, byte b
-//     holding k = b, b+4, b+8, b+12 in its bit pairs.  (word << (6-2c)) &
-//     0xC0C0C0C0 puts the trits k = 4c..4c+3 in the top two bits of bytes
-//     0..3: as int8 that is 64 * w.  Four such dwords form one 16-byte MFMA
-//     operand in natural k order.
-//   * INT8 codes are used as loaded (natural k order).
-//   * INT4 codes (low nibble = even k) are spread with v_perm so that each
-//     code lands in the top nibble of its byte: as int8 that is 16 * q.
-// The i8 MFMA therefore accumulates 64*acc (INT8) or 1024*acc (INT4), exact
-// in int32 for K <= 32768, and the epilogue shifts it back.
-// For a given lane both operands hold the same k set, so the k order inside
-// an operand does not matter to the result.
-#include "hbl_device.h"
+// Operand unpacking (ternary weights to 64*w, INT4 codes to 16*q, both as
+// int8) and the rescale are in int_dot.h.  For a given lane both MFMA
+// operands hold the same k set, so the k order inside an operand does not
+// matter to the result.
+#include "int_dot.h"
 
 namespace hbl {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
-
-HBL_DEVINL v4i unpack_w(uint32_t y) {
-    v4i r;
-    r[0] = (int)((y << 6) & 0xC0C0C0C0u);
-    r[1] = (int)((y << 4) & 0xC0C0C0C0u);
-    r[2] = (int)((y << 2) & 0xC0C0C0C0u);
-    r[3] = (int)(y & 0xC0C0C0C0u);
-    return r;
-}
-
-// 16 INT4 codes (k ascending, low nibble first) -> 16 bytes, code in the top nibble.
-HBL_DEVINL v4i unpack_a4(uint32_t x0, uint32_t x1) {
-    const uint32_t l0 = x0 << 4, l1 = x1 << 4;
-    v4i r;
-    r[0] = (int)(__builtin_amdgcn_perm(x0, l0, 0x05010400u) & 0xF0F0F0F0u);
-    r[1] = (int)(__builtin_amdgcn_perm(x0, l0, 0x07030602u) & 0xF0F0F0F0u);
-    r[2] = (int)(__builtin_amdgcn_perm(x1, l1, 0x05010400u) & 0xF0F0F0F0u);
-    r[3] = (int)(__builtin_amdgcn_perm(x1, l1, 0x07030602u) & 0xF0F0F0F0u);
-    return r;
-}
-
-typedef float v2f __attribute__((ext_vector_type(2)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-
-template <int BITS>
-struct Shift {
-    static constexpr int value = BITS == 8 ? 6 : 10;
-};
-
-template <typename YT>
-HBL_DEVINL void store_y(YT* p, float v);
-template <>
-HBL_DEVINL void store_y<float>(float* p, float v) { *p = v; }
-template <>
-HBL_DEVINL void store_y<uint16_t>(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16_bits(v); }
 
 // Buffer stores: an offset outside the resource is dropped by the hardware.
 constexpr uint32_t kDropOffset = 0x80000000u;  // beyond every resource: store dropped
-
-HBL_DEVINL float rescale(int acc, float d, float alpha) {
-    const float t = (float)acc * d;  // two separately rounded fp32 products
-    return t * alpha;
-}
 
 // ============================================================ prefill GEMM ==
 // Block tile (64*TA) x (64*TB), K step 128, 4 waves in a 2 x 2 grid, each wave
@@ -417,27 +367,10 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const uint8_t*
 }
 
 // ======================================================= small-M GEMV ==
-// M <= 4 tokens, K a power of two in [1024, 16384]: a matrix-vector product
-// on the vector ALU (v_dot4_i32_i8), so that the weight stream is read with
-// fully coalesced 16-byte loads like a plain copy.  One block of 256 threads
-// per 16 output columns; the block's 16 weight rows are contiguous in memory
-// (16 * K/4 bytes).  Vector v of that slice (64 trits) is row v / CPR, chunk
-// v % CPR, with CPR = K/64 chunks per row; thread t takes v = t + 256 j, so
-// it always sees chunk c = t % CPR (one set of activation codes, kept in
-// registers) of rows t / CPR + j * (256 / CPR).  Each instruction of a wave
-// reads 1 KiB of consecutive bytes.  Partial dot products are summed over the
-// CPR threads of a row: DPP adds inside each 16-lane row, then LDS.
-constexpr int kGvThreads = 256, kGvRows = 16, kGvMaxM = 4;
-
-// Sum over the 16 lanes of a DPP row (every lane of the row gets the sum):
-// swap neighbours, swap pairs, rotate the row by 4, rotate it by 8.
-HBL_DEVINL int row16_sum(int x) {
-    x += __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-    x += __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-    x += __builtin_amdgcn_mov_dpp(x, 0x124, 0xF, 0xF, false);  // row_ror:4
-    x += __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror:8
-    return x;
-}
+// M <= 4 tokens, K a power of two in [1024, 16384]: the GEMV routines of
+// int_dot.h with 256 threads per 16 output columns, codes from global memory
+// (loaded first, a few KiB from L2), then the weight stream.
+constexpr int kGvThreads = 256;
 
 template <int BITS, int LCPR, int MS, typename YT>
 __global__ __launch_bounds__(kGvThreads) void gemv_small_kernel(const uint8_t* __restrict__ A,
@@ -445,85 +378,18 @@ __global__ __launch_bounds__(kGvThreads) void gemv_small_kernel(const uint8_t* _
                                                                 const uint8_t* __restrict__ Wp,
                                                                 const float* __restrict__ alpha_p, int64_t N,
                                                                 YT* __restrict__ Y) {
-    constexpr int CPR = 1 << LCPR;                 // 64-trit chunks per weight row
-    constexpr int K = 64 * CPR;
-    constexpr int V = kGvRows * CPR / kGvThreads;  // weight vectors per thread
-    constexpr int RS = kGvThreads / CPR;           // row stride between a thread's vectors
-    constexpr int ABytes = 64 * BITS / 8;          // code bytes per chunk and token
-    static_assert(V >= 1 && RS * V == kGvRows, "K outside [1024, 16384]");
-    __shared__ int part[V][MS][kGvThreads / 16];
-
-    const int tid = threadIdx.x, lane = tid & (kWave - 1);
-    const int c = tid & (CPR - 1);
+    using G = Gv<BITS, LCPR, MS, kGvThreads>;
+    __shared__ typename G::Part part;
     const int64_t n0 = (int64_t)blockIdx.x * kGvRows;
-    // Codes first (a few KiB, from L2), then the weight stream: the weight
-    // vectors are consumed in the order they were issued, so the dot products
-    // of vector j overlap the arrival of vectors j+1, j+2, ...
-    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A, (int64_t)M * (K * BITS / 8));  // tokens past M: zeros
-    uint4 a[MS][ABytes / 16];
-#pragma unroll
-    for (int m = 0; m < MS; m++)
-#pragma unroll
-        for (int q = 0; q < ABytes / 16; q++)
-            a[m][q] = buf_load16(a_rsrc, (uint32_t)(m * (K * BITS / 8) + c * ABytes + q * 16));
-    const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(Wp + n0 * (K / 4), (int64_t)kGvRows * (K / 4));
-    uint4 w[V];
-#pragma unroll
-    for (int j = 0; j < V; j++) w[j] = buf_load16(w_rsrc, (uint32_t)((tid + j * kGvThreads) * 16));
-
-    // activation operands of the chunk's four 16-k groups, as int8 dwords
-    v4i av[MS][4];
-#pragma unroll
-    for (int m = 0; m < MS; m++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            if constexpr (BITS == 8) {
-                const uint4 q = a[m][i];
-                av[m][i] = v4i{(int)q.x, (int)q.y, (int)q.z, (int)q.w};
-            } else {
-                const uint4 q = a[m][i / 2];
-                av[m][i] = (i & 1) ? unpack_a4(q.z, q.w) : unpack_a4(q.x, q.y);
-            }
-        }
-    int acc[V][MS];
-#pragma unroll
-    for (int j = 0; j < V; j++) {
-#pragma unroll
-        for (int m = 0; m < MS; m++) acc[j][m] = 0;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {  // 16-k group i of the chunk
-            const uint32_t word = i == 0 ? w[j].x : i == 1 ? w[j].y : i == 2 ? w[j].z : w[j].w;
-            const v4i b = unpack_w(word);
-#pragma unroll
-            for (int m = 0; m < MS; m++) {
-                int t = acc[j][m];
-#pragma unroll
-                for (int d = 0; d < 4; d++) t = __builtin_amdgcn_sdot4(b[d], av[m][i][d], t, false);
-                acc[j][m] = t;
-            }
-        }
-    }
-    // Sum over the CPR threads of a row group: DPP adds over each 16-lane row
-    // of the wave (exact integer adds), then the row sums through LDS.
-    const float alpha = *alpha_p;
-#pragma unroll
-    for (int j = 0; j < V; j++)
-#pragma unroll
-        for (int m = 0; m < MS; m++) {
-            const int t = row16_sum(acc[j][m]);
-            if ((lane & 15) == 0) part[j][m][tid >> 4] = t;
-        }
-    __syncthreads();
-    // output (row r, token m): row group r % RS, which owns the 16-lane rows
-    // (r % RS) * CPR/16 .. +CPR/16-1, vector j = r / RS
-    if (tid < kGvRows * MS) {
-        const int r = tid / MS, m = tid % MS;
-        const int gr = r % RS, j = r / RS;
-        int sum = 0;
-#pragma unroll
-        for (int x = 0; x < CPR / 16; x++) sum += part[j][m][gr * (CPR / 16) + x];
-        if (m < M) store_y<YT>(Y + m * N + n0 + r, rescale(sum >> Shift<BITS>::value, xscale[m], alpha));
-    }
+    typename G::ARegs a;
+    G::load_codes(A, M, a);
+    typename G::WRegs w;
+    G::load_w(Wp, n0, w);
+    typename G::AOps av;
+    G::unpack_codes(a, av);
+    typename G::Acc acc;
+    G::dot(w, av, acc);
+    G::template finish<YT>(acc, part, M, xscale, *alpha_p, N, Y, n0);
 }
 
 template <int BITS, int MS, typename YT>

@@ -115,4 +115,12 @@ hipError_t launch_act_quant(const void* X, int x_dtype, int64_t M, int64_t K, co
 hipError_t launch_gemm(const void* codes, const float* xscale, int act_bits, int64_t M, int64_t K,
                        const uint8_t* W_packed, const float* alpha, int64_t N, void* Y, int y_dtype,
                        hipStream_t s);
+
+// The whole forward for M = kForwardSmallMaxM = 1 token and K a power of two
+// in [1024, 16384], in one launch (codes and scale stay on chip).
+constexpr int kForwardSmallMaxM = 1;
+bool forward_small_eligible(int64_t M, int64_t K);
+hipError_t launch_forward_small(const void* X, int x_dtype, int64_t M, int64_t K, const float* gain,
+                                const hbl_config& cfg, const uint8_t* W_packed, const float* alpha, int64_t N,
+                                void* Y, int y_dtype, hipStream_t s);
 }  // namespace hbl

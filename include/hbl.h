@@ -150,9 +150,12 @@ hbl_status hbl_gemm(const void* codes, const float* xscale, int32_t act_bits, in
 
 /*
  * The whole H-BitLinear (or plain BitLinear) forward: hbl_quantize_activations
- * into the workspace, then hbl_gemm.  Y [M][N] fp32 or bf16.  ws (16-byte
- * aligned) must hold hbl_workspace_bytes(M, K, cfg): the codes followed by
- * xscale.  Constraints: those of both stages.
+ * into the workspace, then hbl_gemm.  Y [M][N] fp32 or bf16, bit for bit the
+ * result of those two calls.  ws (16-byte aligned) must hold
+ * hbl_workspace_bytes(M, K, cfg) (room for the codes followed by xscale); its
+ * contents afterwards are unspecified: for one token (M = 1) with K a power
+ * of two in [1024, 16384] the whole forward runs as a single launch and the
+ * codes never leave the chip.  Constraints: those of both stages.
  */
 hbl_status hbl_forward(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
                        const uint8_t* W_packed, const float* alpha, int64_t N, const hbl_config* cfg,

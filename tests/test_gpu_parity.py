@@ -273,6 +273,56 @@ def test_forward_chain_3b_sampled(layer):
     _check_layer(layer, workloads.sample_rows(layer.M, 32))
 
 
+# One token and K a power of two in [1024, 16384]: hbl_forward runs as one fused
+# launch (each block quantises the row itself).  It must equal the two stage
+# entry points bit for bit, for every K, width, norm and dtype it serves (and
+# the few-token shapes next to it, which take the two stage kernels).
+SMALL_M_CASES = [
+    # (M, K, N, bits, hadamard, x dtype, y dtype, norm, gain)
+    (1, 8192, 4096, 4, True, "f32", "bf16", hbl.HBL_NORM_RMS, False),
+    (1, 1024, 64, 8, True, "bf16", "f32", hbl.HBL_NORM_RMS, False),
+    (1, 2048, 128, 4, True, "f32", "f32", hbl.HBL_NORM_LN, False),
+    (1, 4096, 256, 8, False, "bf16", "bf16", hbl.HBL_NORM_RMS, True),
+    (1, 16384, 96, 4, True, "bf16", "bf16", hbl.HBL_NORM_LN, True),
+    (1, 8192, 512, 8, True, "f32", "f32", hbl.HBL_NORM_NONE, False),
+    (1, 16384, 32, 8, False, "f32", "bf16", hbl.HBL_NORM_RMS, False),
+    (1, 1024, 48, 4, False, "f32", "f32", hbl.HBL_NORM_LN, False),
+    (1, 4096, 64, 4, True, "bf16", "f32", hbl.HBL_NORM_RMS, True),
+    (2, 2048, 128, 4, True, "f32", "f32", hbl.HBL_NORM_LN, False),
+    (4, 8192, 512, 8, True, "f32", "bf16", hbl.HBL_NORM_RMS, False),
+]
+
+
+@pytest.mark.parametrize("M,K,N,bits,had,xdt,ydt,norm,use_gain", SMALL_M_CASES)
+def test_forward_small_m_matches_stages(M, K, N, bits, had, xdt, ydt, norm, use_gain):
+    import torch
+    _announce("forward small M=%d K=%d N=%d a%d had=%d %s->%s norm=%d gain=%d" % (M, K, N, bits, had, xdt, ydt,
+                                                                                norm, use_gain))
+    rng = np.random.default_rng(M * 7 + K + N + bits)
+    X, _ = workloads.x_outlier_gaussian(rng, M, K, 4, 30.0)
+    if norm == hbl.HBL_NORM_LN:
+        X = (X + np.float32(2.0)).astype(np.float32)
+    W = workloads.w_latent(rng, N, K)
+    gain = (rng.standard_normal(K).astype(np.float32) * 0.5 + 1.0) if use_gain else None
+    Xh = workloads.f32_to_bf16_bits(X) if xdt == "bf16" else X
+    Xd = to_dev(Xh)
+    gd = None if gain is None else to_dev(gain)
+    cfg = hbl.Config(act_bits=bits, hadamard=had, norm=norm)
+    Wp, alpha = hbl.hbl_quantize_weights(to_dev(W))
+    yt = torch.float32 if ydt == "f32" else torch.bfloat16
+    Y = hbl.hbl_forward(Xd, Wp, alpha, N, cfg, y_dtype=yt, gain=gd)
+    codes, xs, _, _ = hbl.hbl_quantize_activations(Xd, cfg, gain=gd)
+    Y2 = hbl.hbl_gemm(codes, xs, bits, K, Wp, alpha, N, y_dtype=yt)
+    _sync()
+    assert np.array_equal(to_host(Y), to_host(Y2))
+    # and against the oracle's arithmetic on those codes and scales
+    q = unpack_codes(to_host(codes), K, bits)
+    Wq = oracle.ternarize(W, to_host(alpha)[0], 1e-5)
+    y_exact = oracle.rescale(oracle.int_gemm(q, Wq), to_host(xs), to_host(alpha)[0])
+    got = to_host(Y)
+    assert np.array_equal(got, y_exact if ydt == "f32" else oracle.f32_to_bf16(y_exact))
+
+
 def test_forward_deterministic_and_empty():
     import torch
     layer = workloads.WO_1P3B
