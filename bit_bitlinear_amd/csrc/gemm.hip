@@ -23,61 +23,104 @@ constexpr uint32_t kDropOffset = 0x80000000u;  // beyond every resource: store d
 
 // ============================================================ prefill GEMM ==
 // Block tile (64*TA) x (64*TB), K step 128, 4 waves in a 2 x 2 grid, each wave
-// (32*TA) x (32*TB) = TA x TB MFMA 32x32x32 tiles.  LDS bandwidth is the
-// binding resource of this kernel (the i8 MFMA itself sustains 4.2 POP/s even
-// at one wave per SIMD with VALU work interleaved), and the fragment bytes a
-// wave reads from LDS per MFMA are A/TB + W/TA (1 KiB and 256 B per 32x32
-// fragment for INT8; 512 B and 256 B for INT4), so the default wave tile is
-// 2 x 4 for large problems (>= 512 such tiles); small ones use 2 x 2 so that
-// every CU still gets at least two blocks.  Both are built for two waves per
-// SIMD (<= 256 registers).  Packed A and W tiles go global -> registers ->
-// LDS (double buffered); kPF register buffers keep the global loads kPF-1 K
-// steps ahead of their use.  Operands are unpacked in registers right before
-// the MFMA.
+// (32*TA) x (32*TB) = TA x TB MFMA 32x32x32 tiles.  The fragment bytes a wave
+// reads from LDS per MFMA are A/TB + W/TA (1 KiB and 256 B per 32x32 fragment
+// for INT8; 512 B and 256 B for INT4), so the default wave tile is 2 x 4 for
+// large problems (>= 512 such tiles); small ones use 2 x 2 so that every CU
+// still gets at least two blocks.  Both are built for two waves per SIMD
+// (<= 256 registers).  Operands are unpacked in registers right before the
+// MFMA.
 //
 // Tile order: blocks are dealt to the 8 XCDs round robin (block b -> XCD b%8);
 // the kernel maps block b to tile (b%8)*T8 + b/8, so every XCD works on a
 // contiguous band of M tiles and its L2 holds that band of A plus all of W.
-constexpr int kBK = 128, kGemmThreads = 256, kPF = 2;
+constexpr int kBK = 128, kGemmThreads = 256;
 
 // k order inside a K step: 32-k MFMA step s of lane group g (lanes 32g..32g+31)
 // takes the 16-k group 4g + s of the step, for both operands.  A lane's
 // weight words for the whole step are then 16 contiguous bytes (one LDS read)
 // and its INT4 codes 32 contiguous bytes.
-template <int BITS, int BM>
-struct ATile {
-    static constexpr int row_bytes = BITS == 8 ? kBK : kBK / 2;  // bytes of one row per K step
-    // padded LDS row (144 B INT8, 80 B INT4): 16 consecutive rows of 16-byte
-    // reads at one column hit disjoint banks
-    static constexpr int stride = row_bytes + 16;
-    static constexpr int chunks = BM * row_bytes / 16;           // 16-byte chunks per tile
-    static constexpr int per_thread = chunks / kGemmThreads;
-    static constexpr int cpr = row_bytes / 16;                   // chunks per row
+//
+// Loads: the packed tiles travel global -> LDS directly (buffer_load_dwordx4
+// ... lds: lane l of a wave instruction writes its 16 bytes at LDS base +
+// 16*l) through a ring of S stages, with no register staging and no LDS store
+// instructions (about 10-15% faster than staging through registers).
+// A wave instruction fills 1 KiB of LDS, so the LDS rows are unpadded; bank
+// conflicts are avoided by an XOR swizzle of the 16-byte chunks instead,
+// chosen so that 16 consecutive rows read at one logical chunk hit 16
+// different 16-byte bank groups:
+//   INT8 codes (128-byte rows): physical chunk = logical ^ ((row >> 1) & 7)
+//   INT4 codes  (64-byte rows): physical chunk = logical ^ ((row >> 2) & 3)
+//   weights     (32-byte rows): physical chunk = logical ^ ((row >> 3) & 1)
+// The swizzle is applied on the global side (each lane fetches the logical
+// chunk that belongs at its LDS position).  Out-of-range rows are zero-filled
+// by the buffer range check, as for register loads.
+template <int BITS, int TA, int TB>
+struct DmaTile {
+    static constexpr int BM = 64 * TA, BN = 64 * TB;
+    static constexpr int a_row = BITS == 8 ? kBK : kBK / 2;  // code bytes per row and K step
+    static constexpr int a_cpr = a_row / 16;                 // 16-byte chunks per code row
+    static constexpr int a_bytes = BM * a_row;
+    static constexpr int w_row = kBK / 4;                    // 32 bytes of packed W per row and K step
+    static constexpr int w_bytes = BN * w_row;
+    static constexpr int stage_bytes = a_bytes + w_bytes;
+    static constexpr int a_inst = a_bytes / 1024 / 4;        // 1 KiB DMA instructions per wave and K step
+    static constexpr int w_inst = w_bytes / 1024 / 4;
+    static constexpr int inst = a_inst + w_inst;
+    static_assert(a_bytes % 4096 == 0 && w_bytes % 4096 == 0, "tile must split into whole wave instructions");
+    static HBL_DEVINL int a_swz(int row) { return BITS == 8 ? (row >> 1) & 7 : (row >> 2) & 3; }
+    static HBL_DEVINL int w_swz(int row) { return (row >> 3) & 1; }
 };
-constexpr int kBRow = kBK / 4;        // 32 bytes of packed W per row and K step
-constexpr int kBStride = kBRow + 16;  // 48 B: 16 consecutive columns of 16-byte reads hit disjoint banks
 
-template <int BITS, int BM, int BN>
-struct Regs {
-    uint4 a[ATile<BITS, BM>::per_thread];
-    uint4 b[BN * kBRow / 16 / kGemmThreads];
-};
+// Raw buffer descriptor words (base, stride 0, byte range, format word) as
+// four scalar registers; the same resource make_rsrc builds.
+HBL_DEVINL v4u rsrc_words(const void* base, int64_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    const int64_t lim = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes);
+    return v4u{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, (uint32_t)lim, 0x00020000u};
+}
 
-template <int BITS, typename YT, int TA, int TB>
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_mfma_kernel(const uint8_t* __restrict__ A,
-                                                                    const float* __restrict__ xscale, int64_t M,
-                                                                    int64_t K, const uint8_t* __restrict__ Wp,
-                                                                    const float* __restrict__ alpha_p, int64_t N,
-                                                                    YT* __restrict__ Y, int tiles_n, int tiles_total) {
-    constexpr int BM = 64 * TA, BN = 64 * TB;
-    using AT = ATile<BITS, BM>;
-    constexpr int kBPerThread = BN * kBRow / 16 / kGemmThreads;
-    __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * AT::stride];
-    __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * kBStride];
+// One LDS-direct load: every lane fetches 16 bytes at voff of the resource and
+// the wave's 64 results land contiguously at LDS byte address lds_addr (taken
+// from M0, which is restored).  Written as inline asm so that the compiler
+// does not treat every later LDS read as dependent on it: the kernel waits
+// for these loads itself (wait_vmcnt) before the barrier that publishes them.
+// The instruction has no register result.
+HBL_DEVINL void lds_dma16(v4u desc, uint32_t lds_addr, uint32_t voff) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_addr), "v"(voff), "s"(desc)
+        : "memory");
+}
+
+// s_waitcnt that waits for the vector-memory counter only (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+HBL_DEVINL void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier with no implied memory wait (the caller has waited for
+// what it publishes); the memory clobber keeps LDS accesses on their side.
+HBL_DEVINL void barrier_no_wait() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int BITS, typename YT, int TA, int TB, int S>
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_dma_kernel(const uint8_t* __restrict__ A,
+                                                                   const float* __restrict__ xscale, int64_t M,
+                                                                   int64_t K, const uint8_t* __restrict__ Wp,
+                                                                   const float* __restrict__ alpha_p, int64_t N,
+                                                                   YT* __restrict__ Y, int tiles_n, int tiles_total) {
+    using DT = DmaTile<BITS, TA, TB>;
+    constexpr int BM = DT::BM, BN = DT::BN;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * DT::stage_bytes];
     __shared__ __attribute__((aligned(16))) float xs_tile[BM];  // per-token scales of this tile's rows (0 past M)
 
-    // XCD-aware tile order (see above); falls back to linear order when the
-    // tile count is not a multiple of 8.
     const int b = blockIdx.x;
     const int tile = (tiles_total % 8 == 0) ? (b % 8) * (tiles_total / 8) + b / 8 : b;
     const int64_t m0 = (int64_t)(tile / tiles_n) * BM;
@@ -91,36 +134,37 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_mfma_kernel(const uint8_
     const int64_t w_ld = K / 4;         // bytes per weight row
     const int KT = (int)(K / kBK);
 
-    // rows past M (columns past N) lie outside these resources and load as zeros
-    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A + m0 * a_ld, (M - m0) * a_ld);
-    const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(Wp + n0 * w_ld, (N - n0) * w_ld);
-    auto load_tile = [&](Regs<BITS, BM, BN>& r, int kt) {
+    const v4u a_desc = rsrc_words(A + m0 * a_ld, (M - m0) * a_ld);
+    const v4u w_desc = rsrc_words(Wp + n0 * w_ld, (N - n0) * w_ld);
+
+    // Per-lane global offsets (within one K step) of the chunks this lane
+    // fetches in each of its DMA instructions; the K step adds kt * row bytes.
+    uint32_t a_off[DT::a_inst], w_off[DT::w_inst];
 #pragma unroll
-        for (int i = 0; i < AT::per_thread; i++) {
-            const int q = tid + i * kGemmThreads;
-            const int row = q / AT::cpr, c16 = q % AT::cpr;
-            r.a[i] = buf_load16(a_rsrc, (uint32_t)(row * a_ld + kt * AT::row_bytes + c16 * 16));
-        }
+    for (int u = 0; u < DT::a_inst; u++) {
+        const int c = (wave * DT::a_inst + u) * 64 + lane;  // physical chunk index in the tile
+        const int row = c / DT::a_cpr, p = c % DT::a_cpr;
+        a_off[u] = (uint32_t)(row * a_ld + (p ^ DT::a_swz(row)) * 16);
+    }
 #pragma unroll
-        for (int i = 0; i < kBPerThread; i++) {
-            const int q = tid + i * kGemmThreads;
-            const int row = q / (kBRow / 16), c16 = q % (kBRow / 16);
-            r.b[i] = buf_load16(w_rsrc, (uint32_t)(row * w_ld + kt * kBRow + c16 * 16));
-        }
-    };
-    auto store_tile = [&](const Regs<BITS, BM, BN>& r, int st) {
+    for (int u = 0; u < DT::w_inst; u++) {
+        const int c = (wave * DT::w_inst + u) * 64 + lane;
+        const int row = c / 2, p = c % 2;
+        w_off[u] = (uint32_t)(row * w_ld + (p ^ DT::w_swz(row)) * 16);
+    }
+    // LDS byte address of the ring (wave-uniform)
+    const uint32_t smem_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+    auto issue = [&](int kt, int st) {
+        const uint32_t base = smem_addr + (uint32_t)(st * DT::stage_bytes);
 #pragma unroll
-        for (int i = 0; i < AT::per_thread; i++) {
-            const int q = tid + i * kGemmThreads;
-            const int row = q / AT::cpr, c16 = q % AT::cpr;
-            *reinterpret_cast<uint4*>(&As[st][row * AT::stride + c16 * 16]) = r.a[i];
-        }
+        for (int u = 0; u < DT::a_inst; u++)
+            lds_dma16(a_desc, __builtin_amdgcn_readfirstlane(base + (uint32_t)((wave * DT::a_inst + u) * 1024)),
+                      a_off[u] + (uint32_t)(kt * DT::a_row));
 #pragma unroll
-        for (int i = 0; i < kBPerThread; i++) {
-            const int q = tid + i * kGemmThreads;
-            const int row = q / (kBRow / 16), c16 = q % (kBRow / 16);
-            *reinterpret_cast<uint4*>(&Bs[st][row * kBStride + c16 * 16]) = r.b[i];
-        }
+        for (int u = 0; u < DT::w_inst; u++)
+            lds_dma16(w_desc,
+                      __builtin_amdgcn_readfirstlane(base + (uint32_t)(DT::a_bytes + (wave * DT::w_inst + u) * 1024)),
+                      w_off[u] + (uint32_t)(kt * DT::w_row));
     };
 
     v16i acc[TA][TB];
@@ -132,37 +176,34 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_mfma_kernel(const uint8_
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0;
 
     const int lr = lane & 31;  // row (A) / column (W) inside a 32-wide MFMA tile
-    const int lg = lane >> 5;  // which 16-k half of the 32-k MFMA step
-    // Per K step a lane reads, for each of its TB columns, the four weight
-    // words of its k groups (one 16-byte read), and for each of its TA rows
-    // 16 bytes per MFMA step (INT8) or 32 bytes for all four (INT4).
+    const int lg = lane >> 5;  // lane group: takes the 16-k groups 4*lg .. 4*lg+3 of each K step
     struct AFrag {
         v4i a[TA];
     };
-    auto read_a = [&](AFrag& f, int st, int s) {
+    auto read_a = [&](AFrag& f, const uint8_t* stage, int rd) {
 #pragma unroll
         for (int i = 0; i < TA; i++) {
             const int row = wm * 32 * TA + i * 32 + lr;
-            const uint4 q = *reinterpret_cast<const uint4*>(&As[st][row * AT::stride + (BITS == 8 ? (4 * lg + s) * 16 : lg * 32 + s * 16)]);
+            const int g = BITS == 8 ? 4 * lg + rd : 2 * lg + rd;  // logical 16-byte chunk
+            const uint4 q = *reinterpret_cast<const uint4*>(stage + row * DT::a_row + ((g ^ DT::a_swz(row)) * 16));
             f.a[i][0] = (int)q.x; f.a[i][1] = (int)q.y; f.a[i][2] = (int)q.z; f.a[i][3] = (int)q.w;
         }
     };
-    // Software pipeline: the A reads of step s+1 (INT8) or of the second
-    // half (INT4) are issued before the MFMAs that precede them.
     auto compute = [&](int st) {
+        const uint8_t* stage = smem + st * DT::stage_bytes;
         uint4 wq[TB];
 #pragma unroll
         for (int j = 0; j < TB; j++) {
             const int col = wn * 32 * TB + j * 32 + lr;
-            wq[j] = *reinterpret_cast<const uint4*>(&Bs[st][col * kBStride + lg * 16]);
+            wq[j] = *reinterpret_cast<const uint4*>(stage + DT::a_bytes + col * DT::w_row + ((lg ^ DT::w_swz(col)) * 16));
         }
         constexpr int kReads = BITS == 8 ? kBK / 32 : kBK / 64;  // A reads per K step
         AFrag f[2];
-        read_a(f[0], st, 0);
+        read_a(f[0], stage, 0);
 #pragma unroll
         for (int s = 0; s < kBK / 32; s++) {
             const int rd = BITS == 8 ? s : s / 2;
-            if ((BITS == 8 || s % 2 == 0) && rd + 1 < kReads) read_a(f[(rd + 1) & 1], st, rd + 1);
+            if ((BITS == 8 || s % 2 == 0) && rd + 1 < kReads) read_a(f[(rd + 1) & 1], stage, rd + 1);
             const AFrag& cur = f[rd & 1];
             v4i bw[TB];
 #pragma unroll
@@ -188,28 +229,19 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_mfma_kernel(const uint8_
         xs_tile[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xs_rsrc, r * 4, 0, 0));
     }
 
-    // prologue: tiles 0..kPF-1 in flight, tile 0 in LDS stage 0
-    Regs<BITS, BM, BN> R[kPF];
+    // prologue: K steps 0..S-2 in flight (past the last step the loads repeat
+    // step KT-1, so every wave always has the same number in flight)
 #pragma unroll
-    for (int u = 0; u < kPF; u++) load_tile(R[u], min(u, KT - 1));
-    store_tile(R[0], 0);
-    __syncthreads();
-
-    // Loads and LDS stores are unconditional (past the last tile they re-load
-    // tile KT-1 and fill the idle LDS stage), so the compiler sees the same
-    // number of loads in flight on every path and waits only for the oldest.
-    for (int kt0 = 0; kt0 < KT; kt0 += kPF) {
-#pragma unroll
-        for (int u = 0; u < kPF; u++) {
-            const int kt = kt0 + u;
-            // R[(u+1)%kPF] holds tile kt+1; R[u] held tile kt (already in LDS)
-            store_tile(R[(u + 1) % kPF], (kt + 1) & 1);
-            load_tile(R[u], min(kt + kPF, KT - 1));
-            if (kt < KT) compute(kt & 1);
-            __syncthreads();
-        }
+    for (int u = 0; u < S - 1; u++) issue(min(u, KT - 1), u);
+    __syncthreads();  // xs_tile
+    for (int kt = 0; kt < KT; kt++) {
+        wait_vmcnt<(S - 2) * DT::inst>();  // this wave's loads of step kt have landed
+        barrier_no_wait();                 // ... and every wave's; stage (kt-1)%S is free
+        issue(min(kt + S - 1, KT - 1), (kt + S - 1) % S);
+        compute(kt % S);
     }
-
+    wait_vmcnt<0>();  // no LDS-direct load may still be in flight when the block ends
+    __syncthreads();
     // ---- epilogue: lane holds column lr, rows 8*(r/4) + 4*lg + r%4 of each 32x32 tile.
     // Y is written through a buffer resource over this tile's rows: rows past M
     // fall outside it, columns past N start from an out-of-range offset; both
@@ -406,6 +438,9 @@ hipError_t launch_gemv_small(const uint8_t* A, const float* xscale, int64_t M, i
     return hipGetLastError();
 }
 
+// Ring depth 3 (loads two K steps ahead); 2 and 4 measured within 3% of it.
+constexpr int kDmaStages = 3;
+
 template <int BITS, typename YT>
 hipError_t launch_typed(const uint8_t* A, const float* xscale, int64_t M, int64_t K, const uint8_t* Wp,
                         const float* alpha, int64_t N, YT* Y, hipStream_t s) {
@@ -432,12 +467,12 @@ hipError_t launch_typed(const uint8_t* A, const float* xscale, int64_t M, int64_
     if (big_tiles >= 512) {
         const int tiles_n = (int)((N + 255) / 256);
         const int tiles_total = (int)big_tiles;
-        hipLaunchKernelGGL((gemm_mfma_kernel<BITS, YT, 2, 4>), dim3(tiles_total), dim3(kGemmThreads), 0, s, A, xscale,
+        hipLaunchKernelGGL((gemm_dma_kernel<BITS, YT, 2, 4, kDmaStages>), dim3(tiles_total), dim3(kGemmThreads), 0, s, A, xscale,
                            M, K, Wp, alpha, N, Y, tiles_n, tiles_total);
     } else {
         const int tiles_n = (int)((N + 127) / 128);
         const int tiles_total = tiles_n * (int)((M + 127) / 128);
-        hipLaunchKernelGGL((gemm_mfma_kernel<BITS, YT, 2, 2>), dim3(tiles_total), dim3(kGemmThreads), 0, s, A, xscale,
+        hipLaunchKernelGGL((gemm_dma_kernel<BITS, YT, 2, 2, kDmaStages>), dim3(tiles_total), dim3(kGemmThreads), 0, s, A, xscale,
                            M, K, Wp, alpha, N, Y, tiles_n, tiles_total);
     }
     return hipGetLastError();
