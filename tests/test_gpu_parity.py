@@ -144,6 +144,8 @@ GEMM_CASES = [
     (2, 1024, 32, 4), (3, 8192, 64, 4), (1, 4096, 1024, 4), (2, 512, 64, 8), (3, 32768, 32, 4),
     # >= 512 tiles of 128 x 256: the large-tile kernel, ragged in M and N
     (4100, 256, 4000, 4), (4100, 384, 4000, 8),
+    # the largest K (accumulators up to 2^28 before the shift back)
+    (200, 32768, 256, 8), (130, 32768, 272, 4),
 ]
 
 
@@ -161,6 +163,28 @@ def test_gemm_int32_accumulators_exact(M, K, N, bits):
     Y = hbl.hbl_gemm(to_dev(packed), ones, bits, K, to_dev(Wp), one, N)
     _sync()
     acc = oracle.int_gemm(q, Wq)
+    assert np.array_equal(to_host(Y), acc.astype(np.float32))
+
+
+@pytest.mark.parametrize("M,K,bits", [(130, 32768, 8), (130, 32768, 4), (20, 32768, 8), (3, 16384, 4), (1, 16384, 8)])
+def test_gemm_extreme_accumulators(M, K, bits):
+    """Largest |acc| the formats allow: every code at the negative end of its
+    range against all -1 weights (and the positive end in alternate rows)."""
+    _announce("gemm extremes M=%d K=%d a%d" % (M, K, bits))
+    N = 64
+    lo, hi = (-128, 127) if bits == 8 else (-8, 7)
+    q = np.full((M, K), lo, dtype=np.int8)
+    q[1::2] = hi
+    packed = q if bits == 8 else oracle.pack_int4(q)
+    Wq = -np.ones((N, K), dtype=np.int8)
+    Wq[:, : K // 2][N // 2:] = 1
+    import torch
+    ones = torch.ones(M, dtype=torch.float32, device="cuda:0")
+    one = torch.ones(1, dtype=torch.float32, device="cuda:0")
+    Y = hbl.hbl_gemm(to_dev(packed), ones, bits, K, to_dev(oracle.pack_ternary(Wq)), one, N)
+    _sync()
+    acc = oracle.int_gemm(q, Wq)
+    assert np.abs(acc).max() == -lo * K
     assert np.array_equal(to_host(Y), acc.astype(np.float32))
 
 
