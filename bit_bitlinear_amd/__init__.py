@@ -17,7 +17,7 @@ import re
 __all__ = [
     "HblError", "HblLibraryError", "Config", "load_library", "declared_symbols",
     "hbl_packed_weight_bytes", "hbl_weight_workspace_bytes", "hbl_quantize_weights",
-    "hbl_workspace_bytes", "hbl_quantize_activations", "hbl_gemm", "hbl_forward",
+    "hbl_workspace_bytes", "hbl_quantize_activations", "hbl_gemm", "hbl_forward", "hbl_forward_latent",
     "hbl_status_string", "hbl_last_hip_error",
     "HBL_F32", "HBL_BF16", "HBL_NORM_RMS", "HBL_NORM_LN", "HBL_NORM_NONE",
     "HBL_A4_ABSMEAN_SQRT7", "HBL_A4_ABSMAX_7",
@@ -98,6 +98,7 @@ def load_library(path: str | None = None):
         "hbl_quantize_activations": [P, I32, I64, I64, P, PCFG, P, P, P, P, P],
         "hbl_gemm": [P, P, I32, I64, I64, P, P, I64, P, I32, P],
         "hbl_forward": [P, I32, I64, I64, P, P, P, I64, PCFG, P, I32, P, SZ, P],
+        "hbl_forward_latent": [P, I32, I64, I64, P, P, I32, I64, F, PCFG, P, P, P, I32, P, SZ, P, SZ, P],
     }
     for name, argtypes in sigs.items():
         f = getattr(lib, name)
@@ -269,3 +270,35 @@ def hbl_forward(X, W_packed, alpha, N: int, cfg: Config, y_dtype=None, gain=None
                                           ctypes.byref(c), _ptr(Y), _dtype_code(Y), _ptr(ws),
                                           ws.numel() * ws.element_size(), _stream(stream)))
     return Y
+
+
+def hbl_forward_latent(X, W, cfg: Config, eps: float = 1e-5, y_dtype=None, gain=None, W_packed=None, alpha=None,
+                       Y=None, ws=None, wws=None, stream=None):
+    """Ternarise latent weights W [N][K] and run the forward of X [M][K] with
+    them (hbl_quantize_weights + hbl_forward, fused to three launches).
+    Returns (Y [M][N], W_packed uint8 [N][K/4], alpha float32 [1])."""
+    torch = _torch()
+    lib = load_library()
+    _dev(X, "X"); _dev(W, "W"); _dev(gain, "gain")
+    M, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("W has %d columns, X has %d" % (W.shape[1], K))
+    if W_packed is None:
+        W_packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+    if alpha is None:
+        alpha = torch.empty(1, dtype=torch.float32, device=W.device)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=y_dtype or X.dtype, device=X.device)
+    if ws is None:
+        ws = torch.empty(max(1, hbl_workspace_bytes(M, K, cfg)), dtype=torch.uint8, device=X.device)
+    if wws is None:
+        wws = torch.empty(hbl_weight_workspace_bytes(N, K), dtype=torch.uint8, device=W.device)
+    for t, n in ((W_packed, "W_packed"), (alpha, "alpha"), (Y, "Y"), (ws, "ws"), (wws, "wws")):
+        _dev(t, n)
+    c = cfg.c()
+    _check("hbl_forward_latent", lib.hbl_forward_latent(
+        _ptr(X), _dtype_code(X), M, K, _ptr(gain), _ptr(W), _dtype_code(W), N, float(eps), ctypes.byref(c),
+        _ptr(W_packed), _ptr(alpha), _ptr(Y), _dtype_code(Y), _ptr(ws), ws.numel() * ws.element_size(),
+        _ptr(wws), wws.numel() * wws.element_size(), _stream(stream)))
+    return Y, W_packed, alpha

@@ -1,0 +1,134 @@
+// act_pack.hip -- one launch that runs the per-token activation quantisation
+// (norm, online Hadamard, per-token scale, codes) and the weight packing of
+// the per-tensor absmean ternarisation side by side (gfx950).
+//
+// The two steps do not depend on each other: the codes need only X, the
+// packed weights only W and the partial |W| sums of the launch before.  On
+// one stream each would otherwise be a launch of its own, and at the sizes of
+// one layer both are bound by launch and memory latency rather than by
+// throughput, so sharing a grid overlaps them.  M blocks run the row
+// routine of act_row.h (the same code and thread count as the standalone
+// activation kernel, so codes and scales are bit-identical); the other blocks
+// run the packing block routine of weight_pack.h with the same thread count
+// (each packed word depends only on its 16 weights and alpha, so the packed
+// bytes are identical too).  The two kinds are interleaved over the grid.
+//
+// Follows the "新智元: 微软 BitNet v2" repost, section "H-BitLinear模块".
+#include "act_row.h"
+#include "weight_pack.h"
+
+namespace hbl {
+namespace {
+
+template <int LK, int NT, typename Tin, int BITS, bool HAD, typename TW>
+__global__ __launch_bounds__(NT) void act_pack_kernel(const Tin* __restrict__ X, int64_t M,
+                                                      const float* __restrict__ gain, int norm, float norm_eps,
+                                                      float quant_eps, int a4_mode, uint8_t* __restrict__ codes,
+                                                      float* __restrict__ xscale, const TW* __restrict__ W,
+                                                      int64_t n_groups, int64_t count, float w_eps,
+                                                      const double* __restrict__ partial, int n_partial,
+                                                      uint32_t* __restrict__ Wp, float* __restrict__ alpha) {
+    using S = ActShape<LK, NT, Tin>;
+    extern __shared__ __attribute__((aligned(16))) float lds[];  // float4 accesses
+    __shared__ ActPartF<LK, NT, Tin> partf;
+    __shared__ ActPartD<LK, NT, Tin> partd;
+    // The P packing blocks are spread evenly among the M + P blocks (blocks
+    // are dispatched in index order, so a contiguous range of either kind
+    // would run mostly alone): block b packs iff floor((b+1)P/T) > floor(bP/T);
+    // floor(bP/T) blocks before it pack, so b is row b - floor(bP/T) or
+    // packing block floor(bP/T).
+    const int64_t b = blockIdx.x, T = (int64_t)gridDim.x, P = T - M;
+    const int64_t p_lo = b * P / T, p_hi = (b + 1) * P / T;
+    if (p_hi == p_lo) {
+        const int64_t row = b - p_lo;
+        ActRegs<LK, NT, Tin> v;
+        act_row_load<LK, NT, Tin>(X + row * S::K, v);
+        act_row_quantise<LK, NT, Tin, BITS, HAD>(v, gain, norm, norm_eps, quant_eps, a4_mode, lds, partf, partd,
+                                                 codes + row * (S::K * BITS / 8), xscale + row, nullptr, nullptr);
+    } else {
+        wq_pack_block<TW, NT>(W, n_groups, count, w_eps, partial, n_partial, Wp, alpha, p_lo);
+    }
+}
+
+template <int LK, typename Tin, int BITS, bool HAD, typename TW>
+hipError_t launch_ap(const Tin* X, int64_t M, const float* gain, const hbl_config& cfg, void* codes, float* xscale,
+                     const TW* W, int64_t NK, float w_eps, const double* partial, int n_partial, uint8_t* Wp,
+                     float* alpha, hipStream_t s) {
+    constexpr int NT = threads_for(LK);
+    const size_t lds_bytes = HAD ? (size_t)ActShape<LK, NT, Tin>::lds_floats * sizeof(float) : 0;
+    auto kern = act_pack_kernel<LK, NT, Tin, BITS, HAD, TW>;
+    static bool attr_set = false;  // one attribute call per instantiation
+    if (!attr_set && lds_bytes > 0) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int64_t n_groups = NK / 16;
+    const int64_t pack_blocks = (n_groups + 2 * NT - 1) / (2 * NT);
+    const int64_t grid = M + pack_blocks;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NT), lds_bytes, s, X, M, gain, cfg.norm, cfg.norm_eps,
+                       cfg.quant_eps, cfg.a4_mode, (uint8_t*)codes, xscale, W, n_groups, NK, w_eps, partial,
+                       n_partial, (uint32_t*)Wp, alpha);
+    return hipGetLastError();
+}
+
+template <typename Tin, int BITS, bool HAD, typename TW>
+hipError_t dispatch_k(const Tin* X, int64_t M, int64_t K, const float* gain, const hbl_config& cfg, void* codes,
+                      float* xscale, const TW* W, int64_t NK, float w_eps, const double* partial, int n_partial,
+                      uint8_t* Wp, float* alpha, hipStream_t s) {
+#define HBL_AP(LK) launch_ap<LK, Tin, BITS, HAD, TW>(X, M, gain, cfg, codes, xscale, W, NK, w_eps, partial, n_partial, Wp, alpha, s)
+    switch (K) {
+        case 256: return HBL_AP(8);
+        case 512: return HBL_AP(9);
+        case 1024: return HBL_AP(10);
+        case 2048: return HBL_AP(11);
+        case 4096: return HBL_AP(12);
+        case 8192: return HBL_AP(13);
+        case 16384: return HBL_AP(14);
+        case 32768: return HBL_AP(15);
+        default: return hipErrorInvalidValue;
+    }
+#undef HBL_AP
+}
+
+template <typename Tin, typename TW>
+hipError_t dispatch_mode(const Tin* X, int64_t M, int64_t K, const float* gain, const hbl_config& cfg, void* codes,
+                         float* xscale, const TW* W, int64_t NK, float w_eps, const double* partial, int n_partial,
+                         uint8_t* Wp, float* alpha, hipStream_t s) {
+    if (cfg.act_bits == 8)
+        return cfg.hadamard ? dispatch_k<Tin, 8, true, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
+                                                          n_partial, Wp, alpha, s)
+                            : dispatch_k<Tin, 8, false, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
+                                                           n_partial, Wp, alpha, s);
+    return cfg.hadamard ? dispatch_k<Tin, 4, true, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
+                                                      n_partial, Wp, alpha, s)
+                        : dispatch_k<Tin, 4, false, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
+                                                       n_partial, Wp, alpha, s);
+}
+
+template <typename Tin>
+hipError_t dispatch_w(const Tin* X, int64_t M, int64_t K, const float* gain, const hbl_config& cfg, void* codes,
+                      float* xscale, const void* W, int w_dtype, int64_t NK, float w_eps, const double* partial,
+                      int n_partial, uint8_t* Wp, float* alpha, hipStream_t s) {
+    if (w_dtype == HBL_F32)
+        return dispatch_mode<Tin, float>(X, M, K, gain, cfg, codes, xscale, (const float*)W, NK, w_eps, partial,
+                                         n_partial, Wp, alpha, s);
+    return dispatch_mode<Tin, uint16_t>(X, M, K, gain, cfg, codes, xscale, (const uint16_t*)W, NK, w_eps, partial,
+                                        n_partial, Wp, alpha, s);
+}
+
+}  // namespace
+
+hipError_t launch_act_and_pack(const void* X, int x_dtype, int64_t M, int64_t K, const float* gain,
+                               const hbl_config& cfg, void* codes, float* xscale, const void* W, int w_dtype,
+                               int64_t NK, float w_eps, const double* partial, int n_partial, uint8_t* W_packed,
+                               float* alpha, hipStream_t s) {
+    if (x_dtype == HBL_F32)
+        return dispatch_w<float>((const float*)X, M, K, gain, cfg, codes, xscale, W, w_dtype, NK, w_eps, partial,
+                                 n_partial, W_packed, alpha, s);
+    return dispatch_w<uint16_t>((const uint16_t*)X, M, K, gain, cfg, codes, xscale, W, w_dtype, NK, w_eps, partial,
+                                n_partial, W_packed, alpha, s);
+}
+
+}  // namespace hbl

@@ -23,6 +23,10 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr int64_t kMaxGemmM = int64_t(1) << 23;
 constexpr int64_t kMaxGemmN = int64_t(1) << 20;  // keeps a 128-row output tile's byte offsets in 32 bits
+// Activation quantisation and weight packing share a grid up to this row
+// length; for longer rows (one workgroup of 128-512 threads per row, 17-147
+// KiB of LDS) the shared grid measured no faster than two launches.
+constexpr int64_t kFuseActPackMaxK = 2048;
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 
 hbl_status check_weight_shape(int64_t N, int64_t K) {
@@ -185,6 +189,52 @@ hbl_status hbl_forward(const void* X, int32_t x_dtype, int64_t M, int64_t K, con
                                          (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     e = hbl::launch_gemm(codes, xscale, cfg->act_bits, M, K, W_packed, alpha, N, Y, y_dtype, (hipStream_t)stream);
+    return e == hipSuccess ? HBL_OK : hip_fail(e);
+}
+
+hbl_status hbl_forward_latent(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain, const void* W,
+                              int32_t w_dtype, int64_t N, float w_eps, const hbl_config* cfg, uint8_t* W_packed,
+                              float* alpha, void* Y, int32_t y_dtype, void* ws, size_t ws_bytes, void* wws,
+                              size_t wws_bytes, void* stream) {
+    hbl_status st = check_config(cfg);
+    if (st != HBL_OK) return st;
+    if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype) || !dtype_ok(w_dtype)) return HBL_ERR_DTYPE;
+    if ((st = check_weight_shape(N, K)) != HBL_OK) return st;
+    if ((st = check_act_shape(M, K)) != HBL_OK) return st;
+    if ((st = check_gemm_shape(M, K, N)) != HBL_OK) return st;
+    if (!(w_eps >= 0.f)) return HBL_ERR_SHAPE;
+    if (!W || !W_packed || !alpha || !wws) return HBL_ERR_NULL;
+    if (M > 0 && (!X || !Y || !ws)) return HBL_ERR_NULL;
+    if (!aligned16(W) || !aligned16(W_packed) || !aligned(alpha, 4) || !aligned(wws, 8)) return HBL_ERR_ALIGN;
+    if (M > 0 && (!aligned16(X) || !aligned16(Y) || !aligned16(ws) || !aligned(gain, 4))) return HBL_ERR_ALIGN;
+    const int n_partial = hbl::weight_partial_count(N * K);
+    if (wws_bytes < (size_t)n_partial * sizeof(double)) return HBL_ERR_WORKSPACE;
+    const size_t cb = round_up(codes_bytes(M, K, cfg->act_bits), 256);
+    if (M > 0 && ws_bytes < cb + round_up((size_t)M * sizeof(float), 256)) return HBL_ERR_WORKSPACE;
+    const hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (M == 0 || hbl::forward_small_eligible(M, K)) {
+        // no rows, or one token whose whole forward is a single launch
+        e = hbl::launch_weight_quant(W, w_dtype, N, K, w_eps, W_packed, alpha, (double*)wws, n_partial, s);
+        if (e == hipSuccess && M > 0)
+            e = hbl::launch_forward_small(X, x_dtype, M, K, gain, *cfg, W_packed, alpha, N, Y, y_dtype, s);
+        return e == hipSuccess ? HBL_OK : hip_fail(e);
+    }
+    void* codes = ws;
+    float* xscale = (float*)((uint8_t*)ws + cb);
+    if (K <= kFuseActPackMaxK) {
+        // short rows: the activation blocks and the packing blocks share one grid
+        e = hbl::launch_weight_partial(W, w_dtype, N * K, (double*)wws, n_partial, s);
+        if (e == hipSuccess)
+            e = hbl::launch_act_and_pack(X, x_dtype, M, K, gain, *cfg, codes, xscale, W, w_dtype, N * K, w_eps,
+                                         (const double*)wws, n_partial, W_packed, alpha, s);
+    } else {
+        e = hbl::launch_weight_quant(W, w_dtype, N, K, w_eps, W_packed, alpha, (double*)wws, n_partial, s);
+        if (e == hipSuccess)
+            e = hbl::launch_act_quant(X, x_dtype, M, K, gain, *cfg, codes, xscale, nullptr, nullptr, s);
+    }
+    if (e == hipSuccess)
+        e = hbl::launch_gemm(codes, xscale, cfg->act_bits, M, K, W_packed, alpha, N, Y, y_dtype, s);
     return e == hipSuccess ? HBL_OK : hip_fail(e);
 }
 

@@ -107,6 +107,17 @@ namespace hbl {
 hipError_t launch_weight_quant(const void* W, int w_dtype, int64_t N, int64_t K, float eps, uint8_t* W_packed,
                                float* alpha, double* partial, int n_partial, hipStream_t s);
 int weight_partial_count(int64_t count);
+// the first of the two weight launches alone: partial |W| sums into `partial`
+hipError_t launch_weight_partial(const void* W, int w_dtype, int64_t count, double* partial, int n_partial,
+                                 hipStream_t s);
+
+// Activation quantisation of M rows and the weight packing (after
+// launch_weight_partial) in one launch: blocks [0, M) quantise rows, the
+// rest pack weight groups.
+hipError_t launch_act_and_pack(const void* X, int x_dtype, int64_t M, int64_t K, const float* gain,
+                               const hbl_config& cfg, void* codes, float* xscale, const void* W, int w_dtype,
+                               int64_t NK, float w_eps, const double* partial, int n_partial, uint8_t* W_packed,
+                               float* alpha, hipStream_t s);
 
 hipError_t launch_act_quant(const void* X, int x_dtype, int64_t M, int64_t K, const float* gain,
                             const hbl_config& cfg, void* codes, float* xscale, float* z_debug, float* s_debug,

@@ -161,6 +161,24 @@ hbl_status hbl_forward(const void* X, int32_t x_dtype, int64_t M, int64_t K, con
                        const uint8_t* W_packed, const float* alpha, int64_t N, const hbl_config* cfg,
                        void* Y, int32_t y_dtype, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * The whole hot path from latent weights, for callers that re-ternarise the
+ * weights on every forward (training with latent weights): the results of
+ * hbl_quantize_weights(W, w_dtype, N, K, w_eps, W_packed, alpha, wws, ...)
+ * followed by hbl_forward(X, ..., W_packed, alpha, ..., Y, ..., ws, ...),
+ * bit for bit.  For K <= 2048 it takes three launches instead of four: the
+ * activation quantisation and the weight packing share one grid (they do not
+ * depend on each other).  W_packed and alpha are outputs (device memory the caller
+ * owns, reusable by hbl_forward).  ws must hold hbl_workspace_bytes(M, K,
+ * cfg) and wws hbl_weight_workspace_bytes(N, K); contents afterwards are
+ * unspecified.  M = 0 only ternarises the weights (X, Y, ws may be NULL).
+ * Constraints: those of hbl_quantize_weights and hbl_forward together.
+ */
+hbl_status hbl_forward_latent(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
+                              const void* W, int32_t w_dtype, int64_t N, float w_eps, const hbl_config* cfg,
+                              uint8_t* W_packed, float* alpha, void* Y, int32_t y_dtype, void* ws,
+                              size_t ws_bytes, void* wws, size_t wws_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* hbl_status_string(hbl_status status);
 

@@ -20,7 +20,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = hbl.declared_symbols()
-    assert len(names) == 9
+    assert len(names) == 10
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
 
@@ -110,3 +110,24 @@ def test_forward_validation(lib):
     assert f(A16, 0, 64, 1024, None, None, A16b, 256, ctypes.byref(cfg), A16b, 0, A16b, need, None) == 1
     assert f(A16, 0, 64, 1024, None, A16b, A16b, 256, None, A16b, 0, A16b, need, None) == 1
     assert f(A16, 0, 0, 1024, None, A16b, A16b, 256, ctypes.byref(cfg), A16b, 0, A16b, 0, None) == 0
+
+
+def test_forward_latent_validation(lib):
+    cfg = hbl.Config(act_bits=8).c()
+    f = lib.hbl_forward_latent
+    M, K, N = 64, 1024, 256
+    need = hbl.hbl_workspace_bytes(M, K, hbl.Config(act_bits=8))
+    wneed = hbl.hbl_weight_workspace_bytes(N, K)
+
+    def call(X=A16, xdt=0, M=M, K=K, W=A16b, wdt=0, N=N, eps=1e-5, c=ctypes.byref(cfg), Wp=A16b, alpha=A16b,
+             Y=A16b, ydt=0, ws=A16b, wsb=need, wws=A16b, wwsb=wneed):
+        return f(X, xdt, M, K, None, W, wdt, N, eps, c, Wp, alpha, Y, ydt, ws, wsb, wws, wwsb, None)
+
+    assert call(wdt=4) == 5 and call(xdt=2) == 5 and call(ydt=7) == 5
+    assert call(K=1008) == 3                         # a multiple of 16 but not a power of two
+    assert call(N=250) == 4                          # N % 16
+    assert call(eps=-1.0) == 2
+    assert call(W=None) == 1 and call(Wp=None) == 1 and call(alpha=None) == 1 and call(wws=None) == 1
+    assert call(X=None) == 1 and call(ws=None) == 1 and call(c=None) == 1
+    assert call(W=MIS) == 4 and call(X=MIS) == 4
+    assert call(wsb=need - 1) == 7 and call(wwsb=wneed - 1) == 7

@@ -347,6 +347,42 @@ def test_forward_small_m_matches_stages(M, K, N, bits, had, xdt, ydt, norm, use_
     assert np.array_equal(got, y_exact if ydt == "f32" else oracle.f32_to_bf16(y_exact))
 
 
+# hbl_forward_latent: weights ternarised and the forward run in three launches
+# (activation quantisation and weight packing share a grid); Y, W_packed and
+# alpha must equal hbl_quantize_weights + hbl_forward bit for bit.
+LATENT_CASES = [
+    # (M, K, N, bits, hadamard, x dtype, W dtype, y dtype)
+    (300, 2048, 2048, 8, True, "bf16", "f32", "bf16"),
+    (37, 256, 272, 4, True, "f32", "f32", "f32"),
+    (16, 8192, 4096, 4, True, "f32", "f32", "bf16"),
+    (1, 8192, 1024, 4, True, "f32", "bf16", "bf16"),
+    (129, 4096, 512, 4, False, "bf16", "bf16", "bf16"),
+    (70, 32768, 96, 8, True, "bf16", "f32", "f32"),
+    (0, 2048, 512, 8, True, "bf16", "f32", "bf16"),
+]
+
+
+@pytest.mark.parametrize("M,K,N,bits,had,xdt,wdt,ydt", LATENT_CASES)
+def test_forward_latent_matches_two_calls(M, K, N, bits, had, xdt, wdt, ydt):
+    import torch
+    _announce("forward_latent M=%d K=%d N=%d a%d had=%d x %s W %s y %s" % (M, K, N, bits, had, xdt, wdt, ydt))
+    rng = np.random.default_rng(M + K + N + bits)
+    X, _ = workloads.x_outlier_gaussian(rng, max(M, 1), K, 4, 30.0)
+    X = X[:M]
+    W = workloads.w_latent(rng, N, K)
+    Xd = to_dev(workloads.f32_to_bf16_bits(X) if xdt == "bf16" else X)
+    Wd = to_dev(workloads.f32_to_bf16_bits(W) if wdt == "bf16" else W)
+    cfg = hbl.Config(act_bits=bits, hadamard=had)
+    yt = torch.float32 if ydt == "f32" else torch.bfloat16
+    Y, Wp, alpha = hbl.hbl_forward_latent(Xd, Wd, cfg, eps=1e-5, y_dtype=yt)
+    Wp2, alpha2 = hbl.hbl_quantize_weights(Wd, eps=1e-5)
+    Y2 = hbl.hbl_forward(Xd, Wp2, alpha2, N, cfg, y_dtype=yt)
+    _sync()
+    assert np.array_equal(to_host(alpha), to_host(alpha2))
+    assert np.array_equal(to_host(Wp), to_host(Wp2))
+    assert Y.shape == (M, N) and np.array_equal(to_host(Y), to_host(Y2))
+
+
 def test_forward_deterministic_and_empty():
     import torch
     layer = workloads.WO_1P3B
