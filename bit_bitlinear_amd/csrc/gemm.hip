@@ -298,9 +298,16 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_dma_kernel(const uint8_t
 // operand uses the same chunk, so a lane's codes for one super-step are
 // contiguous (32 bytes INT4, 64 bytes INT8).  The waves' int32 partial sums
 // are added in LDS (exact) before the rescale.
+// With NB = 2 a block covers 32 columns: every activation operand feeds two
+// MFMAs, which halves the activation codes read from L2 (the dominant
+// traffic at 17-64 tokens); the weight vectors per wave double, so this form
+// is used for K <= 8192 (at most MAXSS = 4 super-steps per wave), and only
+// when it still leaves >= 256 blocks (N >= 8192): with fewer blocks the
+// weight stream loses more than the halved activation reads gain (measured:
+// 48 x 2048 x 8192 INT8 11.4 -> 6.9 us; 64 x 8192 x 4096 INT4 13.9 -> 14.6 us).
 constexpr int kDecWaves = 8, kDecThreads = kDecWaves * 64, kDecBN = 16, kDecMaxSS = 16, kDecSB = 4;
 
-template <int BITS, int MT, typename YT>
+template <int BITS, int MT, typename YT, int NB, int MAXSS>
 __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const uint8_t* __restrict__ A,
                                                                   const float* __restrict__ xscale, int64_t M,
                                                                   int64_t K, const uint8_t* __restrict__ Wp,
@@ -308,13 +315,13 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const uint8_t*
                                                                   YT* __restrict__ Y) {
     constexpr int kAVec = (BITS == 8 ? 64 : 32) / 16;              // 16-byte A vectors per super-step and tile
     constexpr int TG = (MT * kDecSB * kAVec <= 32) ? MT : 32 / (kDecSB * kAVec);  // token tiles per A batch
-    __shared__ int red[kDecWaves][MT][4][64];
+    __shared__ int red[kDecWaves][NB][MT][4][64];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int l16 = lane & 15;  // weight column (W) / token row (A) inside the 16-wide tile
     const int g = lane >> 4;    // lane group: 64-k quarter of each super-step
-    const int64_t n0 = (int64_t)blockIdx.x * kDecBN;
+    const int64_t n0 = (int64_t)blockIdx.x * kDecBN * NB;
     const int64_t a_ld = K * BITS / 8;
     const int64_t w_ld = K / 4;
     const int SS = (int)(K / 256);  // super-steps in K
@@ -324,19 +331,24 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const uint8_t*
 
     const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(Wp + n0 * w_ld, (N - n0) * w_ld);
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A, M * a_ld);  // rows past M load as zeros
-    const uint32_t w_lane = (uint32_t)(l16 * w_ld + g * 16);
 
-    uint4 wv[kDecMaxSS];
+    uint4 wv[NB][MAXSS];
 #pragma unroll
-    for (int u = 0; u < kDecMaxSS; u++)
-        if (u < cnt) wv[u] = buf_load16(w_rsrc, w_lane + (uint32_t)(ss0 + u) * 64);
+    for (int nb = 0; nb < NB; nb++) {
+        const uint32_t w_lane = (uint32_t)((nb * kDecBN + l16) * w_ld + g * 16);
+#pragma unroll
+        for (int u = 0; u < MAXSS; u++)
+            if (u < cnt) wv[nb][u] = buf_load16(w_rsrc, w_lane + (uint32_t)(ss0 + u) * 64);
+    }
 
-    v4i acc[MT];
+    v4i acc[NB][MT];
 #pragma unroll
-    for (int t = 0; t < MT; t++) acc[t] = v4i{0, 0, 0, 0};
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+        for (int t = 0; t < MT; t++) acc[nb][t] = v4i{0, 0, 0, 0};
 
 #pragma unroll
-    for (int sb = 0; sb < kDecMaxSS; sb += kDecSB) {
+    for (int sb = 0; sb < MAXSS; sb += kDecSB) {
         if (sb < cnt) {
 #pragma unroll
             for (int tg = 0; tg < MT; tg += TG) {
@@ -355,10 +367,14 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const uint8_t*
 #pragma unroll
                 for (int u = 0; u < kDecSB; u++) {
                     if (sb + u < cnt) {
-                        const uint32_t wd[4] = {wv[sb + u].x, wv[sb + u].y, wv[sb + u].z, wv[sb + u].w};
 #pragma unroll
                         for (int d = 0; d < 4; d++) {
-                            const v4i b = unpack_w(wd[d]);
+                            v4i bw[NB];
+#pragma unroll
+                            for (int nb = 0; nb < NB; nb++) {
+                                const uint4 q = wv[nb][sb + u];
+                                bw[nb] = unpack_w(d == 0 ? q.x : d == 1 ? q.y : d == 2 ? q.z : q.w);
+                            }
 #pragma unroll
                             for (int t = 0; t < TG; t++) {
                                 v4i a;
@@ -369,7 +385,9 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const uint8_t*
                                     const uint4 q = aq[u][t][d >> 1];
                                     a = (d & 1) ? unpack_a4(q.z, q.w) : unpack_a4(q.x, q.y);
                                 }
-                                acc[tg + t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[tg + t], 0, 0, 0);
+#pragma unroll
+                                for (int nb = 0; nb < NB; nb++)
+                                    acc[nb][tg + t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bw[nb], acc[nb][tg + t], 0, 0, 0);
                             }
                         }
                     }
@@ -379,19 +397,23 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const uint8_t*
     }
 
 #pragma unroll
-    for (int t = 0; t < MT; t++)
+    for (int nb = 0; nb < NB; nb++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) red[wave][t][r][lane] = acc[t][r];
+        for (int t = 0; t < MT; t++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) red[wave][nb][t][r][lane] = acc[nb][t][r];
     __syncthreads();
-    // wave w finishes token tiles t = w, w+8, ... (output: column l16, rows 4*g + r)
+    // wave w finishes (column tile, token tile) pairs p = w, w+8, ... (output:
+    // column l16 of the tile, rows 4*g + r)
     const float alpha = *alpha_p;
-    const int64_t n = n0 + l16;
-    for (int t = wave; t < MT; t += kDecWaves) {
+    for (int p = wave; p < NB * MT; p += kDecWaves) {
+        const int nb = p / MT, t = p % MT;
+        const int64_t n = n0 + nb * kDecBN + l16;
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             int sum = 0;
 #pragma unroll
-            for (int w = 0; w < kDecWaves; w++) sum += red[w][t][r][lane];
+            for (int w = 0; w < kDecWaves; w++) sum += red[w][nb][t][r][lane];
             const int64_t m = t * 16 + 4 * g + r;
             if (m < M && n < N) store_y<YT>(Y + m * N + n, rescale(sum >> Shift<BITS>::value, xscale[m], alpha));
         }
@@ -450,16 +472,26 @@ hipError_t launch_typed(const uint8_t* A, const float* xscale, int64_t M, int64_
         return launch_gemv_small<BITS, 4, YT>(A, xscale, M, K, Wp, alpha, N, Y, s);
     }
     if (M <= 64 && K % 256 == 0 && K / 256 <= kDecWaves * kDecMaxSS) {
+        if (M > 16 && K / 256 <= kDecWaves * 4 && N >= 256 * 2 * kDecBN) {
+            const dim3 grid((unsigned)((N + 2 * kDecBN - 1) / (2 * kDecBN)));
+            if (M <= 32)
+                hipLaunchKernelGGL((gemm_decode_kernel<BITS, 2, YT, 2, 4>), grid, dim3(kDecThreads), 0, s, A, xscale, M,
+                                   K, Wp, alpha, N, Y);
+            else
+                hipLaunchKernelGGL((gemm_decode_kernel<BITS, 4, YT, 2, 4>), grid, dim3(kDecThreads), 0, s, A, xscale, M,
+                                   K, Wp, alpha, N, Y);
+            return hipGetLastError();
+        }
         const dim3 grid((unsigned)((N + kDecBN - 1) / kDecBN));
         if (M <= 16)
-            hipLaunchKernelGGL((gemm_decode_kernel<BITS, 1, YT>), grid, dim3(kDecThreads), 0, s, A, xscale, M, K, Wp,
-                               alpha, N, Y);
+            hipLaunchKernelGGL((gemm_decode_kernel<BITS, 1, YT, 1, kDecMaxSS>), grid, dim3(kDecThreads), 0, s, A,
+                               xscale, M, K, Wp, alpha, N, Y);
         else if (M <= 32)
-            hipLaunchKernelGGL((gemm_decode_kernel<BITS, 2, YT>), grid, dim3(kDecThreads), 0, s, A, xscale, M, K, Wp,
-                               alpha, N, Y);
+            hipLaunchKernelGGL((gemm_decode_kernel<BITS, 2, YT, 1, kDecMaxSS>), grid, dim3(kDecThreads), 0, s, A,
+                               xscale, M, K, Wp, alpha, N, Y);
         else
-            hipLaunchKernelGGL((gemm_decode_kernel<BITS, 4, YT>), grid, dim3(kDecThreads), 0, s, A, xscale, M, K, Wp,
-                               alpha, N, Y);
+            hipLaunchKernelGGL((gemm_decode_kernel<BITS, 4, YT, 1, kDecMaxSS>), grid, dim3(kDecThreads), 0, s, A,
+                               xscale, M, K, Wp, alpha, N, Y);
         return hipGetLastError();
     }
     if (K % kBK != 0) return hipErrorInvalidValue;  // the C ABI only admits K % 128 == 0

@@ -139,6 +139,8 @@ GEMM_CASES = [
     (300, 2048, 272, 8), (300, 2048, 272, 4), (129, 256, 16, 8), (128, 1024, 128, 4), (257, 128, 400, 8), (1024, 4096, 1024, 8), (520, 16384, 384, 4),
     (1, 8192, 4096, 4), (7, 8192, 512, 8), (16, 4096, 1024, 4), (17, 2048, 256, 4), (33, 1024, 64, 8),
     (64, 8192, 1024, 4), (65, 512, 192, 4), (64, 128, 32, 8),
+    # 17..64 tokens, K <= 8192, N >= 8192: 32 columns per decode block (N not a multiple of 32 too)
+    (40, 4096, 8208, 8), (20, 8192, 8192, 4), (64, 256, 8240, 4), (33, 2048, 16384, 8), (17, 16384, 64, 8),
     # M <= 4 with K a power of two in [1024, 16384]: the vector-ALU GEMV, every K and M
     (1, 1024, 48, 8), (2, 2048, 64, 4), (3, 4096, 32, 8), (4, 8192, 16, 8), (4, 16384, 80, 4), (1, 16384, 4096, 8),
     (2, 1024, 32, 4), (3, 8192, 64, 4), (1, 4096, 1024, 4), (2, 512, 64, 8), (3, 32768, 32, 4),
