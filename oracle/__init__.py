@@ -44,9 +44,14 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    # HBL_ORACLE_SO points at another build of an oracle source; the mutation
+    # test uses it to run the pins against deliberately broken copies.
+    path = os.environ.get("HBL_ORACLE_SO")
+    if not path:
+        path = _LIB
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
     F = ctypes.c_float

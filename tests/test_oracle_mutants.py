@@ -1,0 +1,88 @@
+"""The oracle's pins are strong enough to catch plausible mistakes.
+
+Each case plants one mistake in a copy of oracle/hbl_oracle.c (a dropped
+term, a wrong sign, index or constant, a transposed operand, another rounding
+mode, a misplaced epsilon), builds that copy with the oracle's own compiler
+flags, and runs tests/test_oracle_pins.py against it in a fresh process
+(HBL_ORACLE_SO selects the library): at least one pin must fail.  The
+unmodified source, built the same way, must pass every pin.  CPU only.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "hbl_oracle.c")
+
+# (name, text in the source, replacement)
+MUTANTS = [
+    ("ternary_round_half_away", "float r = rintf(t);\n        if (r > 1.0f) r = 1.0f;",
+     "float r = roundf(t);\n        if (r > 1.0f) r = 1.0f;"),
+    ("codes_round_half_away", "float r = rintf(t);\n        if (r > hi) r = hi;",
+     "float r = roundf(t);\n        if (r > hi) r = hi;"),
+    ("alpha_without_abs", "for (int64_t i = 0; i < count; i++) s += fabs((double)W[i]);",
+     "for (int64_t i = 0; i < count; i++) s += (double)W[i];"),
+    ("weight_eps_dropped", "float den = alpha + eps;", "float den = alpha;"),
+    ("act_eps_dropped", "float den = stat + eps;", "float den = stat;"),
+    ("dequant_factor_wrong", "*d_out = stat / num;", "*d_out = stat / (num + 1.0f);"),
+    ("hadamard_index_reversed", "(unsigned long long)(i & j)", "(unsigned long long)(i & (K - 1 - j))"),
+    ("hadamard_sign_flipped", "acc += (odd ? -1.0 : 1.0) * r[j];", "acc += (odd ? 1.0 : -1.0) * r[j];"),
+    ("hadamard_scale_missing", "z[i] = acc * inv;", "z[i] = acc;"),
+    ("absmax_without_abs", "float a = fabsf(z[k]);", "float a = z[k];"),
+    ("absmean_over_k_minus_1", "stat = (float)(s / (double)K);", "stat = (float)(s / (double)(K - 1));"),
+    ("sqrt7_one_ulp_off", "v.u = 0x402953FDu;", "v.u = 0x402953FEu;"),
+    ("int4_clip_symmetric", "lo = -8.0f; hi = 7.0f;", "lo = -7.0f; hi = 7.0f;"),
+    ("int8_clip_narrow", "lo = -128.0f; hi = 127.0f;", "lo = -127.0f; hi = 126.0f;"),
+    ("ternary_pack_field", "return (int)(2 * ((k % 16) / 4));", "return (int)(2 * (k % 4));"),
+    ("ternary_pack_byte", "return 4 * (k / 16) + (k % 4);", "return 4 * (k / 16) + ((k / 4) % 4);"),
+    ("int4_nibbles_swapped", "p[m * (K / 2) + k2] = (uint8_t)(lo | (hi << 4));",
+     "p[m * (K / 2) + k2] = (uint8_t)(hi | (lo << 4));"),
+    ("gemm_operand_transposed", "(int64_t)Wq[n * K + k]", "(int64_t)Wq[k * N + n]"),
+    ("norm_eps_outside_sqrt", "double den = sqrt(ss / (double)K + (double)eps);",
+     "double den = sqrt(ss / (double)K) + (double)eps;"),
+    ("norm_gain_dropped", "r[k] = v * (gain ? (double)gain[k] : 1.0);", "r[k] = v;"),
+    ("layernorm_mean_wrong", "mu /= (double)K;", "mu /= (double)(K - 1);"),
+    ("rescale_without_d", "float t = (float)acc[m * N + n] * d[m];", "float t = (float)acc[m * N + n];"),
+    ("rescale_without_alpha", "y[m * N + n] = t * alpha;", "y[m * N + n] = t;"),
+]
+
+
+def _build(src_text, out_dir, name):
+    src = os.path.join(out_dir, name + ".c")
+    so = os.path.join(out_dir, name + ".so")
+    with open(src, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", src, "-o", so,
+                    "-lm"], check=True)
+    return so
+
+
+def _run_pins(so):
+    env = dict(os.environ, HBL_ORACLE_SO=so, OMP_NUM_THREADS="4")
+    r = subprocess.run([sys.executable, "-m", "pytest", os.path.join(ROOT, "tests", "test_oracle_pins.py"), "-x",
+                        "-q", "-p", "no:cacheprovider", "-m", "not gpu"],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return r.returncode, r.stdout[-2000:]
+
+
+@pytest.fixture(scope="module")
+def source():
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    with open(SRC) as f:
+        return f.read()
+
+
+def test_unmodified_oracle_passes_pins(source, tmp_path):
+    rc, out = _run_pins(_build(source, str(tmp_path), "unmodified"))
+    assert rc == 0, out
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_fails_a_pin(source, tmp_path, name, old, new):
+    assert source.count(old) == 1, "mutation site for %s not unique or not found" % name
+    rc, out = _run_pins(_build(source.replace(old, new), str(tmp_path), name))
+    assert rc != 0, "no pin caught the planted mistake %s" % name
