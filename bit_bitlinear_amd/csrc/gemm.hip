@@ -22,14 +22,14 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 constexpr uint32_t kDropOffset = 0x80000000u;  // beyond every resource: store dropped
 
 // ============================================================ prefill GEMM ==
-// Block tile (64*TA) x (64*TB), K step 128, 4 waves in a 2 x 2 grid, each wave
-// (32*TA) x (32*TB) = TA x TB MFMA 32x32x32 tiles.  The fragment bytes a wave
-// reads from LDS per MFMA are A/TB + W/TA (1 KiB and 256 B per 32x32 fragment
-// for INT8; 512 B and 256 B for INT4), so the default wave tile is 2 x 4 for
-// large problems (>= 512 such tiles); small ones use 2 x 2 so that every CU
-// still gets at least two blocks.  Both are built for two waves per SIMD
-// (<= 256 registers).  Operands are unpacked in registers right before the
-// MFMA.
+// Block tile (64*TA) x (32*WGN*TB), K step 128, waves in a 2 x WGN grid, each
+// wave (32*TA) x (32*TB) = TA x TB MFMA 32x32x32 tiles.  The fragment bytes a
+// wave reads from LDS per MFMA are A/TB + W/TA (1 KiB and 256 B per 32x32
+// fragment for INT8; 512 B and 256 B for INT4), so large problems (>= 512
+// tiles of 128 x 256) use 4 waves with 2 x 4 wave tiles; smaller ones use 8
+// waves with 2 x 2 wave tiles on the same 128 x 256 block.  Both run two
+// waves per SIMD (<= 256 registers).  Operands are unpacked in registers
+// right before the MFMA.
 //
 // Tile order: blocks are dealt to the 8 XCDs round robin (block b -> XCD b%8);
 // the kernel maps block b to tile (b%8)*T8 + b/8, so every XCD works on a
@@ -55,19 +55,21 @@ constexpr int kBK = 128, kGemmThreads = 256;
 // The swizzle is applied on the global side (each lane fetches the logical
 // chunk that belongs at its LDS position).  Out-of-range rows are zero-filled
 // by the buffer range check, as for register loads.
-template <int BITS, int TA, int TB>
+template <int BITS, int TA, int TB, int WGN = 2>
 struct DmaTile {
-    static constexpr int BM = 64 * TA, BN = 64 * TB;
+    static constexpr int NWAVES = 2 * WGN;                   // waves in a 2 x WGN grid
+    static constexpr int BM = 64 * TA, BN = 32 * WGN * TB;
     static constexpr int a_row = BITS == 8 ? kBK : kBK / 2;  // code bytes per row and K step
     static constexpr int a_cpr = a_row / 16;                 // 16-byte chunks per code row
     static constexpr int a_bytes = BM * a_row;
     static constexpr int w_row = kBK / 4;                    // 32 bytes of packed W per row and K step
     static constexpr int w_bytes = BN * w_row;
     static constexpr int stage_bytes = a_bytes + w_bytes;
-    static constexpr int a_inst = a_bytes / 1024 / 4;        // 1 KiB DMA instructions per wave and K step
-    static constexpr int w_inst = w_bytes / 1024 / 4;
+    static constexpr int a_inst = a_bytes / 1024 / NWAVES;   // 1 KiB DMA instructions per wave and K step
+    static constexpr int w_inst = w_bytes / 1024 / NWAVES;
     static constexpr int inst = a_inst + w_inst;
-    static_assert(a_bytes % 4096 == 0 && w_bytes % 4096 == 0, "tile must split into whole wave instructions");
+    static_assert(a_bytes % (1024 * NWAVES) == 0 && w_bytes % (1024 * NWAVES) == 0,
+                  "tile must split into whole wave instructions");
     static HBL_DEVINL int a_swz(int row) { return BITS == 8 ? (row >> 1) & 7 : (row >> 2) & 3; }
     static HBL_DEVINL int w_swz(int row) { return (row >> 3) & 1; }
 };
@@ -110,14 +112,15 @@ HBL_DEVINL void wait_vmcnt() {
 // what it publishes); the memory clobber keeps LDS accesses on their side.
 HBL_DEVINL void barrier_no_wait() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int BITS, typename YT, int TA, int TB, int S>
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_dma_kernel(const uint8_t* __restrict__ A,
+template <int BITS, typename YT, int TA, int TB, int S, int WGN = 2>
+__global__ __launch_bounds__(128 * WGN, 4 / WGN) void gemm_dma_kernel(const uint8_t* __restrict__ A,
                                                                    const float* __restrict__ xscale, int64_t M,
                                                                    int64_t K, const uint8_t* __restrict__ Wp,
                                                                    const float* __restrict__ alpha_p, int64_t N,
                                                                    YT* __restrict__ Y, int tiles_n, int tiles_total) {
-    using DT = DmaTile<BITS, TA, TB>;
+    using DT = DmaTile<BITS, TA, TB, WGN>;
     constexpr int BM = DT::BM, BN = DT::BN;
+    constexpr int NT = 64 * DT::NWAVES;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[S * DT::stage_bytes];
     __shared__ __attribute__((aligned(16))) float xs_tile[BM];  // per-token scales of this tile's rows (0 past M)
 
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_dma_kernel(const uint8_t
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
     const int64_t a_ld = K * BITS / 8;  // bytes per activation row
     const int64_t w_ld = K / 4;         // bytes per weight row
     const int KT = (int)(K / kBK);
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_dma_kernel(const uint8_t
         }
     };
 
-    for (int r = tid; r < BM; r += kGemmThreads) {
+    for (int r = tid; r < BM; r += NT) {
         const __amdgpu_buffer_rsrc_t xs_rsrc = make_rsrc(xscale + m0, (M - m0) * 4);
         xs_tile[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xs_rsrc, r * 4, 0, 0));
     }
@@ -502,10 +505,14 @@ hipError_t launch_typed(const uint8_t* A, const float* xscale, int64_t M, int64_
         hipLaunchKernelGGL((gemm_dma_kernel<BITS, YT, 2, 4, kDmaStages>), dim3(tiles_total), dim3(kGemmThreads), 0, s, A, xscale,
                            M, K, Wp, alpha, N, Y, tiles_n, tiles_total);
     } else {
-        const int tiles_n = (int)((N + 127) / 128);
+        // smaller problems: 128 x 256 blocks of 8 waves (2 x 4 grid of 64 x 64
+        // wave tiles), one block and two waves per SIMD per CU; the code tile
+        // in LDS serves twice as many columns as a 4-wave 128 x 128 block
+        // (measured 3% faster at 4096 x 2048 x 2048)
+        const int tiles_n = (int)((N + 255) / 256);
         const int tiles_total = tiles_n * (int)((M + 127) / 128);
-        hipLaunchKernelGGL((gemm_dma_kernel<BITS, YT, 2, 2, kDmaStages>), dim3(tiles_total), dim3(kGemmThreads), 0, s, A, xscale,
-                           M, K, Wp, alpha, N, Y, tiles_n, tiles_total);
+        hipLaunchKernelGGL((gemm_dma_kernel<BITS, YT, 2, 2, kDmaStages, 4>), dim3(tiles_total), dim3(512), 0, s, A,
+                           xscale, M, K, Wp, alpha, N, Y, tiles_n, tiles_total);
     }
     return hipGetLastError();
 }
