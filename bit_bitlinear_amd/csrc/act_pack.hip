@@ -12,6 +12,8 @@
 // run the packing block routine of weight_pack.h with the same thread count
 // (each packed word depends only on its 16 weights and alpha, so the packed
 // bytes are identical too).  The two kinds are interleaved over the grid.
+// Rows up to 2048 elements only (longer rows keep the launches separate).
+// With TILED the codes go out in the decode tile layout of hbl_device.h.
 //
 // Follows the "新智元: 微软 BitNet v2" repost, section "H-BitLinear模块".
 #include "act_row.h"
@@ -20,7 +22,7 @@
 namespace hbl {
 namespace {
 
-template <int LK, int NT, typename Tin, int BITS, bool HAD, typename TW>
+template <int LK, int NT, typename Tin, int BITS, bool HAD, typename TW, bool TILED>
 __global__ __launch_bounds__(NT) void act_pack_kernel(const Tin* __restrict__ X, int64_t M,
                                                       const float* __restrict__ gain, int norm, float norm_eps,
                                                       float quant_eps, int a4_mode, uint8_t* __restrict__ codes,
@@ -43,20 +45,21 @@ __global__ __launch_bounds__(NT) void act_pack_kernel(const Tin* __restrict__ X,
         const int64_t row = b - p_lo;
         ActRegs<LK, NT, Tin> v;
         act_row_load<LK, NT, Tin>(X + row * S::K, v);
-        act_row_quantise<LK, NT, Tin, BITS, HAD>(v, gain, norm, norm_eps, quant_eps, a4_mode, lds, partf, partd,
-                                                 codes + row * (S::K * BITS / 8), xscale + row, nullptr, nullptr);
+        uint8_t* const crow = codes + (TILED ? dec_tile_row_base<BITS>(row, S::K) : row * (S::K * BITS / 8));
+        act_row_quantise<LK, NT, Tin, BITS, HAD, TILED>(v, gain, norm, norm_eps, quant_eps, a4_mode, lds, partf,
+                                                        partd, crow, xscale + row, nullptr, nullptr);
     } else {
         wq_pack_block<TW, NT>(W, n_groups, count, w_eps, partial, n_partial, Wp, alpha, p_lo);
     }
 }
 
-template <int LK, typename Tin, int BITS, bool HAD, typename TW>
+template <int LK, typename Tin, int BITS, bool HAD, typename TW, bool TILED>
 hipError_t launch_ap(const Tin* X, int64_t M, const float* gain, const hbl_config& cfg, void* codes, float* xscale,
                      const TW* W, int64_t NK, float w_eps, const double* partial, int n_partial, uint8_t* Wp,
                      float* alpha, hipStream_t s) {
     constexpr int NT = threads_for(LK);
     const size_t lds_bytes = HAD ? (size_t)ActShape<LK, NT, Tin>::lds_floats * sizeof(float) : 0;
-    auto kern = act_pack_kernel<LK, NT, Tin, BITS, HAD, TW>;
+    auto kern = act_pack_kernel<LK, NT, Tin, BITS, HAD, TW, TILED>;
     static bool attr_set = false;  // one attribute call per instantiation
     if (!attr_set && lds_bytes > 0) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
@@ -73,49 +76,56 @@ hipError_t launch_ap(const Tin* X, int64_t M, const float* gain, const hbl_confi
     return hipGetLastError();
 }
 
-template <typename Tin, int BITS, bool HAD, typename TW>
+template <typename Tin, int BITS, bool HAD, typename TW, bool TILED>
 hipError_t dispatch_k(const Tin* X, int64_t M, int64_t K, const float* gain, const hbl_config& cfg, void* codes,
                       float* xscale, const TW* W, int64_t NK, float w_eps, const double* partial, int n_partial,
                       uint8_t* Wp, float* alpha, hipStream_t s) {
-#define HBL_AP(LK) launch_ap<LK, Tin, BITS, HAD, TW>(X, M, gain, cfg, codes, xscale, W, NK, w_eps, partial, n_partial, Wp, alpha, s)
+#define HBL_AP(LK) \
+    launch_ap<LK, Tin, BITS, HAD, TW, TILED>(X, M, gain, cfg, codes, xscale, W, NK, w_eps, partial, n_partial, Wp, alpha, s)
     switch (K) {
         case 256: return HBL_AP(8);
         case 512: return HBL_AP(9);
         case 1024: return HBL_AP(10);
         case 2048: return HBL_AP(11);
-        case 4096: return HBL_AP(12);
-        case 8192: return HBL_AP(13);
-        case 16384: return HBL_AP(14);
-        case 32768: return HBL_AP(15);
         default: return hipErrorInvalidValue;
     }
 #undef HBL_AP
 }
 
+template <typename Tin, int BITS, bool HAD, typename TW>
+hipError_t dispatch_tiled(const Tin* X, int64_t M, int64_t K, const float* gain, const hbl_config& cfg, void* codes,
+                          float* xscale, const TW* W, int64_t NK, float w_eps, const double* partial, int n_partial,
+                          uint8_t* Wp, float* alpha, hipStream_t s, bool tiled) {
+    return tiled ? dispatch_k<Tin, BITS, HAD, TW, true>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
+                                                        n_partial, Wp, alpha, s)
+                 : dispatch_k<Tin, BITS, HAD, TW, false>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
+                                                         n_partial, Wp, alpha, s);
+}
+
 template <typename Tin, typename TW>
 hipError_t dispatch_mode(const Tin* X, int64_t M, int64_t K, const float* gain, const hbl_config& cfg, void* codes,
                          float* xscale, const TW* W, int64_t NK, float w_eps, const double* partial, int n_partial,
-                         uint8_t* Wp, float* alpha, hipStream_t s) {
+                         uint8_t* Wp, float* alpha, hipStream_t s, bool tiled) {
     if (cfg.act_bits == 8)
-        return cfg.hadamard ? dispatch_k<Tin, 8, true, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
-                                                          n_partial, Wp, alpha, s)
-                            : dispatch_k<Tin, 8, false, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
-                                                           n_partial, Wp, alpha, s);
-    return cfg.hadamard ? dispatch_k<Tin, 4, true, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
-                                                      n_partial, Wp, alpha, s)
-                        : dispatch_k<Tin, 4, false, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
-                                                       n_partial, Wp, alpha, s);
+        return cfg.hadamard ? dispatch_tiled<Tin, 8, true, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps,
+                                                              partial, n_partial, Wp, alpha, s, tiled)
+                            : dispatch_tiled<Tin, 8, false, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps,
+                                                               partial, n_partial, Wp, alpha, s, tiled);
+    return cfg.hadamard ? dispatch_tiled<Tin, 4, true, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
+                                                          n_partial, Wp, alpha, s, tiled)
+                        : dispatch_tiled<Tin, 4, false, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
+                                                           n_partial, Wp, alpha, s, tiled);
 }
 
 template <typename Tin>
 hipError_t dispatch_w(const Tin* X, int64_t M, int64_t K, const float* gain, const hbl_config& cfg, void* codes,
                       float* xscale, const void* W, int w_dtype, int64_t NK, float w_eps, const double* partial,
-                      int n_partial, uint8_t* Wp, float* alpha, hipStream_t s) {
+                      int n_partial, uint8_t* Wp, float* alpha, hipStream_t s, bool tiled) {
     if (w_dtype == HBL_F32)
         return dispatch_mode<Tin, float>(X, M, K, gain, cfg, codes, xscale, (const float*)W, NK, w_eps, partial,
-                                         n_partial, Wp, alpha, s);
+                                         n_partial, Wp, alpha, s, tiled);
     return dispatch_mode<Tin, uint16_t>(X, M, K, gain, cfg, codes, xscale, (const uint16_t*)W, NK, w_eps, partial,
-                                        n_partial, Wp, alpha, s);
+                                        n_partial, Wp, alpha, s, tiled);
 }
 
 }  // namespace
@@ -123,12 +133,12 @@ hipError_t dispatch_w(const Tin* X, int64_t M, int64_t K, const float* gain, con
 hipError_t launch_act_and_pack(const void* X, int x_dtype, int64_t M, int64_t K, const float* gain,
                                const hbl_config& cfg, void* codes, float* xscale, const void* W, int w_dtype,
                                int64_t NK, float w_eps, const double* partial, int n_partial, uint8_t* W_packed,
-                               float* alpha, hipStream_t s) {
+                               float* alpha, hipStream_t s, bool dec_tiled) {
     if (x_dtype == HBL_F32)
         return dispatch_w<float>((const float*)X, M, K, gain, cfg, codes, xscale, W, w_dtype, NK, w_eps, partial,
-                                 n_partial, W_packed, alpha, s);
+                                 n_partial, W_packed, alpha, s, dec_tiled);
     return dispatch_w<uint16_t>((const uint16_t*)X, M, K, gain, cfg, codes, xscale, W, w_dtype, NK, w_eps, partial,
-                                n_partial, W_packed, alpha, s);
+                                n_partial, W_packed, alpha, s, dec_tiled);
 }
 
 }  // namespace hbl

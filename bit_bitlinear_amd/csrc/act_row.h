@@ -244,7 +244,9 @@ HBL_DEVINL void act_row_load(const Tin* __restrict__ x, ActRegs<LK, NT, Tin>& v)
 // global or LDS), *xs_out the dequant factor, z_row / s_out the optional
 // parity outputs.  lds holds ActShape::lds_floats floats; partf / partd are
 // the block's reduction slots.  Every thread of the block must call it.
-template <int LK, int NT, typename Tin, int BITS, bool HAD>
+// TILED: crow is the row's base in the decode tile layout (dec_tile_row_base)
+// and code byte kb goes to crow + dec_tile_offset(kb) instead of crow + kb.
+template <int LK, int NT, typename Tin, int BITS, bool HAD, bool TILED = false>
 HBL_DEVINL void act_row_quantise(ActRegs<LK, NT, Tin>& v, const float* __restrict__ gain, int norm, float norm_eps,
                                  float quant_eps, int a4_mode, float* lds, ActPartF<LK, NT, Tin>& partf,
                                  ActPartD<LK, NT, Tin>& partd, uint8_t* crow, float* xs_out, float* z_row,
@@ -406,22 +408,25 @@ HBL_DEVINL void act_row_quantise(ActRegs<LK, NT, Tin>& v, const float* __restric
         uint32_t b[VW];
 #pragma unroll
         for (int x2 = 0; x2 < VW; x2++) b[x2] = code_bits(z[x2], s_mul, lo, hi);
+        // a vector's 2 or 4 code bytes never cross a 16-byte chunk of the tile layout
+        const int kb = BITS == 8 ? e0 : e0 / 2;
+        uint8_t* const cdst = crow + (TILED ? dec_tile_offset<BITS>(kb) : kb);
         if constexpr (BITS == 8) {
             if constexpr (VW == 4) {
                 const uint32_t w01 = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);  // [b0.0, b1.0, 0, 0]
                 const uint32_t w23 = __builtin_amdgcn_perm(b[3], b[2], 0x04000c0cu);  // [0, 0, b2.0, b3.0]
-                *reinterpret_cast<uint32_t*>(crow + e0) = w01 | w23;
+                *reinterpret_cast<uint32_t*>(cdst) = w01 | w23;
             } else {
-                *reinterpret_cast<uint16_t*>(crow + e0) =
+                *reinterpret_cast<uint16_t*>(cdst) =
                     (uint16_t)((b[0] & 0xFFu) | ((b[1] & 0xFFu) << 8));
             }
         } else {
             if constexpr (VW == 4) {
                 const uint32_t lo2 = (b[0] & 0xFu) | ((b[1] & 0xFu) << 4);
                 const uint32_t hi2 = (b[2] & 0xFu) | ((b[3] & 0xFu) << 4);
-                *reinterpret_cast<uint16_t*>(crow + e0 / 2) = (uint16_t)(lo2 | (hi2 << 8));
+                *reinterpret_cast<uint16_t*>(cdst) = (uint16_t)(lo2 | (hi2 << 8));
             } else {
-                crow[e0 / 2] = (uint8_t)((b[0] & 0xFu) | ((b[1] & 0xFu) << 4));
+                *cdst = (uint8_t)((b[0] & 0xFu) | ((b[1] & 0xFu) << 4));
             }
         }
     }

@@ -65,6 +65,12 @@ hbl_status check_gemm_shape(int64_t M, int64_t K, int64_t N) {
 
 size_t codes_bytes(int64_t M, int64_t K, int32_t bits) { return (size_t)M * (size_t)K * (size_t)bits / 8; }
 
+// Bytes of the codes region of the forward workspace: up to 64 rows it is
+// padded to whole 16-row tiles, which the decode tile layout needs.
+size_t ws_codes_bytes(int64_t M, int64_t K, int32_t bits) {
+    return round_up(codes_bytes(M <= 64 ? (M + 15) / 16 * 16 : M, K, bits), 256);
+}
+
 }  // namespace
 
 extern "C" {
@@ -123,7 +129,7 @@ hbl_status hbl_workspace_bytes(int64_t M, int64_t K, const hbl_config* cfg, size
     hbl_status st = check_config(cfg);
     if (st != HBL_OK) return st;
     if (M < 0 || M > kMaxRows || K < 1 || K > HBL_MAX_K) return HBL_ERR_SHAPE;
-    *bytes = round_up(codes_bytes(M, K, cfg->act_bits), 256) + round_up((size_t)M * sizeof(float), 256);
+    *bytes = ws_codes_bytes(M, K, cfg->act_bits) + round_up((size_t)M * sizeof(float), 256);
     return HBL_OK;
 }
 
@@ -175,7 +181,7 @@ hbl_status hbl_forward(const void* X, int32_t x_dtype, int64_t M, int64_t K, con
     if (!aligned16(X) || !aligned16(W_packed) || !aligned(alpha, 4) || !aligned16(Y) || !aligned16(ws) ||
         !aligned(gain, 4))
         return HBL_ERR_ALIGN;
-    const size_t cb = round_up(codes_bytes(M, K, cfg->act_bits), 256);
+    const size_t cb = ws_codes_bytes(M, K, cfg->act_bits);
     const size_t need = cb + round_up((size_t)M * sizeof(float), 256);
     if (ws_bytes < need) return HBL_ERR_WORKSPACE;
     if (hbl::forward_small_eligible(M, K)) {
@@ -185,10 +191,13 @@ hbl_status hbl_forward(const void* X, int32_t x_dtype, int64_t M, int64_t K, con
     }
     void* codes = ws;
     float* xscale = (float*)((uint8_t*)ws + cb);
+    // codes that only the decode GEMM reads go out in its tile layout
+    const bool tiled = hbl::gemm_uses_decode_kernel(M, K);
     hipError_t e = hbl::launch_act_quant(X, x_dtype, M, K, gain, *cfg, codes, xscale, nullptr, nullptr,
-                                         (hipStream_t)stream);
+                                         (hipStream_t)stream, tiled);
     if (e != hipSuccess) return hip_fail(e);
-    e = hbl::launch_gemm(codes, xscale, cfg->act_bits, M, K, W_packed, alpha, N, Y, y_dtype, (hipStream_t)stream);
+    e = hbl::launch_gemm(codes, xscale, cfg->act_bits, M, K, W_packed, alpha, N, Y, y_dtype, (hipStream_t)stream,
+                         tiled);
     return e == hipSuccess ? HBL_OK : hip_fail(e);
 }
 
@@ -209,7 +218,7 @@ hbl_status hbl_forward_latent(const void* X, int32_t x_dtype, int64_t M, int64_t
     if (M > 0 && (!aligned16(X) || !aligned16(Y) || !aligned16(ws) || !aligned(gain, 4))) return HBL_ERR_ALIGN;
     const int n_partial = hbl::weight_partial_count(N * K);
     if (wws_bytes < (size_t)n_partial * sizeof(double)) return HBL_ERR_WORKSPACE;
-    const size_t cb = round_up(codes_bytes(M, K, cfg->act_bits), 256);
+    const size_t cb = ws_codes_bytes(M, K, cfg->act_bits);
     if (M > 0 && ws_bytes < cb + round_up((size_t)M * sizeof(float), 256)) return HBL_ERR_WORKSPACE;
     const hipStream_t s = (hipStream_t)stream;
     hipError_t e;
@@ -222,19 +231,20 @@ hbl_status hbl_forward_latent(const void* X, int32_t x_dtype, int64_t M, int64_t
     }
     void* codes = ws;
     float* xscale = (float*)((uint8_t*)ws + cb);
+    const bool tiled = hbl::gemm_uses_decode_kernel(M, K);
     if (K <= kFuseActPackMaxK) {
         // short rows: the activation blocks and the packing blocks share one grid
         e = hbl::launch_weight_partial(W, w_dtype, N * K, (double*)wws, n_partial, s);
         if (e == hipSuccess)
             e = hbl::launch_act_and_pack(X, x_dtype, M, K, gain, *cfg, codes, xscale, W, w_dtype, N * K, w_eps,
-                                         (const double*)wws, n_partial, W_packed, alpha, s);
+                                         (const double*)wws, n_partial, W_packed, alpha, s, tiled);
     } else {
         e = hbl::launch_weight_quant(W, w_dtype, N, K, w_eps, W_packed, alpha, (double*)wws, n_partial, s);
         if (e == hipSuccess)
-            e = hbl::launch_act_quant(X, x_dtype, M, K, gain, *cfg, codes, xscale, nullptr, nullptr, s);
+            e = hbl::launch_act_quant(X, x_dtype, M, K, gain, *cfg, codes, xscale, nullptr, nullptr, s, tiled);
     }
     if (e == hipSuccess)
-        e = hbl::launch_gemm(codes, xscale, cfg->act_bits, M, K, W_packed, alpha, N, Y, y_dtype, s);
+        e = hbl::launch_gemm(codes, xscale, cfg->act_bits, M, K, W_packed, alpha, N, Y, y_dtype, s, tiled);
     return e == hipSuccess ? HBL_OK : hip_fail(e);
 }
 

@@ -308,9 +308,14 @@ __global__ __launch_bounds__(128 * WGN, 4 / WGN) void gemm_dma_kernel(const uint
 // when it still leaves >= 256 blocks (N >= 8192): with fewer blocks the
 // weight stream loses more than the halved activation reads gain (measured:
 // 48 x 2048 x 8192 INT8 11.4 -> 6.9 us; 64 x 8192 x 4096 INT4 13.9 -> 14.6 us).
+// With row-major codes each activation instruction reads 16 rows x 64 (INT4:
+// 32) contiguous bytes; with TILED the codes are in the decode tile layout of
+// hbl_device.h (written so by the activation kernel) and every instruction
+// reads 1 KiB of consecutive bytes (measured 64 x 8192 x 4096 INT4 13.7 ->
+// 9.9 us).
 constexpr int kDecWaves = 8, kDecThreads = kDecWaves * 64, kDecBN = 16, kDecMaxSS = 16, kDecSB = 4;
 
-template <int BITS, int MT, typename YT, int NB, int MAXSS>
+template <int BITS, int MT, typename YT, int NB, int MAXSS, bool TILED>
 __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const uint8_t* __restrict__ A,
                                                                   const float* __restrict__ xscale, int64_t M,
                                                                   int64_t K, const uint8_t* __restrict__ Wp,
@@ -333,7 +338,10 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const uint8_t*
     const int cnt = max(0, min(SS, ss0 + per_wave) - ss0);
 
     const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(Wp + n0 * w_ld, (N - n0) * w_ld);
-    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A, M * a_ld);  // rows past M load as zeros
+    // rows past M load as zeros (row-major) or as the unwritten padding rows of
+    // the last tile (TILED); either way they reach only output rows >= M,
+    // which are not stored
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(A, (TILED ? (M + 15) / 16 * 16 : M) * a_ld);
 
     uint4 wv[NB][MAXSS];
 #pragma unroll
@@ -358,13 +366,18 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const uint8_t*
                 uint4 aq[kDecSB][TG][kAVec];
 #pragma unroll
                 for (int u = 0; u < kDecSB; u++) {
-                    const uint32_t k_byte = (uint32_t)(ss0 + sb + u) * (256 * BITS / 8) + g * (kAVec * 16);
+                    constexpr uint32_t SSB = 256 * BITS / 8;  // bytes per row and super-step
+                    const uint32_t ss = (uint32_t)(ss0 + sb + u);
 #pragma unroll
                     for (int t = 0; t < TG; t++) {
-                        const uint32_t a_lane = (uint32_t)(((tg + t) * 16 + l16) * a_ld) + k_byte;
+                        // tile (tg + t) starts at byte 16 * a_ld in both layouts
+                        const uint32_t a_lane =
+                            TILED ? (uint32_t)((tg + t) * 16 * a_ld) + ss * 16 * SSB + lane * 16
+                                  : (uint32_t)(((tg + t) * 16 + l16) * a_ld) + ss * SSB + g * (kAVec * 16);
 #pragma unroll
                         for (int v = 0; v < kAVec; v++)
-                            aq[u][t][v] = (sb + u < cnt) ? buf_load16(a_rsrc, a_lane + v * 16) : make_uint4(0, 0, 0, 0);
+                            aq[u][t][v] = (sb + u < cnt) ? buf_load16(a_rsrc, a_lane + v * (TILED ? 1024 : 16))
+                                                         : make_uint4(0, 0, 0, 0);
                     }
                 }
 #pragma unroll
@@ -466,37 +479,48 @@ hipError_t launch_gemv_small(const uint8_t* A, const float* xscale, int64_t M, i
 // Ring depth 3 (loads two K steps ahead); 2 and 4 measured within 3% of it.
 constexpr int kDmaStages = 3;
 
+bool gemv_small_shape(int64_t M, int64_t K) {
+    return M <= kGvMaxM && K >= 1024 && K <= 16384 && (K & (K - 1)) == 0;
+}
+
+template <int BITS, typename YT, bool TILED>
+hipError_t launch_decode(const uint8_t* A, const float* xscale, int64_t M, int64_t K, const uint8_t* Wp,
+                         const float* alpha, int64_t N, YT* Y, hipStream_t s) {
+    if (M > 16 && K / 256 <= kDecWaves * 4 && N >= 256 * 2 * kDecBN) {
+        const dim3 grid((unsigned)((N + 2 * kDecBN - 1) / (2 * kDecBN)));
+        if (M <= 32)
+            hipLaunchKernelGGL((gemm_decode_kernel<BITS, 2, YT, 2, 4, TILED>), grid, dim3(kDecThreads), 0, s, A,
+                               xscale, M, K, Wp, alpha, N, Y);
+        else
+            hipLaunchKernelGGL((gemm_decode_kernel<BITS, 4, YT, 2, 4, TILED>), grid, dim3(kDecThreads), 0, s, A,
+                               xscale, M, K, Wp, alpha, N, Y);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)((N + kDecBN - 1) / kDecBN));
+    if (M <= 16)
+        hipLaunchKernelGGL((gemm_decode_kernel<BITS, 1, YT, 1, kDecMaxSS, TILED>), grid, dim3(kDecThreads), 0, s, A,
+                           xscale, M, K, Wp, alpha, N, Y);
+    else if (M <= 32)
+        hipLaunchKernelGGL((gemm_decode_kernel<BITS, 2, YT, 1, kDecMaxSS, TILED>), grid, dim3(kDecThreads), 0, s, A,
+                           xscale, M, K, Wp, alpha, N, Y);
+    else
+        hipLaunchKernelGGL((gemm_decode_kernel<BITS, 4, YT, 1, kDecMaxSS, TILED>), grid, dim3(kDecThreads), 0, s, A,
+                           xscale, M, K, Wp, alpha, N, Y);
+    return hipGetLastError();
+}
+
 template <int BITS, typename YT>
 hipError_t launch_typed(const uint8_t* A, const float* xscale, int64_t M, int64_t K, const uint8_t* Wp,
-                        const float* alpha, int64_t N, YT* Y, hipStream_t s) {
-    if (M <= kGvMaxM && K >= 1024 && K <= 16384 && (K & (K - 1)) == 0) {
+                        const float* alpha, int64_t N, YT* Y, hipStream_t s, bool dec_tiled) {
+    if (gemv_small_shape(M, K)) {
         if (M == 1) return launch_gemv_small<BITS, 1, YT>(A, xscale, M, K, Wp, alpha, N, Y, s);
         if (M == 2) return launch_gemv_small<BITS, 2, YT>(A, xscale, M, K, Wp, alpha, N, Y, s);
         return launch_gemv_small<BITS, 4, YT>(A, xscale, M, K, Wp, alpha, N, Y, s);
     }
-    if (M <= 64 && K % 256 == 0 && K / 256 <= kDecWaves * kDecMaxSS) {
-        if (M > 16 && K / 256 <= kDecWaves * 4 && N >= 256 * 2 * kDecBN) {
-            const dim3 grid((unsigned)((N + 2 * kDecBN - 1) / (2 * kDecBN)));
-            if (M <= 32)
-                hipLaunchKernelGGL((gemm_decode_kernel<BITS, 2, YT, 2, 4>), grid, dim3(kDecThreads), 0, s, A, xscale, M,
-                                   K, Wp, alpha, N, Y);
-            else
-                hipLaunchKernelGGL((gemm_decode_kernel<BITS, 4, YT, 2, 4>), grid, dim3(kDecThreads), 0, s, A, xscale, M,
-                                   K, Wp, alpha, N, Y);
-            return hipGetLastError();
-        }
-        const dim3 grid((unsigned)((N + kDecBN - 1) / kDecBN));
-        if (M <= 16)
-            hipLaunchKernelGGL((gemm_decode_kernel<BITS, 1, YT, 1, kDecMaxSS>), grid, dim3(kDecThreads), 0, s, A,
-                               xscale, M, K, Wp, alpha, N, Y);
-        else if (M <= 32)
-            hipLaunchKernelGGL((gemm_decode_kernel<BITS, 2, YT, 1, kDecMaxSS>), grid, dim3(kDecThreads), 0, s, A,
-                               xscale, M, K, Wp, alpha, N, Y);
-        else
-            hipLaunchKernelGGL((gemm_decode_kernel<BITS, 4, YT, 1, kDecMaxSS>), grid, dim3(kDecThreads), 0, s, A,
-                               xscale, M, K, Wp, alpha, N, Y);
-        return hipGetLastError();
-    }
+    if (gemm_uses_decode_kernel(M, K))
+        return dec_tiled ? launch_decode<BITS, YT, true>(A, xscale, M, K, Wp, alpha, N, Y, s)
+                         : launch_decode<BITS, YT, false>(A, xscale, M, K, Wp, alpha, N, Y, s);
+    if (dec_tiled) return hipErrorInvalidValue;  // the tile layout is only read by the decode GEMM
     if (K % kBK != 0) return hipErrorInvalidValue;  // the C ABI only admits K % 128 == 0
     const int64_t big_tiles = ((M + 127) / 128) * ((N + 255) / 256);
     if (big_tiles >= 512) {
@@ -519,16 +543,23 @@ hipError_t launch_typed(const uint8_t* A, const float* xscale, int64_t M, int64_
 
 }  // namespace
 
+bool gemm_uses_decode_kernel(int64_t M, int64_t K) {
+    return M >= 1 && M <= 64 && !gemv_small_shape(M, K) && K % 256 == 0 && K / 256 <= kDecWaves * kDecMaxSS;
+}
+
 hipError_t launch_gemm(const void* codes, const float* xscale, int act_bits, int64_t M, int64_t K,
-                       const uint8_t* W_packed, const float* alpha, int64_t N, void* Y, int y_dtype, hipStream_t s) {
+                       const uint8_t* W_packed, const float* alpha, int64_t N, void* Y, int y_dtype, hipStream_t s,
+                       bool dec_tiled) {
     if (M == 0) return hipSuccess;
     const uint8_t* A = (const uint8_t*)codes;
     if (act_bits == 8) {
-        return y_dtype == HBL_F32 ? launch_typed<8, float>(A, xscale, M, K, W_packed, alpha, N, (float*)Y, s)
-                                  : launch_typed<8, uint16_t>(A, xscale, M, K, W_packed, alpha, N, (uint16_t*)Y, s);
+        return y_dtype == HBL_F32
+                   ? launch_typed<8, float>(A, xscale, M, K, W_packed, alpha, N, (float*)Y, s, dec_tiled)
+                   : launch_typed<8, uint16_t>(A, xscale, M, K, W_packed, alpha, N, (uint16_t*)Y, s, dec_tiled);
     }
-    return y_dtype == HBL_F32 ? launch_typed<4, float>(A, xscale, M, K, W_packed, alpha, N, (float*)Y, s)
-                              : launch_typed<4, uint16_t>(A, xscale, M, K, W_packed, alpha, N, (uint16_t*)Y, s);
+    return y_dtype == HBL_F32
+               ? launch_typed<4, float>(A, xscale, M, K, W_packed, alpha, N, (float*)Y, s, dec_tiled)
+               : launch_typed<4, uint16_t>(A, xscale, M, K, W_packed, alpha, N, (uint16_t*)Y, s, dec_tiled);
 }
 
 }  // namespace hbl

@@ -40,6 +40,26 @@ HBL_DEVINL uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// ---- activation codes in the decode tile layout ----
+// For the decode GEMM (up to 64 tokens), hbl_forward writes the codes tiled so
+// that every wave instruction of the GEMM reads 1 KiB of consecutive bytes.
+// Tokens are grouped in tiles of 16 rows and K in super-steps of 256 k
+// (SSB = 32*BITS bytes per row).  Block (tile t, super-step ss) is 16 * SSB
+// bytes at (t * K/256 + ss) * 16 * SSB; inside it, 16-byte chunk v*64 + g*16 + r
+// holds bytes [g*SSB/4 + 16v, +16) of row r's super-step (g = 0..3 is the
+// lane group of the 16x16x64 MFMA operand, v = 0 .. SSB/64 - 1).
+template <int BITS>
+HBL_DEVINL int64_t dec_tile_row_base(int64_t m, int64_t K) {
+    constexpr int64_t SSB = 32 * BITS;
+    return (m / 16) * (K / 256) * 16 * SSB + (m % 16) * 16;
+}
+template <int BITS>
+HBL_DEVINL int dec_tile_offset(int kb) {  // kb: byte index of the code inside its row (>= 0)
+    constexpr int SSB = 32 * BITS, Q = SSB / 4;
+    const int rem = kb % SSB;
+    return (kb / SSB) * 16 * SSB + ((rem % Q) / 16 * 64 + rem / Q * 16) * 16 + kb % 16;
+}
+
 // ---- wave / block reductions (fixed butterfly order: deterministic) ----
 HBL_DEVINL float wave_sum_f32(float v) {
 #pragma unroll
@@ -117,15 +137,18 @@ hipError_t launch_weight_partial(const void* W, int w_dtype, int64_t count, doub
 hipError_t launch_act_and_pack(const void* X, int x_dtype, int64_t M, int64_t K, const float* gain,
                                const hbl_config& cfg, void* codes, float* xscale, const void* W, int w_dtype,
                                int64_t NK, float w_eps, const double* partial, int n_partial, uint8_t* W_packed,
-                               float* alpha, hipStream_t s);
+                               float* alpha, hipStream_t s, bool dec_tiled = false);  // K <= 2048
 
 hipError_t launch_act_quant(const void* X, int x_dtype, int64_t M, int64_t K, const float* gain,
                             const hbl_config& cfg, void* codes, float* xscale, float* z_debug, float* s_debug,
-                            hipStream_t s);
+                            hipStream_t s, bool dec_tiled = false);
 
 hipError_t launch_gemm(const void* codes, const float* xscale, int act_bits, int64_t M, int64_t K,
                        const uint8_t* W_packed, const float* alpha, int64_t N, void* Y, int y_dtype,
-                       hipStream_t s);
+                       hipStream_t s, bool dec_tiled = false);
+// true when launch_gemm runs the decode GEMM for this shape; the codes may
+// then be in the decode tile layout (rows padded to a multiple of 16)
+bool gemm_uses_decode_kernel(int64_t M, int64_t K);
 
 // The whole forward for M = kForwardSmallMaxM = 1 token and K a power of two
 // in [1024, 16384], in one launch (codes and scale stay on chip).

@@ -110,7 +110,9 @@ hbl_status hbl_weight_workspace_bytes(int64_t N, int64_t K, size_t* bytes);
 hbl_status hbl_quantize_weights(const void* W, int32_t w_dtype, int64_t N, int64_t K, float eps,
                                 uint8_t* W_packed, float* alpha, void* ws, size_t ws_bytes, void* stream);
 
-/* Device workspace needed by hbl_forward (activation codes + per-token scale). */
+/* Device workspace needed by hbl_forward and hbl_forward_latent (activation
+ * codes + per-token scale; for M <= 64 the codes region is padded to whole
+ * 16-row tiles). */
 hbl_status hbl_workspace_bytes(int64_t M, int64_t K, const hbl_config* cfg, size_t* bytes);
 
 /*
@@ -155,7 +157,9 @@ hbl_status hbl_gemm(const void* codes, const float* xscale, int32_t act_bits, in
  * hbl_workspace_bytes(M, K, cfg) (room for the codes followed by xscale); its
  * contents afterwards are unspecified: for one token (M = 1) with K a power
  * of two in [1024, 16384] the whole forward runs as a single launch and the
- * codes never leave the chip.  Constraints: those of both stages.
+ * codes never leave the chip; for the other shapes up to 64 tokens that the
+ * decode GEMM serves, the codes are kept in a tiled order private to the
+ * library.  Constraints: those of both stages.
  */
 hbl_status hbl_forward(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
                        const uint8_t* W_packed, const float* alpha, int64_t N, const hbl_config* cfg,

@@ -45,6 +45,9 @@ def test_size_queries():
     ws4 = hbl.hbl_workspace_bytes(4096, 2048, hbl.Config(act_bits=4))
     assert ws8 >= 4096 * 2048 + 4096 * 4 and ws4 >= 4096 * 1024 + 4096 * 4 and ws4 < ws8
     assert hbl.hbl_workspace_bytes(0, 2048, hbl.Config()) == 0
+    # up to 64 tokens the codes region holds whole 16-row tiles
+    assert hbl.hbl_workspace_bytes(5, 1024, hbl.Config(act_bits=8)) >= 16 * 1024 + 5 * 4
+    assert hbl.hbl_workspace_bytes(65, 1024, hbl.Config(act_bits=8)) < 80 * 1024
     with pytest.raises(hbl.HblError) as e:
         hbl.hbl_packed_weight_bytes(16, 40)
     assert e.value.status == 4

@@ -349,6 +349,52 @@ def test_forward_small_m_matches_stages(M, K, N, bits, had, xdt, ydt, norm, use_
     assert np.array_equal(got, y_exact if ydt == "f32" else oracle.f32_to_bf16(y_exact))
 
 
+# Up to 64 tokens (outside the one-token fused shapes) the decode GEMM reads
+# the codes that hbl_forward keeps in its tiled order; the result must equal
+# the stage entry points (row-major codes) bit for bit, and the oracle's
+# arithmetic on sampled columns.  Covers one and several 16-row tiles, partial
+# last tiles, 32-column blocks (17-64 tokens, N >= 8192, K <= 8192), K from
+# one super-step (256) to the maximum (32768), and few-token shapes the GEMV
+# does not serve (K below 1024 or above 16384).
+DECODE_TILED_CASES = [
+    # (M, K, N, bits, hadamard, x dtype, y dtype)
+    (5, 4096, 1024, 8, True, "f32", "f32"),
+    (16, 8192, 4096, 4, True, "bf16", "bf16"),
+    (17, 2048, 8192, 8, True, "f32", "bf16"),
+    (33, 8192, 8192, 4, True, "bf16", "f32"),
+    (64, 32768, 512, 8, True, "f32", "f32"),
+    (64, 256, 16384, 4, False, "f32", "bf16"),
+    (48, 1024, 2048, 4, True, "bf16", "bf16"),
+    (2, 512, 64, 4, True, "f32", "f32"),
+    (4, 32768, 64, 8, False, "bf16", "f32"),
+    (31, 16384, 1024, 8, True, "bf16", "bf16"),
+]
+
+
+@pytest.mark.parametrize("M,K,N,bits,had,xdt,ydt", DECODE_TILED_CASES)
+def test_forward_decode_tiled_matches_stages(M, K, N, bits, had, xdt, ydt):
+    import torch
+    _announce("forward decode-tiled M=%d K=%d N=%d a%d had=%d %s->%s" % (M, K, N, bits, had, xdt, ydt))
+    rng = np.random.default_rng(M * 13 + K + N + bits)
+    X, _ = workloads.x_outlier_gaussian(rng, M, K, 4, 30.0)
+    W = workloads.w_latent(rng, N, K)
+    Xd = to_dev(workloads.f32_to_bf16_bits(X) if xdt == "bf16" else X)
+    cfg = hbl.Config(act_bits=bits, hadamard=had)
+    Wp, alpha = hbl.hbl_quantize_weights(to_dev(W))
+    yt = torch.float32 if ydt == "f32" else torch.bfloat16
+    Y = hbl.hbl_forward(Xd, Wp, alpha, N, cfg, y_dtype=yt)
+    codes, xs, _, _ = hbl.hbl_quantize_activations(Xd, cfg)
+    Y2 = hbl.hbl_gemm(codes, xs, bits, K, Wp, alpha, N, y_dtype=yt)
+    _sync()
+    got = to_host(Y)
+    assert np.array_equal(got, to_host(Y2))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 40)]))
+    q = unpack_codes(to_host(codes), K, bits)
+    a = to_host(alpha)[0]
+    y_exact = oracle.rescale(oracle.int_gemm(q, oracle.ternarize(W[cols], a, 1e-5)), to_host(xs), a)
+    assert np.array_equal(got[:, cols], y_exact if ydt == "f32" else oracle.f32_to_bf16(y_exact))
+
+
 # hbl_forward_latent: weights ternarised and the forward run in three launches
 # (activation quantisation and weight packing share a grid); Y, W_packed and
 # alpha must equal hbl_quantize_weights + hbl_forward bit for bit.
@@ -361,6 +407,8 @@ LATENT_CASES = [
     (129, 4096, 512, 4, False, "bf16", "bf16", "bf16"),
     (70, 32768, 96, 8, True, "bf16", "f32", "f32"),
     (0, 2048, 512, 8, True, "bf16", "f32", "bf16"),
+    (64, 2048, 8192, 8, True, "f32", "f32", "bf16"),
+    (5, 1024, 512, 8, True, "bf16", "bf16", "f32"),
 ]
 
 
