@@ -113,7 +113,7 @@ HBL_DEVINL void wait_vmcnt() {
 HBL_DEVINL void barrier_no_wait() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int BITS, typename YT, int TA, int TB, int S, int WGN = 2>
-__global__ __launch_bounds__(128 * WGN, 4 / WGN) void gemm_dma_kernel(const uint8_t* __restrict__ A,
+__global__ __launch_bounds__(128 * WGN, TA == 1 ? 4 : 4 / WGN) void gemm_dma_kernel(const uint8_t* __restrict__ A,
                                                                    const float* __restrict__ xscale, int64_t M,
                                                                    int64_t K, const uint8_t* __restrict__ Wp,
                                                                    const float* __restrict__ alpha_p, int64_t N,
@@ -227,16 +227,20 @@ __global__ __launch_bounds__(128 * WGN, 4 / WGN) void gemm_dma_kernel(const uint
         }
     };
 
-    for (int r = tid; r < BM; r += NT) {
+    // The per-token scales of the tile's rows (0 past M) are loaded into
+    // registers first and written to LDS only for the epilogue, so their
+    // latency hides behind the main loop instead of delaying the first loads.
+    static_assert(BM <= NT, "one scale per thread");
+    float xs_r = 0.f;
+    if (tid < BM) {
         const __amdgpu_buffer_rsrc_t xs_rsrc = make_rsrc(xscale + m0, (M - m0) * 4);
-        xs_tile[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xs_rsrc, r * 4, 0, 0));
+        xs_r = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xs_rsrc, tid * 4, 0, 0));
     }
 
     // prologue: K steps 0..S-2 in flight (past the last step the loads repeat
     // step KT-1, so every wave always has the same number in flight)
 #pragma unroll
     for (int u = 0; u < S - 1; u++) issue(min(u, KT - 1), u);
-    __syncthreads();  // xs_tile
     for (int kt = 0; kt < KT; kt++) {
         wait_vmcnt<(S - 2) * DT::inst>();  // this wave's loads of step kt have landed
         barrier_no_wait();                 // ... and every wave's; stage (kt-1)%S is free
@@ -244,6 +248,7 @@ __global__ __launch_bounds__(128 * WGN, 4 / WGN) void gemm_dma_kernel(const uint
         compute(kt % S);
     }
     wait_vmcnt<0>();  // no LDS-direct load may still be in flight when the block ends
+    if (tid < BM) xs_tile[tid] = xs_r;
     __syncthreads();
     // ---- epilogue: lane holds column lr, rows 8*(r/4) + 4*lg + r%4 of each 32x32 tile.
     // Y is written through a buffer resource over this tile's rows: rows past M
@@ -528,7 +533,7 @@ hipError_t launch_typed(const uint8_t* A, const float* xscale, int64_t M, int64_
         const int tiles_total = (int)big_tiles;
         hipLaunchKernelGGL((gemm_dma_kernel<BITS, YT, 2, 4, kDmaStages>), dim3(tiles_total), dim3(kGemmThreads), 0, s, A, xscale,
                            M, K, Wp, alpha, N, Y, tiles_n, tiles_total);
-    } else {
+    } else if (big_tiles >= 128) {
         // smaller problems: 128 x 256 blocks of 8 waves (2 x 4 grid of 64 x 64
         // wave tiles), one block and two waves per SIMD per CU; the code tile
         // in LDS serves twice as many columns as a 4-wave 128 x 128 block
@@ -536,6 +541,21 @@ hipError_t launch_typed(const uint8_t* A, const float* xscale, int64_t M, int64_
         const int tiles_n = (int)((N + 255) / 256);
         const int tiles_total = tiles_n * (int)((M + 127) / 128);
         hipLaunchKernelGGL((gemm_dma_kernel<BITS, YT, 2, 2, kDmaStages, 4>), dim3(tiles_total), dim3(512), 0, s, A,
+                           xscale, M, K, Wp, alpha, N, Y, tiles_n, tiles_total);
+    } else if constexpr (BITS == 8) {
+        // fewer than 128 tiles of 128 x 256 (a few hundred tokens): 64-row
+        // tiles, 8 waves of 32 x 64, up to two blocks per CU, so twice as
+        // many CUs take part (measured 256 x 4096 x 4096: 26.3 -> 18.6 us)
+        const int tiles_n = (int)((N + 255) / 256);
+        const int tiles_total = tiles_n * (int)((M + 63) / 64);
+        hipLaunchKernelGGL((gemm_dma_kernel<BITS, YT, 1, 2, kDmaStages, 4>), dim3(tiles_total), dim3(512), 0, s, A,
+                           xscale, M, K, Wp, alpha, N, Y, tiles_n, tiles_total);
+    } else {
+        // the same for INT4 codes (64-byte rows: a 64-row code tile is too
+        // small for 8 waves' LDS-direct loads): 64 x 128 tiles of 4 waves
+        const int tiles_n = (int)((N + 127) / 128);
+        const int tiles_total = tiles_n * (int)((M + 63) / 64);
+        hipLaunchKernelGGL((gemm_dma_kernel<BITS, YT, 1, 2, kDmaStages, 2>), dim3(tiles_total), dim3(256), 0, s, A,
                            xscale, M, K, Wp, alpha, N, Y, tiles_n, tiles_total);
     }
     return hipGetLastError();
