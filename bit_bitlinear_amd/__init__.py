@@ -17,7 +17,7 @@ import re
 __all__ = [
     "HblError", "HblLibraryError", "Config", "load_library", "declared_symbols",
     "hbl_packed_weight_bytes", "hbl_weight_workspace_bytes", "hbl_quantize_weights",
-    "hbl_workspace_bytes", "hbl_quantize_activations", "hbl_gemm", "hbl_forward", "hbl_forward_latent",
+    "hbl_workspace_bytes", "hbl_forward_workspace_bytes", "hbl_quantize_activations", "hbl_gemm", "hbl_forward", "hbl_forward_latent",
     "hbl_status_string", "hbl_last_hip_error",
     "HBL_F32", "HBL_BF16", "HBL_NORM_RMS", "HBL_NORM_LN", "HBL_NORM_NONE",
     "HBL_A4_ABSMEAN_SQRT7", "HBL_A4_ABSMAX_7",
@@ -95,6 +95,7 @@ def load_library(path: str | None = None):
         "hbl_weight_workspace_bytes": [I64, I64, PSZ],
         "hbl_quantize_weights": [P, I32, I64, I64, F, P, P, P, SZ, P],
         "hbl_workspace_bytes": [I64, I64, PCFG, PSZ],
+        "hbl_forward_workspace_bytes": [I64, I64, I64, PCFG, PSZ],
         "hbl_quantize_activations": [P, I32, I64, I64, P, PCFG, P, P, P, P, P],
         "hbl_gemm": [P, P, I32, I64, I64, P, P, I64, P, I32, P],
         "hbl_forward": [P, I32, I64, I64, P, P, P, I64, PCFG, P, I32, P, SZ, P],
@@ -190,6 +191,12 @@ def hbl_weight_workspace_bytes(N: int, K: int) -> int:
     return _size_out(load_library().hbl_weight_workspace_bytes, N, K)
 
 
+def hbl_forward_workspace_bytes(M: int, K: int, N: int, cfg: Config) -> int:
+    """Workspace for the fastest hbl_forward / hbl_forward_latent path of an M x K by N x K layer."""
+    c = cfg.c()
+    return _size_out(load_library().hbl_forward_workspace_bytes, M, K, N, ctypes.byref(c))
+
+
 def hbl_workspace_bytes(M: int, K: int, cfg: Config) -> int:
     c = cfg.c()
     return _size_out(load_library().hbl_workspace_bytes, M, K, ctypes.byref(c))
@@ -263,7 +270,7 @@ def hbl_forward(X, W_packed, alpha, N: int, cfg: Config, y_dtype=None, gain=None
     if Y is None:
         Y = torch.empty((M, N), dtype=y_dtype or X.dtype, device=X.device)
     if ws is None:
-        ws = torch.empty(max(1, hbl_workspace_bytes(M, K, cfg)), dtype=torch.uint8, device=X.device)
+        ws = torch.empty(max(1, hbl_forward_workspace_bytes(M, K, N, cfg)), dtype=torch.uint8, device=X.device)
     _dev(Y, "Y"); _dev(ws, "ws")
     c = cfg.c()
     _check("hbl_forward", lib.hbl_forward(_ptr(X), _dtype_code(X), M, K, _ptr(gain), _ptr(W_packed), _ptr(alpha), N,
@@ -291,7 +298,7 @@ def hbl_forward_latent(X, W, cfg: Config, eps: float = 1e-5, y_dtype=None, gain=
     if Y is None:
         Y = torch.empty((M, N), dtype=y_dtype or X.dtype, device=X.device)
     if ws is None:
-        ws = torch.empty(max(1, hbl_workspace_bytes(M, K, cfg)), dtype=torch.uint8, device=X.device)
+        ws = torch.empty(max(1, hbl_forward_workspace_bytes(M, K, N, cfg)), dtype=torch.uint8, device=X.device)
     if wws is None:
         wws = torch.empty(hbl_weight_workspace_bytes(N, K), dtype=torch.uint8, device=W.device)
     for t, n in ((W_packed, "W_packed"), (alpha, "alpha"), (Y, "Y"), (ws, "ws"), (wws, "wws")):

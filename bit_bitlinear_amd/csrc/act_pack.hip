@@ -13,7 +13,8 @@
 // (each packed word depends only on its 16 weights and alpha, so the packed
 // bytes are identical too).  The two kinds are interleaved over the grid.
 // Rows up to 2048 elements only (longer rows keep the launches separate).
-// With TILED the codes go out in the decode tile layout of hbl_device.h.
+// The codes go out in one of the layouts of hbl_device.h (row-major, decode
+// tiles or FP6).
 //
 // Follows the "新智元: 微软 BitNet v2" repost, section "H-BitLinear模块".
 #include "act_row.h"
@@ -22,7 +23,7 @@
 namespace hbl {
 namespace {
 
-template <int LK, int NT, typename Tin, int BITS, bool HAD, typename TW, bool TILED>
+template <int LK, int NT, typename Tin, int BITS, bool HAD, typename TW, int LAYOUT>
 __global__ __launch_bounds__(NT) void act_pack_kernel(const Tin* __restrict__ X, int64_t M,
                                                       const float* __restrict__ gain, int norm, float norm_eps,
                                                       float quant_eps, int a4_mode, uint8_t* __restrict__ codes,
@@ -45,21 +46,21 @@ __global__ __launch_bounds__(NT) void act_pack_kernel(const Tin* __restrict__ X,
         const int64_t row = b - p_lo;
         ActRegs<LK, NT, Tin> v;
         act_row_load<LK, NT, Tin>(X + row * S::K, v);
-        uint8_t* const crow = codes + (TILED ? dec_tile_row_base<BITS>(row, S::K) : row * (S::K * BITS / 8));
-        act_row_quantise<LK, NT, Tin, BITS, HAD, TILED>(v, gain, norm, norm_eps, quant_eps, a4_mode, lds, partf,
+        uint8_t* const crow = codes + (LAYOUT == kCodesDecTiled ? dec_tile_row_base<BITS>(row, S::K) : row * (LAYOUT == kCodesFp6 ? S::K * 3 / 4 : S::K * BITS / 8));
+        act_row_quantise<LK, NT, Tin, BITS, HAD, LAYOUT>(v, gain, norm, norm_eps, quant_eps, a4_mode, lds, partf,
                                                         partd, crow, xscale + row, nullptr, nullptr);
     } else {
         wq_pack_block<TW, NT>(W, n_groups, count, w_eps, partial, n_partial, Wp, alpha, p_lo);
     }
 }
 
-template <int LK, typename Tin, int BITS, bool HAD, typename TW, bool TILED>
+template <int LK, typename Tin, int BITS, bool HAD, typename TW, int LAYOUT>
 hipError_t launch_ap(const Tin* X, int64_t M, const float* gain, const hbl_config& cfg, void* codes, float* xscale,
                      const TW* W, int64_t NK, float w_eps, const double* partial, int n_partial, uint8_t* Wp,
                      float* alpha, hipStream_t s) {
     constexpr int NT = threads_for(LK);
     const size_t lds_bytes = HAD ? (size_t)ActShape<LK, NT, Tin>::lds_floats * sizeof(float) : 0;
-    auto kern = act_pack_kernel<LK, NT, Tin, BITS, HAD, TW, TILED>;
+    auto kern = act_pack_kernel<LK, NT, Tin, BITS, HAD, TW, LAYOUT>;
     static bool attr_set = false;  // one attribute call per instantiation
     if (!attr_set && lds_bytes > 0) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
@@ -76,14 +77,16 @@ hipError_t launch_ap(const Tin* X, int64_t M, const float* gain, const hbl_confi
     return hipGetLastError();
 }
 
-template <typename Tin, int BITS, bool HAD, typename TW, bool TILED>
+template <typename Tin, int BITS, bool HAD, typename TW, int LAYOUT>
 hipError_t dispatch_k(const Tin* X, int64_t M, int64_t K, const float* gain, const hbl_config& cfg, void* codes,
                       float* xscale, const TW* W, int64_t NK, float w_eps, const double* partial, int n_partial,
                       uint8_t* Wp, float* alpha, hipStream_t s) {
 #define HBL_AP(LK) \
-    launch_ap<LK, Tin, BITS, HAD, TW, TILED>(X, M, gain, cfg, codes, xscale, W, NK, w_eps, partial, n_partial, Wp, alpha, s)
+    launch_ap<LK, Tin, BITS, HAD, TW, LAYOUT>(X, M, gain, cfg, codes, xscale, W, NK, w_eps, partial, n_partial, Wp, alpha, s)
     switch (K) {
-        case 256: return HBL_AP(8);
+        case 256:
+            if constexpr (LAYOUT == kCodesFp6) return hipErrorInvalidValue;  // two values per vector
+            else return HBL_AP(8);
         case 512: return HBL_AP(9);
         case 1024: return HBL_AP(10);
         case 2048: return HBL_AP(11);
@@ -93,39 +96,45 @@ hipError_t dispatch_k(const Tin* X, int64_t M, int64_t K, const float* gain, con
 }
 
 template <typename Tin, int BITS, bool HAD, typename TW>
-hipError_t dispatch_tiled(const Tin* X, int64_t M, int64_t K, const float* gain, const hbl_config& cfg, void* codes,
-                          float* xscale, const TW* W, int64_t NK, float w_eps, const double* partial, int n_partial,
-                          uint8_t* Wp, float* alpha, hipStream_t s, bool tiled) {
-    return tiled ? dispatch_k<Tin, BITS, HAD, TW, true>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
-                                                        n_partial, Wp, alpha, s)
-                 : dispatch_k<Tin, BITS, HAD, TW, false>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
-                                                         n_partial, Wp, alpha, s);
+hipError_t dispatch_layout(const Tin* X, int64_t M, int64_t K, const float* gain, const hbl_config& cfg,
+                           void* codes, float* xscale, const TW* W, int64_t NK, float w_eps, const double* partial,
+                           int n_partial, uint8_t* Wp, float* alpha, hipStream_t s, int layout) {
+#define HBL_APL(L) dispatch_k<Tin, BITS, HAD, TW, L>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial, n_partial, Wp, alpha, s)
+    switch (layout) {
+        case kCodesRowMajor: return HBL_APL(kCodesRowMajor);
+        case kCodesDecTiled: return HBL_APL(kCodesDecTiled);
+        case kCodesFp6:
+            if constexpr (BITS == 4) return HBL_APL(kCodesFp6);
+            else return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
+#undef HBL_APL
 }
 
 template <typename Tin, typename TW>
 hipError_t dispatch_mode(const Tin* X, int64_t M, int64_t K, const float* gain, const hbl_config& cfg, void* codes,
                          float* xscale, const TW* W, int64_t NK, float w_eps, const double* partial, int n_partial,
-                         uint8_t* Wp, float* alpha, hipStream_t s, bool tiled) {
+                         uint8_t* Wp, float* alpha, hipStream_t s, int layout) {
     if (cfg.act_bits == 8)
-        return cfg.hadamard ? dispatch_tiled<Tin, 8, true, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps,
-                                                              partial, n_partial, Wp, alpha, s, tiled)
-                            : dispatch_tiled<Tin, 8, false, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps,
-                                                               partial, n_partial, Wp, alpha, s, tiled);
-    return cfg.hadamard ? dispatch_tiled<Tin, 4, true, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
-                                                          n_partial, Wp, alpha, s, tiled)
-                        : dispatch_tiled<Tin, 4, false, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
-                                                           n_partial, Wp, alpha, s, tiled);
+        return cfg.hadamard ? dispatch_layout<Tin, 8, true, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps,
+                                                              partial, n_partial, Wp, alpha, s, layout)
+                            : dispatch_layout<Tin, 8, false, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps,
+                                                               partial, n_partial, Wp, alpha, s, layout);
+    return cfg.hadamard ? dispatch_layout<Tin, 4, true, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
+                                                          n_partial, Wp, alpha, s, layout)
+                        : dispatch_layout<Tin, 4, false, TW>(X, M, K, gain, cfg, codes, xscale, W, NK, w_eps, partial,
+                                                           n_partial, Wp, alpha, s, layout);
 }
 
 template <typename Tin>
 hipError_t dispatch_w(const Tin* X, int64_t M, int64_t K, const float* gain, const hbl_config& cfg, void* codes,
                       float* xscale, const void* W, int w_dtype, int64_t NK, float w_eps, const double* partial,
-                      int n_partial, uint8_t* Wp, float* alpha, hipStream_t s, bool tiled) {
+                      int n_partial, uint8_t* Wp, float* alpha, hipStream_t s, int layout) {
     if (w_dtype == HBL_F32)
         return dispatch_mode<Tin, float>(X, M, K, gain, cfg, codes, xscale, (const float*)W, NK, w_eps, partial,
-                                         n_partial, Wp, alpha, s, tiled);
+                                         n_partial, Wp, alpha, s, layout);
     return dispatch_mode<Tin, uint16_t>(X, M, K, gain, cfg, codes, xscale, (const uint16_t*)W, NK, w_eps, partial,
-                                        n_partial, Wp, alpha, s, tiled);
+                                        n_partial, Wp, alpha, s, layout);
 }
 
 }  // namespace
@@ -133,12 +142,12 @@ hipError_t dispatch_w(const Tin* X, int64_t M, int64_t K, const float* gain, con
 hipError_t launch_act_and_pack(const void* X, int x_dtype, int64_t M, int64_t K, const float* gain,
                                const hbl_config& cfg, void* codes, float* xscale, const void* W, int w_dtype,
                                int64_t NK, float w_eps, const double* partial, int n_partial, uint8_t* W_packed,
-                               float* alpha, hipStream_t s, bool dec_tiled) {
+                               float* alpha, hipStream_t s, int layout) {
     if (x_dtype == HBL_F32)
         return dispatch_w<float>((const float*)X, M, K, gain, cfg, codes, xscale, W, w_dtype, NK, w_eps, partial,
-                                 n_partial, W_packed, alpha, s, dec_tiled);
+                                 n_partial, W_packed, alpha, s, layout);
     return dispatch_w<uint16_t>((const uint16_t*)X, M, K, gain, cfg, codes, xscale, W, w_dtype, NK, w_eps, partial,
-                                n_partial, W_packed, alpha, s, dec_tiled);
+                                n_partial, W_packed, alpha, s, layout);
 }
 
 }  // namespace hbl

@@ -244,9 +244,12 @@ HBL_DEVINL void act_row_load(const Tin* __restrict__ x, ActRegs<LK, NT, Tin>& v)
 // global or LDS), *xs_out the dequant factor, z_row / s_out the optional
 // parity outputs.  lds holds ActShape::lds_floats floats; partf / partd are
 // the block's reduction slots.  Every thread of the block must call it.
-// TILED: crow is the row's base in the decode tile layout (dec_tile_row_base)
-// and code byte kb goes to crow + dec_tile_offset(kb) instead of crow + kb.
-template <int LK, int NT, typename Tin, int BITS, bool HAD, bool TILED = false>
+// LAYOUT kCodesRowMajor: code byte kb of the row goes to crow + kb.
+// kCodesDecTiled: crow is the row's base in the decode tile layout
+// (dec_tile_row_base) and byte kb goes to crow + dec_tile_offset(kb).
+// kCodesFp6 (INT4 only, four values per vector): the codes go out as FP6 E3M2
+// in the FP6 GEMM layout (fp6_byte_offset), crow at the row's K*3/4 bytes.
+template <int LK, int NT, typename Tin, int BITS, bool HAD, int LAYOUT = kCodesRowMajor>
 HBL_DEVINL void act_row_quantise(ActRegs<LK, NT, Tin>& v, const float* __restrict__ gain, int norm, float norm_eps,
                                  float quant_eps, int a4_mode, float* lds, ActPartF<LK, NT, Tin>& partf,
                                  ActPartD<LK, NT, Tin>& partd, uint8_t* crow, float* xs_out, float* z_row,
@@ -408,9 +411,20 @@ HBL_DEVINL void act_row_quantise(ActRegs<LK, NT, Tin>& v, const float* __restric
         uint32_t b[VW];
 #pragma unroll
         for (int x2 = 0; x2 < VW; x2++) b[x2] = code_bits(z[x2], s_mul, lo, hi);
+        if constexpr (LAYOUT == kCodesFp6) {
+            static_assert(BITS == 4 && VW == 4, "FP6 codes: INT4 values, four per vector");
+            // four 6-bit fields = 3 whole bytes at natural byte 3*e0/4
+            uint32_t f = 0;
+#pragma unroll
+            for (int x2 = 0; x2 < 4; x2++) f |= fp6_e3m2((int)(b[x2] << 28) >> 28) << (6 * x2);
+            const int nb = 3 * e0 / 4;
+#pragma unroll
+            for (int x2 = 0; x2 < 3; x2++) crow[fp6_byte_offset(nb + x2)] = (uint8_t)(f >> (8 * x2));
+            continue;
+        }
         // a vector's 2 or 4 code bytes never cross a 16-byte chunk of the tile layout
         const int kb = BITS == 8 ? e0 : e0 / 2;
-        uint8_t* const cdst = crow + (TILED ? dec_tile_offset<BITS>(kb) : kb);
+        uint8_t* const cdst = crow + (LAYOUT == kCodesDecTiled ? dec_tile_offset<BITS>(kb) : kb);
         if constexpr (BITS == 8) {
             if constexpr (VW == 4) {
                 const uint32_t w01 = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);  // [b0.0, b1.0, 0, 0]

@@ -65,6 +65,19 @@ hbl_status check_gemm_shape(int64_t M, int64_t K, int64_t N) {
 
 size_t codes_bytes(int64_t M, int64_t K, int32_t bits) { return (size_t)M * (size_t)K * (size_t)bits / 8; }
 
+// Workspace of the FP6 x FP4 path: FP6 codes (K*3/4 bytes per row), the
+// per-token scales, and the weights as FP4 (K/2 bytes per row).
+size_t f6f4_ws_bytes(int64_t M, int64_t K, int64_t N) {
+    return round_up((size_t)M * (size_t)K * 3 / 4, 256) + round_up((size_t)M * sizeof(float), 256) +
+           round_up((size_t)N * (size_t)K / 2, 256);
+}
+
+// The forward takes the FP6 x FP4 GEMM for INT4 prefill shapes when the
+// caller's workspace holds its larger layout (hbl_forward_workspace_bytes).
+bool use_f6f4(int64_t M, int64_t K, int64_t N, const hbl_config* cfg, size_t ws_bytes) {
+    return cfg->act_bits == 4 && hbl::gemm_f6f4_eligible(M, K, N) && ws_bytes >= f6f4_ws_bytes(M, K, N);
+}
+
 // Bytes of the codes region of the forward workspace: up to 64 rows it is
 // padded to whole 16-row tiles, which the decode tile layout needs.
 size_t ws_codes_bytes(int64_t M, int64_t K, int32_t bits) {
@@ -133,6 +146,18 @@ hbl_status hbl_workspace_bytes(int64_t M, int64_t K, const hbl_config* cfg, size
     return HBL_OK;
 }
 
+hbl_status hbl_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, const hbl_config* cfg, size_t* bytes) {
+    if (!bytes) return HBL_ERR_NULL;
+    hbl_status st = hbl_workspace_bytes(M, K, cfg, bytes);
+    if (st != HBL_OK) return st;
+    if (N < 1 || N > kMaxGemmN) return HBL_ERR_SHAPE;
+    if (cfg->act_bits == 4 && hbl::gemm_f6f4_eligible(M, K, N)) {
+        const size_t f = f6f4_ws_bytes(M, K, N);
+        if (f > *bytes) *bytes = f;
+    }
+    return HBL_OK;
+}
+
 hbl_status hbl_quantize_activations(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
                                     const hbl_config* cfg, void* codes, float* xscale, float* z_debug,
                                     float* s_debug, void* stream) {
@@ -189,15 +214,25 @@ hbl_status hbl_forward(const void* X, int32_t x_dtype, int64_t M, int64_t K, con
                                                        (hipStream_t)stream);
         return e == hipSuccess ? HBL_OK : hip_fail(e);
     }
+    const hipStream_t s = (hipStream_t)stream;
+    if (use_f6f4(M, K, N, cfg, ws_bytes)) {
+        uint8_t* codes6 = (uint8_t*)ws;
+        float* xs = (float*)(codes6 + round_up((size_t)M * (size_t)K * 3 / 4, 256));
+        uint8_t* W4 = (uint8_t*)xs + round_up((size_t)M * sizeof(float), 256);
+        hipError_t e = hbl::launch_act_quant(X, x_dtype, M, K, gain, *cfg, codes6, xs, nullptr, nullptr, s,
+                                             hbl::kCodesFp6);
+        if (e == hipSuccess) e = hbl::launch_weights_to_fp4(W_packed, N, K, W4, s);
+        if (e == hipSuccess) e = hbl::launch_gemm_f6f4(codes6, xs, M, K, W4, alpha, N, Y, y_dtype, s);
+        return e == hipSuccess ? HBL_OK : hip_fail(e);
+    }
     void* codes = ws;
     float* xscale = (float*)((uint8_t*)ws + cb);
     // codes that only the decode GEMM reads go out in its tile layout
     const bool tiled = hbl::gemm_uses_decode_kernel(M, K);
-    hipError_t e = hbl::launch_act_quant(X, x_dtype, M, K, gain, *cfg, codes, xscale, nullptr, nullptr,
-                                         (hipStream_t)stream, tiled);
+    hipError_t e = hbl::launch_act_quant(X, x_dtype, M, K, gain, *cfg, codes, xscale, nullptr, nullptr, s,
+                                         tiled ? hbl::kCodesDecTiled : hbl::kCodesRowMajor);
     if (e != hipSuccess) return hip_fail(e);
-    e = hbl::launch_gemm(codes, xscale, cfg->act_bits, M, K, W_packed, alpha, N, Y, y_dtype, (hipStream_t)stream,
-                         tiled);
+    e = hbl::launch_gemm(codes, xscale, cfg->act_bits, M, K, W_packed, alpha, N, Y, y_dtype, s, tiled);
     return e == hipSuccess ? HBL_OK : hip_fail(e);
 }
 
@@ -229,22 +264,30 @@ hbl_status hbl_forward_latent(const void* X, int32_t x_dtype, int64_t M, int64_t
             e = hbl::launch_forward_small(X, x_dtype, M, K, gain, *cfg, W_packed, alpha, N, Y, y_dtype, s);
         return e == hipSuccess ? HBL_OK : hip_fail(e);
     }
+    const bool f6 = use_f6f4(M, K, N, cfg, ws_bytes);
     void* codes = ws;
-    float* xscale = (float*)((uint8_t*)ws + cb);
+    float* xscale = (float*)((uint8_t*)ws + (f6 ? round_up((size_t)M * (size_t)K * 3 / 4, 256) : cb));
+    uint8_t* W4 = (uint8_t*)xscale + round_up((size_t)M * sizeof(float), 256);  // FP6 x FP4 path only
     const bool tiled = hbl::gemm_uses_decode_kernel(M, K);
+    const int layout = f6 ? hbl::kCodesFp6 : tiled ? hbl::kCodesDecTiled : hbl::kCodesRowMajor;
     if (K <= kFuseActPackMaxK) {
         // short rows: the activation blocks and the packing blocks share one grid
         e = hbl::launch_weight_partial(W, w_dtype, N * K, (double*)wws, n_partial, s);
         if (e == hipSuccess)
             e = hbl::launch_act_and_pack(X, x_dtype, M, K, gain, *cfg, codes, xscale, W, w_dtype, N * K, w_eps,
-                                         (const double*)wws, n_partial, W_packed, alpha, s, tiled);
+                                         (const double*)wws, n_partial, W_packed, alpha, s, layout);
     } else {
         e = hbl::launch_weight_quant(W, w_dtype, N, K, w_eps, W_packed, alpha, (double*)wws, n_partial, s);
         if (e == hipSuccess)
-            e = hbl::launch_act_quant(X, x_dtype, M, K, gain, *cfg, codes, xscale, nullptr, nullptr, s, tiled);
+            e = hbl::launch_act_quant(X, x_dtype, M, K, gain, *cfg, codes, xscale, nullptr, nullptr, s, layout);
     }
-    if (e == hipSuccess)
+    if (f6) {
+        if (e == hipSuccess) e = hbl::launch_weights_to_fp4(W_packed, N, K, W4, s);
+        if (e == hipSuccess)
+            e = hbl::launch_gemm_f6f4((const uint8_t*)codes, xscale, M, K, W4, alpha, N, Y, y_dtype, s);
+    } else if (e == hipSuccess) {
         e = hbl::launch_gemm(codes, xscale, cfg->act_bits, M, K, W_packed, alpha, N, Y, y_dtype, s, tiled);
+    }
     return e == hipSuccess ? HBL_OK : hip_fail(e);
 }
 

@@ -561,7 +561,237 @@ hipError_t launch_typed(const uint8_t* A, const float* xscale, int64_t M, int64_
     return hipGetLastError();
 }
 
+// ===================================================== FP6 x FP4 GEMM ==
+// INT4 codes x ternary weights on v_mfma_f32_32x32x64_f8f6f4 with the codes
+// as FP6 E3M2 and the weights as FP4 E2M1 (formats in hbl_device.h): on gfx950
+// this runs at twice the INT8 MFMA rate.  Every product is an integer and
+// every partial sum is below 2^24 in magnitude (|acc| <= 8*K <= 2^18), so the
+// fp32 accumulation is exact in any order and equals the INT8 path's int32
+// accumulator; the epilogue applies the same two rounded products, so the
+// outputs are the same bit for bit.
+// Block 256 x 256, 8 waves in a 4 x 2 grid of 64 x 128 wave tiles (2 x 4 MFMA
+// tiles of 32 x 32), K step 128 = two MFMA k-steps.  Per K step a row moves
+// 96 bytes of codes and 64 bytes of weights global -> LDS directly (as in the
+// INT8 kernel), through a ring of 3 stages of 40 KiB.  Physical 16-byte chunk
+// of logical chunk L of row r in LDS (bank-conflict-free 16-byte reads):
+//   codes, 16-byte pieces (chunks 0..3): L ^ ((r >> 3) & 1)
+//   codes, 8-byte pieces  (chunks 4, 5): 4 + ((L - 4) ^ ((r >> 3) & 1))
+//   weights (chunks 0..3):               L ^ ((r >> 2) & 3)
+// Both maps are their own inverse; they are applied on the global side.
+constexpr int kF6BM = 256, kF6BN = 256, kF6Waves = 8, kF6Stages = 3;
+constexpr int kF6ARow = 96, kF6WRow = 64;  // bytes per row and K step
+constexpr int kF6ABytes = kF6BM * kF6ARow, kF6WBytes = kF6BN * kF6WRow;
+constexpr int kF6Stage = kF6ABytes + kF6WBytes;
+constexpr int kF6AInst = kF6ABytes / 1024 / kF6Waves, kF6WInst = kF6WBytes / 1024 / kF6Waves;
+constexpr int kF6Inst = kF6AInst + kF6WInst;
+static_assert(kF6ABytes % (1024 * kF6Waves) == 0 && kF6WBytes % (1024 * kF6Waves) == 0, "whole wave instructions");
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+HBL_DEVINL int f6_a_chunk(int L, int r) {
+    const int f = (r >> 3) & 1;
+    return L < 4 ? (L ^ f) : 4 + ((L - 4) ^ f);
+}
+HBL_DEVINL int f6_w_chunk(int L, int r) { return L ^ ((r >> 2) & 3); }
+
+template <typename YT>
+__global__ __launch_bounds__(64 * kF6Waves, 2) void gemm_f6f4_kernel(const uint8_t* __restrict__ A6,
+                                                                   const float* __restrict__ xscale, int64_t M,
+                                                                   int64_t K, const uint8_t* __restrict__ W4,
+                                                                   const float* __restrict__ alpha_p, int64_t N,
+                                                                   YT* __restrict__ Y, int tiles_n, int tiles_total) {
+    constexpr int S = kF6Stages;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * kF6Stage];
+    __shared__ __attribute__((aligned(16))) float xs_tile[kF6BM];
+
+    const int b = blockIdx.x;
+    const int tile = (tiles_total % 8 == 0) ? (b % 8) * (tiles_total / 8) + b / 8 : b;
+    const int64_t m0 = (int64_t)(tile / tiles_n) * kF6BM;
+    const int64_t n0 = (int64_t)(tile % tiles_n) * kF6BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t a_ld = K * 3 / 4;  // bytes per code row
+    const int64_t w_ld = K / 2;      // bytes per weight row
+    const int KT = (int)(K / kBK);
+
+    const v4u a_desc = rsrc_words(A6 + m0 * a_ld, (M - m0) * a_ld);
+    const v4u w_desc = rsrc_words(W4 + n0 * w_ld, (N - n0) * w_ld);
+    uint32_t a_off[kF6AInst], w_off[kF6WInst];
+#pragma unroll
+    for (int u = 0; u < kF6AInst; u++) {
+        const int c = (wave * kF6AInst + u) * 64 + lane;  // physical chunk index in the tile
+        const int row = c / 6, p = c % 6;
+        a_off[u] = (uint32_t)(row * a_ld + f6_a_chunk(p, row) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < kF6WInst; u++) {
+        const int c = (wave * kF6WInst + u) * 64 + lane;
+        const int row = c / 4, p = c % 4;
+        w_off[u] = (uint32_t)(row * w_ld + f6_w_chunk(p, row) * 16);
+    }
+    const uint32_t smem_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+    auto issue = [&](int kt, int st) {
+        const uint32_t base = smem_addr + (uint32_t)(st * kF6Stage);
+#pragma unroll
+        for (int u = 0; u < kF6AInst; u++)
+            lds_dma16(a_desc, __builtin_amdgcn_readfirstlane(base + (uint32_t)((wave * kF6AInst + u) * 1024)),
+                      a_off[u] + (uint32_t)(kt * kF6ARow));
+#pragma unroll
+        for (int u = 0; u < kF6WInst; u++)
+            lds_dma16(w_desc,
+                      __builtin_amdgcn_readfirstlane(base + (uint32_t)(kF6ABytes + (wave * kF6WInst + u) * 1024)),
+                      w_off[u] + (uint32_t)(kt * kF6WRow));
+    };
+
+    v16f acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+    const int lr = lane & 31;  // row (codes) / column (weights) inside a 32-wide MFMA tile
+    const int lh = lane >> 5;  // lane half: k 32*lh .. +31 of each 64-k MFMA step
+    auto compute = [&](int st) {
+        const uint8_t* stage = smem + st * kF6Stage;
+#pragma unroll
+        for (int s = 0; s < 2; s++) {
+            v8i a[2], w[4];
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const int row = wm * 64 + i * 32 + lr;
+                const uint8_t* rp = stage + row * kF6ARow;
+                const uint4 q = *reinterpret_cast<const uint4*>(rp + f6_a_chunk(2 * s + lh, row) * 16);
+                const uint2 t = *reinterpret_cast<const uint2*>(rp + f6_a_chunk(4 + lh, row) * 16 + 8 * s);
+                a[i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, (int)t.x, (int)t.y, 0, 0};
+            }
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int col = wn * 128 + j * 32 + lr;
+                const uint4 q = *reinterpret_cast<const uint4*>(stage + kF6ABytes + col * kF6WRow +
+                                                                f6_w_chunk(2 * s + lh, col) * 16);
+                w[j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)  // formats: 3 = FP6 E3M2 (codes), 4 = FP4 E2M1 (weights); unscaled
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], w[j], acc[i][j], 3, 4, 0, 0,
+                                                                              0, 0);
+        }
+    };
+
+    float xs_r = 0.f;  // scale of row tid (0 past M), used only in the epilogue
+    {
+        const __amdgpu_buffer_rsrc_t xs_rsrc = make_rsrc(xscale + m0, (M - m0) * 4);
+        xs_r = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xs_rsrc, (tid & (kF6BM - 1)) * 4, 0, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < S - 1; u++) issue(min(u, KT - 1), u);
+    for (int kt = 0; kt < KT; kt++) {
+        wait_vmcnt<(S - 2) * kF6Inst>();  // this wave's loads of step kt have landed
+        barrier_no_wait();                // ... and every wave's; stage (kt-1)%S is free
+        issue(min(kt + S - 1, KT - 1), (kt + S - 1) % S);
+        compute(kt % S);
+    }
+    wait_vmcnt<0>();  // no LDS-direct load may still be in flight when the block ends
+    if (tid < kF6BM) xs_tile[tid] = xs_r;
+    __syncthreads();
+
+    // epilogue as in the INT8 kernel: lane holds column lr, rows 8*(r/4) + 4*lh + r%4 of each tile
+    const float alpha = *alpha_p;
+    const int rows_here = (int)min<int64_t>(kF6BM, M - m0);
+    const uint32_t row_bytes = (uint32_t)(N * (int64_t)sizeof(YT));
+    const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(Y + m0 * N, (int64_t)rows_here * row_bytes);
+    const int row0 = wm * 64 + 4 * lh;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int64_t n = n0 + wn * 128 + j * 32 + lr;
+        const uint32_t lane_off = n < N ? (uint32_t)row0 * row_bytes + (uint32_t)(n * (int64_t)sizeof(YT)) : kDropOffset;
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const float4 xs4 = *reinterpret_cast<const float4*>(&xs_tile[row0 + i * 32 + 8 * q]);
+                const float xsr[4] = {xs4.x, xs4.y, xs4.z, xs4.w};
+                float y[4];
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const float t = acc[i][j][4 * q + r] * xsr[r];  // two separately rounded products
+                    y[r] = t * alpha;
+                }
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const uint32_t off = lane_off + (uint32_t)(i * 32 + 8 * q + r) * row_bytes;
+                    if constexpr (sizeof(YT) == 4) {
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y[r]), y_rsrc, (int)off, 0, 0);
+                    } else if (r % 2 == 0) {
+                        const v2bf h = __builtin_convertvector((v2f){y[r], y[r + 1]}, v2bf);
+                        const uint32_t hp = __builtin_bit_cast(uint32_t, h);
+                        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(hp & 0xFFFFu), y_rsrc, (int)off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(hp >> 16), y_rsrc, (int)(off + row_bytes), 0, 0);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// 2-bit packed weights -> FP4 E2M1: one 32-bit word (16 weights; weight e of
+// the group at bits 8*(e%4) + 2*(e/4)) -> 8 bytes (weight e at nibble e).
+// The 2-bit code c (00 = 0, 01 = +1, 11 = -1) becomes (c & 1) << 1 | (c & 2) << 2:
+// 0000 = 0, 0010 = +1.0, 1010 = -1.0.
+__global__ __launch_bounds__(256) void weights_to_fp4_kernel(const uint32_t* __restrict__ Wp, int64_t n_words,
+                                                             uint2* __restrict__ W4) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_words) return;
+    const uint32_t w = Wp[i];
+    uint32_t o[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16; e++) {
+        const uint32_t c = (w >> (8 * (e & 3) + 2 * (e >> 2))) & 3u;
+        o[e >> 3] |= (((c & 1u) << 1) | ((c & 2u) << 2)) << (4 * (e & 7));
+    }
+    W4[i] = make_uint2(o[0], o[1]);
+}
+
 }  // namespace
+
+bool gemm_f6f4_eligible(int64_t M, int64_t K, int64_t N) {
+    // prefill shapes with at least 128 tiles of 256 x 256 (fewer tiles leave
+    // CUs idle; the INT8 path then has smaller tiles); K >= 512 so that the
+    // activation kernel writes whole FP6 bytes
+    return M > 64 && K >= 512 && K % kBK == 0 && ((M + kF6BM - 1) / kF6BM) * ((N + kF6BN - 1) / kF6BN) >= 128;
+}
+
+hipError_t launch_gemm_f6f4(const uint8_t* codes6, const float* xscale, int64_t M, int64_t K, const uint8_t* W4,
+                            const float* alpha, int64_t N, void* Y, int y_dtype, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    const int tiles_n = (int)((N + kF6BN - 1) / kF6BN);
+    const int64_t tiles = (int64_t)tiles_n * ((M + kF6BM - 1) / kF6BM);
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int tt = (int)tiles;
+    if (y_dtype == HBL_F32)
+        hipLaunchKernelGGL(gemm_f6f4_kernel<float>, dim3(tt), dim3(64 * kF6Waves), 0, s, codes6, xscale, M, K, W4,
+                           alpha, N, (float*)Y, tiles_n, tt);
+    else
+        hipLaunchKernelGGL(gemm_f6f4_kernel<uint16_t>, dim3(tt), dim3(64 * kF6Waves), 0, s, codes6, xscale, M, K, W4,
+                           alpha, N, (uint16_t*)Y, tiles_n, tt);
+    return hipGetLastError();
+}
+
+hipError_t launch_weights_to_fp4(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W4, hipStream_t s) {
+    const int64_t n_words = N * K / 16;
+    const int64_t blocks = (n_words + 255) / 256;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(weights_to_fp4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint32_t*)W_packed,
+                       n_words, (uint2*)W4);
+    return hipGetLastError();
+}
 
 bool gemm_uses_decode_kernel(int64_t M, int64_t K) {
     return M >= 1 && M <= 64 && !gemv_small_shape(M, K) && K % 256 == 0 && K / 256 <= kDecWaves * kDecMaxSS;

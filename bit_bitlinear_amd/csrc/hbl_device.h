@@ -60,6 +60,32 @@ HBL_DEVINL int dec_tile_offset(int kb) {  // kb: byte index of the code inside i
     return (kb / SSB) * 16 * SSB + ((rem % Q) / 16 * 64 + rem / Q * 16) * 16 + kb % 16;
 }
 
+// ---- INT4 codes as FP6 E3M2 for the FP6 x FP4 prefill GEMM ----
+// The gfx950 matrix cores multiply FP6 by FP4 at twice the INT8 rate, and
+// every INT4 code in [-8, 7] is exact in FP6 E3M2 (1 sign, 3 exponent bits
+// with bias 3, 2 mantissa bits); a ternary weight is exact in FP4 E2M1.
+// Code k of a row in natural order is the 6-bit field at bit 6k of a bit
+// string, so 128 codes (one GEMM K step) are 96 bytes.  Inside a step, the 32
+// codes k = 64s + 32h + j (j = 0..31) form one MFMA operand of 24 bytes; its
+// first 16 bytes are stored as 16-byte chunk 2s + h of the step and its last
+// 8 bytes as half s of chunk 4 + h, so that every lane reads one 16-byte and
+// one 8-byte piece.  A row is K*3/4 bytes.
+enum { kCodesRowMajor = 0, kCodesDecTiled = 1, kCodesFp6 = 2 };
+
+// Position of byte nb of a row's natural FP6 bit string in the layout above.
+HBL_DEVINL int fp6_byte_offset(int nb) {
+    const int o = nb % 96, op = o / 24, ob = o % 24, s = op >> 1, h = op & 1;
+    return nb - o + (ob < 16 ? (2 * s + h) * 16 + ob : (4 + h) * 16 + 8 * s + (ob - 16));
+}
+
+// FP6 E3M2 encoding of an integer v in [-8, 8]: magnitudes 0..8 map to
+// 0, 12, 16, 18, 20, 21, 22, 23, 24 (exponent field e, mantissa m: (1 + m/4) * 2^(e-3)).
+HBL_DEVINL uint32_t fp6_e3m2(int v) {
+    const uint32_t a = (uint32_t)(v < 0 ? -v : v);
+    const uint32_t mag = a >= 8 ? 24u : (__builtin_amdgcn_perm(0x17161514u, 0x12100C00u, a) & 0xFFu);
+    return mag | (v < 0 ? 32u : 0u);
+}
+
 // ---- wave / block reductions (fixed butterfly order: deterministic) ----
 HBL_DEVINL float wave_sum_f32(float v) {
 #pragma unroll
@@ -137,15 +163,24 @@ hipError_t launch_weight_partial(const void* W, int w_dtype, int64_t count, doub
 hipError_t launch_act_and_pack(const void* X, int x_dtype, int64_t M, int64_t K, const float* gain,
                                const hbl_config& cfg, void* codes, float* xscale, const void* W, int w_dtype,
                                int64_t NK, float w_eps, const double* partial, int n_partial, uint8_t* W_packed,
-                               float* alpha, hipStream_t s, bool dec_tiled = false);  // K <= 2048
+                               float* alpha, hipStream_t s, int layout = kCodesRowMajor);  // K <= 2048
 
+// layout: kCodesRowMajor (the ABI's), kCodesDecTiled, or kCodesFp6 (INT4, K >= 512)
 hipError_t launch_act_quant(const void* X, int x_dtype, int64_t M, int64_t K, const float* gain,
                             const hbl_config& cfg, void* codes, float* xscale, float* z_debug, float* s_debug,
-                            hipStream_t s, bool dec_tiled = false);
+                            hipStream_t s, int layout = kCodesRowMajor);
 
 hipError_t launch_gemm(const void* codes, const float* xscale, int act_bits, int64_t M, int64_t K,
                        const uint8_t* W_packed, const float* alpha, int64_t N, void* Y, int y_dtype,
                        hipStream_t s, bool dec_tiled = false);
+// FP6 x FP4 prefill GEMM (INT4 activation codes only): codes in the FP6
+// layout above, weights as FP4 E2M1 nibbles (W4: N rows of K/2 bytes, code k
+// at nibble k, low nibble first).  Same results as launch_gemm, bit for bit.
+bool gemm_f6f4_eligible(int64_t M, int64_t K, int64_t N);
+hipError_t launch_gemm_f6f4(const uint8_t* codes6, const float* xscale, int64_t M, int64_t K, const uint8_t* W4,
+                            const float* alpha, int64_t N, void* Y, int y_dtype, hipStream_t s);
+// 2-bit packed ternary weights -> FP4 E2M1 nibbles (W4 as above)
+hipError_t launch_weights_to_fp4(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W4, hipStream_t s);
 // true when launch_gemm runs the decode GEMM for this shape; the codes may
 // then be in the decode tile layout (rows padded to a multiple of 16)
 bool gemm_uses_decode_kernel(int64_t M, int64_t K);

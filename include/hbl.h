@@ -116,6 +116,20 @@ hbl_status hbl_quantize_weights(const void* W, int32_t w_dtype, int64_t N, int64
 hbl_status hbl_workspace_bytes(int64_t M, int64_t K, const hbl_config* cfg, size_t* bytes);
 
 /*
+ * Workspace with which hbl_forward and hbl_forward_latent take their fastest
+ * path for an M x K by N x K layer: >= hbl_workspace_bytes(M, K, cfg).  For
+ * INT4 activations at prefill sizes (M > 64, K >= 512, at least 128 output
+ * tiles of 256 x 256) it adds room for the codes as FP6 and the weights as
+ * FP4, and a workspace of this size lets the forward multiply them on the
+ * gfx950 FP6 x FP4 matrix cores (twice the INT8 rate).  The products and
+ * sums are exact integers there as well, so Y is the same bit for bit with
+ * either workspace size (the hardware-format reading of the pages' remark
+ * that 4-bit activations suit native low-bit compute, "新智元: 微软 BitNet v2",
+ * section "原生4比特盘算").  N in [1, 2^20]; other errors as hbl_workspace_bytes.
+ */
+hbl_status hbl_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, const hbl_config* cfg, size_t* bytes);
+
+/*
  * Activation half of the layer, per token row m of X [M][K] (fp32 or bf16):
  *   r = norm(x) * gain   (RMS: x/sqrt(mean x^2 + norm_eps); LN: (x-mean)/
  *                          sqrt(var + norm_eps); NONE: x; gain NULL = 1)

@@ -20,7 +20,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = hbl.declared_symbols()
-    assert len(names) == 10
+    assert len(names) == 11
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
 
@@ -48,6 +48,16 @@ def test_size_queries():
     # up to 64 tokens the codes region holds whole 16-row tiles
     assert hbl.hbl_workspace_bytes(5, 1024, hbl.Config(act_bits=8)) >= 16 * 1024 + 5 * 4
     assert hbl.hbl_workspace_bytes(65, 1024, hbl.Config(act_bits=8)) < 80 * 1024
+    # the FP6 x FP4 path's workspace: INT4 prefill shapes only
+    c4, c8 = hbl.Config(act_bits=4), hbl.Config(act_bits=8)
+    big = hbl.hbl_forward_workspace_bytes(8192, 16384, 4096, c4)
+    assert big >= 8192 * 16384 * 3 // 4 + 8192 * 4 + 4096 * 16384 // 2
+    assert hbl.hbl_forward_workspace_bytes(8192, 16384, 4096, c8) == hbl.hbl_workspace_bytes(8192, 16384, c8)
+    assert hbl.hbl_forward_workspace_bytes(64, 8192, 4096, c4) == hbl.hbl_workspace_bytes(64, 8192, c4)
+    assert hbl.hbl_forward_workspace_bytes(256, 4096, 4096, c4) == hbl.hbl_workspace_bytes(256, 4096, c4)
+    with pytest.raises(hbl.HblError) as e:
+        hbl.hbl_forward_workspace_bytes(8, 256, 0, c4)
+    assert e.value.status == 2
     with pytest.raises(hbl.HblError) as e:
         hbl.hbl_packed_weight_bytes(16, 40)
     assert e.value.status == 4

@@ -395,6 +395,83 @@ def test_forward_decode_tiled_matches_stages(M, K, N, bits, had, xdt, ydt):
     assert np.array_equal(got[:, cols], y_exact if ydt == "f32" else oracle.f32_to_bf16(y_exact))
 
 
+# INT4 prefill shapes with the larger workspace (hbl_forward_workspace_bytes)
+# run on the FP6 x FP4 matrix cores: codes as FP6 E3M2, weights as FP4 E2M1,
+# exact fp32 sums.  Y must equal the INT8-MFMA path (the smaller workspace)
+# and the stage entry points bit for bit, and the oracle's arithmetic on
+# sampled columns.  Ragged M and N, K from 512 to the maximum, both norms,
+# with and without the Hadamard, both input and output dtypes.
+F6F4_CASES = [
+    # (M, K, N, hadamard, x dtype, y dtype, norm)
+    (300, 2048, 32768, True, "bf16", "bf16", hbl.HBL_NORM_RMS),
+    (4100, 512, 8000, True, "f32", "f32", hbl.HBL_NORM_RMS),
+    (1024, 4096, 8192, False, "bf16", "bf16", hbl.HBL_NORM_RMS),
+    (4096, 32768, 2048, True, "bf16", "f32", hbl.HBL_NORM_LN),
+    (8192, 16384, 4096, True, "bf16", "bf16", hbl.HBL_NORM_RMS),
+]
+
+
+@pytest.mark.parametrize("M,K,N,had,xdt,ydt,norm", F6F4_CASES)
+def test_forward_f6f4_matches_int8_path(M, K, N, had, xdt, ydt, norm):
+    import torch
+    _announce("forward fp6xfp4 M=%d K=%d N=%d had=%d %s->%s norm=%d" % (M, K, N, had, xdt, ydt, norm))
+    rng = np.random.default_rng(M + K * 3 + N)
+    X, _ = workloads.x_outlier_gaussian(rng, M, K, 4, 30.0)
+    if norm == hbl.HBL_NORM_LN:
+        X = (X + np.float32(2.0)).astype(np.float32)
+    W = workloads.w_latent(rng, N, K)
+    Xd = to_dev(workloads.f32_to_bf16_bits(X) if xdt == "bf16" else X)
+    cfg = hbl.Config(act_bits=4, hadamard=had, norm=norm)
+    small = hbl.hbl_workspace_bytes(M, K, cfg)
+    big = hbl.hbl_forward_workspace_bytes(M, K, N, cfg)
+    assert big > small  # the shape takes the FP6 x FP4 path with the larger workspace
+    Wp, alpha = hbl.hbl_quantize_weights(to_dev(W))
+    yt = torch.float32 if ydt == "f32" else torch.bfloat16
+    Y6 = hbl.hbl_forward(Xd, Wp, alpha, N, cfg, y_dtype=yt,
+                         ws=torch.empty(big, dtype=torch.uint8, device="cuda:0"))
+    Y8 = hbl.hbl_forward(Xd, Wp, alpha, N, cfg, y_dtype=yt,
+                         ws=torch.empty(small, dtype=torch.uint8, device="cuda:0"))
+    codes, xs, _, _ = hbl.hbl_quantize_activations(Xd, cfg)
+    Y2 = hbl.hbl_gemm(codes, xs, 4, K, Wp, alpha, N, y_dtype=yt)
+    _sync()
+    got = to_host(Y6)
+    assert np.array_equal(got, to_host(Y8))
+    assert np.array_equal(got, to_host(Y2))
+    rows = workloads.sample_rows(M, 24)
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 24)]))
+    q = unpack_codes(to_host(codes)[rows], K, 4)
+    a = to_host(alpha)[0]
+    y_exact = oracle.rescale(oracle.int_gemm(q, oracle.ternarize(W[cols], a, 1e-5)), to_host(xs)[rows], a)
+    sub = got[np.ix_(rows, cols)]
+    assert np.array_equal(sub, y_exact if ydt == "f32" else oracle.f32_to_bf16(y_exact))
+
+
+@pytest.mark.parametrize("M,K,N,xdt,wdt", [(4096, 2048, 4096, "bf16", "f32"), (2048, 8192, 8192, "f32", "bf16")])
+def test_forward_latent_f6f4_matches_two_calls(M, K, N, xdt, wdt):
+    """Latent weights with the larger workspace: activation codes as FP6 (in
+    the shared activation / packing grid for K <= 2048), weights packed, then
+    converted to FP4; equal to hbl_quantize_weights + hbl_forward (INT8 path)."""
+    import torch
+    _announce("forward_latent fp6xfp4 M=%d K=%d N=%d x %s W %s" % (M, K, N, xdt, wdt))
+    rng = np.random.default_rng(M + K + N + 4)
+    X, _ = workloads.x_outlier_gaussian(rng, M, K, 4, 30.0)
+    W = workloads.w_latent(rng, N, K)
+    Xd = to_dev(workloads.f32_to_bf16_bits(X) if xdt == "bf16" else X)
+    Wd = to_dev(workloads.f32_to_bf16_bits(W) if wdt == "bf16" else W)
+    cfg = hbl.Config(act_bits=4, hadamard=True)
+    big = hbl.hbl_forward_workspace_bytes(M, K, N, cfg)
+    assert big > hbl.hbl_workspace_bytes(M, K, cfg)
+    Y, Wp, alpha = hbl.hbl_forward_latent(Xd, Wd, cfg, eps=1e-5, y_dtype=torch.bfloat16,
+                                          ws=torch.empty(big, dtype=torch.uint8, device="cuda:0"))
+    Wp2, alpha2 = hbl.hbl_quantize_weights(Wd, eps=1e-5)
+    small = torch.empty(hbl.hbl_workspace_bytes(M, K, cfg), dtype=torch.uint8, device="cuda:0")
+    Y2 = hbl.hbl_forward(Xd, Wp2, alpha2, N, cfg, y_dtype=torch.bfloat16, ws=small)
+    _sync()
+    assert np.array_equal(to_host(alpha), to_host(alpha2))
+    assert np.array_equal(to_host(Wp), to_host(Wp2))
+    assert np.array_equal(to_host(Y), to_host(Y2))
+
+
 # hbl_forward_latent: weights ternarised and the forward run in three launches
 # (activation quantisation and weight packing share a grid); Y, W_packed and
 # alpha must equal hbl_quantize_weights + hbl_forward bit for bit.
