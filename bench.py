@@ -98,7 +98,10 @@ def main():
     Wd = torch.from_numpy(W).to(dev)
     ydt = torch.bfloat16 if layer.y_dtype == "bf16" else torch.float32
     cfg = hbl.Config(act_bits=bits, hadamard=layer.hadamard)
-    ws_bytes = hbl.hbl_workspace_bytes(M, K, cfg)
+    # the workspace that selects the fastest forward path (FP6 x FP4 matrix
+    # cores for INT4 prefill shapes, else the INT8 ones)
+    ws_bytes = hbl.hbl_forward_workspace_bytes(M, K, N, cfg)
+    f6f4 = ws_bytes > hbl.hbl_workspace_bytes(M, K, cfg)
     wws_bytes = hbl.hbl_weight_workspace_bytes(N, K)
     y_bytes = M * N * (2 if ydt == torch.bfloat16 else 4)
     set_bytes = Xd.numel() * Xd.element_size() + Wd.numel() * 4 + N * K // 4 + ws_bytes + y_bytes
@@ -259,12 +262,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8",
+        "dtype": "fp6xfp4" if f6f4 else "i8",
         "data": "synthetic (seeded; outlier-channel activations, N(0,0.02) latent weights)",
         "config": {"workload": layer.desc, "M": M, "K": K, "N": N, "act_bits": bits,
                    "hadamard": layer.hadamard, "x_dtype": layer.x_dtype, "y_dtype": layer.y_dtype,
                    "step": "hbl_forward_latent (ternarise latent W + forward; = hbl_quantize_weights then "
                            "hbl_forward, bit for bit)", "rotating_sets": R,
+                   "gemm": ("FP6 x FP4 matrix cores (INT4 codes as FP6 E3M2, ternary as FP4 E2M1, exact fp32 sums)"
+                            if f6f4 else "INT8 matrix cores (int32 sums)"),
                    "timing": "HIP graph replay of captured launches"},
         "tops": round(2.0 * M * N * K * timed_steps / wall / 1e12, 2),
         "ms_per_step_two_calls": round(wall_two / timed_steps * 1e3, 5),

@@ -59,7 +59,9 @@ hipError_t launch_ap(const Tin* X, int64_t M, const float* gain, const hbl_confi
                      const TW* W, int64_t NK, float w_eps, const double* partial, int n_partial, uint8_t* Wp,
                      float* alpha, hipStream_t s) {
     constexpr int NT = threads_for(LK);
-    const size_t lds_bytes = HAD ? (size_t)ActShape<LK, NT, Tin>::lds_floats * sizeof(float) : 0;
+    // the Hadamard's fp32 row; the FP6 layout stages its K*3/4 code bytes there too
+    const size_t row_bytes = HAD ? (size_t)ActShape<LK, NT, Tin>::lds_floats * sizeof(float) : 0;
+    const size_t lds_bytes = LAYOUT == kCodesFp6 && row_bytes < (size_t)(3 << LK) / 4 ? (size_t)(3 << LK) / 4 : row_bytes;
     auto kern = act_pack_kernel<LK, NT, Tin, BITS, HAD, TW, LAYOUT>;
     static bool attr_set = false;  // one attribute call per instantiation
     if (!attr_set && lds_bytes > 0) {

@@ -31,7 +31,9 @@ template <int LK, typename Tin, int BITS, bool HAD, int LAYOUT>
 hipError_t launch_one(const Tin* X, int64_t M, const float* gain, const hbl_config& cfg, void* codes, float* xscale,
                       float* z_debug, float* s_debug, hipStream_t s) {
     constexpr int NT = threads_for(LK);
-    const size_t lds_bytes = HAD ? (size_t)ActShape<LK, NT, Tin>::lds_floats * sizeof(float) : 0;
+    // the Hadamard's fp32 row; the FP6 layout stages its K*3/4 code bytes there too
+    const size_t row_bytes = HAD ? (size_t)ActShape<LK, NT, Tin>::lds_floats * sizeof(float) : 0;
+    const size_t lds_bytes = LAYOUT == kCodesFp6 && row_bytes < (size_t)(3 << LK) / 4 ? (size_t)(3 << LK) / 4 : row_bytes;
     auto kern = act_quant_kernel<LK, NT, Tin, BITS, HAD, LAYOUT>;
     static bool attr_set = false;  // one attribute call per instantiation
     if (!attr_set && lds_bytes > 0) {

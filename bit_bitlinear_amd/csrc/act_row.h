@@ -413,13 +413,15 @@ HBL_DEVINL void act_row_quantise(ActRegs<LK, NT, Tin>& v, const float* __restric
         for (int x2 = 0; x2 < VW; x2++) b[x2] = code_bits(z[x2], s_mul, lo, hi);
         if constexpr (LAYOUT == kCodesFp6) {
             static_assert(BITS == 4 && VW == 4, "FP6 codes: INT4 values, four per vector");
-            // four 6-bit fields = 3 whole bytes at natural byte 3*e0/4
-            uint32_t f = 0;
+            // four 6-bit fields = 3 whole bytes at natural byte nb = 3*e0/4,
+            // staged in LDS (free since the statistic's barrier) in their
+            // final order; one 16-byte piece and one 8-byte piece per operand
+            const uint32_t f = fp6_e3m2_x4(b[0], b[1], b[2], b[3]);
+            const int nb = 3 * e0 / 4, o = nb % 96, op = o / 24, ob = o % 24;
+            const int base16 = nb - o + op * 16, base8 = nb - o + (4 + (op & 1)) * 16 + 8 * (op >> 1) - 16;
+            uint8_t* const st = reinterpret_cast<uint8_t*>(lds);
 #pragma unroll
-            for (int x2 = 0; x2 < 4; x2++) f |= fp6_e3m2((int)(b[x2] << 28) >> 28) << (6 * x2);
-            const int nb = 3 * e0 / 4;
-#pragma unroll
-            for (int x2 = 0; x2 < 3; x2++) crow[fp6_byte_offset(nb + x2)] = (uint8_t)(f >> (8 * x2));
+            for (int x2 = 0; x2 < 3; x2++) st[(ob + x2 < 16 ? base16 : base8) + ob + x2] = (uint8_t)(f >> (8 * x2));
             continue;
         }
         // a vector's 2 or 4 code bytes never cross a 16-byte chunk of the tile layout
@@ -443,6 +445,12 @@ HBL_DEVINL void act_row_quantise(ActRegs<LK, NT, Tin>& v, const float* __restric
                 *cdst = (uint8_t)((b[0] & 0xFu) | ((b[1] & 0xFu) << 4));
             }
         }
+    }
+    if constexpr (LAYOUT == kCodesFp6) {
+        // the staged FP6 row (K*3/4 bytes) leaves in 16-byte stores
+        __syncthreads();
+        const uint4* src = reinterpret_cast<const uint4*>(lds);
+        for (int c = tid; c < K * 3 / 64; c += NT) reinterpret_cast<uint4*>(crow)[c] = src[c];
     }
 }
 

@@ -750,11 +750,16 @@ __global__ __launch_bounds__(256) void weights_to_fp4_kernel(const uint32_t* __r
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n_words) return;
     const uint32_t w = Wp[i];
-    uint32_t o[2] = {0u, 0u};
+    uint32_t o[2];
 #pragma unroll
-    for (int e = 0; e < 16; e++) {
-        const uint32_t c = (w >> (8 * (e & 3) + 2 * (e >> 2))) & 3u;
-        o[e >> 3] |= (((c & 1u) << 1) | ((c & 2u) << 2)) << (4 * (e & 7));
+    for (int half = 0; half < 2; half++) {
+        // bit pairs 2*half, 2*half+1 of each byte: weights b + 8*half and b + 4 + 8*half of byte b
+        const uint32_t x = (w >> (4 * half)) & 0x0F0F0F0Fu;
+        const uint32_t t = (x & 0x03030303u) | ((x & 0x0C0C0C0Cu) << 2);     // byte b: [pair lo | pair hi << 4]
+        const uint32_t u = ((t & 0x11111111u) << 1) | ((t & 0x22222222u) << 2);  // each 2-bit code -> FP4 nibble
+        // nibble transpose: low nibbles of bytes 0..3, then the high nibbles
+        const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
+        o[half] = __builtin_amdgcn_perm(hi | (hi >> 4), lo | (lo >> 4), 0x06040200u);
     }
     W4[i] = make_uint2(o[0], o[1]);
 }

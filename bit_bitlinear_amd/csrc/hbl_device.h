@@ -86,6 +86,21 @@ HBL_DEVINL uint32_t fp6_e3m2(int v) {
     return mag | (v < 0 ? 32u : 0u);
 }
 
+// Four INT4 codes (two's complement in the low 4 bits of c0..c3) -> their
+// FP6 E3M2 fields packed at bits 0, 6, 12, 18: a 16-entry byte table looked
+// up with two byte permutes (codes 0..7 and -8..-1), the same values as
+// fp6_e3m2.
+HBL_DEVINL uint32_t fp6_e3m2_x4(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3) {
+    const uint32_t idx = (__builtin_amdgcn_perm(c1, c0, 0x0c0c0400u) | __builtin_amdgcn_perm(c3, c2, 0x04000c0cu)) &
+                         0x0F0F0F0Fu;  // one code per byte
+    const uint32_t i7 = idx & 0x07070707u;
+    const uint32_t pos = __builtin_amdgcn_perm(0x17161514u, 0x12100C00u, i7);  // 0..7: 0 12 16 18 20 21 22 23
+    const uint32_t neg = __builtin_amdgcn_perm(0x2C303234u, 0x35363738u, i7);  // -8..-1: 56 55 54 53 52 50 48 44
+    const uint32_t m = ((idx >> 3) & 0x01010101u) * 0xFFu;                      // bytes holding a negative code
+    const uint32_t y = (neg & m) | (pos & ~m);
+    return (y & 0x3Fu) | ((y >> 2) & 0xFC0u) | ((y >> 4) & 0x3F000u) | ((y >> 6) & 0xFC0000u);
+}
+
 // ---- wave / block reductions (fixed butterfly order: deterministic) ----
 HBL_DEVINL float wave_sum_f32(float v) {
 #pragma unroll
