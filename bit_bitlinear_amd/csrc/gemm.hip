@@ -578,13 +578,7 @@ hipError_t launch_typed(const uint8_t* A, const float* xscale, int64_t M, int64_
 //   codes, 8-byte pieces  (chunks 4, 5): 4 + ((L - 4) ^ ((r >> 3) & 1))
 //   weights (chunks 0..3):               L ^ ((r >> 2) & 3)
 // Both maps are their own inverse; they are applied on the global side.
-constexpr int kF6BM = 256, kF6BN = 256, kF6Waves = 8, kF6Stages = 3;
 constexpr int kF6ARow = 96, kF6WRow = 64;  // bytes per row and K step
-constexpr int kF6ABytes = kF6BM * kF6ARow, kF6WBytes = kF6BN * kF6WRow;
-constexpr int kF6Stage = kF6ABytes + kF6WBytes;
-constexpr int kF6AInst = kF6ABytes / 1024 / kF6Waves, kF6WInst = kF6WBytes / 1024 / kF6Waves;
-constexpr int kF6Inst = kF6AInst + kF6WInst;
-static_assert(kF6ABytes % (1024 * kF6Waves) == 0 && kF6WBytes % (1024 * kF6Waves) == 0, "whole wave instructions");
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -595,125 +589,136 @@ HBL_DEVINL int f6_a_chunk(int L, int r) {
 }
 HBL_DEVINL int f6_w_chunk(int L, int r) { return L ^ ((r >> 2) & 3); }
 
-template <typename YT>
-__global__ __launch_bounds__(64 * kF6Waves, 2) void gemm_f6f4_kernel(const uint8_t* __restrict__ A6,
-                                                                   const float* __restrict__ xscale, int64_t M,
-                                                                   int64_t K, const uint8_t* __restrict__ W4,
-                                                                   const float* __restrict__ alpha_p, int64_t N,
-                                                                   YT* __restrict__ Y, int tiles_n, int tiles_total) {
-    constexpr int S = kF6Stages;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * kF6Stage];
-    __shared__ __attribute__((aligned(16))) float xs_tile[kF6BM];
+// Block BM x BN, WGM x WGN waves of (BM/WGM) x (BN/WGN), S-stage ring.
+template <int BM, int BN, int WGM, int WGN, int S>
+struct F6Tile {
+    static constexpr int NW = WGM * WGN, NT = 64 * NW;
+    static constexpr int TA = BM / WGM / 32, TB = BN / WGN / 32;  // 32 x 32 MFMA tiles per wave
+    static constexpr int a_bytes = BM * kF6ARow, w_bytes = BN * kF6WRow, stage = a_bytes + w_bytes;
+    static constexpr int a_inst = a_bytes / 1024 / NW, w_inst = w_bytes / 1024 / NW, inst = a_inst + w_inst;
+    static_assert(a_bytes % (1024 * NW) == 0 && w_bytes % (1024 * NW) == 0, "whole wave instructions");
+    static_assert(BM <= NT, "one scale per thread");
+};
+
+template <typename YT, int BM, int BN, int WGM, int WGN, int S>
+__global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_f6f4_kernel(
+    const uint8_t* __restrict__ A6, const float* __restrict__ xscale, int64_t M, int64_t K,
+    const uint8_t* __restrict__ W4, const float* __restrict__ alpha_p, int64_t N, YT* __restrict__ Y, int tiles_n,
+    int tiles_total) {
+    using T = F6Tile<BM, BN, WGM, WGN, S>;
+    constexpr int TA = T::TA, TB = T::TB;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * T::stage];
+    __shared__ __attribute__((aligned(16))) float xs_tile[BM];
 
     const int b = blockIdx.x;
     const int tile = (tiles_total % 8 == 0) ? (b % 8) * (tiles_total / 8) + b / 8 : b;
-    const int64_t m0 = (int64_t)(tile / tiles_n) * kF6BM;
-    const int64_t n0 = (int64_t)(tile % tiles_n) * kF6BN;
+    const int64_t m0 = (int64_t)(tile / tiles_n) * BM;
+    const int64_t n0 = (int64_t)(tile % tiles_n) * BN;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
     const int64_t a_ld = K * 3 / 4;  // bytes per code row
     const int64_t w_ld = K / 2;      // bytes per weight row
     const int KT = (int)(K / kBK);
 
     const v4u a_desc = rsrc_words(A6 + m0 * a_ld, (M - m0) * a_ld);
     const v4u w_desc = rsrc_words(W4 + n0 * w_ld, (N - n0) * w_ld);
-    uint32_t a_off[kF6AInst], w_off[kF6WInst];
+    uint32_t a_off[T::a_inst], w_off[T::w_inst];
 #pragma unroll
-    for (int u = 0; u < kF6AInst; u++) {
-        const int c = (wave * kF6AInst + u) * 64 + lane;  // physical chunk index in the tile
+    for (int u = 0; u < T::a_inst; u++) {
+        const int c = (wave * T::a_inst + u) * 64 + lane;  // physical chunk index in the tile
         const int row = c / 6, p = c % 6;
         a_off[u] = (uint32_t)(row * a_ld + f6_a_chunk(p, row) * 16);
     }
 #pragma unroll
-    for (int u = 0; u < kF6WInst; u++) {
-        const int c = (wave * kF6WInst + u) * 64 + lane;
+    for (int u = 0; u < T::w_inst; u++) {
+        const int c = (wave * T::w_inst + u) * 64 + lane;
         const int row = c / 4, p = c % 4;
         w_off[u] = (uint32_t)(row * w_ld + f6_w_chunk(p, row) * 16);
     }
     const uint32_t smem_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
     auto issue = [&](int kt, int st) {
-        const uint32_t base = smem_addr + (uint32_t)(st * kF6Stage);
+        const uint32_t base = smem_addr + (uint32_t)(st * T::stage);
 #pragma unroll
-        for (int u = 0; u < kF6AInst; u++)
-            lds_dma16(a_desc, __builtin_amdgcn_readfirstlane(base + (uint32_t)((wave * kF6AInst + u) * 1024)),
+        for (int u = 0; u < T::a_inst; u++)
+            lds_dma16(a_desc, __builtin_amdgcn_readfirstlane(base + (uint32_t)((wave * T::a_inst + u) * 1024)),
                       a_off[u] + (uint32_t)(kt * kF6ARow));
 #pragma unroll
-        for (int u = 0; u < kF6WInst; u++)
+        for (int u = 0; u < T::w_inst; u++)
             lds_dma16(w_desc,
-                      __builtin_amdgcn_readfirstlane(base + (uint32_t)(kF6ABytes + (wave * kF6WInst + u) * 1024)),
+                      __builtin_amdgcn_readfirstlane(base + (uint32_t)(T::a_bytes + (wave * T::w_inst + u) * 1024)),
                       w_off[u] + (uint32_t)(kt * kF6WRow));
     };
 
-    v16f acc[2][4];
+    v16f acc[TA][TB];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < TA; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < TB; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
     const int lr = lane & 31;  // row (codes) / column (weights) inside a 32-wide MFMA tile
     const int lh = lane >> 5;  // lane half: k 32*lh .. +31 of each 64-k MFMA step
     auto compute = [&](int st) {
-        const uint8_t* stage = smem + st * kF6Stage;
+        const uint8_t* stage = smem + st * T::stage;
 #pragma unroll
         for (int s = 0; s < 2; s++) {
-            v8i a[2], w[4];
+            v8i a[TA], w[TB];
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
-                const int row = wm * 64 + i * 32 + lr;
+            for (int i = 0; i < TA; i++) {
+                const int row = wm * 32 * TA + i * 32 + lr;
                 const uint8_t* rp = stage + row * kF6ARow;
                 const uint4 q = *reinterpret_cast<const uint4*>(rp + f6_a_chunk(2 * s + lh, row) * 16);
                 const uint2 t = *reinterpret_cast<const uint2*>(rp + f6_a_chunk(4 + lh, row) * 16 + 8 * s);
                 a[i] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, (int)t.x, (int)t.y, 0, 0};
             }
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int col = wn * 128 + j * 32 + lr;
-                const uint4 q = *reinterpret_cast<const uint4*>(stage + kF6ABytes + col * kF6WRow +
+            for (int j = 0; j < TB; j++) {
+                const int col = wn * 32 * TB + j * 32 + lr;
+                const uint4 q = *reinterpret_cast<const uint4*>(stage + T::a_bytes + col * kF6WRow +
                                                                 f6_w_chunk(2 * s + lh, col) * 16);
                 w[j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
             }
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+            for (int i = 0; i < TA; i++)
 #pragma unroll
-                for (int j = 0; j < 4; j++)  // formats: 3 = FP6 E3M2 (codes), 4 = FP4 E2M1 (weights); unscaled
+                for (int j = 0; j < TB; j++)  // formats: 3 = FP6 E3M2 (codes), 4 = FP4 E2M1 (weights); unscaled
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], w[j], acc[i][j], 3, 4, 0, 0,
                                                                               0, 0);
         }
     };
 
     float xs_r = 0.f;  // scale of row tid (0 past M), used only in the epilogue
-    {
+    if (tid < BM) {
         const __amdgpu_buffer_rsrc_t xs_rsrc = make_rsrc(xscale + m0, (M - m0) * 4);
-        xs_r = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xs_rsrc, (tid & (kF6BM - 1)) * 4, 0, 0));
+        xs_r = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xs_rsrc, tid * 4, 0, 0));
     }
 #pragma unroll
     for (int u = 0; u < S - 1; u++) issue(min(u, KT - 1), u);
     for (int kt = 0; kt < KT; kt++) {
-        wait_vmcnt<(S - 2) * kF6Inst>();  // this wave's loads of step kt have landed
+        wait_vmcnt<(S - 2) * T::inst>();  // this wave's loads of step kt have landed
         barrier_no_wait();                // ... and every wave's; stage (kt-1)%S is free
         issue(min(kt + S - 1, KT - 1), (kt + S - 1) % S);
         compute(kt % S);
     }
     wait_vmcnt<0>();  // no LDS-direct load may still be in flight when the block ends
-    if (tid < kF6BM) xs_tile[tid] = xs_r;
+    if (tid < BM) xs_tile[tid] = xs_r;
     __syncthreads();
 
     // epilogue as in the INT8 kernel: lane holds column lr, rows 8*(r/4) + 4*lh + r%4 of each tile
     const float alpha = *alpha_p;
-    const int rows_here = (int)min<int64_t>(kF6BM, M - m0);
+    const int rows_here = (int)min<int64_t>(BM, M - m0);
     const uint32_t row_bytes = (uint32_t)(N * (int64_t)sizeof(YT));
     const __amdgpu_buffer_rsrc_t y_rsrc = make_rsrc(Y + m0 * N, (int64_t)rows_here * row_bytes);
-    const int row0 = wm * 64 + 4 * lh;
+    const int row0 = wm * 32 * TA + 4 * lh;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int64_t n = n0 + wn * 128 + j * 32 + lr;
+    for (int j = 0; j < TB; j++) {
+        const int64_t n = n0 + wn * 32 * TB + j * 32 + lr;
         const uint32_t lane_off = n < N ? (uint32_t)row0 * row_bytes + (uint32_t)(n * (int64_t)sizeof(YT)) : kDropOffset;
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
+        for (int i = 0; i < TA; i++) {
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 const float4 xs4 = *reinterpret_cast<const float4*>(&xs_tile[row0 + i * 32 + 8 * q]);
@@ -740,6 +745,9 @@ __global__ __launch_bounds__(64 * kF6Waves, 2) void gemm_f6f4_kernel(const uint8
         }
     }
 }
+
+// Shape used: 256 x 256 blocks of 8 waves (4 x 2 grid of 64 x 128 wave tiles), 3 stages.
+constexpr int kF6BM = 256, kF6BN = 256, kF6WGM = 4, kF6WGN = 2, kF6Stages = 3;
 
 // 2-bit packed weights -> FP4 E2M1: one 32-bit word (16 weights; weight e of
 // the group at bits 8*(e%4) + 2*(e/4)) -> 8 bytes (weight e at nibble e).
@@ -780,12 +788,13 @@ hipError_t launch_gemm_f6f4(const uint8_t* codes6, const float* xscale, int64_t 
     const int64_t tiles = (int64_t)tiles_n * ((M + kF6BM - 1) / kF6BM);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
     const int tt = (int)tiles;
+    constexpr int NT = 64 * kF6WGM * kF6WGN;
     if (y_dtype == HBL_F32)
-        hipLaunchKernelGGL(gemm_f6f4_kernel<float>, dim3(tt), dim3(64 * kF6Waves), 0, s, codes6, xscale, M, K, W4,
-                           alpha, N, (float*)Y, tiles_n, tt);
+        hipLaunchKernelGGL((gemm_f6f4_kernel<float, kF6BM, kF6BN, kF6WGM, kF6WGN, kF6Stages>), dim3(tt), dim3(NT), 0,
+                           s, codes6, xscale, M, K, W4, alpha, N, (float*)Y, tiles_n, tt);
     else
-        hipLaunchKernelGGL(gemm_f6f4_kernel<uint16_t>, dim3(tt), dim3(64 * kF6Waves), 0, s, codes6, xscale, M, K, W4,
-                           alpha, N, (uint16_t*)Y, tiles_n, tt);
+        hipLaunchKernelGGL((gemm_f6f4_kernel<uint16_t, kF6BM, kF6BN, kF6WGM, kF6WGN, kF6Stages>), dim3(tt), dim3(NT),
+                           0, s, codes6, xscale, M, K, W4, alpha, N, (uint16_t*)Y, tiles_n, tt);
     return hipGetLastError();
 }
 
