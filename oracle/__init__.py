@@ -9,7 +9,8 @@ Every function here returns fresh numpy arrays and takes host arrays:
   * ``X`` as float32 ``[M][K]`` or bf16 bit patterns (uint16) ``[M][K]``
   * latent weights ``W`` as float32 ``[N][K]`` (bf16 patterns are converted exactly)
 
-Steps and the passages they follow are documented in ``hbl_oracle.c`` (O1-O10).
+Steps and the passages they follow are documented in ``hbl_oracle.c`` (O1-O10 for
+the layer, O11 for the low-bit attention states beside it).
 """
 from __future__ import annotations
 
@@ -84,6 +85,10 @@ def _load():
     lib.hbo_int_gemm.argtypes = [P, P, I64, I64, I64, P]
     lib.hbo_int_gemm.restype = I
     lib.hbo_rescale.argtypes = [P, P, F, I64, I64, P]
+    lib.hbo_quantize_heads.argtypes = [P, I64, I64, I64, I, F, P, P]
+    lib.hbo_quantize_heads.restype = I
+    lib.hbo_unpack_heads.argtypes = [P, I64, I64, I, P]
+    lib.hbo_unpack_heads.restype = I
     _lib = lib
     return lib
 
@@ -281,3 +286,29 @@ def forward(X: np.ndarray, Wq: np.ndarray, alpha: float, *, bits: int, hadamard:
     y = rescale(acc, qa["d"], alpha)
     qa.update({"acc": acc, "y": y})
     return qa
+
+
+# ---------------------------------------------------------------- O11 ------
+def quantize_heads(X: np.ndarray, bits: int, eps: float = 1e-5):
+    """O11: X [M][H][D] (fp32, or bf16 bit patterns) -> (packed codes uint8
+    [M][H][D*bits/8], dequant factors float32 [M][H])."""
+    x = as_f32(X)
+    if x.ndim != 3:
+        raise ValueError("X must be [M][H][D]")
+    M, H, D = x.shape
+    x = _c(x, np.float32)
+    codes = np.empty((M, H, D * bits // 8), np.uint8)
+    d = np.empty((M, H), np.float32)
+    _check(_load().hbo_quantize_heads(_ptr(x), M, H, D, int(bits), float(np.float32(eps)), _ptr(codes), _ptr(d)),
+           "quantize_heads")
+    return codes, d
+
+
+def unpack_heads(codes: np.ndarray, D: int, bits: int) -> np.ndarray:
+    """Packed head codes [..][D*bits/8] -> one uint8 code per element [..][D]."""
+    c = _c(codes, np.uint8)
+    lead = c.shape[:-1]
+    V = int(np.prod(lead)) if lead else 1
+    u = np.empty(lead + (D,), np.uint8)
+    _check(_load().hbo_unpack_heads(_ptr(c), V, D, int(bits), _ptr(u)), "unpack_heads")
+    return u

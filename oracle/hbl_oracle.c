@@ -27,6 +27,8 @@
  *   O8  q       = clamp(rint(fp32(z*s)), lo, hi)   INT8 [-128,127], INT4 [-8,7]; INT4 packs 2/byte
  *   O9  acc     = sum_k q[m][k] * W_q[n][k]   (int64 triple loop, stored as int32)
  *   O10 y       = fp32(fp32(acc * d[m]) * alpha)
+ *   O11 beside the layer: low-bit attention states, per (token, head) absmax
+ *               to unsigned b-bit integers (b = 3, 4, 8)   ([XZY] 实验结果)
  *
  * Rounding is round-half-to-even (rint under the default FP environment)
  * everywhere.  No step is fused, blocked or reordered beyond these definitions.
@@ -376,4 +378,72 @@ int hbo_forward(const float* X, int64_t M, int64_t K, const float* gain, int nor
     if (!d_out) free(d);
     if (!acc_out) free(acc);
     return rc;
+}
+
+/* --------------------------------------------------------------- O11 ---- */
+/* Low-bit attention states, the step beside the layer in [XZY] "实验结果"
+ * (low-bit attention, tables 2 and 3): after RoPE the Q, K and V states of
+ * every head are quantised directly to unsigned integers by absmax, with no
+ * calibration data, and a 3-bit KV cache keeps the accuracy of a full one.
+ * The formula is not on the pages; the reading taken: a symmetric absmax
+ * quantiser per (token, head) whose signed codes are stored with the offset
+ * 2^(b-1), so every code is an unsigned b-bit integer:
+ *   gamma = max_d |x[d]|  (x = fp32 values of one head vector, D of them)
+ *   Qp = 2^(b-1) - 1;  s = fp32(Qp / fp32(gamma + eps));  d = fp32(gamma / Qp)
+ *   u[d] = clamp(rint(fp32(x[d] * s)), -Qp, Qp) + 2^(b-1)      in [1, 2^b - 1]
+ *   gamma == 0: s = 0, d = 0, every u = 2^(b-1).   Dequantised: (u - 2^(b-1)) * d.
+ * Packing of one head vector (D codes): b = 8 one byte per code; b = 4 two per
+ * byte, even index in the low nibble; b = 3 code j in bits 3j .. 3j+2 of the
+ * vector's little-endian bit string (8 codes per 3 bytes).
+ * X [M][H][D] fp32, codes [M][H][D*b/8], d_out [M][H]. */
+int hbo_quantize_heads(const float* X, int64_t M, int64_t H, int64_t D, int bits, float eps, uint8_t* codes,
+                       float* d_out) {
+    if (M < 0 || H < 1 || D < 8 || D % 8 != 0 || (bits != 3 && bits != 4 && bits != 8)) return HBO_ERR;
+    const int zp = 1 << (bits - 1), qp = zp - 1;
+    const int64_t vb = D * bits / 8;  /* bytes per packed head vector */
+    for (int64_t v = 0; v < M * H; v++) {
+        const float* x = X + v * D;
+        float gamma = 0.f;
+        for (int64_t j = 0; j < D; j++) {
+            const float a = fabsf(x[j]);
+            if (a > gamma) gamma = a;
+        }
+        const float den = gamma + eps;
+        const float s = gamma == 0.f ? 0.f : (float)qp / den;
+        d_out[v] = gamma == 0.f ? 0.f : gamma / (float)qp;
+        uint8_t* out = codes + v * vb;
+        memset(out, 0, (size_t)vb);
+        for (int64_t j = 0; j < D; j++) {
+            float t = x[j] * s;
+            if (t < (float)-qp) t = (float)-qp;
+            if (t > (float)qp) t = (float)qp;
+            const int u = (int)rintf(t) + zp;
+            if (bits == 8) {
+                out[j] = (uint8_t)u;
+            } else if (bits == 4) {
+                out[j / 2] |= (uint8_t)(u << (4 * (j % 2)));
+            } else {
+                for (int b = 0; b < 3; b++)
+                    if ((u >> b) & 1) out[(3 * j + b) / 8] |= (uint8_t)(1u << ((3 * j + b) % 8));
+            }
+        }
+    }
+    return HBO_OK;
+}
+
+/* The inverse of O11's packing: D codes per head vector back to one byte each. */
+int hbo_unpack_heads(const uint8_t* codes, int64_t V, int64_t D, int bits, uint8_t* u) {
+    if (V < 0 || D < 8 || D % 8 != 0 || (bits != 3 && bits != 4 && bits != 8)) return HBO_ERR;
+    const int64_t vb = D * bits / 8;
+    for (int64_t v = 0; v < V; v++)
+        for (int64_t j = 0; j < D; j++) {
+            const uint8_t* in = codes + v * vb;
+            int c = 0;
+            if (bits == 8) c = in[j];
+            else if (bits == 4) c = (in[j / 2] >> (4 * (j % 2))) & 15;
+            else
+                for (int b = 0; b < 3; b++) c |= ((in[(3 * j + b) / 8] >> ((3 * j + b) % 8)) & 1) << b;
+            u[v * D + j] = (uint8_t)c;
+        }
+    return HBO_OK;
 }

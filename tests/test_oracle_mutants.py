@@ -47,6 +47,17 @@ MUTANTS = [
     ("layernorm_mean_wrong", "mu /= (double)K;", "mu /= (double)(K - 1);"),
     ("rescale_without_d", "float t = (float)acc[m * N + n] * d[m];", "float t = (float)acc[m * N + n];"),
     ("rescale_without_alpha", "y[m * N + n] = t * alpha;", "y[m * N + n] = t;"),
+    ("heads_eps_dropped", "const float s = gamma == 0.f ? 0.f : (float)qp / den;",
+     "const float s = gamma == 0.f ? 0.f : (float)qp / gamma;"),
+    ("heads_absmax_without_abs", "const float a = fabsf(x[j]);", "const float a = x[j];"),
+    ("heads_round_half_away", "const int u = (int)rintf(t) + zp;", "const int u = (int)roundf(t) + zp;"),
+    ("heads_zero_point_off", "const int zp = 1 << (bits - 1), qp = zp - 1;",
+     "const int zp = (1 << (bits - 1)) - 1, qp = zp;"),
+    ("heads_3bit_order_reversed", "if ((u >> b) & 1) out[(3 * j + b) / 8]", "if ((u >> (2 - b)) & 1) out[(3 * j + b) / 8]"),
+    ("heads_nibbles_swapped", "out[j / 2] |= (uint8_t)(u << (4 * (j % 2)));",
+     "out[j / 2] |= (uint8_t)(u << (4 * (1 - j % 2)));"),
+    ("heads_dequant_factor_wrong", "d_out[v] = gamma == 0.f ? 0.f : gamma / (float)qp;",
+     "d_out[v] = gamma == 0.f ? 0.f : gamma / (float)(qp + 1);"),
 ]
 
 

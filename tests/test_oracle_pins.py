@@ -339,3 +339,67 @@ def test_forward_rejects_bad_shapes():
         oracle.quantize_activations(np.zeros((2, 96), np.float32), bits=8, hadamard=True)   # not a power of two
     with pytest.raises(ValueError):
         oracle.quantize_activations(np.zeros((2, 64), np.float32), bits=5)
+
+
+# ------------------------------------------------ low-bit attention states (O11)
+def test_heads_hand_cases(golden):
+    g = golden("head_quant_hand.txt")
+    x = np.array(g["x"], np.float32).reshape(1, 1, 8)
+    for bits, key in ((3, "b3"), (4, "b4"), (8, "b8")):
+        codes, d = oracle.quantize_heads(x, bits, eps=0.0)
+        assert oracle.unpack_heads(codes, 8, bits).ravel().tolist() == g[key + "_codes"]
+        if bits != 8:
+            assert codes.ravel().tolist() == g[key + "_bytes"]
+        assert d[0, 0] == np.float32(1.0) / np.float32((1 << (bits - 1)) - 1)
+    codes, d = oracle.quantize_heads(np.zeros((1, 1, 8), np.float32), 3, eps=0.0)
+    assert d[0, 0] == 0.0 and oracle.unpack_heads(codes, 8, 3).ravel().tolist() == g["zero_b3_codes"]
+    codes, d = oracle.quantize_heads(np.array(g["ties_x"], np.float32).reshape(1, 1, 8), 3, eps=0.0)
+    assert oracle.unpack_heads(codes, 8, 3).ravel().tolist() == g["ties_b3_codes"] and d[0, 0] == 1.0
+
+
+@pytest.mark.parametrize("bits", [3, 4, 8])
+def test_heads_properties(bits):
+    """Range, the extreme element, reconstruction within half a step, sign
+    symmetry u(-x) = 2^b - u(x), and per-head independence."""
+    rng = np.random.default_rng(bits)
+    X = rng.standard_normal((5, 3, 64)).astype(np.float32)
+    X[1, 2] *= 100.0
+    zp, qp = 1 << (bits - 1), (1 << (bits - 1)) - 1
+    codes, d = oracle.quantize_heads(X, bits, eps=0.0)
+    u = oracle.unpack_heads(codes, 64, bits).astype(np.int64)
+    assert u.min() >= 1 and u.max() <= 2 * zp - 1
+    q = u - zp
+    amax = np.argmax(np.abs(X), axis=2)
+    ext = np.take_along_axis(q, amax[..., None], axis=2)[..., 0]
+    assert np.array_equal(np.abs(ext), np.full(ext.shape, qp))
+    err = np.abs(X.astype(np.float64) - q * d[..., None].astype(np.float64))
+    assert np.all(err <= 0.5 * d[..., None] * (1 + 1e-6) + 1e-12)
+    codes_n, d_n = oracle.quantize_heads(-X, bits, eps=0.0)
+    assert np.array_equal(d_n, d)
+    assert np.array_equal(oracle.unpack_heads(codes_n, 64, bits).astype(np.int64), 2 * zp - u)
+    one, d1 = oracle.quantize_heads(X[1:2, 2:3], bits, eps=0.0)
+    assert np.array_equal(one[0, 0], codes[1, 2]) and d1[0, 0] == d[1, 2]
+
+
+def test_heads_packing_brute_force():
+    """3- and 4-bit packing against bit strings assembled by hand in Python."""
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((2, 2, 16)).astype(np.float32)
+    for bits in (3, 4):
+        codes, _ = oracle.quantize_heads(X, bits, eps=1e-5)
+        u = oracle.unpack_heads(codes, 16, bits)
+        for m in range(2):
+            for h in range(2):
+                bitstr = sum(int(c) << (bits * j) for j, c in enumerate(u[m, h]))
+                assert codes[m, h].tolist() == list(bitstr.to_bytes(16 * bits // 8, "little"))
+
+
+def test_heads_eps_in_denominator():
+    """s = Qp/(gamma+eps): with eps the extreme element no longer lands exactly on Qp."""
+    x = np.array([[[2.0, 1.0, 0.5, 0.0, 0.0, 0.0, 0.0, -1.5]]], np.float32)
+    c0, _ = oracle.quantize_heads(x, 8, eps=0.0)
+    c1, _ = oracle.quantize_heads(x, 8, eps=0.5)
+    u0 = oracle.unpack_heads(c0, 8, 8).ravel().astype(int) - 128
+    u1 = oracle.unpack_heads(c1, 8, 8).ravel().astype(int) - 128
+    assert u0.tolist()[:3] == [127, 64, 32]          # 2*63.5 = 127, 63.5 -> 64 (half even), 31.75 -> 32
+    assert u1.tolist()[:3] == [102, 51, 25]          # s = 127/2.5 = 50.8: 101.6, 50.8, 25.4
