@@ -18,7 +18,7 @@ __all__ = [
     "HblError", "HblLibraryError", "Config", "load_library", "declared_symbols",
     "hbl_packed_weight_bytes", "hbl_weight_workspace_bytes", "hbl_quantize_weights",
     "hbl_workspace_bytes", "hbl_forward_workspace_bytes", "hbl_quantize_activations", "hbl_gemm", "hbl_forward", "hbl_forward_latent",
-    "hbl_status_string", "hbl_last_hip_error",
+    "hbl_quantize_heads", "hbl_status_string", "hbl_last_hip_error",
     "HBL_F32", "HBL_BF16", "HBL_NORM_RMS", "HBL_NORM_LN", "HBL_NORM_NONE",
     "HBL_A4_ABSMEAN_SQRT7", "HBL_A4_ABSMAX_7",
 ]
@@ -96,6 +96,7 @@ def load_library(path: str | None = None):
         "hbl_quantize_weights": [P, I32, I64, I64, F, P, P, P, SZ, P],
         "hbl_workspace_bytes": [I64, I64, PCFG, PSZ],
         "hbl_forward_workspace_bytes": [I64, I64, I64, PCFG, PSZ],
+        "hbl_quantize_heads": [P, I32, I64, I64, I64, I32, F, P, P, P],
         "hbl_quantize_activations": [P, I32, I64, I64, P, PCFG, P, P, P, P, P],
         "hbl_gemm": [P, P, I32, I64, I64, P, P, I64, P, I32, P],
         "hbl_forward": [P, I32, I64, I64, P, P, P, I64, PCFG, P, I32, P, SZ, P],
@@ -309,3 +310,22 @@ def hbl_forward_latent(X, W, cfg: Config, eps: float = 1e-5, y_dtype=None, gain=
         _ptr(W_packed), _ptr(alpha), _ptr(Y), _dtype_code(Y), _ptr(ws), ws.numel() * ws.element_size(),
         _ptr(wws), wws.numel() * wws.element_size(), _stream(stream)))
     return Y, W_packed, alpha
+
+
+def hbl_quantize_heads(X, H: int, bits: int, eps: float = 1e-5, codes=None, scales=None, stream=None):
+    """Per-(token, head) absmax quantisation of attention states X [M][H][D]
+    (or [M][H*D]) to unsigned bits-bit codes.  Returns (codes uint8
+    [M][H][D*bits/8], scales float32 [M][H])."""
+    torch = _torch()
+    lib = load_library()
+    _dev(X, "X")
+    M = X.shape[0]
+    D = X[0].numel() // H if M > 0 else (X.shape[-1] if X.dim() == 3 else X.shape[1] // H)
+    if codes is None:
+        codes = torch.empty((M, H, D * bits // 8), dtype=torch.uint8, device=X.device)
+    if scales is None:
+        scales = torch.empty((M, H), dtype=torch.float32, device=X.device)
+    _dev(codes, "codes"); _dev(scales, "scales")
+    _check("hbl_quantize_heads", lib.hbl_quantize_heads(_ptr(X), _dtype_code(X), M, H, D, int(bits), float(eps),
+                                                        _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales

@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhbl.so")
-SOURCES = ["api.hip", "weight_quant.hip", "act_quant.hip", "act_pack.hip", "gemm.hip", "forward_small.hip"]
+SOURCES = ["api.hip", "weight_quant.hip", "act_quant.hip", "act_pack.hip", "gemm.hip", "forward_small.hip",
+           "head_quant.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

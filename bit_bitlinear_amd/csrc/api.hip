@@ -158,6 +158,20 @@ hbl_status hbl_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, const hb
     return HBL_OK;
 }
 
+hbl_status hbl_quantize_heads(const void* X, int32_t x_dtype, int64_t M, int64_t H, int64_t D, int32_t bits,
+                              float eps, uint8_t* codes, float* scales, void* stream) {
+    if (!dtype_ok(x_dtype)) return HBL_ERR_DTYPE;
+    if (bits != 3 && bits != 4 && bits != 8) return HBL_ERR_BITS;
+    if (M < 0 || H < 1 || !(eps >= 0.f)) return HBL_ERR_SHAPE;
+    if (D != 32 && D != 64 && D != 128 && D != 256) return HBL_ERR_SHAPE;
+    if (M > ((int64_t)1 << 40) / (H * D)) return HBL_ERR_SHAPE;  // M*H*D < 2^40 elements
+    if (M == 0) return HBL_OK;
+    if (!X || !codes || !scales) return HBL_ERR_NULL;
+    if (!aligned16(X) || !aligned16(codes) || !aligned(scales, 4)) return HBL_ERR_ALIGN;
+    const hipError_t e = hbl::launch_head_quant(X, x_dtype, M * H, D, bits, eps, codes, scales, (hipStream_t)stream);
+    return e == hipSuccess ? HBL_OK : hip_fail(e);
+}
+
 hbl_status hbl_quantize_activations(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
                                     const hbl_config* cfg, void* codes, float* xscale, float* z_debug,
                                     float* s_debug, void* stream) {

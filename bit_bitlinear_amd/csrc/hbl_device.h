@@ -196,6 +196,10 @@ hipError_t launch_gemm_f6f4(const uint8_t* codes6, const float* xscale, int64_t 
                             const float* alpha, int64_t N, void* Y, int y_dtype, hipStream_t s);
 // 2-bit packed ternary weights -> FP4 E2M1 nibbles (W4 as above)
 hipError_t launch_weights_to_fp4(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W4, hipStream_t s);
+// per-(token, head) absmax quantisation of attention states to unsigned codes:
+// V head vectors of D elements (fp32 or bf16) -> codes (D*bits/8 bytes each), d_out [V]
+hipError_t launch_head_quant(const void* X, int x_dtype, int64_t V, int64_t D, int bits, float eps, uint8_t* codes,
+                             float* d_out, hipStream_t s);
 // true when launch_gemm runs the decode GEMM for this shape; the codes may
 // then be in the decode tile layout (rows padded to a multiple of 16)
 bool gemm_uses_decode_kernel(int64_t M, int64_t K);

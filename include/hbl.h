@@ -197,6 +197,27 @@ hbl_status hbl_forward_latent(const void* X, int32_t x_dtype, int64_t M, int64_t
                               uint8_t* W_packed, float* alpha, void* Y, int32_t y_dtype, void* ws,
                               size_t ws_bytes, void* wws, size_t wws_bytes, void* stream);
 
+/*
+ * Low-bit attention states, beside the layer ("新智元: 微软 BitNet v2" repost,
+ * section "实验结果": after RoPE the Q, K and V heads are quantised directly to
+ * unsigned integers by absmax, with no calibration; a 3-bit KV cache keeps
+ * the accuracy of a full-precision one).  For every token m and head h of
+ * X [M][H][D] (fp32 or bf16; post-RoPE states; row-major, so also [M][H*D]):
+ *   gamma = max_d |x|, Qp = 2^(bits-1) - 1, s = Qp/(gamma + eps) (fp32),
+ *   d = gamma/Qp,  u = clamp(rint(x*s), -Qp, Qp) + 2^(bits-1)  in [1, 2^bits - 1]
+ *   (round half to even; gamma == 0 gives d = 0 and every u = 2^(bits-1);
+ *   dequantised value (u - 2^(bits-1)) * d).  The formula is the reading of
+ *   the page taken here: a symmetric absmax quantiser stored with an offset.
+ * codes: uint8 [M][H][D*bits/8]: bits = 8 one byte per code; 4 two per byte,
+ * even d in the low nibble; 3 code d at bits 3d..3d+2 of the head vector's
+ * little-endian bit string.  scales: fp32 [M][H] = d.  All device memory.
+ * Constraints: bits in {3, 4, 8}; D in {32, 64, 128, 256}; H >= 1; M >= 0
+ * (M == 0 queues nothing); M*H*D < 2^40; eps >= 0; X and codes 16-byte
+ * aligned, scales 4-byte aligned.
+ */
+hbl_status hbl_quantize_heads(const void* X, int32_t x_dtype, int64_t M, int64_t H, int64_t D, int32_t bits,
+                              float eps, uint8_t* codes, float* scales, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* hbl_status_string(hbl_status status);
 

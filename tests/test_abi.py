@@ -20,7 +20,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = hbl.declared_symbols()
-    assert len(names) == 11
+    assert len(names) == 12
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
 
@@ -144,3 +144,19 @@ def test_forward_latent_validation(lib):
     assert call(X=None) == 1 and call(ws=None) == 1 and call(c=None) == 1
     assert call(W=MIS) == 4 and call(X=MIS) == 4
     assert call(wsb=need - 1) == 7 and call(wwsb=wneed - 1) == 7
+
+
+def test_quantize_heads_validation(lib):
+    q = lib.hbl_quantize_heads
+    ok = dict(X=A16, xdt=1, M=8, H=4, D=128, bits=3, eps=1e-5, codes=A16b, scales=A16b)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return q(a["X"], a["xdt"], a["M"], a["H"], a["D"], a["bits"], a["eps"], a["codes"], a["scales"], None)
+
+    assert call(xdt=3) == 5
+    assert call(bits=5) == 6 and call(bits=2) == 6
+    assert call(D=48) == 2 and call(D=512) == 2 and call(H=0) == 2 and call(M=-1) == 2 and call(eps=-1.0) == 2
+    assert call(M=(1 << 40) // 512 + 1, H=4, D=128) == 2
+    assert call(X=None) == 1 and call(codes=None) == 1 and call(scales=None) == 1
+    assert call(M=0, X=None, codes=None, scales=None) == 0

@@ -523,3 +523,45 @@ def test_forward_deterministic_and_empty():
     Y0 = hbl.hbl_forward(Xd[:0], Wp, alpha, layer.N, cfg)
     _sync()
     assert Y0.shape == (0, layer.N)
+
+
+# ====================================================== attention states ==
+# Per-(token, head) absmax quantisation to unsigned codes: codes and scales
+# bit for bit against the oracle (both sides decide in fp32 with the same
+# correctly rounded division and one fp32 product per element), for every
+# bit width and head size, both input dtypes, ragged counts of head vectors
+# (not a multiple of the block), zero vectors and large magnitudes.
+HEAD_CASES = [
+    # (M, H, D, bits, x dtype)
+    (37, 5, 128, 3, "bf16"), (37, 5, 128, 4, "f32"), (37, 5, 128, 8, "bf16"),
+    (3, 7, 32, 3, "f32"), (9, 3, 64, 4, "bf16"), (11, 2, 256, 3, "bf16"), (5, 9, 256, 8, "f32"),
+    (1, 1, 32, 3, "bf16"), (2048, 32, 128, 3, "bf16"),
+]
+
+
+@pytest.mark.parametrize("M,H,D,bits,xdt", HEAD_CASES)
+def test_quantize_heads_parity(M, H, D, bits, xdt):
+    _announce("heads M=%d H=%d D=%d b%d %s" % (M, H, D, bits, xdt))
+    rng = np.random.default_rng(M * 7 + H * 3 + D + bits)
+    X = (rng.standard_normal((M, H, D)) * rng.choice([0.01, 1.0, 300.0], size=(M, H, 1))).astype(np.float32)
+    X[0, 0] = 0.0                                    # a zero head vector
+    if M > 1:
+        X[1, 0, 5] = 1e30 if xdt == "f32" else 3e38  # one huge element (bf16 keeps its exponent)
+    Xh = workloads.f32_to_bf16_bits(X) if xdt == "bf16" else X
+    codes, scales = hbl.hbl_quantize_heads(to_dev(Xh), H, bits, eps=1e-5)
+    _sync()
+    c_ref, d_ref = oracle.quantize_heads(Xh, bits, eps=1e-5)
+    assert np.array_equal(to_host(scales), d_ref)
+    assert np.array_equal(to_host(codes), c_ref)
+
+
+def test_quantize_heads_eps_zero_and_ties():
+    """eps = 0 puts the extreme element exactly on +-Qp and exact halves on ties
+    (round half to even), like the oracle's hand-derived cases."""
+    _announce("heads eps=0 ties")
+    x = np.array([3.0, 0.5, 1.5, 2.5, -0.5, -2.5, 0.0, 1.0] * 4, np.float32).reshape(1, 1, 32)
+    for bits in (3, 4, 8):
+        codes, scales = hbl.hbl_quantize_heads(to_dev(x), 1, bits, eps=0.0)
+        _sync()
+        c_ref, d_ref = oracle.quantize_heads(x, bits, eps=0.0)
+        assert np.array_equal(to_host(codes), c_ref) and np.array_equal(to_host(scales), d_ref)
