@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=40)
     p.add_argument("--layer", default="wo_1.3b")
+    p.add_argument("--op", choices=("layer", "heads"), default="layer",
+                   help="layer: the H-BitLinear step (default); heads: the low-bit attention-state quantiser "
+                        "(per-head absmax to a 3-bit KV cache) on the 3B-like KV shape")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-iters", type=int, default=200)
     p.add_argument("--counter-run", action="store_true",
@@ -83,6 +86,8 @@ def main():
     import bit_bitlinear_amd as hbl
     import workloads
 
+    if args.op == "heads":
+        return bench_heads(args)
     layer = workloads.by_name(args.layer)
     M, K, N, bits = layer.M, layer.K, layer.N, layer.act_bits
     dev = torch.device("cuda:0")
@@ -310,6 +315,81 @@ def cpu_baseline(layer, X, W):
             "sample": "full weight ternarisation once (%.3f s) + forward of the first %d of %d rows (%.3f s), "
                       "scaled to all rows; %d OpenMP threads" % (t_wq, S, layer.M, t_rows, cores),
             "cpu_seconds": round((t_wq + t_rows) * cores, 1)}
+
+
+def bench_heads(args):
+    """The low-bit attention-state quantiser: one step = hbl_quantize_heads over
+    the post-RoPE K (or V) states of 8192 tokens x 32 heads x 128 (bf16) to
+    3-bit codes; HBM-bound (reads 2 bytes, writes 3/8 byte per element)."""
+    import numpy as np
+    import torch
+
+    import bit_bitlinear_amd as hbl
+    import workloads
+
+    name, M, H, D, bits = workloads.KV_3B
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hbl.load_library()
+    rng = np.random.default_rng(0)
+    X = workloads.head_states(rng, M, H, D)
+    Xb = workloads.f32_to_bf16_bits(X)
+    Xd = torch.from_numpy(Xb.view(np.int16)).view(torch.bfloat16).to(dev)
+    set_bytes = Xd.numel() * 2 + M * H * D * bits // 8 + 4 * M * H
+    R = max(2, -(-ROTATE_BYTES // set_bytes))
+    sets = [(Xd if r == 0 else Xd.clone(), torch.empty((M, H, D * bits // 8), dtype=torch.uint8, device=dev),
+             torch.empty((M, H), dtype=torch.float32, device=dev)) for r in range(R)]
+
+    def step(s):
+        hbl.hbl_quantize_heads(s[0], H, bits, 1e-5, codes=s[1], scales=s[2])
+
+    for i in range(args.warmup):
+        step(sets[i % R])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in range(R):
+            step(sets[r])
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, -(-args.steps // R))
+    timed = reps * R
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = ev0.elapsed_time(ev1) / timed * 1e3   # per launch, events on the launch stream
+    work = M * H * D * 2 + M * H * D * bits // 8 + 4 * M * H
+    achieved = work / (us * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        oracle.quantize_heads(Xb, bits, eps=1e-5)
+        t = time.perf_counter() - t0
+        cpu = {"value": round(M / t, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": "the whole workload (%d x %d heads x %d), single-threaded C, %.3f s" % (M, H, D, t)}
+    print(json.dumps({
+        "metric": "low-bit attention-state quantisation tokens/s (per-head absmax to a 3-bit KV cache)",
+        "value": round(M * timed / wall, 1), "unit": "tokens/s", "n_gpus": 1, "steps": timed,
+        "warmup": args.warmup, "ms_per_step": round(wall / timed * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) with a log-normal scale per token and head)",
+        "config": {"workload": "%s: %d tokens x %d heads x %d, bf16 in, %d-bit codes" % (name, M, H, D, bits),
+                   "rotating_sets": R, "timing": "HIP graph replay of captured launches"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "head_quant_kernel", "us_per_launch": round(us, 3),
+                     "work_desc": "read X (bf16) + write codes + write scales, %d bytes per launch" % work},
+        "cpu_baseline": cpu,
+    }))
 
 
 if __name__ == "__main__":

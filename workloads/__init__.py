@@ -74,6 +74,19 @@ def x_gaussian(rng, M, K):
     return rng.standard_normal((M, K), dtype=np.float32), np.zeros(0, np.int64)
 
 
+def head_states(rng, M, H, D):
+    """Post-RoPE attention states [M][H][D]: N(0,1) values with a log-normal
+    scale per (token, head) (sigma 1), so head vectors span several orders of
+    magnitude as keys and values of different heads do."""
+    x = rng.standard_normal((M, H, D)).astype(np.float32)
+    return (x * np.exp(rng.standard_normal((M, H, 1))).astype(np.float32)).astype(np.float32)
+
+
+# Attention states of a 3B-like model (hidden 4096 = 32 heads x 128) for 8192
+# tokens, quantised to a 3-bit KV cache: (name, M, H, D, bits).
+KV_3B = ("kv_3b", 8192, 32, 128, 3)
+
+
 def w_latent(rng, N, K, std=0.02):
     return (rng.standard_normal((N, K), dtype=np.float32) * np.float32(std)).astype(np.float32)
 
