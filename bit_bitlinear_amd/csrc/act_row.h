@@ -198,6 +198,13 @@ HBL_DEVINL uint32_t code_bits(float z, float s, float lo, float hi) {
     const float t = z * s;  // one rounded fp32 product
     return __float_as_uint(fminf(fmaxf(t, lo), hi) + 12582912.0f);
 }
+// The same where the clamp cannot bind; the product must still be rounded to
+// fp32 before the add (no fused multiply-add).
+HBL_DEVINL uint32_t code_bits_unclamped(float z, float s) {
+#pragma clang fp contract(off)
+    const float t = z * s;
+    return __float_as_uint(t + 12582912.0f);
+}
 
 // Threads per row: E = K/NT values per thread (32 from K = 2048 to 16384).
 constexpr int kActE = 32;
@@ -410,7 +417,13 @@ HBL_DEVINL void act_row_quantise(ActRegs<LK, NT, Tin>& v, const float* __restric
         }
         uint32_t b[VW];
 #pragma unroll
-        for (int x2 = 0; x2 < VW; x2++) b[x2] = code_bits(z[x2], s_mul, lo, hi);
+        for (int x2 = 0; x2 < VW; x2++) {
+            // INT8: |z| <= gamma and s = 127/(gamma+eps) keep |z*s| <= 127 (at
+            // most one rounding above it, which still rounds to 127), so the
+            // clamp cannot bind and is skipped
+            if constexpr (BITS == 8) b[x2] = code_bits_unclamped(z[x2], s_mul);
+            else b[x2] = code_bits(z[x2], s_mul, lo, hi);
+        }
         if constexpr (LAYOUT == kCodesFp6) {
             static_assert(BITS == 4 && VW == 4, "FP6 codes: INT4 values, four per vector");
             // four 6-bit fields = 3 whole bytes at natural byte nb = 3*e0/4,
