@@ -10,7 +10,8 @@ Every function here returns fresh numpy arrays and takes host arrays:
   * latent weights ``W`` as float32 ``[N][K]`` (bf16 patterns are converted exactly)
 
 Steps and the passages they follow are documented in ``hbl_oracle.c`` (O1-O10 for
-the layer, O11 for the low-bit attention states beside it).
+the layer, O11 for the low-bit attention states beside it, O12 for the layer's
+straight-through backward).
 """
 from __future__ import annotations
 
@@ -89,6 +90,8 @@ def _load():
     lib.hbo_quantize_heads.restype = I
     lib.hbo_unpack_heads.argtypes = [P, I64, I64, I, P]
     lib.hbo_unpack_heads.restype = I
+    lib.hbo_backward.argtypes = [P, P, I64, I64, P, I, F, I, I, I, F, P, F, I64, P, P]
+    lib.hbo_backward.restype = I
     _lib = lib
     return lib
 
@@ -312,3 +315,24 @@ def unpack_heads(codes: np.ndarray, D: int, bits: int) -> np.ndarray:
     u = np.empty(lead + (D,), np.uint8)
     _check(_load().hbo_unpack_heads(_ptr(c), V, D, int(bits), _ptr(u)), "unpack_heads")
     return u
+
+
+# ---------------------------------------------------------------- O12 ------
+def backward(dY: np.ndarray, X: np.ndarray, Wq: np.ndarray, alpha: float, *, bits: int, hadamard: bool = True,
+             gain=None, norm: int = NORM_RMS, norm_eps: float = 1e-5, quant_eps: float = 1e-5,
+             a4_mode: int = A4_ABSMEAN, want_dW: bool = True):
+    """O12: the straight-through backward.  dY [M][N] (fp32 or bf16 bit
+    patterns), X [M][K] as for quantize_activations, Wq int8 [N][K].
+    Returns (dX fp64 [M][K], dW fp64 [N][K] or None)."""
+    dy = as_f32(dY)
+    x = as_f32(X)
+    M, K = x.shape
+    N = Wq.shape[0]
+    g = None if gain is None else _c(gain, np.float32)
+    Wq = _c(Wq, np.int8)
+    dX = np.empty((M, K), np.float64)
+    dW = np.empty((N, K), np.float64) if want_dW else None
+    _check(_load().hbo_backward(_ptr(_c(dy, np.float32)), _ptr(x), M, K, _ptr(g), int(norm), float(norm_eps),
+                                int(bool(hadamard)), int(bits), int(a4_mode), float(quant_eps), _ptr(Wq),
+                                float(np.float32(alpha)), N, _ptr(dX), _ptr(dW)), "backward")
+    return dX, dW

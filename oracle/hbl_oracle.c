@@ -29,6 +29,7 @@
  *   O10 y       = fp32(fp32(acc * d[m]) * alpha)
  *   O11 beside the layer: low-bit attention states, per (token, head) absmax
  *               to unsigned b-bit integers (b = 3, 4, 8)   ([XZY] 实验结果)
+ *   O12 the layer's straight-through backward: dX through H and the norm, dW
  *
  * Rounding is round-half-to-even (rint under the default FP environment)
  * everywhere.  No step is fused, blocked or reordered beyond these definitions.
@@ -446,4 +447,91 @@ int hbo_unpack_heads(const uint8_t* codes, int64_t V, int64_t D, int bits, uint8
             u[v * D + j] = (uint8_t)c;
         }
     return HBO_OK;
+}
+
+/* --------------------------------------------------------------- O12 ---- */
+/* The layer's backward with the straight-through estimator, the training
+ * step beside the forward ([XZY] "BitNet v2：原生4位激活": the model is trained
+ * with low-bit activations and ternary weights; the quantisers are passed
+ * straight through).  With y[m][n] = alpha * d[m] * sum_k q[m][k] Wq[n][k] and
+ * the quantisers taken as identities in the backward (d*q stands for z, and
+ * alpha*Wq for the latent W):
+ *   dz[m][k] = alpha * sum_n dY[m][n] * Wq[n][k]
+ *   dr       = H dz  (H is the symmetric orthonormal Sylvester matrix; = dz
+ *              for plain BitLinear)
+ *   dx       = the transpose of the norm's Jacobian applied to dr, for
+ *              r = norm(x) * g (O5):
+ *     RMS:  c = 1/sqrt(sum x^2 / K + eps):
+ *           dx_j = c g_j dr_j - (c^3 / K) x_j sum_k g_k dr_k x_k
+ *     LN:   c = 1/sqrt(sum (x - mu)^2 / K + eps), xh = (x - mu) c, a = g dr:
+ *           dx_j = c (a_j - mean(a) - xh_j mean(a xh))
+ *     none: dx_j = g_j dr_j
+ *   dW[n][k] = sum_m dY[m][n] * d[m] * q[m][k]   (q, d of the forward, O4-O8)
+ * All in fp64.  dX [M][K] and dW [N][K] (nullable) are fp64 outputs. */
+int hbo_backward(const float* dY, const float* X, int64_t M, int64_t K, const float* gain, int norm, float norm_eps,
+                 int hadamard, int bits, int a4_mode, float quant_eps, const int8_t* Wq, float alpha, int64_t N,
+                 double* dX, double* dW) {
+    if (M < 0 || K <= 0 || N <= 0) return HBO_ERR;
+    if (hadamard && (K & (K - 1))) return HBO_ERR;
+    double* dz = (double*)malloc(sizeof(double) * (size_t)K);
+    double* dr = (double*)malloc(sizeof(double) * (size_t)K);
+    int8_t* q = (int8_t*)malloc((size_t)(M * K > 0 ? M * K : 1));
+    float* s = (float*)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1));
+    float* d = (float*)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1));
+    int rc = HBO_ERR;
+    if (dz && dr && q && s && d) {
+        rc = HBO_OK;
+        for (int64_t m = 0; m < M; m++) {
+            const float* x = X + m * K;
+            for (int64_t k = 0; k < K; k++) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; n++) acc += (double)dY[m * N + n] * (double)Wq[n * K + k];
+                dz[k] = (double)alpha * acc;
+            }
+            if (hadamard) hbo_hadamard_row(dz, K, dr);
+            else memcpy(dr, dz, sizeof(double) * (size_t)K);
+            double* out = dX + m * K;
+            if (norm == 2) {
+                for (int64_t k = 0; k < K; k++) out[k] = (gain ? (double)gain[k] : 1.0) * dr[k];
+            } else if (norm == 0) {
+                double ss = 0.0, t = 0.0;
+                for (int64_t k = 0; k < K; k++) ss += (double)x[k] * (double)x[k];
+                const double c = 1.0 / sqrt(ss / (double)K + (double)norm_eps);
+                for (int64_t k = 0; k < K; k++) t += (gain ? (double)gain[k] : 1.0) * dr[k] * (double)x[k];
+                for (int64_t k = 0; k < K; k++)
+                    out[k] = c * (gain ? (double)gain[k] : 1.0) * dr[k] - c * c * c / (double)K * (double)x[k] * t;
+            } else {
+                double mu = 0.0, var = 0.0, ma = 0.0, max_ = 0.0;
+                for (int64_t k = 0; k < K; k++) mu += (double)x[k];
+                mu /= (double)K;
+                for (int64_t k = 0; k < K; k++) var += ((double)x[k] - mu) * ((double)x[k] - mu);
+                const double c = 1.0 / sqrt(var / (double)K + (double)norm_eps);
+                for (int64_t k = 0; k < K; k++) {
+                    const double a = (gain ? (double)gain[k] : 1.0) * dr[k];
+                    ma += a;
+                    max_ += a * ((double)x[k] - mu) * c;
+                }
+                ma /= (double)K;
+                max_ /= (double)K;
+                for (int64_t k = 0; k < K; k++) {
+                    const double a = (gain ? (double)gain[k] : 1.0) * dr[k];
+                    out[k] = c * (a - ma - ((double)x[k] - mu) * c * max_);
+                }
+            }
+        }
+        if (dW) {
+            rc = hbo_quantize_activations(X, M, K, gain, norm, norm_eps, hadamard, bits, a4_mode, quant_eps, NULL, q,
+                                          s, d);
+            if (rc == HBO_OK)
+                for (int64_t n = 0; n < N; n++)
+                    for (int64_t k = 0; k < K; k++) {
+                        double acc = 0.0;
+                        for (int64_t m = 0; m < M; m++)
+                            acc += (double)dY[m * N + n] * (double)d[m] * (double)q[m * K + k];
+                        dW[n * K + k] = acc;
+                    }
+        }
+    }
+    free(dz); free(dr); free(q); free(s); free(d);
+    return rc;
 }

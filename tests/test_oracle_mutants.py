@@ -56,6 +56,17 @@ MUTANTS = [
     ("heads_3bit_order_reversed", "if ((u >> b) & 1) out[(3 * j + b) / 8]", "if ((u >> (2 - b)) & 1) out[(3 * j + b) / 8]"),
     ("heads_nibbles_swapped", "out[j / 2] |= (uint8_t)(u << (4 * (j % 2)));",
      "out[j / 2] |= (uint8_t)(u << (4 * (1 - j % 2)));"),
+    ("backward_alpha_dropped", "dz[k] = (double)alpha * acc;", "dz[k] = acc;"),
+    ("backward_gemm_transposed", "acc += (double)dY[m * N + n] * (double)Wq[n * K + k];",
+     "acc += (double)dY[m * N + n] * (double)Wq[k * N + n];"),
+    ("backward_hadamard_skipped", "if (hadamard) hbo_hadamard_row(dz, K, dr);", "if (0) hbo_hadamard_row(dz, K, dr);"),
+    ("backward_rms_c_cubed_wrong", "- c * c * c / (double)K * (double)x[k] * t;", "- c * c / (double)K * (double)x[k] * t;"),
+    ("backward_ln_mean_term_dropped", "out[k] = c * (a - ma - ((double)x[k] - mu) * c * max_);",
+     "out[k] = c * (a - ((double)x[k] - mu) * c * max_);"),
+    ("backward_none_gain_dropped", "for (int64_t k = 0; k < K; k++) out[k] = (gain ? (double)gain[k] : 1.0) * dr[k];",
+     "for (int64_t k = 0; k < K; k++) out[k] = dr[k];"),
+    ("backward_dw_without_d", "acc += (double)dY[m * N + n] * (double)d[m] * (double)q[m * K + k];",
+     "acc += (double)dY[m * N + n] * (double)q[m * K + k];"),
     ("heads_dequant_factor_wrong", "d_out[v] = gamma == 0.f ? 0.f : gamma / (float)qp;",
      "d_out[v] = gamma == 0.f ? 0.f : gamma / (float)(qp + 1);"),
 ]

@@ -403,3 +403,69 @@ def test_heads_eps_in_denominator():
     u1 = oracle.unpack_heads(c1, 8, 8).ravel().astype(int) - 128
     assert u0.tolist()[:3] == [127, 64, 32]          # 2*63.5 = 127, 63.5 -> 64 (half even), 31.75 -> 32
     assert u1.tolist()[:3] == [102, 51, 25]          # s = 127/2.5 = 50.8: 101.6, 50.8, 25.4
+
+
+# ------------------------------------------------ straight-through backward (O12)
+def _surrogate_y(x, Wq, alpha, gain, norm, eps, hadamard):
+    """fp64 forward of the layer with both quantisers removed (what the
+    straight-through backward differentiates), written here with numpy and
+    scipy independently of the oracle."""
+    x = np.asarray(x, np.float64)
+    g = 1.0 if gain is None else np.asarray(gain, np.float64)
+    if norm == oracle.NORM_RMS:
+        r = x / np.sqrt((x * x).mean(axis=1, keepdims=True) + eps) * g
+    elif norm == oracle.NORM_LN:
+        c = x - x.mean(axis=1, keepdims=True)
+        r = c / np.sqrt((c * c).mean(axis=1, keepdims=True) + eps) * g
+    else:
+        r = x * g
+    K = x.shape[1]
+    z = r @ (scipy.linalg.hadamard(K).astype(np.float64) / math.sqrt(K)).T if hadamard else r
+    return alpha * (z @ np.asarray(Wq, np.float64).T)
+
+
+@pytest.mark.parametrize("norm", [oracle.NORM_RMS, oracle.NORM_LN, oracle.NORM_NONE])
+@pytest.mark.parametrize("hadamard,use_gain", [(True, False), (True, True), (False, True)])
+def test_backward_dx_finite_differences(norm, hadamard, use_gain):
+    """O12's dX equals the central finite-difference gradient of
+    sum(dY * y) for the quantiser-free forward."""
+    rng = np.random.default_rng(norm * 10 + hadamard * 2 + use_gain)
+    M, K, N = 3, 16, 5
+    X = (rng.standard_normal((M, K)) + (1.5 if norm == oracle.NORM_LN else 0.0)).astype(np.float32)
+    Wq = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    dY = rng.standard_normal((M, N)).astype(np.float32)
+    gain = (rng.standard_normal(K) * 0.5 + 1.0).astype(np.float32) if use_gain else None
+    alpha, eps = np.float32(0.37), float(np.float32(1e-5))
+    dX, _ = oracle.backward(dY, X, Wq, alpha, bits=8, hadamard=hadamard, gain=gain, norm=norm, want_dW=False)
+    h = 1e-6
+    fd = np.empty((M, K))
+    for m in range(M):
+        for j in range(K):
+            xp = X.astype(np.float64); xm = X.astype(np.float64)
+            xp[m, j] += h; xm[m, j] -= h
+            lp = np.sum(dY.astype(np.float64) * _surrogate_y(xp, Wq, float(alpha), gain, norm, eps, hadamard))
+            lm = np.sum(dY.astype(np.float64) * _surrogate_y(xm, Wq, float(alpha), gain, norm, eps, hadamard))
+            fd[m, j] = (lp - lm) / (2 * h)
+    assert np.allclose(dX, fd, rtol=1e-6, atol=1e-7 * np.max(np.abs(fd)))
+
+
+def test_backward_dw_finite_differences():
+    """O12's dW equals the gradient of sum(dY * (xh W^T)) in W, with xh = d*q
+    the dequantised codes of the forward."""
+    rng = np.random.default_rng(5)
+    M, K, N = 4, 16, 3
+    X = rng.standard_normal((M, K)).astype(np.float32)
+    Wq = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    dY = rng.standard_normal((M, N)).astype(np.float32)
+    for bits in (8, 4):
+        _, dW = oracle.backward(dY, X, Wq, 0.5, bits=bits)
+        qa = oracle.quantize_activations(X, bits=bits)
+        xh = qa["q"].astype(np.float64) * qa["d"].astype(np.float64)[:, None]
+        W0 = rng.standard_normal((N, K))
+        fd = np.empty((N, K))
+        for n in range(N):
+            for k in range(K):
+                Wp = W0.copy(); Wm = W0.copy()
+                Wp[n, k] += 0.5; Wm[n, k] -= 0.5
+                fd[n, k] = (np.sum(dY * (xh @ Wp.T)) - np.sum(dY * (xh @ Wm.T))) / 1.0
+        assert np.allclose(dW, fd, rtol=1e-12, atol=1e-12)
