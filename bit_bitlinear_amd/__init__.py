@@ -18,7 +18,8 @@ __all__ = [
     "HblError", "HblLibraryError", "Config", "load_library", "declared_symbols",
     "hbl_packed_weight_bytes", "hbl_weight_workspace_bytes", "hbl_quantize_weights",
     "hbl_workspace_bytes", "hbl_forward_workspace_bytes", "hbl_quantize_activations", "hbl_gemm", "hbl_forward", "hbl_forward_latent",
-    "hbl_quantize_heads", "hbl_status_string", "hbl_last_hip_error",
+    "hbl_quantize_heads", "hbl_backward_workspace_bytes", "hbl_backward", "hbl_status_string",
+    "hbl_last_hip_error",
     "HBL_F32", "HBL_BF16", "HBL_NORM_RMS", "HBL_NORM_LN", "HBL_NORM_NONE",
     "HBL_A4_ABSMEAN_SQRT7", "HBL_A4_ABSMAX_7",
 ]
@@ -97,6 +98,8 @@ def load_library(path: str | None = None):
         "hbl_workspace_bytes": [I64, I64, PCFG, PSZ],
         "hbl_forward_workspace_bytes": [I64, I64, I64, PCFG, PSZ],
         "hbl_quantize_heads": [P, I32, I64, I64, I64, I32, F, P, P, P],
+        "hbl_backward_workspace_bytes": [I64, I64, I64, PCFG, I32, PSZ],
+        "hbl_backward": [P, I32, P, I32, I64, I64, P, P, P, I64, PCFG, P, P, P, SZ, P],
         "hbl_quantize_activations": [P, I32, I64, I64, P, PCFG, P, P, P, P, P],
         "hbl_gemm": [P, P, I32, I64, I64, P, P, I64, P, I32, P],
         "hbl_forward": [P, I32, I64, I64, P, P, P, I64, PCFG, P, I32, P, SZ, P],
@@ -329,3 +332,35 @@ def hbl_quantize_heads(X, H: int, bits: int, eps: float = 1e-5, codes=None, scal
     _check("hbl_quantize_heads", lib.hbl_quantize_heads(_ptr(X), _dtype_code(X), M, H, D, int(bits), float(eps),
                                                         _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
+
+
+def hbl_backward_workspace_bytes(M: int, K: int, N: int, cfg: Config, with_dw: bool = True) -> int:
+    c = cfg.c()
+    return _size_out(load_library().hbl_backward_workspace_bytes, M, K, N, ctypes.byref(c), int(bool(with_dw)))
+
+
+def hbl_backward(dY, X, W_packed, alpha, cfg: Config, gain=None, want_dW: bool = True, dX=None, dW=None, ws=None,
+                 stream=None):
+    """The layer's straight-through backward.  dY [M][N] and X [M][K] (fp32 or
+    bf16), W_packed [N][K/4], alpha [1].  Returns (dX float32 [M][K], dW
+    float32 [N][K] or None)."""
+    torch = _torch()
+    lib = load_library()
+    for t, n in ((dY, "dY"), (X, "X"), (W_packed, "W_packed"), (alpha, "alpha"), (gain, "gain")):
+        _dev(t, n)
+    M, K = X.shape
+    N = dY.shape[1]
+    if dX is None:
+        dX = torch.empty((M, K), dtype=torch.float32, device=X.device)
+    if want_dW and dW is None:
+        dW = torch.empty((N, K), dtype=torch.float32, device=X.device)
+    if not want_dW:
+        dW = None
+    if ws is None:
+        ws = torch.empty(max(1, hbl_backward_workspace_bytes(M, K, N, cfg, want_dW)), dtype=torch.uint8,
+                         device=X.device)
+    c = cfg.c()
+    _check("hbl_backward", lib.hbl_backward(_ptr(dY), _dtype_code(dY), _ptr(X), _dtype_code(X), M, K, _ptr(gain),
+                                            _ptr(W_packed), _ptr(alpha), N, ctypes.byref(c), _ptr(dX), _ptr(dW),
+                                            _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return dX, dW

@@ -158,6 +158,42 @@ hbl_status hbl_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, const hb
     return HBL_OK;
 }
 
+static hbl_status check_backward(int64_t M, int64_t K, int64_t N, const hbl_config* cfg) {
+    hbl_status st = check_config(cfg);
+    if (st != HBL_OK) return st;
+    if ((st = check_act_shape(M, K)) != HBL_OK) return st;
+    if ((st = check_gemm_shape(M, K, N)) != HBL_OK) return st;
+    if (K < 512) return HBL_ERR_SHAPE;                                     // four values per thread vector
+    if (M > ((int64_t)1 << 22) || N > ((int64_t)1 << 22)) return HBL_ERR_SHAPE;  // 32-bit tile offsets
+    return HBL_OK;
+}
+
+hbl_status hbl_backward_workspace_bytes(int64_t M, int64_t K, int64_t N, const hbl_config* cfg, int32_t with_dw,
+                                        size_t* bytes) {
+    if (!bytes) return HBL_ERR_NULL;
+    const hbl_status st = check_backward(M, K, N, cfg);
+    if (st != HBL_OK) return st;
+    *bytes = hbl::backward_ws_bytes(M, K, N, cfg->act_bits, with_dw != 0);
+    return HBL_OK;
+}
+
+hbl_status hbl_backward(const void* dY, int32_t dy_dtype, const void* X, int32_t x_dtype, int64_t M, int64_t K,
+                        const float* gain, const uint8_t* W_packed, const float* alpha, int64_t N,
+                        const hbl_config* cfg, float* dX, float* dW, void* ws, size_t ws_bytes, void* stream) {
+    hbl_status st = check_backward(M, K, N, cfg);
+    if (st != HBL_OK) return st;
+    if (!dtype_ok(dy_dtype) || !dtype_ok(x_dtype)) return HBL_ERR_DTYPE;
+    if (M == 0) return HBL_OK;
+    if (!dY || !X || !W_packed || !alpha || !dX || !ws) return HBL_ERR_NULL;
+    if (!aligned16(dY) || !aligned16(X) || !aligned16(W_packed) || !aligned(alpha, 4) || !aligned16(dX) ||
+        !aligned16(dW) || !aligned16(ws) || !aligned(gain, 4))
+        return HBL_ERR_ALIGN;
+    if (ws_bytes < hbl::backward_ws_bytes(M, K, N, cfg->act_bits, dW != nullptr)) return HBL_ERR_WORKSPACE;
+    const hipError_t e = hbl::launch_backward(dY, dy_dtype, X, x_dtype, M, K, gain, W_packed, alpha, N, *cfg, dX, dW,
+                                              ws, (hipStream_t)stream);
+    return e == hipSuccess ? HBL_OK : hip_fail(e);
+}
+
 hbl_status hbl_quantize_heads(const void* X, int32_t x_dtype, int64_t M, int64_t H, int64_t D, int32_t bits,
                               float eps, uint8_t* codes, float* scales, void* stream) {
     if (!dtype_ok(x_dtype)) return HBL_ERR_DTYPE;

@@ -1,0 +1,430 @@
+// backward.hip -- the layer's backward with the straight-through estimator
+// (gfx950): the quantisers are identities in the backward, so with
+// y = alpha * d * (q . Wq^T):
+//   dZ = alpha * dY . Wq           (bf16 matrix cores, fp32 sums)
+//   dR = H dZ                      (the forward's fast transform: H is symmetric)
+//   dX = norm'(x)^T dR             (RMSNorm / LayerNorm / none, with the gain)
+//   dW = dY^T . (d * q)            (the forward's dequantised codes; bf16 matrix cores)
+// Follows the 新智元 "微软 BitNet v2" repost, section "BitNet v2：原生4位激活"
+// (training with low-bit activations and ternary weights, quantisers passed
+// straight through) and section "H-BitLinear模块" (the forward it differentiates).
+//
+// The two contractions are plain GEMMs on bf16 operands: the ternary weights
+// and the integer codes are exact in bf16; dY (and dY * d for dW) is split
+// into a bf16 high part and a bf16 remainder, two products summed in fp32, so
+// the operands carry about 16 significant bits.  Operands are laid out "NT"
+// (both with the contraction index contiguous, padded with zeros to a
+// multiple of 32) by small decode / split / transpose kernels.
+#include "act_row.h"
+
+namespace hbl {
+namespace {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+HBL_DEVINL uint32_t bf16_bits_rne(float f) { return f32_to_bf16_bits(f); }
+
+// ---------------------------------------------------------- operand prep ----
+// 2-bit packed ternary weights (32-bit word: weight e of the 16-group at bits
+// 8*(e%4) + 2*(e/4)) -> bf16 [N][K] (0, +1.0 = 0x3F80, -1.0 = 0xBF80).
+__global__ __launch_bounds__(256) void tern_to_bf16_kernel(const uint32_t* __restrict__ Wp, int64_t n_words,
+                                                           uint4* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_words) return;
+    const uint32_t w = Wp[i];
+    uint32_t h[16];
+#pragma unroll
+    for (int e = 0; e < 16; e++) {
+        const uint32_t c = (w >> (8 * (e & 3) + 2 * (e >> 2))) & 3u;
+        h[e] = c == 1u ? 0x3F80u : c == 3u ? 0xBF80u : 0u;
+    }
+    out[2 * i] = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
+    out[2 * i + 1] = make_uint4(h[8] | h[9] << 16, h[10] | h[11] << 16, h[12] | h[13] << 16, h[14] | h[15] << 16);
+}
+
+// INT8 codes [count] or INT4 codes [count/2] (low nibble first) -> bf16, 8 per thread.
+template <int BITS>
+__global__ __launch_bounds__(256) void codes_to_bf16_kernel(const uint8_t* __restrict__ codes, int64_t count8,
+                                                            uint4* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= count8) return;
+    int v[8];
+    if constexpr (BITS == 8) {
+        const uint2 q = reinterpret_cast<const uint2*>(codes)[i];
+#pragma unroll
+        for (int e = 0; e < 4; e++) { v[e] = (int8_t)(q.x >> (8 * e)); v[4 + e] = (int8_t)(q.y >> (8 * e)); }
+    } else {
+        const uint32_t q = reinterpret_cast<const uint32_t*>(codes)[i];
+#pragma unroll
+        for (int e = 0; e < 8; e++) v[e] = (int)(q << (28 - 4 * e)) >> 28;
+    }
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) h[e] = bf16_bits_rne((float)v[e]);  // exact: |v| <= 128
+    out[i] = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
+}
+
+// v = in[r][c] * scale[r] (fp32 product; scale nullable) -> hi = bf16(v),
+// lo = bf16(v - hi) (lo nullable), as [R][Cp] with zeros for c >= C.
+template <typename Tin>
+__global__ __launch_bounds__(256) void split_bf16_kernel(const Tin* __restrict__ in, int64_t R, int64_t C,
+                                                         int64_t Cp, const float* __restrict__ scale,
+                                                         uint16_t* __restrict__ hi, uint16_t* __restrict__ lo) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= R * Cp) return;
+    const int64_t r = i / Cp, c = i % Cp;
+    float v = 0.f;
+    if (c < C) {
+        if constexpr (sizeof(Tin) == 4) v = in[r * C + c];
+        else v = __uint_as_float((uint32_t)in[r * C + c] << 16);
+        if (scale) v = v * scale[r];
+    }
+    const uint32_t h = bf16_bits_rne(v);
+    hi[i] = (uint16_t)h;
+    if (lo) lo[i] = (uint16_t)bf16_bits_rne(v - __uint_as_float(h << 16));
+}
+
+// out[c][r] = in[r][c] (r < R; 0 for R <= r < Rp): in [R][C] (row stride ldi), out [C][Rp].
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in, int64_t R, int64_t C,
+                                                             int64_t ldi, uint16_t* __restrict__ out, int64_t Rp) {
+    __shared__ uint16_t t[64][65];
+    const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int y = ty; y < 64; y += 4) {
+        const int64_t r = r0 + y, c = c0 + tx;
+        t[y][tx] = (r < R && c < C) ? in[r * ldi + c] : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int y = ty; y < 64; y += 4) {
+        const int64_t c = c0 + y, r = r0 + tx;
+        if (c < C && r < Rp) out[c * Rp + r] = t[tx][y];
+    }
+}
+
+// ------------------------------------------------------------ bf16 GEMM ----
+// C[r][s] = alpha * sum_t A[r][t] B[s][t] (+ C[r][s] when beta), A [R][T] and
+// B [S][T] bf16 with T % 32 == 0 (zero padded), C fp32 [R][S].  128 x 128
+// blocks of 4 waves (2 x 2 grid of 64 x 64 wave tiles, 2 x 2 tiles of
+// v_mfma_f32_32x32x16_bf16), K step 32 through double-buffered LDS (rows of
+// 64 bytes, 16-byte chunk c of row r stored at c ^ ((r >> 2) & 3): 16
+// consecutive rows read at one chunk hit 16 different bank groups).
+constexpr int kBgTile = 128, kBgK = 32, kBgThreads = 256;
+
+__global__ __launch_bounds__(kBgThreads, 2) void gemm_bf16_nt_kernel(const uint16_t* __restrict__ A,
+                                                                     const uint16_t* __restrict__ B, int64_t R,
+                                                                     int64_t S, int64_t T, float* __restrict__ C,
+                                                                     const float* __restrict__ alpha_dev,
+                                                                     float alpha_host, int beta) {
+    __shared__ __attribute__((aligned(16))) uint8_t sa[2][kBgTile * 64];
+    __shared__ __attribute__((aligned(16))) uint8_t sb[2][kBgTile * 64];
+    const int64_t r0 = (int64_t)blockIdx.y * kBgTile, s0 = (int64_t)blockIdx.x * kBgTile;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t ld = T * 2;  // bytes per operand row
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + r0 * T, (R - r0) * ld);  // rows past R load as zeros
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + s0 * T, (S - s0) * ld);
+    const int KT = (int)(T / kBgK);
+    uint4 qa[2], qb[2];
+    auto load = [&](int kt) {
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int c = tid + u * kBgThreads, row = c >> 2, ch = c & 3;
+            const uint32_t off = (uint32_t)(row * ld + kt * 64 + ch * 16);
+            qa[u] = buf_load16(ra, off);
+            qb[u] = buf_load16(rb, off);
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int c = tid + u * kBgThreads, row = c >> 2, ch = c & 3;
+            const int p = row * 64 + ((ch ^ ((row >> 2) & 3)) << 4);
+            *reinterpret_cast<uint4*>(&sa[buf][p]) = qa[u];
+            *reinterpret_cast<uint4*>(&sb[buf][p]) = qb[u];
+        }
+    };
+    v16f acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+    const int lr = lane & 31, lh = lane >> 5;
+    if (KT > 0) {
+        load(0);
+        stash(0);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < KT; kt++) {
+        const int buf = kt & 1;
+        if (kt + 1 < KT) load(kt + 1);  // in flight during this step's MFMAs
+#pragma unroll
+        for (int s = 0; s < 2; s++) {  // two 16-k MFMA steps; lane half lh takes k 8*lh .. +7 of each
+            v8bf a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const int row = wm * 64 + i * 32 + lr, ch = 2 * s + lh;
+                a[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(&sa[buf][row * 64 + ((ch ^ ((row >> 2) & 3)) << 4)]));
+                const int col = wn * 64 + i * 32 + lr;
+                b[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(&sb[buf][col * 64 + ((ch ^ ((col >> 2) & 3)) << 4)]));
+            }
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < KT) {
+            stash(buf ^ 1);  // the other buffer was last read in step kt-1, before the barrier below it
+            __syncthreads();
+        }
+    }
+    const float alpha = alpha_dev ? *alpha_dev : alpha_host;
+    // lane holds column lr of each 32 x 32 tile, rows 8*(r/4) + 4*lh + r%4
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int64_t s = s0 + wn * 64 + j * 32 + lr;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int64_t row = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (row < R && s < S) {
+                    float* p = C + row * S + s;
+                    const float v = alpha * acc[i][j][r];
+                    *p = beta ? *p + v : v;
+                }
+            }
+        }
+}
+
+// ------------------------------------------------------ rows: H and norm ----
+// One workgroup per row: dZ (fp32, read from and replaced in dzx) -> dR = H dZ
+// with the forward's register / LDS butterflies (act_row.h), then the norm's
+// backward with the row's x and gain at the same element positions.
+template <int LK, int NT, typename Tx, bool HAD>
+__global__ __launch_bounds__(NT) void bwd_rows_kernel(float* __restrict__ dzx, const Tx* __restrict__ X,
+                                                      const float* __restrict__ gain, int norm, float norm_eps) {
+    using S = ActShape<LK, NT, float>;
+    constexpr int K = S::K, E = S::E, V = S::V, LV = S::LV, LT = S::LT, VB = S::VB, VW = S::VW, FREE = S::FREE;
+    constexpr int NVEC = E / VW;
+    using Ph = Phases<NT, E, VB, FREE, LV, LV + LT>;
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    __shared__ double red[NT / kWave];
+    const int tid = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    float* drow = dzx + row * K;
+    const Tx* xrow = X + row * K;
+    ActRegs<LK, NT, float> v;
+    act_row_load<LK, NT, float>(drow, v);
+    if constexpr (HAD) {
+        reg_fwht<E>(v);
+#pragma unroll
+        for (int c = 0; c < S::C; c++)
+#pragma unroll
+            for (int j = 0; j < V; j += VW) {
+                float* p = lds + lds_off<VW>((c * NT + tid) * V + j);
+                *reinterpret_cast<float4*>(p) = make_float4(v[c * V + j], v[c * V + j + 1], v[c * V + j + 2], v[c * V + j + 3]);
+            }
+        __syncthreads();
+        Ph::run(lds, v);
+        const float inv = 1.f / sqrtf((float)K);
+#pragma unroll
+        for (int e = 0; e < E; e++) v[e] *= inv;
+    }
+    constexpr int SLO = HAD ? Ph::LAST_LO : 0;
+    constexpr int SR = HAD ? Ph::LAST_R : 0;
+    auto pos = [&](int u) {  // element index of register vector u
+        if constexpr (HAD) {
+            return phase_base<NT, VB, SLO, SR>(u >> SR, u & ((1 << SR) - 1));
+        } else {
+            const int j = u * VW;
+            return ((j / V) * NT + tid) * V + (j % V);
+        }
+    };
+    // x at the same positions; v becomes a = g * dR (every formula below uses
+    // the gain only in that product), then the output, in place
+    float x[E];
+#pragma unroll
+    for (int u = 0; u < NVEC; u++) {
+        const int e0 = pos(u);
+        if constexpr (sizeof(Tx) == 4) {
+            const float4 q = *reinterpret_cast<const float4*>(xrow + e0);
+            x[4 * u] = q.x; x[4 * u + 1] = q.y; x[4 * u + 2] = q.z; x[4 * u + 3] = q.w;
+        } else {
+            const uint2 q = *reinterpret_cast<const uint2*>(xrow + e0);
+            x[4 * u] = bf16_lo(q.x); x[4 * u + 1] = bf16_hi(q.x); x[4 * u + 2] = bf16_lo(q.y); x[4 * u + 3] = bf16_hi(q.y);
+        }
+        if (gain) {
+#pragma unroll
+            for (int t = 0; t < 4; t++) v[4 * u + t] *= gain[e0 + t];
+        }
+    }
+    // per-thread sums in fp32 (at most 64 terms), the block's sums in fp64
+    if (norm == HBL_NORM_RMS) {
+        float ss = 0.f, t = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; e++) {
+            ss += x[e] * x[e];
+            t += v[e] * x[e];
+        }
+        const double sst = block_sum_f64<NT>((double)ss, red);
+        const double tt = block_sum_f64<NT>((double)t, red);
+        const double c = 1.0 / sqrt(sst / K + (double)norm_eps);
+        const float cf = (float)c, kf = (float)(c * c * c / K * tt);
+#pragma unroll
+        for (int e = 0; e < E; e++) v[e] = cf * v[e] - kf * x[e];
+    } else if (norm == HBL_NORM_LN) {
+        float s1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; e++) s1 += x[e];
+        const float mu = (float)(block_sum_f64<NT>((double)s1, red) / K);
+        float s2 = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; e++) {
+            x[e] -= mu;
+            s2 += x[e] * x[e];
+        }
+        const float c = (float)(1.0 / sqrt(block_sum_f64<NT>((double)s2, red) / K + (double)norm_eps));
+        float sa = 0.f, sax = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; e++) {
+            x[e] *= c;  // xh
+            sa += v[e];
+            sax += v[e] * x[e];
+        }
+        const float ma = (float)(block_sum_f64<NT>((double)sa, red) / K);
+        const float mx = (float)(block_sum_f64<NT>((double)sax, red) / K);
+#pragma unroll
+        for (int e = 0; e < E; e++) v[e] = c * (v[e] - ma - x[e] * mx);
+    }
+    __syncthreads();  // every thread has read its dZ values (the row is rewritten in place)
+#pragma unroll
+    for (int u = 0; u < NVEC; u++)
+        *reinterpret_cast<float4*>(drow + pos(u)) = make_float4(v[4 * u], v[4 * u + 1], v[4 * u + 2], v[4 * u + 3]);
+}
+
+template <int LK, typename Tx, bool HAD>
+hipError_t launch_rows(float* dzx, int64_t M, const Tx* X, const float* gain, const hbl_config& cfg, hipStream_t s) {
+    constexpr int NT = threads_for(LK);
+    static_assert(ActShape<LK, NT, float>::VW == 4, "four values per vector");
+    const size_t lds_bytes = HAD ? (size_t)ActShape<LK, NT, float>::lds_floats * sizeof(float) : 0;
+    auto kern = bwd_rows_kernel<LK, NT, Tx, HAD>;
+    static bool attr_set = false;
+    if (!attr_set && lds_bytes > 0) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)M), dim3(NT), lds_bytes, s, dzx, X, gain, cfg.norm, cfg.norm_eps);
+    return hipGetLastError();
+}
+
+template <typename Tx, bool HAD>
+hipError_t rows_k(float* dzx, int64_t M, int64_t K, const Tx* X, const float* gain, const hbl_config& cfg,
+                  hipStream_t s) {
+    switch (K) {
+        case 512: return launch_rows<9, Tx, HAD>(dzx, M, X, gain, cfg, s);
+        case 1024: return launch_rows<10, Tx, HAD>(dzx, M, X, gain, cfg, s);
+        case 2048: return launch_rows<11, Tx, HAD>(dzx, M, X, gain, cfg, s);
+        case 4096: return launch_rows<12, Tx, HAD>(dzx, M, X, gain, cfg, s);
+        case 8192: return launch_rows<13, Tx, HAD>(dzx, M, X, gain, cfg, s);
+        case 16384: return launch_rows<14, Tx, HAD>(dzx, M, X, gain, cfg, s);
+        case 32768: return launch_rows<15, Tx, HAD>(dzx, M, X, gain, cfg, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t gemm_nt(const uint16_t* A, const uint16_t* B, int64_t R, int64_t S, int64_t T, float* C,
+                   const float* alpha_dev, float alpha_host, int beta, hipStream_t s) {
+    const dim3 grid((unsigned)((S + kBgTile - 1) / kBgTile), (unsigned)((R + kBgTile - 1) / kBgTile));
+    hipLaunchKernelGGL(gemm_bf16_nt_kernel, grid, dim3(kBgThreads), 0, s, A, B, R, S, T, C, alpha_dev, alpha_host,
+                       beta);
+    return hipGetLastError();
+}
+
+unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+}  // namespace
+
+int64_t bwd_pad32(int64_t v) { return (v + 31) / 32 * 32; }
+
+size_t backward_ws_bytes(int64_t M, int64_t K, int64_t N, int act_bits, bool want_dw) {
+    auto r256 = [](size_t v) { return (v + 255) / 256 * 256; };
+    const int64_t Np = bwd_pad32(N), Mp = bwd_pad32(M);
+    size_t b = r256((size_t)N * K * 2) + r256((size_t)K * Np * 2) + 2 * r256((size_t)M * Np * 2);
+    if (want_dw)
+        b += r256((size_t)M * K * act_bits / 8) + r256((size_t)M * 4) + r256((size_t)M * K * 2) +
+             r256((size_t)K * Mp * 2) + 2 * r256((size_t)Np * Mp * 2);
+    return b;
+}
+
+hipError_t launch_backward(const void* dY, int dy_dtype, const void* X, int x_dtype, int64_t M, int64_t K,
+                           const float* gain, const uint8_t* W_packed, const float* alpha, int64_t N,
+                           const hbl_config& cfg, float* dX, float* dW, void* ws, hipStream_t s) {
+    auto r256 = [](size_t v) { return (v + 255) / 256 * 256; };
+    const int64_t Np = bwd_pad32(N), Mp = bwd_pad32(M);
+    uint8_t* p = (uint8_t*)ws;
+    uint16_t* Wb = (uint16_t*)p; p += r256((size_t)N * K * 2);
+    uint16_t* Wt = (uint16_t*)p; p += r256((size_t)K * Np * 2);
+    uint16_t* Yh = (uint16_t*)p; p += r256((size_t)M * Np * 2);
+    uint16_t* Yl = (uint16_t*)p; p += r256((size_t)M * Np * 2);
+    const bool split = dy_dtype == HBL_F32;  // a bf16 dY is exact in one bf16 operand
+    hipError_t e = hipSuccess;
+    // weights: 2-bit -> bf16 [N][K] -> [K][Np]
+    hipLaunchKernelGGL(tern_to_bf16_kernel, dim3(blocks_for(N * K / 16)), dim3(256), 0, s, (const uint32_t*)W_packed,
+                       N * K / 16, (uint4*)Wb);
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((K + 63) / 64), (unsigned)((Np + 63) / 64)), dim3(256),
+                       0, s, Wb, N, K, K, Wt, Np);
+    // dY -> bf16 [M][Np] (+ remainder)
+    if (dy_dtype == HBL_F32)
+        hipLaunchKernelGGL(split_bf16_kernel<float>, dim3(blocks_for(M * Np)), dim3(256), 0, s, (const float*)dY, M, N,
+                           Np, (const float*)nullptr, Yh, Yl);
+    else
+        hipLaunchKernelGGL(split_bf16_kernel<uint16_t>, dim3(blocks_for(M * Np)), dim3(256), 0, s,
+                           (const uint16_t*)dY, M, N, Np, (const float*)nullptr, Yh, (uint16_t*)nullptr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // dZ = alpha * dY . Wq  -> dX (fp32 [M][K]), then H and the norm in place
+    if ((e = gemm_nt(Yh, Wt, M, K, Np, dX, alpha, 0.f, 0, s)) != hipSuccess) return e;
+    if (split && (e = gemm_nt(Yl, Wt, M, K, Np, dX, alpha, 0.f, 1, s)) != hipSuccess) return e;
+    if (x_dtype == HBL_F32)
+        e = cfg.hadamard ? rows_k<float, true>(dX, M, K, (const float*)X, gain, cfg, s)
+                         : rows_k<float, false>(dX, M, K, (const float*)X, gain, cfg, s);
+    else
+        e = cfg.hadamard ? rows_k<uint16_t, true>(dX, M, K, (const uint16_t*)X, gain, cfg, s)
+                         : rows_k<uint16_t, false>(dX, M, K, (const uint16_t*)X, gain, cfg, s);
+    if (e != hipSuccess || !dW) return e;
+    // dW = (dY * d)^T . q: the forward's codes and scales again
+    uint8_t* codes = p; p += r256((size_t)M * K * cfg.act_bits / 8);
+    float* xs = (float*)p; p += r256((size_t)M * 4);
+    uint16_t* Qb = (uint16_t*)p; p += r256((size_t)M * K * 2);
+    uint16_t* Qt = (uint16_t*)p; p += r256((size_t)K * Mp * 2);
+    uint16_t* PTh = (uint16_t*)p; p += r256((size_t)Np * Mp * 2);
+    uint16_t* PTl = (uint16_t*)p;
+    if ((e = launch_act_quant(X, x_dtype, M, K, gain, cfg, codes, xs, nullptr, nullptr, s)) != hipSuccess) return e;
+    if (cfg.act_bits == 8)
+        hipLaunchKernelGGL(codes_to_bf16_kernel<8>, dim3(blocks_for(M * K / 8)), dim3(256), 0, s, codes, M * K / 8,
+                           (uint4*)Qb);
+    else
+        hipLaunchKernelGGL(codes_to_bf16_kernel<4>, dim3(blocks_for(M * K / 8)), dim3(256), 0, s, codes, M * K / 8,
+                           (uint4*)Qb);
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((K + 63) / 64), (unsigned)((Mp + 63) / 64)), dim3(256),
+                       0, s, Qb, M, K, K, Qt, Mp);
+    // P = dY * d (fp32 product) as bf16 high part + remainder [M][Np], then [Np][Mp]
+    if (dy_dtype == HBL_F32)
+        hipLaunchKernelGGL(split_bf16_kernel<float>, dim3(blocks_for(M * Np)), dim3(256), 0, s, (const float*)dY, M, N,
+                           Np, (const float*)xs, Yh, Yl);
+    else
+        hipLaunchKernelGGL(split_bf16_kernel<uint16_t>, dim3(blocks_for(M * Np)), dim3(256), 0, s,
+                           (const uint16_t*)dY, M, N, Np, (const float*)xs, Yh, Yl);
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((Np + 63) / 64), (unsigned)((Mp + 63) / 64)), dim3(256),
+                       0, s, Yh, M, Np, Np, PTh, Mp);
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((Np + 63) / 64), (unsigned)((Mp + 63) / 64)), dim3(256),
+                       0, s, Yl, M, Np, Np, PTl, Mp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = gemm_nt(PTh, Qt, N, K, Mp, dW, nullptr, 1.f, 0, s)) != hipSuccess) return e;
+    return gemm_nt(PTl, Qt, N, K, Mp, dW, nullptr, 1.f, 1, s);
+}
+
+}  // namespace hbl

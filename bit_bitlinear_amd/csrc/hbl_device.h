@@ -196,6 +196,13 @@ hipError_t launch_gemm_f6f4(const uint8_t* codes6, const float* xscale, int64_t 
                             const float* alpha, int64_t N, void* Y, int y_dtype, hipStream_t s);
 // 2-bit packed ternary weights -> FP4 E2M1 nibbles (W4 as above)
 hipError_t launch_weights_to_fp4(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W4, hipStream_t s);
+// The layer's straight-through backward: dX (fp32 [M][K]) and, when dW is not
+// null, dW (fp32 [N][K]); K a power of two in [512, 32768]; ws holds
+// backward_ws_bytes(M, K, N, act_bits, dW != nullptr).
+size_t backward_ws_bytes(int64_t M, int64_t K, int64_t N, int act_bits, bool want_dw);
+hipError_t launch_backward(const void* dY, int dy_dtype, const void* X, int x_dtype, int64_t M, int64_t K,
+                           const float* gain, const uint8_t* W_packed, const float* alpha, int64_t N,
+                           const hbl_config& cfg, float* dX, float* dW, void* ws, hipStream_t s);
 // per-(token, head) absmax quantisation of attention states to unsigned codes:
 // V head vectors of D elements (fp32 or bf16) -> codes (D*bits/8 bytes each), d_out [V]
 hipError_t launch_head_quant(const void* X, int x_dtype, int64_t V, int64_t D, int bits, float eps, uint8_t* codes,

@@ -218,6 +218,33 @@ hbl_status hbl_forward_latent(const void* X, int32_t x_dtype, int64_t M, int64_t
 hbl_status hbl_quantize_heads(const void* X, int32_t x_dtype, int64_t M, int64_t H, int64_t D, int32_t bits,
                               float eps, uint8_t* codes, float* scales, void* stream);
 
+/*
+ * The layer's backward with the straight-through estimator (training with
+ * low-bit activations and ternary weights: "新智元: 微软 BitNet v2" repost,
+ * section "BitNet v2：原生4位激活").  The quantisers are identities in the
+ * backward, so for the forward y = alpha * d * (q . Wq^T) of hbl_forward:
+ *   dZ = alpha * dY . Wq                 [M][K]
+ *   dR = H dZ (normalised Sylvester, symmetric; dR = dZ when cfg->hadamard = 0)
+ *   dX = norm'(x)^T dR: RMS c g dR - (c^3/K) x sum(g dR x); LN
+ *        c (a - mean(a) - xh mean(a xh)) with a = g dR, xh = (x - mu) c;
+ *        none g dR  (c = 1/sqrt(mean + norm_eps) as in the forward)
+ *   dW = dY^T . (d * q)                  [N][K], q and d the forward's codes
+ *        and factors (computed again from X)
+ * dY [M][N] and X [M][K] fp32 or bf16; gain fp32 [K] or NULL; W_packed and
+ * alpha as for hbl_forward.  dX fp32 [M][K]; dW fp32 [N][K] or NULL (then
+ * only dX).  The two products run on the bf16 matrix cores with fp32 sums; dY
+ * (and dY * d) are split into a bf16 high part and a bf16 remainder, so the
+ * result agrees with the exact one to about 1e-5 of the row's largest value.
+ * ws (16-byte aligned) must hold hbl_backward_workspace_bytes(M, K, N, cfg,
+ * dW != NULL).  Constraints: those of hbl_forward, K >= 512, M and N <= 2^22;
+ * dY, X, dX, dW 16-byte aligned, gain 4-byte aligned.
+ */
+hbl_status hbl_backward_workspace_bytes(int64_t M, int64_t K, int64_t N, const hbl_config* cfg, int32_t with_dw,
+                                        size_t* bytes);
+hbl_status hbl_backward(const void* dY, int32_t dy_dtype, const void* X, int32_t x_dtype, int64_t M, int64_t K,
+                        const float* gain, const uint8_t* W_packed, const float* alpha, int64_t N,
+                        const hbl_config* cfg, float* dX, float* dW, void* ws, size_t ws_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* hbl_status_string(hbl_status status);
 

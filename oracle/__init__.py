@@ -92,6 +92,7 @@ def _load():
     lib.hbo_unpack_heads.restype = I
     lib.hbo_backward.argtypes = [P, P, I64, I64, P, I, F, I, I, I, F, P, F, I64, P, P]
     lib.hbo_backward.restype = I
+    lib.hbo_weight_grad.argtypes = [P, P, P, I64, I64, I64, P]
     _lib = lib
     return lib
 
@@ -336,3 +337,16 @@ def backward(dY: np.ndarray, X: np.ndarray, Wq: np.ndarray, alpha: float, *, bit
                                 int(bool(hadamard)), int(bits), int(a4_mode), float(quant_eps), _ptr(Wq),
                                 float(np.float32(alpha)), N, _ptr(dX), _ptr(dW)), "backward")
     return dX, dW
+
+
+def weight_grad(dY: np.ndarray, q: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """O12, weight part: dW = dY^T (d * q) in fp64 for given codes q int8
+    [M][K] and factors d [M]; dY fp32 or bf16 bit patterns [M][N]."""
+    dy = _c(as_f32(dY), np.float32)
+    q = _c(q, np.int8)
+    d = _c(d, np.float32)
+    M, N = dy.shape
+    K = q.shape[1]
+    dW = np.empty((N, K), np.float64)
+    _load().hbo_weight_grad(_ptr(dy), _ptr(q), _ptr(d), M, N, K, _ptr(dW))
+    return dW

@@ -468,6 +468,17 @@ int hbo_unpack_heads(const uint8_t* codes, int64_t V, int64_t D, int bits, uint8
  *     none: dx_j = g_j dr_j
  *   dW[n][k] = sum_m dY[m][n] * d[m] * q[m][k]   (q, d of the forward, O4-O8)
  * All in fp64.  dX [M][K] and dW [N][K] (nullable) are fp64 outputs. */
+/* O12, weight part: dW[n][k] = sum_m dY[m][n] * d[m] * q[m][k] for given codes
+ * q [M][K] and dequantisation factors d [M] (fp64). */
+void hbo_weight_grad(const float* dY, const int8_t* q, const float* d, int64_t M, int64_t N, int64_t K, double* dW) {
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++) {
+            double acc = 0.0;
+            for (int64_t m = 0; m < M; m++) acc += (double)dY[m * N + n] * (double)d[m] * (double)q[m * K + k];
+            dW[n * K + k] = acc;
+        }
+}
+
 int hbo_backward(const float* dY, const float* X, int64_t M, int64_t K, const float* gain, int norm, float norm_eps,
                  int hadamard, int bits, int a4_mode, float quant_eps, const int8_t* Wq, float alpha, int64_t N,
                  double* dX, double* dW) {
@@ -522,14 +533,7 @@ int hbo_backward(const float* dY, const float* X, int64_t M, int64_t K, const fl
         if (dW) {
             rc = hbo_quantize_activations(X, M, K, gain, norm, norm_eps, hadamard, bits, a4_mode, quant_eps, NULL, q,
                                           s, d);
-            if (rc == HBO_OK)
-                for (int64_t n = 0; n < N; n++)
-                    for (int64_t k = 0; k < K; k++) {
-                        double acc = 0.0;
-                        for (int64_t m = 0; m < M; m++)
-                            acc += (double)dY[m * N + n] * (double)d[m] * (double)q[m * K + k];
-                        dW[n * K + k] = acc;
-                    }
+            if (rc == HBO_OK) hbo_weight_grad(dY, q, d, M, N, K, dW);
         }
     }
     free(dz); free(dr); free(q); free(s); free(d);

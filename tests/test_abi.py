@@ -20,7 +20,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = hbl.declared_symbols()
-    assert len(names) == 12
+    assert len(names) == 14
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
 
@@ -160,3 +160,25 @@ def test_quantize_heads_validation(lib):
     assert call(M=(1 << 40) // 512 + 1, H=4, D=128) == 2
     assert call(X=None) == 1 and call(codes=None) == 1 and call(scales=None) == 1
     assert call(M=0, X=None, codes=None, scales=None) == 0
+
+
+def test_backward_validation(lib):
+    cfg = hbl.Config(act_bits=8).c()
+    f = lib.hbl_backward
+    M, K, N = 64, 1024, 256
+    need = hbl.hbl_backward_workspace_bytes(M, K, N, hbl.Config(act_bits=8), True)
+    assert need > hbl.hbl_backward_workspace_bytes(M, K, N, hbl.Config(act_bits=8), False)
+
+    def call(dY=A16, dydt=0, X=A16b, xdt=0, M=M, K=K, W=A16, alpha=A16b, N=N, c=ctypes.byref(cfg), dX=A16,
+             dW=A16b, ws=A16, wsb=need):
+        return f(dY, dydt, X, xdt, M, K, None, W, alpha, N, c, dX, dW, ws, wsb, None)
+
+    assert call(dydt=3) == 5 and call(xdt=3) == 5
+    assert call(K=256) == 2                       # below 512
+    assert call(K=1008) == 3                      # not a power of two
+    assert call(N=250) == 4
+    assert call(dX=None) == 1 and call(W=None) == 1 and call(ws=None) == 1
+    assert call(wsb=need - 1) == 7
+    assert call(M=0, dY=None, X=None, dX=None, ws=None) == 0
+    with pytest.raises(hbl.HblError):
+        hbl.hbl_backward_workspace_bytes(M, K, 1 << 23, hbl.Config(act_bits=8))

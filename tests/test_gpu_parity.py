@@ -565,3 +565,72 @@ def test_quantize_heads_eps_zero_and_ties():
         _sync()
         c_ref, d_ref = oracle.quantize_heads(x, bits, eps=0.0)
         assert np.array_equal(to_host(codes), c_ref) and np.array_equal(to_host(scales), d_ref)
+
+
+# ============================================================== backward ==
+# The straight-through backward against O12: dX within 2e-5 of each row's
+# largest |dX| (fp32 transform and sums against fp64), dW within 2e-5 of each
+# row's largest |dW| against O12's weight part on the GPU's own codes and
+# factors (so a code on a rounding boundary cannot differ); dY in fp32 (split
+# into two bf16 parts) and bf16, both norms and none, with and without the
+# Hadamard and the gain, INT8 and INT4 codes, ragged M and N (not multiples of
+# the 128 x 128 tile), and dX alone.
+BWD_CASES = [
+    # (M, K, N, bits, hadamard, norm, gain, dY dtype, X dtype)
+    (37, 1024, 272, 8, True, hbl.HBL_NORM_RMS, False, "f32", "f32"),
+    (130, 2048, 400, 4, True, hbl.HBL_NORM_LN, True, "bf16", "bf16"),
+    (64, 512, 64, 8, False, hbl.HBL_NORM_NONE, True, "f32", "bf16"),
+    (200, 4096, 128, 4, True, hbl.HBL_NORM_RMS, True, "f32", "f32"),
+    (9, 16384, 48, 8, True, hbl.HBL_NORM_RMS, False, "bf16", "f32"),
+    (3, 32768, 32, 4, False, hbl.HBL_NORM_LN, False, "f32", "bf16"),
+]
+
+
+def _rowwise_close(got, ref, rel):
+    scale = np.maximum(np.max(np.abs(ref), axis=1, keepdims=True), 1e-30)
+    return np.all(np.abs(got - ref) <= rel * scale)
+
+
+@pytest.mark.parametrize("M,K,N,bits,had,norm,use_gain,dydt,xdt", BWD_CASES)
+def test_backward_parity(M, K, N, bits, had, norm, use_gain, dydt, xdt):
+    _announce("backward M=%d K=%d N=%d a%d had=%d norm=%d gain=%d dY %s X %s" % (M, K, N, bits, had, norm,
+                                                                                use_gain, dydt, xdt))
+    rng = np.random.default_rng(M + K + N * 3 + bits)
+    X, _ = workloads.x_outlier_gaussian(rng, M, K, 4, 30.0)
+    if norm == hbl.HBL_NORM_LN:
+        X = (X + np.float32(2.0)).astype(np.float32)
+    W = workloads.w_latent(rng, N, K)
+    dY = rng.standard_normal((M, N)).astype(np.float32)
+    gain = (rng.standard_normal(K).astype(np.float32) * 0.5 + 1.0) if use_gain else None
+    Xh = workloads.f32_to_bf16_bits(X) if xdt == "bf16" else X
+    dYh = workloads.f32_to_bf16_bits(dY) if dydt == "bf16" else dY
+    cfg = hbl.Config(act_bits=bits, hadamard=had, norm=norm)
+    Wp, alpha = hbl.hbl_quantize_weights(to_dev(W))
+    gd = None if gain is None else to_dev(gain)
+    dX, dW = hbl.hbl_backward(to_dev(dYh), to_dev(Xh), Wp, alpha, cfg, gain=gd)
+    codes, xs, _, _ = hbl.hbl_quantize_activations(to_dev(Xh), cfg, gain=gd)
+    _sync()
+    a = to_host(alpha)[0]
+    Wq = oracle.unpack_ternary(to_host(Wp), K)
+    dX_ref, _ = oracle.backward(dYh, Xh, Wq, a, bits=bits, hadamard=had, gain=gain, norm=norm, want_dW=False)
+    assert _rowwise_close(to_host(dX).astype(np.float64), dX_ref, 2e-5)
+    dW_ref = oracle.weight_grad(dYh, unpack_codes(to_host(codes), K, bits), to_host(xs))
+    assert _rowwise_close(to_host(dW).astype(np.float64), dW_ref, 2e-5)
+
+
+def test_backward_dx_only_and_empty():
+    import torch
+    _announce("backward dX only, M = 0")
+    rng = np.random.default_rng(3)
+    M, K, N = 70, 2048, 96
+    X, _ = workloads.x_outlier_gaussian(rng, M, K, 4, 30.0)
+    W = workloads.w_latent(rng, N, K)
+    dY = rng.standard_normal((M, N)).astype(np.float32)
+    cfg = hbl.Config(act_bits=8)
+    Wp, alpha = hbl.hbl_quantize_weights(to_dev(W))
+    dX, dW = hbl.hbl_backward(to_dev(dY), to_dev(X), Wp, alpha, cfg, want_dW=False)
+    dX2, _ = hbl.hbl_backward(to_dev(dY), to_dev(X), Wp, alpha, cfg)
+    e = hbl.hbl_backward(to_dev(dY[:0]), to_dev(X[:0]), Wp, alpha, cfg)
+    _sync()
+    assert dW is None and np.array_equal(to_host(dX), to_host(dX2))
+    assert e[0].shape == (0, K)
