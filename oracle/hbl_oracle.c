@@ -514,7 +514,7 @@ int hbo_backward(const float* dY, const float* X, int64_t M, int64_t K, const fl
             } else {
                 double mu = 0.0, var = 0.0, ma = 0.0, max_ = 0.0;
                 for (int64_t k = 0; k < K; k++) mu += (double)x[k];
-                mu /= (double)K;
+                mu = mu / (double)K;
                 for (int64_t k = 0; k < K; k++) var += ((double)x[k] - mu) * ((double)x[k] - mu);
                 const double c = 1.0 / sqrt(var / (double)K + (double)norm_eps);
                 for (int64_t k = 0; k < K; k++) {
