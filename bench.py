@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_I8_TOPS = 5000.0          # MI355X dense INT8 MFMA, TOP/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 ROTATE_BYTES = 576 << 20       # > 2 x 256 MB last-level cache
 
 
@@ -41,9 +42,10 @@ def parse():
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=40)
     p.add_argument("--layer", default="wo_1.3b")
-    p.add_argument("--op", choices=("layer", "heads"), default="layer",
+    p.add_argument("--op", choices=("layer", "heads", "backward"), default="layer",
                    help="layer: the H-BitLinear step (default); heads: the low-bit attention-state quantiser "
-                        "(per-head absmax to a 3-bit KV cache) on the 3B-like KV shape")
+                        "(per-head absmax to a 3-bit KV cache) on the 3B-like KV shape; backward: the layer's "
+                        "straight-through backward (dX and dW) on --layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-iters", type=int, default=200)
     p.add_argument("--counter-run", action="store_true",
@@ -88,6 +90,8 @@ def main():
 
     if args.op == "heads":
         return bench_heads(args)
+    if args.op == "backward":
+        return bench_backward(args)
     layer = workloads.by_name(args.layer)
     M, K, N, bits = layer.M, layer.K, layer.N, layer.act_bits
     dev = torch.device("cuda:0")
@@ -315,6 +319,95 @@ def cpu_baseline(layer, X, W):
             "sample": "full weight ternarisation once (%.3f s) + forward of the first %d of %d rows (%.3f s), "
                       "scaled to all rows; %d OpenMP threads" % (t_wq, S, layer.M, t_rows, cores),
             "cpu_seconds": round((t_wq + t_rows) * cores, 1)}
+
+
+def bench_backward(args):
+    """The straight-through backward of --layer: one step = hbl_backward with
+    bf16 dY (dX through the Hadamard and the norm, and dW).  Its contractions
+    run on the bf16 matrix cores: dZ = alpha dY Wq (one product for a bf16 dY)
+    and dW = (dY d)^T q (two: high part and remainder), 6 M N K flops."""
+    import numpy as np
+    import torch
+
+    import bit_bitlinear_amd as hbl
+    import workloads
+
+    layer = workloads.by_name(args.layer)
+    M, K, N, bits = layer.M, layer.K, layer.N, layer.act_bits
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hbl.load_library()
+    X, W, _ = workloads.make_inputs(layer, 0)
+    rng = np.random.default_rng(1)
+    dY = workloads.f32_to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    to_t = lambda a: (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16
+                      else torch.from_numpy(a)).to(dev)
+    Xd, dYd = to_t(X), to_t(dY)
+    cfg = hbl.Config(act_bits=bits, hadamard=layer.hadamard)
+    Wp, alpha = hbl.hbl_quantize_weights(torch.from_numpy(W).to(dev))
+    ws_bytes = hbl.hbl_backward_workspace_bytes(M, K, N, cfg, True)
+    set_bytes = Xd.numel() * Xd.element_size() + dYd.numel() * 2 + ws_bytes + 4 * M * K + 4 * N * K
+    R = max(2, -(-ROTATE_BYTES // set_bytes))
+    sets = [(Xd if r == 0 else Xd.clone(), dYd if r == 0 else dYd.clone(),
+             torch.empty((M, K), dtype=torch.float32, device=dev), torch.empty((N, K), dtype=torch.float32, device=dev),
+             torch.empty(ws_bytes, dtype=torch.uint8, device=dev)) for r in range(R)]
+
+    def step(s):
+        hbl.hbl_backward(s[1], s[0], Wp, alpha, cfg, dX=s[2], dW=s[3], ws=s[4])
+
+    for i in range(max(2, args.warmup // 4)):
+        step(sets[i % R])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in range(R):
+            step(sets[r])
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, -(-max(R, args.steps // 4) // R))
+    timed = reps * R
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = ev0.elapsed_time(ev1) / timed * 1e3
+    flops = 6.0 * M * N * K
+    achieved = flops / (us * 1e-6) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        S = 16
+        Wq = oracle.unpack_ternary(Wp.cpu().numpy(), K)
+        a = float(alpha.cpu().numpy()[0])
+        t0 = time.perf_counter()
+        oracle.backward(dY[:S], X[:S], Wq, a, bits=bits, hadamard=layer.hadamard)
+        t = time.perf_counter() - t0
+        cpu = {"value": round(S / t, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": "dX and dW of the first %d of %d rows (%.2f s, single-threaded C; dW of a row subset is "
+                         "the same work per row)" % (S, M, t)}
+    print(json.dumps({
+        "metric": "H-BitLinear straight-through backward tokens/s (dX and dW)",
+        "value": round(M * timed / wall, 1), "unit": "tokens/s", "n_gpus": 1, "steps": timed,
+        "warmup": max(2, args.warmup // 4), "ms_per_step": round(wall / timed * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (the layer's seeded inputs; dY ~ N(0,1) in bf16)",
+        "config": {"workload": "backward of %s" % layer.desc, "M": M, "K": K, "N": N,
+                   "rotating_sets": R, "timing": "HIP graph replay of captured launches"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "gemm_bf16_nt_kernel (three products per step)", "us_per_step": round(us, 3),
+                     "work_desc": "6 M N K flops of the three bf16 products over the whole step's time (the "
+                                  "operand preparation and the row kernel included), a lower bound for the "
+                                  "products alone"},
+        "cpu_baseline": cpu,
+    }))
 
 
 def bench_heads(args):

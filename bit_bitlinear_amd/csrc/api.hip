@@ -164,7 +164,7 @@ static hbl_status check_backward(int64_t M, int64_t K, int64_t N, const hbl_conf
     if ((st = check_act_shape(M, K)) != HBL_OK) return st;
     if ((st = check_gemm_shape(M, K, N)) != HBL_OK) return st;
     if (K < 512) return HBL_ERR_SHAPE;                                     // four values per thread vector
-    if (M > ((int64_t)1 << 22) || N > ((int64_t)1 << 22)) return HBL_ERR_SHAPE;  // 32-bit tile offsets
+    if (M > ((int64_t)1 << 21) || N > ((int64_t)1 << 21)) return HBL_ERR_SHAPE;  // tile offsets, grid sizes
     return HBL_OK;
 }
 

@@ -14,7 +14,7 @@
 // into a bf16 high part and a bf16 remainder, two products summed in fp32, so
 // the operands carry about 16 significant bits.  Operands are laid out "NT"
 // (both with the contraction index contiguous, padded with zeros to a
-// multiple of 32) by small decode / split / transpose kernels.
+// multiple of 64) by small decode / split / transpose kernels.
 #include "act_row.h"
 
 namespace hbl {
@@ -66,23 +66,44 @@ __global__ __launch_bounds__(256) void codes_to_bf16_kernel(const uint8_t* __res
 }
 
 // v = in[r][c] * scale[r] (fp32 product; scale nullable) -> hi = bf16(v),
-// lo = bf16(v - hi) (lo nullable), as [R][Cp] with zeros for c >= C.
+// lo = bf16(v - hi) (lo nullable), as [R][Cp] with zeros for c >= C; C and
+// Cp multiples of 8; one thread per 8 consecutive elements of a row.
 template <typename Tin>
 __global__ __launch_bounds__(256) void split_bf16_kernel(const Tin* __restrict__ in, int64_t R, int64_t C,
                                                          int64_t Cp, const float* __restrict__ scale,
                                                          uint16_t* __restrict__ hi, uint16_t* __restrict__ lo) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= R * Cp) return;
-    const int64_t r = i / Cp, c = i % Cp;
-    float v = 0.f;
-    if (c < C) {
-        if constexpr (sizeof(Tin) == 4) v = in[r * C + c];
-        else v = __uint_as_float((uint32_t)in[r * C + c] << 16);
-        if (scale) v = v * scale[r];
+    const int64_t c8 = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 8, r = blockIdx.x;
+    if (c8 >= Cp) return;
+    float v[8];
+    if (c8 < C) {
+        const Tin* p = in + r * C + c8;
+        if constexpr (sizeof(Tin) == 4) {
+            const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+            const uint4 q = *reinterpret_cast<const uint4*>(p);
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int i = 0; i < 4; i++) { v[2 * i] = bf16_lo(w[i]); v[2 * i + 1] = bf16_hi(w[i]); }
+        }
+        if (scale) {
+            const float sc = scale[r];
+#pragma unroll
+            for (int i = 0; i < 8; i++) v[i] = v[i] * sc;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[i] = 0.f;
     }
-    const uint32_t h = bf16_bits_rne(v);
-    hi[i] = (uint16_t)h;
-    if (lo) lo[i] = (uint16_t)bf16_bits_rne(v - __uint_as_float(h << 16));
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        h[i] = bf16_bits_rne(v[i]);
+        l[i] = bf16_bits_rne(v[i] - __uint_as_float(h[i] << 16));
+    }
+    *reinterpret_cast<uint4*>(hi + r * Cp + c8) = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
+    if (lo)
+        *reinterpret_cast<uint4*>(lo + r * Cp + c8) = make_uint4(l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16, l[6] | l[7] << 16);
 }
 
 // out[c][r] = in[r][c] (r < R; 0 for R <= r < Rp): in [R][C] (row stride ldi), out [C][Rp].
@@ -104,20 +125,22 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
 
 // ------------------------------------------------------------ bf16 GEMM ----
 // C[r][s] = alpha * sum_t A[r][t] B[s][t] (+ C[r][s] when beta), A [R][T] and
-// B [S][T] bf16 with T % 32 == 0 (zero padded), C fp32 [R][S].  128 x 128
+// B [S][T] bf16 with T % 64 == 0 (zero padded), C fp32 [R][S].  128 x 128
 // blocks of 4 waves (2 x 2 grid of 64 x 64 wave tiles, 2 x 2 tiles of
-// v_mfma_f32_32x32x16_bf16), K step 32 through double-buffered LDS (rows of
-// 64 bytes, 16-byte chunk c of row r stored at c ^ ((r >> 2) & 3): 16
-// consecutive rows read at one chunk hit 16 different bank groups).
-constexpr int kBgTile = 128, kBgK = 32, kBgThreads = 256;
+// v_mfma_f32_32x32x16_bf16), K step 64 through double-buffered LDS (rows of
+// 128 bytes; 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7), so 16
+// consecutive rows read at one chunk hit 16 different bank groups); the next
+// step's global loads are in flight during the current step's MFMAs.
+constexpr int kBgTile = 128, kBgK = 64, kBgThreads = 256, kBgRow = kBgK * 2;
 
 __global__ __launch_bounds__(kBgThreads, 2) void gemm_bf16_nt_kernel(const uint16_t* __restrict__ A,
                                                                      const uint16_t* __restrict__ B, int64_t R,
                                                                      int64_t S, int64_t T, float* __restrict__ C,
                                                                      const float* __restrict__ alpha_dev,
                                                                      float alpha_host, int beta) {
-    __shared__ __attribute__((aligned(16))) uint8_t sa[2][kBgTile * 64];
-    __shared__ __attribute__((aligned(16))) uint8_t sb[2][kBgTile * 64];
+    __shared__ __attribute__((aligned(16))) uint8_t sa[2][kBgTile * kBgRow];
+    __shared__ __attribute__((aligned(16))) uint8_t sb[2][kBgTile * kBgRow];
+    constexpr int kLoads = kBgTile * kBgRow / 16 / kBgThreads;  // 16-byte loads per thread and operand
     const int64_t r0 = (int64_t)blockIdx.y * kBgTile, s0 = (int64_t)blockIdx.x * kBgTile;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -125,23 +148,23 @@ __global__ __launch_bounds__(kBgThreads, 2) void gemm_bf16_nt_kernel(const uint1
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + r0 * T, (R - r0) * ld);  // rows past R load as zeros
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + s0 * T, (S - s0) * ld);
     const int KT = (int)(T / kBgK);
-    uint4 qa[2], qb[2];
+    uint4 qa[kLoads], qb[kLoads];
     auto load = [&](int kt) {
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-            const int c = tid + u * kBgThreads, row = c >> 2, ch = c & 3;
-            const uint32_t off = (uint32_t)(row * ld + kt * 64 + ch * 16);
+        for (int u = 0; u < kLoads; u++) {
+            const int c = tid + u * kBgThreads, row = c >> 3, ch = c & 7;
+            const uint32_t off = (uint32_t)(row * ld + kt * kBgRow + ch * 16);
             qa[u] = buf_load16(ra, off);
             qb[u] = buf_load16(rb, off);
         }
     };
+    auto slot = [](int row, int ch) { return row * kBgRow + ((ch ^ ((row >> 1) & 7)) << 4); };
     auto stash = [&](int buf) {
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-            const int c = tid + u * kBgThreads, row = c >> 2, ch = c & 3;
-            const int p = row * 64 + ((ch ^ ((row >> 2) & 3)) << 4);
-            *reinterpret_cast<uint4*>(&sa[buf][p]) = qa[u];
-            *reinterpret_cast<uint4*>(&sb[buf][p]) = qb[u];
+        for (int u = 0; u < kLoads; u++) {
+            const int c = tid + u * kBgThreads, row = c >> 3, ch = c & 7;
+            *reinterpret_cast<uint4*>(&sa[buf][slot(row, ch)]) = qa[u];
+            *reinterpret_cast<uint4*>(&sb[buf][slot(row, ch)]) = qb[u];
         }
     };
     v16f acc[2][2];
@@ -161,14 +184,13 @@ __global__ __launch_bounds__(kBgThreads, 2) void gemm_bf16_nt_kernel(const uint1
         const int buf = kt & 1;
         if (kt + 1 < KT) load(kt + 1);  // in flight during this step's MFMAs
 #pragma unroll
-        for (int s = 0; s < 2; s++) {  // two 16-k MFMA steps; lane half lh takes k 8*lh .. +7 of each
+        for (int s = 0; s < kBgK / 16; s++) {  // 16-k MFMA steps; lane half lh takes k 8*lh .. +7 of each
             v8bf a[2], b[2];
 #pragma unroll
             for (int i = 0; i < 2; i++) {
-                const int row = wm * 64 + i * 32 + lr, ch = 2 * s + lh;
-                a[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(&sa[buf][row * 64 + ((ch ^ ((row >> 2) & 3)) << 4)]));
-                const int col = wn * 64 + i * 32 + lr;
-                b[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(&sb[buf][col * 64 + ((ch ^ ((col >> 2) & 3)) << 4)]));
+                const int ch = 2 * s + lh;
+                a[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(&sa[buf][slot(wm * 64 + i * 32 + lr, ch)]));
+                b[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(&sb[buf][slot(wn * 64 + i * 32 + lr, ch)]));
             }
 #pragma unroll
             for (int i = 0; i < 2; i++)
@@ -348,11 +370,11 @@ unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 }  // namespace
 
-int64_t bwd_pad32(int64_t v) { return (v + 31) / 32 * 32; }
+int64_t bwd_pad64(int64_t v) { return (v + 63) / 64 * 64; }  // whole GEMM K steps
 
 size_t backward_ws_bytes(int64_t M, int64_t K, int64_t N, int act_bits, bool want_dw) {
     auto r256 = [](size_t v) { return (v + 255) / 256 * 256; };
-    const int64_t Np = bwd_pad32(N), Mp = bwd_pad32(M);
+    const int64_t Np = bwd_pad64(N), Mp = bwd_pad64(M);
     size_t b = r256((size_t)N * K * 2) + r256((size_t)K * Np * 2) + 2 * r256((size_t)M * Np * 2);
     if (want_dw)
         b += r256((size_t)M * K * act_bits / 8) + r256((size_t)M * 4) + r256((size_t)M * K * 2) +
@@ -364,7 +386,7 @@ hipError_t launch_backward(const void* dY, int dy_dtype, const void* X, int x_dt
                            const float* gain, const uint8_t* W_packed, const float* alpha, int64_t N,
                            const hbl_config& cfg, float* dX, float* dW, void* ws, hipStream_t s) {
     auto r256 = [](size_t v) { return (v + 255) / 256 * 256; };
-    const int64_t Np = bwd_pad32(N), Mp = bwd_pad32(M);
+    const int64_t Np = bwd_pad64(N), Mp = bwd_pad64(M);
     uint8_t* p = (uint8_t*)ws;
     uint16_t* Wb = (uint16_t*)p; p += r256((size_t)N * K * 2);
     uint16_t* Wt = (uint16_t*)p; p += r256((size_t)K * Np * 2);
@@ -379,10 +401,10 @@ hipError_t launch_backward(const void* dY, int dy_dtype, const void* X, int x_dt
                        0, s, Wb, N, K, K, Wt, Np);
     // dY -> bf16 [M][Np] (+ remainder)
     if (dy_dtype == HBL_F32)
-        hipLaunchKernelGGL(split_bf16_kernel<float>, dim3(blocks_for(M * Np)), dim3(256), 0, s, (const float*)dY, M, N,
+        hipLaunchKernelGGL(split_bf16_kernel<float>, dim3((unsigned)M, blocks_for(Np / 8)), dim3(256), 0, s, (const float*)dY, M, N,
                            Np, (const float*)nullptr, Yh, Yl);
     else
-        hipLaunchKernelGGL(split_bf16_kernel<uint16_t>, dim3(blocks_for(M * Np)), dim3(256), 0, s,
+        hipLaunchKernelGGL(split_bf16_kernel<uint16_t>, dim3((unsigned)M, blocks_for(Np / 8)), dim3(256), 0, s,
                            (const uint16_t*)dY, M, N, Np, (const float*)nullptr, Yh, (uint16_t*)nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // dZ = alpha * dY . Wq  -> dX (fp32 [M][K]), then H and the norm in place
@@ -413,10 +435,10 @@ hipError_t launch_backward(const void* dY, int dy_dtype, const void* X, int x_dt
                        0, s, Qb, M, K, K, Qt, Mp);
     // P = dY * d (fp32 product) as bf16 high part + remainder [M][Np], then [Np][Mp]
     if (dy_dtype == HBL_F32)
-        hipLaunchKernelGGL(split_bf16_kernel<float>, dim3(blocks_for(M * Np)), dim3(256), 0, s, (const float*)dY, M, N,
+        hipLaunchKernelGGL(split_bf16_kernel<float>, dim3((unsigned)M, blocks_for(Np / 8)), dim3(256), 0, s, (const float*)dY, M, N,
                            Np, (const float*)xs, Yh, Yl);
     else
-        hipLaunchKernelGGL(split_bf16_kernel<uint16_t>, dim3(blocks_for(M * Np)), dim3(256), 0, s,
+        hipLaunchKernelGGL(split_bf16_kernel<uint16_t>, dim3((unsigned)M, blocks_for(Np / 8)), dim3(256), 0, s,
                            (const uint16_t*)dY, M, N, Np, (const float*)xs, Yh, Yl);
     hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((Np + 63) / 64), (unsigned)((Mp + 63) / 64)), dim3(256),
                        0, s, Yh, M, Np, Np, PTh, Mp);

@@ -236,7 +236,7 @@ hbl_status hbl_quantize_heads(const void* X, int32_t x_dtype, int64_t M, int64_t
  * (and dY * d) are split into a bf16 high part and a bf16 remainder, so the
  * result agrees with the exact one to about 1e-5 of the row's largest value.
  * ws (16-byte aligned) must hold hbl_backward_workspace_bytes(M, K, N, cfg,
- * dW != NULL).  Constraints: those of hbl_forward, K >= 512, M and N <= 2^22;
+ * dW != NULL).  Constraints: those of hbl_forward, K >= 512, M and N <= 2^21;
  * dY, X, dX, dW 16-byte aligned, gain 4-byte aligned.
  */
 hbl_status hbl_backward_workspace_bytes(int64_t M, int64_t K, int64_t N, const hbl_config* cfg, int32_t with_dw,

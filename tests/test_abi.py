@@ -181,4 +181,4 @@ def test_backward_validation(lib):
     assert call(wsb=need - 1) == 7
     assert call(M=0, dY=None, X=None, dX=None, ws=None) == 0
     with pytest.raises(hbl.HblError):
-        hbl.hbl_backward_workspace_bytes(M, K, 1 << 23, hbl.Config(act_bits=8))
+        hbl.hbl_backward_workspace_bytes(M, K, (1 << 21) + 16, hbl.Config(act_bits=8))
