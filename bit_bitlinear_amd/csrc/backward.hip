@@ -125,45 +125,55 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
 
 // ------------------------------------------------------------ bf16 GEMM ----
 // C[r][s] = alpha * sum_t A[r][t] B[s][t] (+ C[r][s] when beta), A [R][T] and
-// B [S][T] bf16 with T % 64 == 0 (zero padded), C fp32 [R][S].  128 x 128
-// blocks of 4 waves (2 x 2 grid of 64 x 64 wave tiles, 2 x 2 tiles of
+// B [S][T] bf16 with T % 64 == 0 (zero padded), C fp32 [R][S].  Blocks of
+// WGM x WGN waves, each a 64 x 64 wave tile (2 x 2 tiles of
 // v_mfma_f32_32x32x16_bf16), K step 64 through double-buffered LDS (rows of
 // 128 bytes; 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7), so 16
 // consecutive rows read at one chunk hit 16 different bank groups); the next
 // step's global loads are in flight during the current step's MFMAs.
-constexpr int kBgTile = 128, kBgK = 64, kBgThreads = 256, kBgRow = kBgK * 2;
+constexpr int kBgK = 64, kBgRow = kBgK * 2;
 
-__global__ __launch_bounds__(kBgThreads, 2) void gemm_bf16_nt_kernel(const uint16_t* __restrict__ A,
+template <int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_bf16_nt_kernel(const uint16_t* __restrict__ A,
                                                                      const uint16_t* __restrict__ B, int64_t R,
                                                                      int64_t S, int64_t T, float* __restrict__ C,
                                                                      const float* __restrict__ alpha_dev,
                                                                      float alpha_host, int beta) {
-    __shared__ __attribute__((aligned(16))) uint8_t sa[2][kBgTile * kBgRow];
-    __shared__ __attribute__((aligned(16))) uint8_t sb[2][kBgTile * kBgRow];
-    constexpr int kLoads = kBgTile * kBgRow / 16 / kBgThreads;  // 16-byte loads per thread and operand
-    const int64_t r0 = (int64_t)blockIdx.y * kBgTile, s0 = (int64_t)blockIdx.x * kBgTile;
+    constexpr int BM = 64 * WGM, BN = 64 * WGN, NT = 64 * WGM * WGN;
+    __shared__ __attribute__((aligned(16))) uint8_t sa[2][BM * kBgRow];
+    __shared__ __attribute__((aligned(16))) uint8_t sb[2][BN * kBgRow];
+    constexpr int kLa = BM * kBgRow / 16 / NT, kLb = BN * kBgRow / 16 / NT;  // 16-byte loads per thread
+    static_assert(BM * kBgRow % (16 * NT) == 0 && BN * kBgRow % (16 * NT) == 0, "whole loads per thread");
+    const int64_t r0 = (int64_t)blockIdx.y * BM, s0 = (int64_t)blockIdx.x * BN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
     const int64_t ld = T * 2;  // bytes per operand row
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + r0 * T, (R - r0) * ld);  // rows past R load as zeros
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + s0 * T, (S - s0) * ld);
     const int KT = (int)(T / kBgK);
-    uint4 qa[kLoads], qb[kLoads];
+    uint4 qa[kLa], qb[kLb];
     auto load = [&](int kt) {
 #pragma unroll
-        for (int u = 0; u < kLoads; u++) {
-            const int c = tid + u * kBgThreads, row = c >> 3, ch = c & 7;
-            const uint32_t off = (uint32_t)(row * ld + kt * kBgRow + ch * 16);
-            qa[u] = buf_load16(ra, off);
-            qb[u] = buf_load16(rb, off);
+        for (int u = 0; u < kLa; u++) {
+            const int c = tid + u * NT, row = c >> 3, ch = c & 7;
+            qa[u] = buf_load16(ra, (uint32_t)(row * ld + kt * kBgRow + ch * 16));
+        }
+#pragma unroll
+        for (int u = 0; u < kLb; u++) {
+            const int c = tid + u * NT, row = c >> 3, ch = c & 7;
+            qb[u] = buf_load16(rb, (uint32_t)(row * ld + kt * kBgRow + ch * 16));
         }
     };
     auto slot = [](int row, int ch) { return row * kBgRow + ((ch ^ ((row >> 1) & 7)) << 4); };
     auto stash = [&](int buf) {
 #pragma unroll
-        for (int u = 0; u < kLoads; u++) {
-            const int c = tid + u * kBgThreads, row = c >> 3, ch = c & 7;
+        for (int u = 0; u < kLa; u++) {
+            const int c = tid + u * NT, row = c >> 3, ch = c & 7;
             *reinterpret_cast<uint4*>(&sa[buf][slot(row, ch)]) = qa[u];
+        }
+#pragma unroll
+        for (int u = 0; u < kLb; u++) {
+            const int c = tid + u * NT, row = c >> 3, ch = c & 7;
             *reinterpret_cast<uint4*>(&sb[buf][slot(row, ch)]) = qb[u];
         }
     };
@@ -358,12 +368,24 @@ hipError_t rows_k(float* dzx, int64_t M, int64_t K, const Tx* X, const float* ga
     }
 }
 
+template <int WGM, int WGN>
+hipError_t gemm_nt_shape(const uint16_t* A, const uint16_t* B, int64_t R, int64_t S, int64_t T, float* C,
+                         const float* alpha_dev, float alpha_host, int beta, hipStream_t s) {
+    constexpr int BM = 64 * WGM, BN = 64 * WGN;
+    const dim3 grid((unsigned)((S + BN - 1) / BN), (unsigned)((R + BM - 1) / BM));
+    hipLaunchKernelGGL((gemm_bf16_nt_kernel<WGM, WGN>), grid, dim3(64 * WGM * WGN), 0, s, A, B, R, S, T, C, alpha_dev,
+                       alpha_host, beta);
+    return hipGetLastError();
+}
+
+// 256 x 256 blocks of 16 waves once they fill the 256 compute units (a
+// quarter less time than 128 x 128 blocks on an 8192-token 16384 x 4096 layer);
+// 128 x 128 blocks of 4 waves below that, where more blocks matter more.
 hipError_t gemm_nt(const uint16_t* A, const uint16_t* B, int64_t R, int64_t S, int64_t T, float* C,
                    const float* alpha_dev, float alpha_host, int beta, hipStream_t s) {
-    const dim3 grid((unsigned)((S + kBgTile - 1) / kBgTile), (unsigned)((R + kBgTile - 1) / kBgTile));
-    hipLaunchKernelGGL(gemm_bf16_nt_kernel, grid, dim3(kBgThreads), 0, s, A, B, R, S, T, C, alpha_dev, alpha_host,
-                       beta);
-    return hipGetLastError();
+    if (((R + 255) / 256) * ((S + 255) / 256) >= 256)
+        return gemm_nt_shape<4, 4>(A, B, R, S, T, C, alpha_dev, alpha_host, beta, s);
+    return gemm_nt_shape<2, 2>(A, B, R, S, T, C, alpha_dev, alpha_host, beta, s);
 }
 
 unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }

@@ -608,14 +608,52 @@ def test_backward_parity(M, K, N, bits, had, norm, use_gain, dydt, xdt):
     Wp, alpha = hbl.hbl_quantize_weights(to_dev(W))
     gd = None if gain is None else to_dev(gain)
     dX, dW = hbl.hbl_backward(to_dev(dYh), to_dev(Xh), Wp, alpha, cfg, gain=gd)
-    codes, xs, _, _ = hbl.hbl_quantize_activations(to_dev(Xh), cfg, gain=gd)
+    codes, _, _, _ = hbl.hbl_quantize_activations(to_dev(Xh), cfg, gain=gd)
     _sync()
     a = to_host(alpha)[0]
     Wq = oracle.unpack_ternary(to_host(Wp), K)
     dX_ref, _ = oracle.backward(dYh, Xh, Wq, a, bits=bits, hadamard=had, gain=gain, norm=norm, want_dW=False)
     assert _rowwise_close(to_host(dX).astype(np.float64), dX_ref, 2e-5)
-    dW_ref = oracle.weight_grad(dYh, unpack_codes(to_host(codes), K, bits), to_host(xs))
+    q, d = _backward_codes(Xh, to_host(codes), K, bits, had, gain, norm)
+    dW_ref = oracle.weight_grad(dYh, q, d)
     assert _rowwise_close(to_host(dW).astype(np.float64), dW_ref, 2e-5)
+
+
+def _backward_codes(Xh, codes_gpu, K, bits, had, gain, norm):
+    """The oracle's activation codes and factors for the weight gradient.  A
+    code may sit on a rounding boundary that the oracle's fp64 and the GPU's
+    fp32 decide differently (by 1, checked); there the weight gradient uses
+    the GPU's code, as the forward parity does."""
+    ref = oracle.quantize_activations(Xh, bits=bits, hadamard=had, gain=gain, norm=norm)
+    q_gpu = unpack_codes(codes_gpu, K, bits)
+    check_codes_end_to_end(q_gpu, ref["z"], ref["s"], ref["q"], "backward codes")
+    return np.where(q_gpu != ref["q"], q_gpu, ref["q"]), ref["d"]
+
+
+@pytest.mark.parametrize("M,K,N,bits", [(4096, 2048, 2048, 8), (4100, 4096, 4000, 4)])
+def test_backward_large_sampled(M, K, N, bits):
+    """Full-size layer (4096 tokens, 2048 x 2048, INT8) and a ragged shape whose
+    products both take the 256 x 256 GEMM blocks: 40 sampled rows of dX, 48
+    sampled columns of dW, against the oracle."""
+    _announce("backward large M=%d K=%d N=%d a%d" % (M, K, N, bits))
+    rng = np.random.default_rng(M + K + N)
+    X = workloads.f32_to_bf16_bits(workloads.x_outlier_gaussian(rng, M, K, 4, 30.0)[0])
+    W = workloads.w_latent(rng, N, K)
+    dY = workloads.f32_to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    cfg = hbl.Config(act_bits=bits)
+    Wp, alpha = hbl.hbl_quantize_weights(to_dev(W))
+    dX, dW = hbl.hbl_backward(to_dev(dY), to_dev(X), Wp, alpha, cfg)
+    codes, _, _, _ = hbl.hbl_quantize_activations(to_dev(X), cfg)
+    _sync()
+    rows = workloads.sample_rows(M, 40)
+    cols = np.unique(np.concatenate([np.arange(8), K - 8 + np.arange(8), rng.choice(K, 32, replace=False)]))
+    a = to_host(alpha)[0]
+    Wq = oracle.unpack_ternary(to_host(Wp), K)
+    dX_ref, _ = oracle.backward(dY[rows], X[rows], Wq, a, bits=bits, want_dW=False)
+    assert _rowwise_close(to_host(dX)[rows].astype(np.float64), dX_ref, 2e-5)
+    q, d = _backward_codes(X, to_host(codes), K, bits, True, None, hbl.HBL_NORM_RMS)
+    dW_ref = oracle.weight_grad(dY, np.ascontiguousarray(q[:, cols]), d)
+    assert _rowwise_close(to_host(dW)[:, cols].astype(np.float64), dW_ref, 2e-5)
 
 
 def test_backward_dx_only_and_empty():
