@@ -93,6 +93,12 @@ def _load():
     lib.hbo_backward.argtypes = [P, P, I64, I64, P, I, F, I, I, I, F, P, F, I64, P, P]
     lib.hbo_backward.restype = I
     lib.hbo_weight_grad.argtypes = [P, P, P, I64, I64, I64, P]
+    lib.hbo_base3_row_bytes.argtypes = [I64]
+    lib.hbo_base3_row_bytes.restype = I64
+    lib.hbo_pack_base3.argtypes = [P, I64, I64, P]
+    lib.hbo_pack_base3.restype = I
+    lib.hbo_unpack_base3.argtypes = [P, I64, I64, P]
+    lib.hbo_unpack_base3.restype = I
     _lib = lib
     return lib
 
@@ -350,3 +356,30 @@ def weight_grad(dY: np.ndarray, q: np.ndarray, d: np.ndarray) -> np.ndarray:
     dW = np.empty((N, K), np.float64)
     _load().hbo_weight_grad(_ptr(dy), _ptr(q), _ptr(d), M, N, K, _ptr(dW))
     return dW
+
+
+# ---------------------------------------------------------------- O13 ------
+def base3_row_bytes(K: int) -> int:
+    """Bytes per row of the base-3 weight format (16 * ceil(K / 80))."""
+    return int(_load().hbo_base3_row_bytes(int(K)))
+
+
+def pack_base3(Wq: np.ndarray) -> np.ndarray:
+    """O13: ternary int8 [N][K] -> uint8 [N][base3_row_bytes(K)], five weights
+    per byte as base-3 digits t + 1, the first weight least significant."""
+    Wq = _c(Wq, np.int8)
+    N, K = Wq.shape
+    out = np.empty((N, base3_row_bytes(K)), np.uint8)
+    _check(_load().hbo_pack_base3(_ptr(Wq), N, K, _ptr(out)), "pack_base3")
+    return out
+
+
+def unpack_base3(W3: np.ndarray, K: int) -> np.ndarray:
+    """The inverse of pack_base3 (rejects bytes above 242 and nonzero padding)."""
+    W3 = _c(W3, np.uint8)
+    N = W3.shape[0]
+    if W3.shape[1] != base3_row_bytes(K):
+        raise ValueError("row length does not match K")
+    out = np.empty((N, K), np.int8)
+    _check(_load().hbo_unpack_base3(_ptr(W3), N, K, _ptr(out)), "unpack_base3")
+    return out

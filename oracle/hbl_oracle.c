@@ -30,6 +30,7 @@
  *   O11 beside the layer: low-bit attention states, per (token, head) absmax
  *               to unsigned b-bit integers (b = 3, 4, 8)   ([XZY] 实验结果)
  *   O12 the layer's straight-through backward: dX through H and the norm, dW
+ *   O13 base-3 weight storage: five ternary weights per byte   ([CSDN] 掩码存储)
  *
  * Rounding is round-half-to-even (rint under the default FP environment)
  * everywhere.  No step is fused, blocked or reordered beyond these definitions.
@@ -538,4 +539,55 @@ int hbo_backward(const float* dY, const float* X, int64_t M, int64_t K, const fl
     }
     free(dz); free(dr); free(q); free(s); free(d);
     return rc;
+}
+
+/* --------------------------------------------------------------- O13 ---- */
+/* Base-3 weight storage.  [CSDN] "掩码存储" lists two ways of storing ternary
+ * weights; the first packs several weights into one integer, five per 8-bit
+ * byte (3^5 = 243 <= 256, 1.6 bits per weight).  The digit order and the row
+ * layout are not given; the reading taken: byte j of row n holds the weights
+ * k = 5j .. 5j+4 as base-3 digits t + 1 (t in {-1, 0, +1}), the first weight
+ * least significant,
+ *   byte = sum_{i=0..4} (W_q[n][5j+i] + 1) * 3^i,
+ * weights past K count as 0 (digit 1), and every row is padded to a whole
+ * number of 16-byte vectors: 16 * ceil(K / 80) bytes.  Bytes 243..255 never
+ * occur. */
+int64_t hbo_base3_row_bytes(int64_t K) { return 16 * ((K + 79) / 80); }
+
+int hbo_pack_base3(const int8_t* Wq, int64_t N, int64_t K, uint8_t* out) {
+    if (N < 0 || K < 1) return HBO_ERR;
+    const int64_t RB = hbo_base3_row_bytes(K);
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t j = 0; j < RB; j++) {
+            int v = 0, place = 1;
+            for (int i = 0; i < 5; i++) {
+                const int64_t k = 5 * j + i;
+                const int t = k < K ? Wq[n * K + k] : 0;
+                if (t < -1 || t > 1) return HBO_ERR;
+                v += (t + 1) * place;
+                place *= 3;
+            }
+            out[n * RB + j] = (uint8_t)v;
+        }
+    return HBO_OK;
+}
+
+/* The inverse: base-3 digits of each byte, least significant first, minus 1.
+ * A byte above 242, or a padding weight that is not 0, is an error. */
+int hbo_unpack_base3(const uint8_t* in, int64_t N, int64_t K, int8_t* Wq) {
+    if (N < 0 || K < 1) return HBO_ERR;
+    const int64_t RB = hbo_base3_row_bytes(K);
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t j = 0; j < RB; j++) {
+            int v = in[n * RB + j];
+            if (v > 242) return HBO_ERR;
+            for (int i = 0; i < 5; i++) {
+                const int t = v % 3 - 1;
+                v /= 3;
+                const int64_t k = 5 * j + i;
+                if (k < K) Wq[n * K + k] = (int8_t)t;
+                else if (t != 0) return HBO_ERR;
+            }
+        }
+    return HBO_OK;
 }

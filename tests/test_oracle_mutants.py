@@ -69,6 +69,12 @@ MUTANTS = [
      "acc += (double)dY[m * N + n] * (double)q[m * K + k];"),
     ("heads_dequant_factor_wrong", "d_out[v] = gamma == 0.f ? 0.f : gamma / (float)qp;",
      "d_out[v] = gamma == 0.f ? 0.f : gamma / (float)(qp + 1);"),
+    ("base3_digit_order_reversed", "v += (t + 1) * place;", "v += (t + 1) * (81 / place);"),
+    ("base3_sign_convention_swapped", "v += (t + 1) * place;", "v += (1 - t) * place;"),
+    ("base3_padding_weight_minus_one", "const int t = k < K ? Wq[n * K + k] : 0;",
+     "const int t = k < K ? Wq[n * K + k] : -1;"),
+    ("base3_row_bytes_wrong", "return 16 * ((K + 79) / 80);", "return 16 * (K / 80 + 1);"),
+    ("base3_unpack_sign_swapped", "const int t = v % 3 - 1;", "const int t = 1 - v % 3;"),
 ]
 
 

@@ -7,6 +7,7 @@ matmul), invariants, and brute force on tiny inputs.  Together they are chosen
 so that a dropped term, a wrong sign or index, a transposed operand, a wrong
 rounding mode or a misplaced epsilon in the oracle fails at least one test.
 """
+import itertools
 import math
 
 import numpy as np
@@ -469,3 +470,56 @@ def test_backward_dw_finite_differences():
                 Wp[n, k] += 0.5; Wm[n, k] -= 0.5
                 fd[n, k] = (np.sum(dY * (xh @ Wp.T)) - np.sum(dY * (xh @ Wm.T))) / 1.0
         assert np.allclose(dW, fd, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------ base-3 storage (O13)
+def test_base3_hand_packed(golden):
+    g = golden("pack_base3_k16.txt")
+    W = np.array([g["ternary"]], np.int8)
+    b = oracle.pack_base3(W)
+    assert b[0].tolist() == g["bytes"]
+    assert oracle.unpack_base3(b, 16).tolist() == W.tolist()
+
+
+def test_base3_every_digit_group():
+    """All 3^5 groups of five weights: each byte equals Python's own parse of
+    the digits t + 1 as a base-3 numeral (most significant digit = last
+    weight), so the bytes are 0..242, each exactly once."""
+    groups = list(itertools.product((-1, 0, 1), repeat=5))
+    W = np.array([t for grp in groups for t in grp], np.int8)[None, :]     # K = 1215
+    b = oracle.pack_base3(W)[0]
+    for j, grp in enumerate(groups):
+        assert b[j] == int("".join(str(t + 1) for t in reversed(grp)), 3)
+    assert sorted(b[:243].tolist()) == list(range(243))
+    assert np.all(b[243:] == 121) and b.size == 16 * math.ceil(1215 / 80)
+    assert np.array_equal(oracle.unpack_base3(oracle.pack_base3(W), 1215), W)
+
+
+@pytest.mark.parametrize("K", [16, 80, 96, 1024, 8192, 4000])
+def test_base3_round_trip_and_padding(K):
+    rng = np.random.default_rng(K)
+    W = rng.integers(-1, 2, size=(5, K)).astype(np.int8)
+    b = oracle.pack_base3(W)
+    assert b.shape == (5, 16 * ((K + 79) // 80)) and b.max() <= 242
+    assert np.array_equal(oracle.unpack_base3(b, K), W)
+    # a byte is a function of its own five weights only
+    W2 = W.copy()
+    W2[:, 7] = -W2[:, 7] if np.any(W2[:, 7]) else 1
+    b2 = oracle.pack_base3(W2)
+    changed = np.nonzero(np.any(b2 != b, axis=0))[0]
+    assert changed.tolist() == [1]
+    # the padding weights past K are zero: all-zero rows are all 121
+    assert np.all(oracle.pack_base3(np.zeros((2, K), np.int8)) == 121)
+
+
+def test_base3_rejects_bad_input():
+    with pytest.raises(ValueError):
+        oracle.pack_base3(np.array([[2, 0, 0, 0]], np.int8))
+    bad = oracle.pack_base3(np.zeros((1, 16), np.int8))
+    bad[0, 0] = 243
+    with pytest.raises(ValueError):
+        oracle.unpack_base3(bad, 16)
+    bad[0, 0] = 121
+    bad[0, 3] = 124        # digits 1,2,1,1,1: k = 15 is 0, the padding weight k = 16 is +1
+    with pytest.raises(ValueError):
+        oracle.unpack_base3(bad, 16)
