@@ -42,7 +42,7 @@ def parse():
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=40)
     p.add_argument("--layer", default="wo_1.3b")
-    p.add_argument("--op", choices=("layer", "heads", "backward"), default="layer",
+    p.add_argument("--op", choices=("layer", "heads", "backward", "base3"), default="layer",
                    help="layer: the H-BitLinear step (default); heads: the low-bit attention-state quantiser "
                         "(per-head absmax to a 3-bit KV cache) on the 3B-like KV shape; backward: the layer's "
                         "straight-through backward (dX and dW) on --layer")
@@ -92,6 +92,8 @@ def main():
         return bench_heads(args)
     if args.op == "backward":
         return bench_backward(args)
+    if args.op == "base3":
+        return bench_base3(args)
     layer = workloads.by_name(args.layer)
     M, K, N, bits = layer.M, layer.K, layer.N, layer.act_bits
     dev = torch.device("cuda:0")
@@ -483,6 +485,100 @@ def bench_heads(args):
                      "work_desc": "read X (bf16) + write codes + write scales, %d bytes per launch" % work},
         "cpu_baseline": cpu,
     }))
+
+
+def _graph_us(step, R, reps):
+    """Capture step(0..R-1) in one HIP graph; microseconds per step over reps
+    replays (events on the launch stream)."""
+    import torch
+    for r in range(R):
+        step(r)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in range(R):
+            step(r)
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / (reps * R) * 1e3, wall / (reps * R), g
+
+
+def bench_base3(args):
+    """Decode with the weights stored five per byte: one step = hbl_forward_base3
+    of the decode layer's tokens (activation quantisation, then the base-3 GEMV)
+    against weights packed once beforehand, as a deployment holds them.  The
+    2-bit forward of the same tokens is timed beside it."""
+    import numpy as np
+    import torch
+
+    import bit_bitlinear_amd as hbl
+    import workloads
+
+    layer = workloads.by_name(args.layer) if args.layer.startswith("decode_m") else workloads.DECODE[0]
+    if layer.M > 4:              # the base-3 GEMV takes 1 to 4 tokens
+        layer = workloads.DECODE[0]
+    M, K, N, bits = layer.M, layer.K, layer.N, layer.act_bits
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hbl.load_library()
+    X, W, _ = workloads.make_inputs(layer, 0)
+    Xd = torch.from_numpy(X).to(dev)
+    cfg = hbl.Config(act_bits=bits, hadamard=layer.hadamard)
+    Wp, alpha = hbl.hbl_quantize_weights(torch.from_numpy(W).to(dev))
+    W3 = hbl.hbl_pack_base3(Wp, K)
+    torch.cuda.synchronize()
+    w3_bytes = W3.numel()
+    R = max(2, -(-ROTATE_BYTES // (w3_bytes + Wp.numel())))
+    W3s = [W3] + [W3.clone() for _ in range(R - 1)]
+    Wps = [Wp] + [Wp.clone() for _ in range(R - 1)]
+    ws = torch.empty(hbl.hbl_workspace_bytes(M, K, cfg), dtype=torch.uint8, device=dev)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    codes = torch.empty((M, K if bits == 8 else K // 2), dtype=torch.int8 if bits == 8 else torch.uint8, device=dev)
+    xs = torch.empty(M, dtype=torch.float32, device=dev)
+    hbl.hbl_quantize_activations(Xd, cfg, codes=codes, xscale=xs)
+    reps = max(1, -(-args.steps // R))
+    fwd_us, wall, g1 = _graph_us(lambda r: hbl.hbl_forward_base3(Xd, W3s[r], alpha, N, cfg, Y=Y, ws=ws), R, reps)
+    gemv_us, _, g2 = _graph_us(lambda r: hbl.hbl_gemm_base3(codes, xs, bits, K, W3s[r], alpha, N, Y=Y), R, reps)
+    fwd2_us, _, g3 = _graph_us(lambda r: hbl.hbl_forward(Xd, Wps[r], alpha, N, cfg, Y=Y, ws=ws), R, reps)
+    gemv2_us, _, g4 = _graph_us(lambda r: hbl.hbl_gemm(codes, xs, bits, K, Wps[r], alpha, N, Y=Y), R, reps)
+    work = w3_bytes + M * K * bits // 8 + 4 * M + 4 + M * N * 2
+    achieved = work / (gemv_us * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        Wq = oracle.unpack_base3(W3.cpu().numpy(), K)
+        oracle.forward(X, Wq, float(alpha.cpu().numpy()[0]), bits=bits, hadamard=layer.hadamard)
+        t = time.perf_counter() - t0
+        cpu = {"value": round(M / t, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": "all %d tokens: base-3 unpack of the weights and the forward (%.2f s)" % (M, t)}
+    print(json.dumps({
+        "metric": "decode tokens/s with base-3 weights (five per byte)",
+        "value": round(M / wall, 1), "unit": "tokens/s", "n_gpus": 1, "steps": reps * R, "warmup": R,
+        "ms_per_step": round(wall * 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8", "data": "synthetic (the decode layer's seeded inputs)",
+        "config": {"workload": "%s with base-3 weights (%d bytes against %d in the 2-bit format)"
+                               % (layer.desc, w3_bytes, Wp.numel()), "M": M, "K": K, "N": N,
+                   "rotating_sets": R, "timing": "HIP graph replay of captured launches"},
+        "forward_us": round(fwd_us, 3), "forward_2bit_us": round(fwd2_us, 3),
+        "gemv_us": round(gemv_us, 3), "gemv_2bit_us": round(gemv2_us, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "gemv_base3_kernel", "us_per_launch": round(gemv_us, 3),
+                     "work_desc": "base-3 weights + codes + scales + bf16 Y, %d bytes per launch" % work},
+        "cpu_baseline": cpu,
+    }))
+    del g1, g2, g3, g4
 
 
 if __name__ == "__main__":

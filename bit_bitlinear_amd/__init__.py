@@ -104,6 +104,10 @@ def load_library(path: str | None = None):
         "hbl_gemm": [P, P, I32, I64, I64, P, P, I64, P, I32, P],
         "hbl_forward": [P, I32, I64, I64, P, P, P, I64, PCFG, P, I32, P, SZ, P],
         "hbl_forward_latent": [P, I32, I64, I64, P, P, I32, I64, F, PCFG, P, P, P, I32, P, SZ, P, SZ, P],
+        "hbl_base3_weight_bytes": [I64, I64, PSZ],
+        "hbl_pack_base3": [P, I64, I64, P, P],
+        "hbl_gemm_base3": [P, P, I32, I64, I64, P, P, I64, P, I32, P],
+        "hbl_forward_base3": [P, I32, I64, I64, P, P, P, I64, PCFG, P, I32, P, SZ, P],
     }
     for name, argtypes in sigs.items():
         f = getattr(lib, name)
@@ -364,3 +368,53 @@ def hbl_backward(dY, X, W_packed, alpha, cfg: Config, gain=None, want_dW: bool =
                                             _ptr(W_packed), _ptr(alpha), N, ctypes.byref(c), _ptr(dX), _ptr(dW),
                                             _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return dX, dW
+
+
+def hbl_base3_weight_bytes(N: int, K: int) -> int:
+    return _size_out(load_library().hbl_base3_weight_bytes, N, K)
+
+
+def hbl_pack_base3(W_packed, K: int, W3=None, stream=None):
+    """2-bit packed ternary weights [N][K/4] -> base-3 storage uint8 [N][16*ceil(K/80)]."""
+    torch = _torch()
+    lib = load_library()
+    _dev(W_packed, "W_packed")
+    N = W_packed.shape[0]
+    if W3 is None:
+        W3 = torch.empty((N, hbl_base3_weight_bytes(1, K)), dtype=torch.uint8, device=W_packed.device)
+    _dev(W3, "W3")
+    _check("hbl_pack_base3", lib.hbl_pack_base3(_ptr(W_packed), N, K, _ptr(W3), _stream(stream)))
+    return W3
+
+
+def hbl_gemm_base3(codes, xscale, act_bits: int, K: int, W3, alpha, N: int, y_dtype=None, Y=None, stream=None):
+    """hbl_gemm with base-3 weights (1 to 4 tokens).  Returns Y [M][N]."""
+    torch = _torch()
+    lib = load_library()
+    for t, n in ((codes, "codes"), (xscale, "xscale"), (W3, "W3"), (alpha, "alpha")):
+        _dev(t, n)
+    M = codes.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=y_dtype or torch.float32, device=codes.device)
+    _dev(Y, "Y")
+    _check("hbl_gemm_base3", lib.hbl_gemm_base3(_ptr(codes), _ptr(xscale), int(act_bits), M, K, _ptr(W3),
+                                                _ptr(alpha), N, _ptr(Y), _dtype_code(Y), _stream(stream)))
+    return Y
+
+
+def hbl_forward_base3(X, W3, alpha, N: int, cfg: Config, y_dtype=None, gain=None, Y=None, ws=None, stream=None):
+    """hbl_forward with base-3 weights (1 to 4 tokens).  Returns Y [M][N]."""
+    torch = _torch()
+    lib = load_library()
+    _dev(X, "X"); _dev(W3, "W3"); _dev(alpha, "alpha"); _dev(gain, "gain")
+    M, K = X.shape
+    if Y is None:
+        Y = torch.empty((M, N), dtype=y_dtype or X.dtype, device=X.device)
+    if ws is None:
+        ws = torch.empty(max(1, hbl_workspace_bytes(M, K, cfg)), dtype=torch.uint8, device=X.device)
+    _dev(Y, "Y"); _dev(ws, "ws")
+    c = cfg.c()
+    _check("hbl_forward_base3", lib.hbl_forward_base3(_ptr(X), _dtype_code(X), M, K, _ptr(gain), _ptr(W3),
+                                                      _ptr(alpha), N, ctypes.byref(c), _ptr(Y), _dtype_code(Y),
+                                                      _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return Y

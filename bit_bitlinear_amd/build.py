@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhbl.so")
 SOURCES = ["api.hip", "weight_quant.hip", "act_quant.hip", "act_pack.hip", "gemm.hip", "forward_small.hip",
-           "head_quant.hip", "backward.hip"]
+           "head_quant.hip", "backward.hip", "base3.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -28,6 +28,9 @@ constexpr int64_t kMaxGemmN = int64_t(1) << 20;  // keeps a 128-row output tile'
 // KiB of LDS) the shared grid measured no faster than two launches.
 constexpr int64_t kFuseActPackMaxK = 2048;
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+// The base-3 GEMV: one lane per 16-byte vector of a row (at most 256 of them)
+// and the codes of up to four tokens in registers.
+constexpr int64_t kMaxBase3M = 4, kMaxBase3K = 16384;
 
 hbl_status check_weight_shape(int64_t N, int64_t K) {
     if (N < 1 || K < 16) return HBL_ERR_SHAPE;
@@ -338,6 +341,70 @@ hbl_status hbl_forward_latent(const void* X, int32_t x_dtype, int64_t M, int64_t
     } else if (e == hipSuccess) {
         e = hbl::launch_gemm(codes, xscale, cfg->act_bits, M, K, W_packed, alpha, N, Y, y_dtype, s, tiled);
     }
+    return e == hipSuccess ? HBL_OK : hip_fail(e);
+}
+
+hbl_status hbl_base3_weight_bytes(int64_t N, int64_t K, size_t* bytes) {
+    if (!bytes) return HBL_ERR_NULL;
+    const hbl_status st = check_weight_shape(N, K);
+    if (st != HBL_OK) return st;
+    *bytes = (size_t)N * (size_t)hbl::base3_row_bytes(K);
+    return HBL_OK;
+}
+
+hbl_status hbl_pack_base3(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W3, void* stream) {
+    const hbl_status st = check_weight_shape(N, K);
+    if (st != HBL_OK) return st;
+    if (!W_packed || !W3) return HBL_ERR_NULL;
+    if (!aligned16(W_packed) || !aligned16(W3)) return HBL_ERR_ALIGN;
+    const hipError_t e = hbl::launch_pack_base3(W_packed, N, K, W3, (hipStream_t)stream);
+    return e == hipSuccess ? HBL_OK : hip_fail(e);
+}
+
+static hbl_status check_base3_gemv_shape(int64_t M, int64_t K, int64_t N) {
+    if (M < 0 || M > kMaxBase3M) return HBL_ERR_SHAPE;
+    if (K < 16 || K > kMaxBase3K) return HBL_ERR_SHAPE;
+    if (K % 16) return HBL_ERR_ALIGN;
+    if (N < 1 || N > kMaxGemmN) return HBL_ERR_SHAPE;
+    return HBL_OK;
+}
+
+hbl_status hbl_gemm_base3(const void* codes, const float* xscale, int32_t act_bits, int64_t M, int64_t K,
+                          const uint8_t* W3, const float* alpha, int64_t N, void* Y, int32_t y_dtype, void* stream) {
+    if (act_bits != 8 && act_bits != 4) return HBL_ERR_BITS;
+    if (!dtype_ok(y_dtype)) return HBL_ERR_DTYPE;
+    const hbl_status st = check_base3_gemv_shape(M, K, N);
+    if (st != HBL_OK) return st;
+    if (M == 0) return HBL_OK;
+    if (!codes || !xscale || !W3 || !alpha || !Y) return HBL_ERR_NULL;
+    if (!aligned16(codes) || !aligned(xscale, 4) || !aligned16(W3) || !aligned(alpha, 4) || !aligned16(Y))
+        return HBL_ERR_ALIGN;
+    const hipError_t e =
+        hbl::launch_gemv_base3(codes, xscale, act_bits, M, K, W3, alpha, N, Y, y_dtype, (hipStream_t)stream);
+    return e == hipSuccess ? HBL_OK : hip_fail(e);
+}
+
+hbl_status hbl_forward_base3(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
+                             const uint8_t* W3, const float* alpha, int64_t N, const hbl_config* cfg, void* Y,
+                             int32_t y_dtype, void* ws, size_t ws_bytes, void* stream) {
+    hbl_status st = check_config(cfg);
+    if (st != HBL_OK) return st;
+    if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return HBL_ERR_DTYPE;
+    st = check_act_shape(M, K);
+    if (st != HBL_OK) return st;
+    st = check_base3_gemv_shape(M, K, N);
+    if (st != HBL_OK) return st;
+    if (M == 0) return HBL_OK;
+    if (!X || !W3 || !alpha || !Y || !ws) return HBL_ERR_NULL;
+    if (!aligned16(X) || !aligned16(W3) || !aligned(alpha, 4) || !aligned16(Y) || !aligned16(ws) ||
+        !aligned(gain, 4))
+        return HBL_ERR_ALIGN;
+    const size_t cb = ws_codes_bytes(M, K, cfg->act_bits);
+    if (ws_bytes < cb + round_up((size_t)M * sizeof(float), 256)) return HBL_ERR_WORKSPACE;
+    const hipStream_t s = (hipStream_t)stream;
+    float* xscale = (float*)((uint8_t*)ws + cb);
+    hipError_t e = hbl::launch_act_quant(X, x_dtype, M, K, gain, *cfg, ws, xscale, nullptr, nullptr, s);
+    if (e == hipSuccess) e = hbl::launch_gemv_base3(ws, xscale, cfg->act_bits, M, K, W3, alpha, N, Y, y_dtype, s);
     return e == hipSuccess ? HBL_OK : hip_fail(e);
 }
 

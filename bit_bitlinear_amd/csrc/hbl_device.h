@@ -207,6 +207,11 @@ hipError_t launch_backward(const void* dY, int dy_dtype, const void* X, int x_dt
 // V head vectors of D elements (fp32 or bf16) -> codes (D*bits/8 bytes each), d_out [V]
 hipError_t launch_head_quant(const void* X, int x_dtype, int64_t V, int64_t D, int bits, float eps, uint8_t* codes,
                              float* d_out, hipStream_t s);
+// base-3 weights (five per byte, rows of 16 * ceil(K/80) bytes)
+int64_t base3_row_bytes(int64_t K);
+hipError_t launch_pack_base3(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W3, hipStream_t s);
+hipError_t launch_gemv_base3(const void* codes, const float* xscale, int act_bits, int64_t M, int64_t K,
+                             const uint8_t* W3, const float* alpha, int64_t N, void* Y, int y_dtype, hipStream_t s);
 // true when launch_gemm runs the decode GEMM for this shape; the codes may
 // then be in the decode tile layout (rows padded to a multiple of 16)
 bool gemm_uses_decode_kernel(int64_t M, int64_t K);

@@ -245,6 +245,44 @@ hbl_status hbl_backward(const void* dY, int32_t dy_dtype, const void* X, int32_t
                         const float* gain, const uint8_t* W_packed, const float* alpha, int64_t N,
                         const hbl_config* cfg, float* dX, float* dW, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Base-3 weight storage for the weight-bandwidth-bound decode regime (the
+ * CSDN post "[论文品鉴] 1-bit LLM", section "掩码存储": several ternary weights
+ * packed into one integer, five per 8-bit byte).  Layout W3 uint8 [N][RB],
+ * RB = 16 * ceil(K / 80): byte j of row n holds the weights k = 5j .. 5j+4 as
+ * base-3 digits, byte = sum_{i<5} (W_q[n][5j+i] + 1) * 3^i (first weight least
+ * significant; weights past K count as 0), 1.6 bits per weight.  The digit
+ * order and the row padding are the reading taken here; the page fixes only
+ * five weights per byte.
+ * hbl_base3_weight_bytes: N * RB.  Constraints as hbl_packed_weight_bytes.
+ * hbl_pack_base3: W_packed (the 2-bit layout of hbl_quantize_weights) -> W3,
+ * the same ternary values.  Both device buffers 16-byte aligned.
+ */
+hbl_status hbl_base3_weight_bytes(int64_t N, int64_t K, size_t* bytes);
+hbl_status hbl_pack_base3(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W3, void* stream);
+
+/*
+ * hbl_gemm with base-3 weights, for 1 to 4 tokens: Y = rescale(sum_k q W_q),
+ * bit for bit the output of hbl_gemm on the same ternary values (int32 sums
+ * on the vector ALU's dot-product instructions, then y = fp32(fp32(acc *
+ * xscale[m]) * alpha)).  codes as for hbl_gemm (row-major).  Constraints:
+ * 0 <= M <= 4 (M == 0 queues nothing); K % 16 == 0, 16 <= K <= 16384;
+ * 1 <= N <= 2^20; codes, W3 and Y 16-byte aligned.
+ */
+hbl_status hbl_gemm_base3(const void* codes, const float* xscale, int32_t act_bits, int64_t M, int64_t K,
+                          const uint8_t* W3, const float* alpha, int64_t N, void* Y, int32_t y_dtype, void* stream);
+
+/*
+ * hbl_forward with base-3 weights for 1 to 4 tokens: hbl_quantize_activations
+ * into the workspace (hbl_workspace_bytes), then hbl_gemm_base3.  Bit for bit
+ * hbl_forward on the same ternary values.  Constraints: those of
+ * hbl_quantize_activations and hbl_gemm_base3 together (K a power of two in
+ * [256, 16384], M <= 4).
+ */
+hbl_status hbl_forward_base3(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
+                             const uint8_t* W3, const float* alpha, int64_t N, const hbl_config* cfg, void* Y,
+                             int32_t y_dtype, void* ws, size_t ws_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* hbl_status_string(hbl_status status);
 

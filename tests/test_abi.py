@@ -20,7 +20,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = hbl.declared_symbols()
-    assert len(names) == 14
+    assert len(names) == 18
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
 
@@ -182,3 +182,38 @@ def test_backward_validation(lib):
     assert call(M=0, dY=None, X=None, dX=None, ws=None) == 0
     with pytest.raises(hbl.HblError):
         hbl.hbl_backward_workspace_bytes(M, K, (1 << 21) + 16, hbl.Config(act_bits=8))
+
+
+def test_base3_size_and_pack_validation(lib):
+    assert hbl.hbl_base3_weight_bytes(4096, 8192) == 4096 * 16 * 103       # ceil(8192 / 80) = 103 vectors
+    assert hbl.hbl_base3_weight_bytes(3, 80) == 3 * 16 and hbl.hbl_base3_weight_bytes(3, 96) == 3 * 32
+    with pytest.raises(hbl.HblError):
+        hbl.hbl_base3_weight_bytes(16, 40)                                   # K % 16
+    p = lib.hbl_pack_base3
+    assert p(A16, 64, 40, A16b, None) == 4 and p(A16, 0, 64, A16b, None) == 2
+    assert p(None, 64, 64, A16b, None) == 1 and p(A16, 64, 64, None, None) == 1
+    assert p(MIS, 64, 64, A16b, None) == 4 and p(A16, 64, 64, MIS, None) == 4
+
+
+def test_base3_gemm_and_forward_validation(lib):
+    g = lib.hbl_gemm_base3
+
+    def gemm(codes=A16, xs=A16b, bits=8, M=1, K=8192, W=A16, alpha=A16b, N=4096, Y=A16b, ydt=0):
+        return g(codes, xs, bits, M, K, W, alpha, N, Y, ydt, None)
+
+    assert gemm(bits=2) == 6 and gemm(ydt=3) == 5
+    assert gemm(M=5) == 2 and gemm(M=-1) == 2 and gemm(K=16384 + 16) == 2 and gemm(K=8) == 2
+    assert gemm(K=1000) == 4 and gemm(N=0) == 2 and gemm(N=(1 << 20) + 1) == 2
+    assert gemm(codes=None) == 1 and gemm(W=None) == 1 and gemm(Y=None) == 1
+    assert gemm(W=MIS) == 4 and gemm(Y=MIS) == 4
+    assert gemm(M=0, codes=None) == 0
+    cfg = hbl.Config(act_bits=4).c()
+    f = lib.hbl_forward_base3
+    need = hbl.hbl_workspace_bytes(4, 8192, hbl.Config(act_bits=4))
+
+    def fwd(X=A16, M=4, K=8192, W=A16b, N=4096, c=ctypes.byref(cfg), wsb=need):
+        return f(X, 0, M, K, None, W, A16b, N, c, A16b, 0, A16, wsb, None)
+
+    assert fwd(wsb=need - 1) == 7 and fwd(M=5) == 2 and fwd(K=32768) == 2 and fwd(K=8000) == 3
+    assert fwd(X=None) == 1 and fwd(W=None) == 1 and fwd(c=None) == 1
+    assert fwd(M=0, X=None, W=None) == 0
