@@ -26,45 +26,6 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 HBL_DEVINL uint32_t bf16_bits_rne(float f) { return f32_to_bf16_bits(f); }
 
 // ---------------------------------------------------------- operand prep ----
-// 2-bit packed ternary weights (32-bit word: weight e of the 16-group at bits
-// 8*(e%4) + 2*(e/4)) -> bf16 [N][K] (0, +1.0 = 0x3F80, -1.0 = 0xBF80).
-__global__ __launch_bounds__(256) void tern_to_bf16_kernel(const uint32_t* __restrict__ Wp, int64_t n_words,
-                                                           uint4* __restrict__ out) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n_words) return;
-    const uint32_t w = Wp[i];
-    uint32_t h[16];
-#pragma unroll
-    for (int e = 0; e < 16; e++) {
-        const uint32_t c = (w >> (8 * (e & 3) + 2 * (e >> 2))) & 3u;
-        h[e] = c == 1u ? 0x3F80u : c == 3u ? 0xBF80u : 0u;
-    }
-    out[2 * i] = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
-    out[2 * i + 1] = make_uint4(h[8] | h[9] << 16, h[10] | h[11] << 16, h[12] | h[13] << 16, h[14] | h[15] << 16);
-}
-
-// INT8 codes [count] or INT4 codes [count/2] (low nibble first) -> bf16, 8 per thread.
-template <int BITS>
-__global__ __launch_bounds__(256) void codes_to_bf16_kernel(const uint8_t* __restrict__ codes, int64_t count8,
-                                                            uint4* __restrict__ out) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= count8) return;
-    int v[8];
-    if constexpr (BITS == 8) {
-        const uint2 q = reinterpret_cast<const uint2*>(codes)[i];
-#pragma unroll
-        for (int e = 0; e < 4; e++) { v[e] = (int8_t)(q.x >> (8 * e)); v[4 + e] = (int8_t)(q.y >> (8 * e)); }
-    } else {
-        const uint32_t q = reinterpret_cast<const uint32_t*>(codes)[i];
-#pragma unroll
-        for (int e = 0; e < 8; e++) v[e] = (int)(q << (28 - 4 * e)) >> 28;
-    }
-    uint32_t h[8];
-#pragma unroll
-    for (int e = 0; e < 8; e++) h[e] = bf16_bits_rne((float)v[e]);  // exact: |v| <= 128
-    out[i] = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
-}
-
 // v = in[r][c] * scale[r] (fp32 product; scale nullable) -> hi = bf16(v),
 // lo = bf16(v - hi) (lo nullable), as [R][Cp] with zeros for c >= C; C and
 // Cp multiples of 8; one thread per 8 consecutive elements of a row.
@@ -106,21 +67,122 @@ __global__ __launch_bounds__(256) void split_bf16_kernel(const Tin* __restrict__
         *reinterpret_cast<uint4*>(lo + r * Cp + c8) = make_uint4(l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16, l[6] | l[7] << 16);
 }
 
-// out[c][r] = in[r][c] (r < R; 0 for R <= r < Rp): in [R][C] (row stride ldi), out [C][Rp].
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in, int64_t R, int64_t C,
-                                                             int64_t ldi, uint16_t* __restrict__ out, int64_t Rp) {
-    __shared__ uint16_t t[64][65];
+// ------------------------------------------- converting transposes ----
+// out_o[c][r] = f_o(source)[r][c] for r < R (0 for R <= r < Rp), c < C: the
+// conversion to bf16 and the transpose in one pass.  64 x 64 tiles, 256
+// threads; each thread converts two runs of 8 consecutive c of one row (one
+// 16-byte result each) into an LDS tile, then writes two runs of 8
+// consecutive r of one output row as 16-byte stores.  C % 8 == 0, Rp % 64 == 0.
+// Sources (load8 fills v[o][0..7] for (r, c .. c+7)):
+//   TernSrc   2-bit weights [R][C/4] (R11 layout) -> 0, +1.0, -1.0
+//   CodesSrc  INT8 [R][C] or INT4 [R][C/2] codes -> exact bf16 integers
+//   SplitSrc  x = fp32(in[r][c] * scale[r]) -> bf16(x) and bf16(x - bf16(x))
+struct TernSrc {
+    static constexpr int NOUT = 1;
+    const uint32_t* Wp;
+    int64_t C;
+    HBL_DEVINL void load8(int64_t r, int64_t c, uint32_t (&v)[2][8]) const {
+        const uint32_t w = Wp[r * (C / 16) + c / 16];
+        const int e0 = (int)(c & 15);
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int e = e0 + j;
+            const uint32_t code = (w >> (8 * (e & 3) + 2 * (e >> 2))) & 3u;
+            v[0][j] = code == 1u ? 0x3F80u : code == 3u ? 0xBF80u : 0u;
+        }
+    }
+};
+
+template <int BITS>
+struct CodesSrc {
+    static constexpr int NOUT = 1;
+    const uint8_t* codes;
+    int64_t C;
+    HBL_DEVINL void load8(int64_t r, int64_t c, uint32_t (&v)[2][8]) const {
+        int q[8];
+        if constexpr (BITS == 8) {
+            const uint2 b = *reinterpret_cast<const uint2*>(codes + r * C + c);
+#pragma unroll
+            for (int e = 0; e < 4; e++) { q[e] = (int8_t)(b.x >> (8 * e)); q[4 + e] = (int8_t)(b.y >> (8 * e)); }
+        } else {
+            const uint32_t b = *reinterpret_cast<const uint32_t*>(codes + (r * C + c) / 2);
+#pragma unroll
+            for (int e = 0; e < 8; e++) q[e] = (int)(b << (28 - 4 * e)) >> 28;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e++) v[0][e] = bf16_bits_rne((float)q[e]);  // exact: |q| <= 128
+    }
+};
+
+template <typename Tin>
+struct SplitSrc {
+    static constexpr int NOUT = 2;
+    const Tin* in;
+    int64_t C;
+    const float* scale;
+    HBL_DEVINL void load8(int64_t r, int64_t c, uint32_t (&v)[2][8]) const {
+        float x[8];
+        const Tin* p = in + r * C + c;
+        if constexpr (sizeof(Tin) == 4) {
+            const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        } else {
+            const uint4 q = *reinterpret_cast<const uint4*>(p);
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int i = 0; i < 4; i++) { x[2 * i] = bf16_lo(w[i]); x[2 * i + 1] = bf16_hi(w[i]); }
+        }
+        const float sc = scale[r];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const float t = x[i] * sc;
+            v[0][i] = bf16_bits_rne(t);
+            v[1][i] = bf16_bits_rne(t - __uint_as_float(v[0][i] << 16));
+        }
+    }
+};
+
+constexpr int kCtRow = 72;  // LDS row stride in bf16 elements (144 bytes: 16-byte aligned, banks spread)
+
+template <class Src>
+__global__ __launch_bounds__(256) void convert_transpose_kernel(Src src, int64_t R, int64_t C, uint16_t* __restrict__ out0,
+                                                                uint16_t* __restrict__ out1, int64_t Rp) {
+    __shared__ __attribute__((aligned(16))) uint16_t t[Src::NOUT][64][kCtRow];
     const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    for (int y = ty; y < 64; y += 4) {
-        const int64_t r = r0 + y, c = c0 + tx;
-        t[y][tx] = (r < R && c < C) ? in[r * ldi + c] : (uint16_t)0;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int idx = (int)threadIdx.x + 256 * i, rr = idx >> 3, cc = (idx & 7) * 8;
+        const int64_t r = r0 + rr, c = c0 + cc;
+        uint32_t v[2][8] = {};
+        if (r < R && c < C) src.load8(r, c, v);
+#pragma unroll
+        for (int o = 0; o < Src::NOUT; o++)
+            *reinterpret_cast<uint4*>(&t[o][rr][cc]) = make_uint4(v[o][0] | v[o][1] << 16, v[o][2] | v[o][3] << 16,
+                                                                  v[o][4] | v[o][5] << 16, v[o][6] | v[o][7] << 16);
     }
     __syncthreads();
-    for (int y = ty; y < 64; y += 4) {
-        const int64_t c = c0 + y, r = r0 + tx;
-        if (c < C && r < Rp) out[c * Rp + r] = t[tx][y];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int idx = (int)threadIdx.x + 256 * i, cr = idx >> 3, rc = (idx & 7) * 8;
+        const int64_t c = c0 + cr, r = r0 + rc;
+        if (c < C && r < Rp) {
+#pragma unroll
+            for (int o = 0; o < Src::NOUT; o++) {
+                uint32_t h[8];
+#pragma unroll
+                for (int j = 0; j < 8; j++) h[j] = t[o][rc + j][cr];
+                *reinterpret_cast<uint4*>((o == 0 ? out0 : out1) + c * Rp + r) =
+                    make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
+            }
+        }
     }
+}
+
+template <class Src>
+void convert_transpose(const Src& src, int64_t R, int64_t C, uint16_t* out0, uint16_t* out1, int64_t Rp,
+                       hipStream_t s) {
+    hipLaunchKernelGGL((convert_transpose_kernel<Src>), dim3((unsigned)((C + 63) / 64), (unsigned)(Rp / 64)),
+                       dim3(256), 0, s, src, R, C, out0, out1, Rp);
 }
 
 // ------------------------------------------------------------ bf16 GEMM ----
@@ -397,10 +459,10 @@ int64_t bwd_pad64(int64_t v) { return (v + 63) / 64 * 64; }  // whole GEMM K ste
 size_t backward_ws_bytes(int64_t M, int64_t K, int64_t N, int act_bits, bool want_dw) {
     auto r256 = [](size_t v) { return (v + 255) / 256 * 256; };
     const int64_t Np = bwd_pad64(N), Mp = bwd_pad64(M);
-    size_t b = r256((size_t)N * K * 2) + r256((size_t)K * Np * 2) + 2 * r256((size_t)M * Np * 2);
+    size_t b = r256((size_t)K * Np * 2) + 2 * r256((size_t)M * Np * 2);
     if (want_dw)
-        b += r256((size_t)M * K * act_bits / 8) + r256((size_t)M * 4) + r256((size_t)M * K * 2) +
-             r256((size_t)K * Mp * 2) + 2 * r256((size_t)Np * Mp * 2);
+        b += r256((size_t)M * K * act_bits / 8) + r256((size_t)M * 4) + r256((size_t)K * Mp * 2) +
+             2 * r256((size_t)Np * Mp * 2);
     return b;
 }
 
@@ -410,17 +472,13 @@ hipError_t launch_backward(const void* dY, int dy_dtype, const void* X, int x_dt
     auto r256 = [](size_t v) { return (v + 255) / 256 * 256; };
     const int64_t Np = bwd_pad64(N), Mp = bwd_pad64(M);
     uint8_t* p = (uint8_t*)ws;
-    uint16_t* Wb = (uint16_t*)p; p += r256((size_t)N * K * 2);
     uint16_t* Wt = (uint16_t*)p; p += r256((size_t)K * Np * 2);
     uint16_t* Yh = (uint16_t*)p; p += r256((size_t)M * Np * 2);
     uint16_t* Yl = (uint16_t*)p; p += r256((size_t)M * Np * 2);
     const bool split = dy_dtype == HBL_F32;  // a bf16 dY is exact in one bf16 operand
     hipError_t e = hipSuccess;
-    // weights: 2-bit -> bf16 [N][K] -> [K][Np]
-    hipLaunchKernelGGL(tern_to_bf16_kernel, dim3(blocks_for(N * K / 16)), dim3(256), 0, s, (const uint32_t*)W_packed,
-                       N * K / 16, (uint4*)Wb);
-    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((K + 63) / 64), (unsigned)((Np + 63) / 64)), dim3(256),
-                       0, s, Wb, N, K, K, Wt, Np);
+    // weights: 2-bit [N][K/4] -> bf16 [K][Np]
+    convert_transpose(TernSrc{(const uint32_t*)W_packed, K}, N, K, Wt, nullptr, Np, s);
     // dY -> bf16 [M][Np] (+ remainder)
     if (dy_dtype == HBL_F32)
         hipLaunchKernelGGL(split_bf16_kernel<float>, dim3((unsigned)M, blocks_for(Np / 8)), dim3(256), 0, s, (const float*)dY, M, N,
@@ -442,30 +500,15 @@ hipError_t launch_backward(const void* dY, int dy_dtype, const void* X, int x_dt
     // dW = (dY * d)^T . q: the forward's codes and scales again
     uint8_t* codes = p; p += r256((size_t)M * K * cfg.act_bits / 8);
     float* xs = (float*)p; p += r256((size_t)M * 4);
-    uint16_t* Qb = (uint16_t*)p; p += r256((size_t)M * K * 2);
     uint16_t* Qt = (uint16_t*)p; p += r256((size_t)K * Mp * 2);
     uint16_t* PTh = (uint16_t*)p; p += r256((size_t)Np * Mp * 2);
     uint16_t* PTl = (uint16_t*)p;
     if ((e = launch_act_quant(X, x_dtype, M, K, gain, cfg, codes, xs, nullptr, nullptr, s)) != hipSuccess) return e;
-    if (cfg.act_bits == 8)
-        hipLaunchKernelGGL(codes_to_bf16_kernel<8>, dim3(blocks_for(M * K / 8)), dim3(256), 0, s, codes, M * K / 8,
-                           (uint4*)Qb);
-    else
-        hipLaunchKernelGGL(codes_to_bf16_kernel<4>, dim3(blocks_for(M * K / 8)), dim3(256), 0, s, codes, M * K / 8,
-                           (uint4*)Qb);
-    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((K + 63) / 64), (unsigned)((Mp + 63) / 64)), dim3(256),
-                       0, s, Qb, M, K, K, Qt, Mp);
-    // P = dY * d (fp32 product) as bf16 high part + remainder [M][Np], then [Np][Mp]
-    if (dy_dtype == HBL_F32)
-        hipLaunchKernelGGL(split_bf16_kernel<float>, dim3((unsigned)M, blocks_for(Np / 8)), dim3(256), 0, s, (const float*)dY, M, N,
-                           Np, (const float*)xs, Yh, Yl);
-    else
-        hipLaunchKernelGGL(split_bf16_kernel<uint16_t>, dim3((unsigned)M, blocks_for(Np / 8)), dim3(256), 0, s,
-                           (const uint16_t*)dY, M, N, Np, (const float*)xs, Yh, Yl);
-    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((Np + 63) / 64), (unsigned)((Mp + 63) / 64)), dim3(256),
-                       0, s, Yh, M, Np, Np, PTh, Mp);
-    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((Np + 63) / 64), (unsigned)((Mp + 63) / 64)), dim3(256),
-                       0, s, Yl, M, Np, Np, PTl, Mp);
+    // codes -> bf16 [K][Mp]; P = dY * d as bf16 high part + remainder, [Np][Mp]
+    if (cfg.act_bits == 8) convert_transpose(CodesSrc<8>{codes, K}, M, K, Qt, nullptr, Mp, s);
+    else convert_transpose(CodesSrc<4>{codes, K}, M, K, Qt, nullptr, Mp, s);
+    if (dy_dtype == HBL_F32) convert_transpose(SplitSrc<float>{(const float*)dY, N, xs}, M, N, PTh, PTl, Mp, s);
+    else convert_transpose(SplitSrc<uint16_t>{(const uint16_t*)dY, N, xs}, M, N, PTh, PTl, Mp, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = gemm_nt(PTh, Qt, N, K, Mp, dW, nullptr, 1.f, 0, s)) != hipSuccess) return e;
     return gemm_nt(PTl, Qt, N, K, Mp, dW, nullptr, 1.f, 1, s);
