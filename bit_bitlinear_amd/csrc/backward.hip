@@ -16,6 +16,7 @@
 // (both with the contraction index contiguous, padded with zeros to a
 // multiple of 64) by small decode / split / transpose kernels.
 #include "act_row.h"
+#include "lds_dma.h"
 
 namespace hbl {
 namespace {
@@ -186,111 +187,131 @@ void convert_transpose(const Src& src, int64_t R, int64_t C, uint16_t* out0, uin
 }
 
 // ------------------------------------------------------------ bf16 GEMM ----
-// C[r][s] = alpha * sum_t A[r][t] B[s][t] (+ C[r][s] when beta), A [R][T] and
-// B [S][T] bf16 with T % 64 == 0 (zero padded), C fp32 [R][S].  Blocks of
-// WGM x WGN waves, each a 64 x 64 wave tile (2 x 2 tiles of
-// v_mfma_f32_32x32x16_bf16), K step 64 through double-buffered LDS (rows of
-// 128 bytes; 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7), so 16
-// consecutive rows read at one chunk hit 16 different bank groups); the next
-// step's global loads are in flight during the current step's MFMAs.
-constexpr int kBgK = 64, kBgRow = kBgK * 2;
-
-template <int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_bf16_nt_kernel(const uint16_t* __restrict__ A,
-                                                                     const uint16_t* __restrict__ B, int64_t R,
-                                                                     int64_t S, int64_t T, float* __restrict__ C,
-                                                                     const float* __restrict__ alpha_dev,
-                                                                     float alpha_host, int beta) {
-    constexpr int BM = 64 * WGM, BN = 64 * WGN, NT = 64 * WGM * WGN;
-    __shared__ __attribute__((aligned(16))) uint8_t sa[2][BM * kBgRow];
-    __shared__ __attribute__((aligned(16))) uint8_t sb[2][BN * kBgRow];
-    constexpr int kLa = BM * kBgRow / 16 / NT, kLb = BN * kBgRow / 16 / NT;  // 16-byte loads per thread
-    static_assert(BM * kBgRow % (16 * NT) == 0 && BN * kBgRow % (16 * NT) == 0, "whole loads per thread");
+// C[r][s] = alpha * sum_t A[r][t] B[s][t], plus sum_t A2[r][t] B[s][t] when A2
+// is given: the contraction then runs twice as long, its second half pairing
+// A2 with the same B (the high part and the remainder of a split operand in
+// one launch, so C is written once).  A, A2 [R][T], B [S][T] bf16 with
+// T % 64 == 0 (zero padded), C fp32 [R][S].  Blocks of WGM x WGN waves, each
+// a 64 x 64 wave tile (2 x 2 tiles of v_mfma_f32_32x32x16_bf16).  K step 64
+// (128-byte operand rows): both tiles travel global -> LDS directly through a
+// ring of S stages (the INT8 GEMM's loads, lds_dma.h), 16-byte chunk c of row
+// r stored at c ^ ((r >> 1) & 7); MFMA step s of lane half h reads chunk
+// 2s + h of its rows.
+template <int WGM, int WGN, int S>
+__global__ __launch_bounds__(64 * WGM * WGN, WGM * WGN == 4 ? 2 : 1) void gemm_bf16_dma_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ A2, const uint16_t* __restrict__ B, int64_t R,
+    int64_t SN, int64_t T, float* __restrict__ C, const float* __restrict__ alpha_dev, float alpha_host) {
+    constexpr int TA = 2, TB = 2, NW = WGM * WGN, BM = 64 * WGM, BN = 64 * WGN;
+    constexpr int a_bytes = BM * 128, b_bytes = BN * 128, stage_bytes = a_bytes + b_bytes;
+    constexpr int a_inst = a_bytes / 1024 / NW, b_inst = b_bytes / 1024 / NW, inst = a_inst + b_inst;
+    static_assert(a_bytes % (1024 * NW) == 0 && b_bytes % (1024 * NW) == 0, "whole wave instructions");
+    static_assert((S - 2) * inst < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * stage_bytes];
     const int64_t r0 = (int64_t)blockIdx.y * BM, s0 = (int64_t)blockIdx.x * BN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
     const int64_t ld = T * 2;  // bytes per operand row
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + r0 * T, (R - r0) * ld);  // rows past R load as zeros
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + s0 * T, (S - s0) * ld);
-    const int KT = (int)(T / kBgK);
-    uint4 qa[kLa], qb[kLb];
-    auto load = [&](int kt) {
+    const int KT1 = (int)(T / 64), KT = A2 ? 2 * KT1 : KT1;
+    const v4u a_desc = rsrc_words(A + r0 * T, (R - r0) * ld);  // rows past R load as zeros
+    const v4u a2_desc = rsrc_words((A2 ? A2 : A) + r0 * T, (R - r0) * ld);
+    const v4u b_desc = rsrc_words(B + s0 * T, (SN - s0) * ld);
+    uint32_t a_off[a_inst], b_off[b_inst];
 #pragma unroll
-        for (int u = 0; u < kLa; u++) {
-            const int c = tid + u * NT, row = c >> 3, ch = c & 7;
-            qa[u] = buf_load16(ra, (uint32_t)(row * ld + kt * kBgRow + ch * 16));
-        }
+    for (int u = 0; u < a_inst; u++) {
+        const int c = (wave * a_inst + u) * 64 + lane, row = c >> 3, p = c & 7;
+        a_off[u] = (uint32_t)(row * ld + ((p ^ ((row >> 1) & 7)) << 4));
+    }
 #pragma unroll
-        for (int u = 0; u < kLb; u++) {
-            const int c = tid + u * NT, row = c >> 3, ch = c & 7;
-            qb[u] = buf_load16(rb, (uint32_t)(row * ld + kt * kBgRow + ch * 16));
-        }
+    for (int u = 0; u < b_inst; u++) {
+        const int c = (wave * b_inst + u) * 64 + lane, row = c >> 3, p = c & 7;
+        b_off[u] = (uint32_t)(row * ld + ((p ^ ((row >> 1) & 7)) << 4));
+    }
+    const uint32_t smem_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+    auto issue = [&](int kt, int st) {
+        const uint32_t base = smem_addr + (uint32_t)(st * stage_bytes);
+        const bool second = kt >= KT1;
+        const uint32_t koff = (uint32_t)((second ? kt - KT1 : kt) * 128);
+        const v4u ad = second ? a2_desc : a_desc;
+#pragma unroll
+        for (int u = 0; u < a_inst; u++)
+            lds_dma16(ad, __builtin_amdgcn_readfirstlane(base + (uint32_t)((wave * a_inst + u) * 1024)), a_off[u] + koff);
+#pragma unroll
+        for (int u = 0; u < b_inst; u++)
+            lds_dma16(b_desc, __builtin_amdgcn_readfirstlane(base + (uint32_t)(a_bytes + (wave * b_inst + u) * 1024)),
+                      b_off[u] + koff);
     };
-    auto slot = [](int row, int ch) { return row * kBgRow + ((ch ^ ((row >> 1) & 7)) << 4); };
-    auto stash = [&](int buf) {
+    v16f acc[TA][TB];
 #pragma unroll
-        for (int u = 0; u < kLa; u++) {
-            const int c = tid + u * NT, row = c >> 3, ch = c & 7;
-            *reinterpret_cast<uint4*>(&sa[buf][slot(row, ch)]) = qa[u];
-        }
+    for (int i = 0; i < TA; i++)
 #pragma unroll
-        for (int u = 0; u < kLb; u++) {
-            const int c = tid + u * NT, row = c >> 3, ch = c & 7;
-            *reinterpret_cast<uint4*>(&sb[buf][slot(row, ch)]) = qb[u];
-        }
-    };
-    v16f acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < TB; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
     const int lr = lane & 31, lh = lane >> 5;
-    if (KT > 0) {
-        load(0);
-        stash(0);
-    }
-    __syncthreads();
+    auto frag = [&](const uint8_t* tile, int row, int ch) {
+        return __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(tile + row * 128 + ((ch ^ ((row >> 1) & 7)) << 4)));
+    };
+    auto compute = [&](int st) {
+        const uint8_t* sa = smem + st * stage_bytes;
+        const uint8_t* sb = sa + a_bytes;
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            v8bf a[TA], b[TB];
+#pragma unroll
+            for (int i = 0; i < TA; i++) a[i] = frag(sa, wm * 32 * TA + i * 32 + lr, 2 * s + lh);
+#pragma unroll
+            for (int j = 0; j < TB; j++) b[j] = frag(sb, wn * 32 * TB + j * 32 + lr, 2 * s + lh);
+#pragma unroll
+            for (int i = 0; i < TA; i++)
+#pragma unroll
+                for (int j = 0; j < TB; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    };
+    // prologue: steps 0 .. S-2 in flight (past the last step the loads repeat
+    // step KT-1, so every wave always has the same number in flight)
+#pragma unroll
+    for (int u = 0; u < S - 1; u++) issue(min(u, KT - 1), u);
     for (int kt = 0; kt < KT; kt++) {
-        const int buf = kt & 1;
-        if (kt + 1 < KT) load(kt + 1);  // in flight during this step's MFMAs
-#pragma unroll
-        for (int s = 0; s < kBgK / 16; s++) {  // 16-k MFMA steps; lane half lh takes k 8*lh .. +7 of each
-            v8bf a[2], b[2];
-#pragma unroll
-            for (int i = 0; i < 2; i++) {
-                const int ch = 2 * s + lh;
-                a[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(&sa[buf][slot(wm * 64 + i * 32 + lr, ch)]));
-                b[i] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(&sb[buf][slot(wn * 64 + i * 32 + lr, ch)]));
-            }
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int j = 0; j < 2; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < KT) {
-            stash(buf ^ 1);  // the other buffer was last read in step kt-1, before the barrier below it
-            __syncthreads();
-        }
+        wait_vmcnt<(S - 2) * inst>();  // this wave's loads of step kt have landed
+        barrier_no_wait();             // ... and every wave's; stage (kt-1)%S is free
+        issue(min(kt + S - 1, KT - 1), (kt + S - 1) % S);
+        compute(kt % S);
     }
+    wait_vmcnt<0>();  // no LDS-direct load may still be in flight when the block ends
     const float alpha = alpha_dev ? *alpha_dev : alpha_host;
     // lane holds column lr of each 32 x 32 tile, rows 8*(r/4) + 4*lh + r%4
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < TA; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int64_t s = s0 + wn * 64 + j * 32 + lr;
+        for (int j = 0; j < TB; j++) {
+            const int64_t sc = s0 + wn * 32 * TB + j * 32 + lr;
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int64_t row = r0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                if (row < R && s < S) {
-                    float* p = C + row * S + s;
-                    const float v = alpha * acc[i][j][r];
-                    *p = beta ? *p + v : v;
-                }
+                const int64_t row = r0 + wm * 32 * TA + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (row < R && sc < SN) C[row * SN + sc] = alpha * acc[i][j][r];
             }
         }
+}
+
+template <int WGM, int WGN, int S>
+hipError_t gemm_pair_shape(const uint16_t* A, const uint16_t* A2, const uint16_t* B, int64_t R, int64_t SN, int64_t T,
+                           float* C, const float* alpha_dev, float alpha_host, hipStream_t s) {
+    constexpr int BM = 64 * WGM, BN = 64 * WGN;
+    const dim3 grid((unsigned)((SN + BN - 1) / BN), (unsigned)((R + BM - 1) / BM));
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<WGM, WGN, S>), grid, dim3(64 * WGM * WGN), 0, s, A, A2, B, R, SN, T, C,
+                       alpha_dev, alpha_host);
+    return hipGetLastError();
+}
+
+// Block shape choice for the products (kBwShape selects).
+constexpr int kBwShape = 0;
+
+hipError_t gemm_pair(const uint16_t* A, const uint16_t* A2, const uint16_t* B, int64_t R, int64_t SN, int64_t T,
+                     float* C, const float* alpha_dev, float alpha_host, hipStream_t s) {
+    const bool big = ((R + 255) / 256) * ((SN + 255) / 256) >= 256;
+    if (kBwShape == 1) return gemm_pair_shape<2, 4, 2>(A, A2, B, R, SN, T, C, alpha_dev, alpha_host, s);
+    if (big) return gemm_pair_shape<4, 4, 2>(A, A2, B, R, SN, T, C, alpha_dev, alpha_host, s);
+    return gemm_pair_shape<2, 2, 2>(A, A2, B, R, SN, T, C, alpha_dev, alpha_host, s);
 }
 
 // ------------------------------------------------------ rows: H and norm ----
@@ -430,26 +451,6 @@ hipError_t rows_k(float* dzx, int64_t M, int64_t K, const Tx* X, const float* ga
     }
 }
 
-template <int WGM, int WGN>
-hipError_t gemm_nt_shape(const uint16_t* A, const uint16_t* B, int64_t R, int64_t S, int64_t T, float* C,
-                         const float* alpha_dev, float alpha_host, int beta, hipStream_t s) {
-    constexpr int BM = 64 * WGM, BN = 64 * WGN;
-    const dim3 grid((unsigned)((S + BN - 1) / BN), (unsigned)((R + BM - 1) / BM));
-    hipLaunchKernelGGL((gemm_bf16_nt_kernel<WGM, WGN>), grid, dim3(64 * WGM * WGN), 0, s, A, B, R, S, T, C, alpha_dev,
-                       alpha_host, beta);
-    return hipGetLastError();
-}
-
-// 256 x 256 blocks of 16 waves once they fill the 256 compute units (a
-// quarter less time than 128 x 128 blocks on an 8192-token 16384 x 4096 layer);
-// 128 x 128 blocks of 4 waves below that, where more blocks matter more.
-hipError_t gemm_nt(const uint16_t* A, const uint16_t* B, int64_t R, int64_t S, int64_t T, float* C,
-                   const float* alpha_dev, float alpha_host, int beta, hipStream_t s) {
-    if (((R + 255) / 256) * ((S + 255) / 256) >= 256)
-        return gemm_nt_shape<4, 4>(A, B, R, S, T, C, alpha_dev, alpha_host, beta, s);
-    return gemm_nt_shape<2, 2>(A, B, R, S, T, C, alpha_dev, alpha_host, beta, s);
-}
-
 unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 }  // namespace
@@ -488,8 +489,7 @@ hipError_t launch_backward(const void* dY, int dy_dtype, const void* X, int x_dt
                            (const uint16_t*)dY, M, N, Np, (const float*)nullptr, Yh, (uint16_t*)nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // dZ = alpha * dY . Wq  -> dX (fp32 [M][K]), then H and the norm in place
-    if ((e = gemm_nt(Yh, Wt, M, K, Np, dX, alpha, 0.f, 0, s)) != hipSuccess) return e;
-    if (split && (e = gemm_nt(Yl, Wt, M, K, Np, dX, alpha, 0.f, 1, s)) != hipSuccess) return e;
+    if ((e = gemm_pair(Yh, split ? Yl : nullptr, Wt, M, K, Np, dX, alpha, 0.f, s)) != hipSuccess) return e;
     if (x_dtype == HBL_F32)
         e = cfg.hadamard ? rows_k<float, true>(dX, M, K, (const float*)X, gain, cfg, s)
                          : rows_k<float, false>(dX, M, K, (const float*)X, gain, cfg, s);
@@ -510,8 +510,7 @@ hipError_t launch_backward(const void* dY, int dy_dtype, const void* X, int x_dt
     if (dy_dtype == HBL_F32) convert_transpose(SplitSrc<float>{(const float*)dY, N, xs}, M, N, PTh, PTl, Mp, s);
     else convert_transpose(SplitSrc<uint16_t>{(const uint16_t*)dY, N, xs}, M, N, PTh, PTl, Mp, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = gemm_nt(PTh, Qt, N, K, Mp, dW, nullptr, 1.f, 0, s)) != hipSuccess) return e;
-    return gemm_nt(PTl, Qt, N, K, Mp, dW, nullptr, 1.f, 1, s);
+    return gemm_pair(PTh, PTl, Qt, N, K, Mp, dW, nullptr, 1.f, s);
 }
 
 }  // namespace hbl
