@@ -326,8 +326,9 @@ def cpu_baseline(layer, X, W):
 def bench_backward(args):
     """The straight-through backward of --layer: one step = hbl_backward with
     bf16 dY (dX through the Hadamard and the norm, and dW).  Its contractions
-    run on the bf16 matrix cores: dZ = alpha dY Wq (one product for a bf16 dY)
-    and dW = (dY d)^T q (two: high part and remainder), 6 M N K flops."""
+    run on the bf16 matrix cores: dZ = alpha dY Wq (one contraction for a bf16
+    dY) and dW = (dY d)^T q (high part and remainder, one launch with a
+    contraction twice as long): 6 M N K flops."""
     import numpy as np
     import torch
 
@@ -404,7 +405,7 @@ def bench_backward(args):
                    "rotating_sets": R, "timing": "HIP graph replay of captured launches"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "gemm_bf16_nt_kernel (three products per step)", "us_per_step": round(us, 3),
+                     "kernel": "gemm_bf16_dma_kernel (dZ, then dW with high part and remainder in one launch)", "us_per_step": round(us, 3),
                      "work_desc": "6 M N K flops of the three bf16 products over the whole step's time (the "
                                   "operand preparation and the row kernel included), a lower bound for the "
                                   "products alone"},
