@@ -5,16 +5,19 @@
 //   dR = H dZ                      (the forward's fast transform: H is symmetric)
 //   dX = norm'(x)^T dR             (RMSNorm / LayerNorm / none, with the gain)
 //   dW = dY^T . (d * q)            (the forward's dequantised codes; bf16 matrix cores)
-// Follows the 新智元 "微软 BitNet v2" repost, section "BitNet v2：原生4位激活"
-// (training with low-bit activations and ternary weights, quantisers passed
-// straight through) and section "H-BitLinear模块" (the forward it differentiates).
+// Follows the xdnf.cn page "【AI论文】BitNet v2：针对1位LLM的原生4位激活和哈达玛
+// 变换", section "研究方法" (training through the low-bit quantisers with a
+// straight-through estimator), the 新智元 "微软 BitNet v2" repost, section
+// "BitNet v2：原生4位激活" (training with low-bit activations and ternary
+// weights), and its section "H-BitLinear模块" (the forward it differentiates).
 //
 // The two contractions are plain GEMMs on bf16 operands: the ternary weights
 // and the integer codes are exact in bf16; dY (and dY * d for dW) is split
-// into a bf16 high part and a bf16 remainder, two products summed in fp32, so
-// the operands carry about 16 significant bits.  Operands are laid out "NT"
-// (both with the contraction index contiguous, padded with zeros to a
-// multiple of 64) by small decode / split / transpose kernels.
+// into a bf16 high part and a bf16 remainder, so the operands carry about 16
+// significant bits, and one launch runs the contraction over both parts
+// (fp32 sums).  Operands are laid out "NT" (both with the contraction index
+// contiguous, padded with zeros to a multiple of 64) by a split kernel and
+// by converting transposes that widen to bf16 and transpose in one pass.
 #include "act_row.h"
 #include "lds_dma.h"
 

@@ -219,9 +219,10 @@ hbl_status hbl_quantize_heads(const void* X, int32_t x_dtype, int64_t M, int64_t
                               float eps, uint8_t* codes, float* scales, void* stream);
 
 /*
- * The layer's backward with the straight-through estimator (training with
- * low-bit activations and ternary weights: "新智元: 微软 BitNet v2" repost,
- * section "BitNet v2：原生4位激活").  The quantisers are identities in the
+ * The layer's backward with the straight-through estimator (training through
+ * the low-bit quantisers with it: the xdnf.cn page on BitNet v2, section
+ * "研究方法"; training with low-bit activations and ternary weights: the
+ * "新智元: 微软 BitNet v2" repost, section "BitNet v2：原生4位激活").  The quantisers are identities in the
  * backward, so for the forward y = alpha * d * (q . Wq^T) of hbl_forward:
  *   dZ = alpha * dY . Wq                 [M][K]
  *   dR = H dZ (normalised Sylvester, symmetric; dR = dZ when cfg->hadamard = 0)
