@@ -149,3 +149,26 @@ def test_forward_base3_decode_layer(M):
     q_cmp = np.where(flipped[:, None], q_gpu, ref["q"])
     check_y(y_to_f32(to_host(Y3)), oracle.rescale(oracle.int_gemm(q_cmp, Wq), ref["d"], a_ref), "base3 y",
             bf16_out=True)
+
+
+@pytest.mark.parametrize("bits,norm,use_gain,xdt,had", [(8, hbl.HBL_NORM_LN, True, "bf16", True),
+                                                        (4, hbl.HBL_NORM_NONE, True, "f32", False),
+                                                        (8, hbl.HBL_NORM_RMS, False, "bf16", False)])
+def test_forward_base3_configs(bits, norm, use_gain, xdt, had):
+    """Norms, gain, bf16 input, INT8 and the plain layer: bit for bit hbl_forward."""
+    import torch
+    M, K, N = 3, 4096, 528
+    _announce("forward base3 a%d norm=%d gain=%d %s had=%d" % (bits, norm, use_gain, xdt, had))
+    rng = np.random.default_rng(bits + norm * 3 + use_gain)
+    X, _ = workloads.x_outlier_gaussian(rng, M, K, 4, 30.0)
+    Xh = workloads.f32_to_bf16_bits(X) if xdt == "bf16" else X
+    W = workloads.w_latent(rng, N, K)
+    Wq, _, a_ref = oracle.quantize_weights(W)
+    gain = to_dev((rng.standard_normal(K) * 0.5 + 1.0).astype(np.float32)) if use_gain else None
+    cfg = hbl.Config(act_bits=bits, hadamard=had, norm=norm)
+    Xd = to_dev(Xh)
+    alpha = to_dev(np.array([a_ref], np.float32))
+    Y3 = hbl.hbl_forward_base3(Xd, to_dev(oracle.pack_base3(Wq)), alpha, N, cfg, y_dtype=torch.float32, gain=gain)
+    Y2 = hbl.hbl_forward(Xd, to_dev(oracle.pack_ternary(Wq)), alpha, N, cfg, y_dtype=torch.float32, gain=gain)
+    _sync()
+    assert np.array_equal(to_host(Y3), to_host(Y2))
