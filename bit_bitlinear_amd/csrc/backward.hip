@@ -306,14 +306,14 @@ hipError_t gemm_pair_shape(const uint16_t* A, const uint16_t* A2, const uint16_t
     return hipGetLastError();
 }
 
-// Block shape choice for the products (kBwShape selects).
-constexpr int kBwShape = 0;
-
+// 256 x 256 blocks of 16 waves once there are at least 256 of them (one per
+// CU); 128 x 128 blocks of 4 waves (two per CU) below that.  Measured against
+// 128 x 256 blocks of 8 waves, 64 x 128 wave tiles and three-stage rings,
+// which were slower at both 4096 x 2048 x 2048 and 8192 x 16384 x 4096.
 hipError_t gemm_pair(const uint16_t* A, const uint16_t* A2, const uint16_t* B, int64_t R, int64_t SN, int64_t T,
                      float* C, const float* alpha_dev, float alpha_host, hipStream_t s) {
-    const bool big = ((R + 255) / 256) * ((SN + 255) / 256) >= 256;
-    if (kBwShape == 1) return gemm_pair_shape<2, 4, 2>(A, A2, B, R, SN, T, C, alpha_dev, alpha_host, s);
-    if (big) return gemm_pair_shape<4, 4, 2>(A, A2, B, R, SN, T, C, alpha_dev, alpha_host, s);
+    if (((R + 255) / 256) * ((SN + 255) / 256) >= 256)
+        return gemm_pair_shape<4, 4, 2>(A, A2, B, R, SN, T, C, alpha_dev, alpha_host, s);
     return gemm_pair_shape<2, 2, 2>(A, A2, B, R, SN, T, C, alpha_dev, alpha_host, s);
 }
 
