@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_I8_TOPS = 5000.0          # MI355X dense INT8 MFMA, TOP/s
+PEAK_F6F4_TOPS = 10100.0       # MI355X dense FP6 / FP4 MFMA, TFLOP/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 ROTATE_BYTES = 576 << 20       # > 2 x 256 MB last-level cache
 
@@ -229,6 +230,13 @@ def main():
             "work": 2 * M * N * K if M > 64 else code_bytes + 4 * M + N * K // 4 + M * N * 2,
             "work_desc": "2*M*N*K integer ops" if M > 64 else "read codes + xscale + 2-bit W, write Y"},
     }
+    if f6f4:
+        # the FP6 x FP4 GEMM runs only inside hbl_forward (with the FP6
+        # activation kernel and the FP4 weight conversion): its ops over the
+        # whole forward's time, a lower bound for the GEMM alone
+        kernels["forward_fp6xfp4"] = {
+            "us": t_fwd, "bound": "mfma", "unit": "TFLOP/s", "work": 2 * M * N * K, "peak": PEAK_F6F4_TOPS,
+            "work_desc": "2*M*N*K ops over hbl_forward (FP6 activation codes, FP4 weights, FP6 x FP4 GEMM)"}
     if fused:
         kernels["forward_small_fused"] = {
             "us": t_fwd, "bound": "hbm", "unit": "GB/s",
@@ -237,11 +245,12 @@ def main():
     for k, v in kernels.items():
         per_s = v["work"] / (v["us"] * 1e-6)
         v["achieved"] = per_s / 1e12 if v["unit"] == "TFLOP/s" else per_s / 1e9
-        v["peak"] = PEAK_I8_TOPS if v["unit"] == "TFLOP/s" else PEAK_HBM_GBS
+        v["peak"] = v.get("peak") or (PEAK_I8_TOPS if v["unit"] == "TFLOP/s" else PEAK_HBM_GBS)
         v["frac"] = v["achieved"] / v["peak"]
-    # the dominant kernel of the step (for a fused forward, the stage kernels it replaces are not in the step)
-    dom_name = max((k for k in kernels if not (fused and k in ("norm_fwht_quant", "gemv_decode"))),
-                   key=lambda k: kernels[k]["us"])
+    # the dominant kernel of the step (for a fused forward or the FP6 x FP4
+    # path, the stage kernels it replaces are not in the step)
+    replaced = ("norm_fwht_quant", "gemv_decode") if fused else ("norm_fwht_quant", "gemm_i8_mfma") if f6f4 else ()
+    dom_name = max((k for k in kernels if k not in replaced), key=lambda k: kernels[k]["us"])
     dom = kernels[dom_name]
 
     # HBM bytes per launch from committed counter passes, only while the
