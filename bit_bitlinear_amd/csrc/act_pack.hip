@@ -19,6 +19,7 @@
 // Follows the "新智元: 微软 BitNet v2" repost, section "H-BitLinear模块".
 #include "act_row.h"
 #include "weight_pack.h"
+#include "lds_attr.h"
 
 namespace hbl {
 namespace {
@@ -63,12 +64,8 @@ hipError_t launch_ap(const Tin* X, int64_t M, const float* gain, const hbl_confi
     const size_t row_bytes = HAD ? (size_t)ActShape<LK, NT, Tin>::lds_floats * sizeof(float) : 0;
     const size_t lds_bytes = LAYOUT == kCodesFp6 && row_bytes < (size_t)(3 << LK) / 4 ? (size_t)(3 << LK) / 4 : row_bytes;
     auto kern = act_pack_kernel<LK, NT, Tin, BITS, HAD, TW, LAYOUT>;
-    static bool attr_set = false;  // one attribute call per instantiation
-    if (!attr_set && lds_bytes > 0) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint32_t> lds_set{0};  // devices with the LDS limit raised for this kernel
+    if (hipError_t e = set_dynamic_lds(kern, lds_bytes, lds_set); e != hipSuccess) return e;
     const int64_t n_groups = NK / 16;
     const int64_t pack_blocks = (n_groups + 2 * NT - 1) / (2 * NT);
     const int64_t grid = M + pack_blocks;

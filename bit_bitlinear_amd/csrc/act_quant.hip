@@ -5,6 +5,7 @@
 // one of the layouts of hbl_device.h: the ABI's row-major one, the decode
 // tile layout (for the decode GEMM) or FP6 (for the FP6 x FP4 GEMM).
 #include "act_row.h"
+#include "lds_attr.h"
 
 namespace hbl {
 namespace {
@@ -35,12 +36,8 @@ hipError_t launch_one(const Tin* X, int64_t M, const float* gain, const hbl_conf
     const size_t row_bytes = HAD ? (size_t)ActShape<LK, NT, Tin>::lds_floats * sizeof(float) : 0;
     const size_t lds_bytes = LAYOUT == kCodesFp6 && row_bytes < (size_t)(3 << LK) / 4 ? (size_t)(3 << LK) / 4 : row_bytes;
     auto kern = act_quant_kernel<LK, NT, Tin, BITS, HAD, LAYOUT>;
-    static bool attr_set = false;  // one attribute call per instantiation
-    if (!attr_set && lds_bytes > 0) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint32_t> lds_set{0};  // devices with the LDS limit raised for this kernel
+    if (hipError_t e = set_dynamic_lds(kern, lds_bytes, lds_set); e != hipSuccess) return e;
     // one workgroup per row; gridDim.x is limited to 2^31-1
     hipLaunchKernelGGL(kern, dim3((unsigned)M), dim3(NT), lds_bytes, s, X, gain, cfg.norm, cfg.norm_eps,
                        cfg.quant_eps, cfg.a4_mode, (uint8_t*)codes, xscale, z_debug, s_debug);

@@ -20,6 +20,7 @@
 // by converting transposes that widen to bf16 and transpose in one pass.
 #include "act_row.h"
 #include "lds_dma.h"
+#include "lds_attr.h"
 
 namespace hbl {
 namespace {
@@ -429,12 +430,8 @@ hipError_t launch_rows(float* dzx, int64_t M, const Tx* X, const float* gain, co
     static_assert(ActShape<LK, NT, float>::VW == 4, "four values per vector");
     const size_t lds_bytes = HAD ? (size_t)ActShape<LK, NT, float>::lds_floats * sizeof(float) : 0;
     auto kern = bwd_rows_kernel<LK, NT, Tx, HAD>;
-    static bool attr_set = false;
-    if (!attr_set && lds_bytes > 0) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint32_t> lds_set{0};  // devices with the LDS limit raised for this kernel
+    if (hipError_t e = set_dynamic_lds(kern, lds_bytes, lds_set); e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)M), dim3(NT), lds_bytes, s, dzx, X, gain, cfg.norm, cfg.norm_eps);
     return hipGetLastError();
 }

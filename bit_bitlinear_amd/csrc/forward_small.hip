@@ -20,6 +20,7 @@
 // ternary weights, rescale).
 #include "act_row.h"
 #include "int_dot.h"
+#include "lds_attr.h"
 
 namespace hbl {
 namespace {
@@ -65,12 +66,8 @@ hipError_t launch_fs(const Tin* X, const float* gain, const hbl_config& cfg, con
     constexpr int NT = threads_for(LK);
     const size_t lds_bytes = HAD ? (size_t)ActShape<LK, NT, Tin>::lds_floats * sizeof(float) : 0;
     auto kern = forward_small_kernel<LK, Tin, BITS, HAD, YT>;
-    static bool attr_set = false;  // one attribute call per instantiation
-    if (!attr_set && lds_bytes > 0) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint32_t> lds_set{0};  // devices with the LDS limit raised for this kernel
+    if (hipError_t e = set_dynamic_lds(kern, lds_bytes, lds_set); e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)(N / kGvRows)), dim3(NT), lds_bytes, s, X, gain, cfg.norm, cfg.norm_eps,
                        cfg.quant_eps, cfg.a4_mode, Wp, alpha, N, Y);
     return hipGetLastError();
