@@ -178,6 +178,17 @@ def _dev(t, name):
         raise ValueError("%s must be contiguous" % name)
 
 
+def _fits(t, nbytes, name):
+    """The C ABI takes bare pointers, so every buffer's size is checked here:
+    a buffer smaller than its shape needs would be written out of bounds."""
+    if t is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError("%s holds %d bytes, the call needs %d" % (name, t.numel() * t.element_size(), nbytes))
+
+
+def _esize(t):
+    return 2 if t.dtype == _torch().bfloat16 else 4
+
+
 def _stream(stream):
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -224,6 +235,7 @@ def hbl_quantize_weights(W, eps: float = 1e-5, W_packed=None, alpha=None, ws=Non
     if ws is None:
         ws = torch.empty(hbl_weight_workspace_bytes(N, K), dtype=torch.uint8, device=W.device)
     _dev(W_packed, "W_packed"); _dev(alpha, "alpha"); _dev(ws, "ws")
+    _fits(W_packed, N * K // 4, "W_packed"); _fits(alpha, 4, "alpha")
     _check("hbl_quantize_weights", lib.hbl_quantize_weights(_ptr(W), _dtype_code(W), N, K, float(eps), _ptr(W_packed),
                                                             _ptr(alpha), _ptr(ws), ws.numel() * ws.element_size(),
                                                             _stream(stream)))
@@ -246,6 +258,7 @@ def hbl_quantize_activations(X, cfg: Config, gain=None, codes=None, xscale=None,
     z = torch.empty((M, K), dtype=torch.float32, device=X.device) if z_debug else None
     s = torch.empty(M, dtype=torch.float32, device=X.device) if s_debug else None
     _dev(codes, "codes"); _dev(xscale, "xscale")
+    _fits(codes, M * K * cfg.act_bits // 8, "codes"); _fits(xscale, 4 * M, "xscale"); _fits(gain, 4 * K, "gain")
     c = cfg.c()
     _check("hbl_quantize_activations",
            lib.hbl_quantize_activations(_ptr(X), _dtype_code(X), M, K, _ptr(gain), ctypes.byref(c), _ptr(codes),
@@ -264,6 +277,8 @@ def hbl_gemm(codes, xscale, act_bits: int, K: int, W_packed, alpha, N: int, y_dt
     if Y is None:
         Y = torch.empty((M, N), dtype=y_dtype or torch.float32, device=codes.device)
     _dev(Y, "Y")
+    _fits(codes, M * K * int(act_bits) // 8, "codes"); _fits(xscale, 4 * M, "xscale")
+    _fits(W_packed, N * K // 4, "W_packed"); _fits(alpha, 4, "alpha"); _fits(Y, M * N * _esize(Y), "Y")
     _check("hbl_gemm", lib.hbl_gemm(_ptr(codes), _ptr(xscale), int(act_bits), M, K, _ptr(W_packed), _ptr(alpha), N,
                                     _ptr(Y), _dtype_code(Y), _stream(stream)))
     return Y
@@ -280,6 +295,8 @@ def hbl_forward(X, W_packed, alpha, N: int, cfg: Config, y_dtype=None, gain=None
     if ws is None:
         ws = torch.empty(max(1, hbl_forward_workspace_bytes(M, K, N, cfg)), dtype=torch.uint8, device=X.device)
     _dev(Y, "Y"); _dev(ws, "ws")
+    _fits(W_packed, N * K // 4, "W_packed"); _fits(alpha, 4, "alpha"); _fits(gain, 4 * K, "gain")
+    _fits(Y, M * N * _esize(Y), "Y")
     c = cfg.c()
     _check("hbl_forward", lib.hbl_forward(_ptr(X), _dtype_code(X), M, K, _ptr(gain), _ptr(W_packed), _ptr(alpha), N,
                                           ctypes.byref(c), _ptr(Y), _dtype_code(Y), _ptr(ws),
@@ -311,6 +328,8 @@ def hbl_forward_latent(X, W, cfg: Config, eps: float = 1e-5, y_dtype=None, gain=
         wws = torch.empty(hbl_weight_workspace_bytes(N, K), dtype=torch.uint8, device=W.device)
     for t, n in ((W_packed, "W_packed"), (alpha, "alpha"), (Y, "Y"), (ws, "ws"), (wws, "wws")):
         _dev(t, n)
+    _fits(W_packed, N * K // 4, "W_packed"); _fits(alpha, 4, "alpha"); _fits(gain, 4 * K, "gain")
+    _fits(Y, M * N * _esize(Y), "Y")
     c = cfg.c()
     _check("hbl_forward_latent", lib.hbl_forward_latent(
         _ptr(X), _dtype_code(X), M, K, _ptr(gain), _ptr(W), _dtype_code(W), N, float(eps), ctypes.byref(c),
@@ -333,6 +352,9 @@ def hbl_quantize_heads(X, H: int, bits: int, eps: float = 1e-5, codes=None, scal
     if scales is None:
         scales = torch.empty((M, H), dtype=torch.float32, device=X.device)
     _dev(codes, "codes"); _dev(scales, "scales")
+    if X.numel() != M * H * D:
+        raise ValueError("X holds %d values, not %d tokens x %d heads x %d" % (X.numel(), M, H, D))
+    _fits(codes, M * H * D * int(bits) // 8, "codes"); _fits(scales, 4 * M * H, "scales")
     _check("hbl_quantize_heads", lib.hbl_quantize_heads(_ptr(X), _dtype_code(X), M, H, D, int(bits), float(eps),
                                                         _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
@@ -363,6 +385,14 @@ def hbl_backward(dY, X, W_packed, alpha, cfg: Config, gain=None, want_dW: bool =
     if ws is None:
         ws = torch.empty(max(1, hbl_backward_workspace_bytes(M, K, N, cfg, want_dW)), dtype=torch.uint8,
                          device=X.device)
+    for t, n in ((dX, "dX"), (dW, "dW"), (ws, "ws")):
+        _dev(t, n)
+        if n != "ws" and t is not None and t.dtype != torch.float32:
+            raise TypeError("%s must be float32" % n)
+    if dY.shape[0] != M:
+        raise ValueError("dY has %d rows, X has %d" % (dY.shape[0], M))
+    _fits(W_packed, N * K // 4, "W_packed"); _fits(alpha, 4, "alpha"); _fits(gain, 4 * K, "gain")
+    _fits(dX, 4 * M * K, "dX"); _fits(dW, 4 * N * K, "dW")
     c = cfg.c()
     _check("hbl_backward", lib.hbl_backward(_ptr(dY), _dtype_code(dY), _ptr(X), _dtype_code(X), M, K, _ptr(gain),
                                             _ptr(W_packed), _ptr(alpha), N, ctypes.byref(c), _ptr(dX), _ptr(dW),
@@ -383,6 +413,7 @@ def hbl_pack_base3(W_packed, K: int, W3=None, stream=None):
     if W3 is None:
         W3 = torch.empty((N, hbl_base3_weight_bytes(1, K)), dtype=torch.uint8, device=W_packed.device)
     _dev(W3, "W3")
+    _fits(W_packed, N * K // 4, "W_packed"); _fits(W3, hbl_base3_weight_bytes(max(N, 1), K) if N else 0, "W3")
     _check("hbl_pack_base3", lib.hbl_pack_base3(_ptr(W_packed), N, K, _ptr(W3), _stream(stream)))
     return W3
 
@@ -397,6 +428,8 @@ def hbl_gemm_base3(codes, xscale, act_bits: int, K: int, W3, alpha, N: int, y_dt
     if Y is None:
         Y = torch.empty((M, N), dtype=y_dtype or torch.float32, device=codes.device)
     _dev(Y, "Y")
+    _fits(codes, M * K * int(act_bits) // 8, "codes"); _fits(xscale, 4 * M, "xscale")
+    _fits(W3, N * hbl_base3_weight_bytes(1, K), "W3"); _fits(alpha, 4, "alpha"); _fits(Y, M * N * _esize(Y), "Y")
     _check("hbl_gemm_base3", lib.hbl_gemm_base3(_ptr(codes), _ptr(xscale), int(act_bits), M, K, _ptr(W3),
                                                 _ptr(alpha), N, _ptr(Y), _dtype_code(Y), _stream(stream)))
     return Y
@@ -413,6 +446,8 @@ def hbl_forward_base3(X, W3, alpha, N: int, cfg: Config, y_dtype=None, gain=None
     if ws is None:
         ws = torch.empty(max(1, hbl_workspace_bytes(M, K, cfg)), dtype=torch.uint8, device=X.device)
     _dev(Y, "Y"); _dev(ws, "ws")
+    _fits(W3, N * hbl_base3_weight_bytes(1, K), "W3"); _fits(alpha, 4, "alpha"); _fits(gain, 4 * K, "gain")
+    _fits(Y, M * N * _esize(Y), "Y")
     c = cfg.c()
     _check("hbl_forward_base3", lib.hbl_forward_base3(_ptr(X), _dtype_code(X), M, K, _ptr(gain), _ptr(W3),
                                                       _ptr(alpha), N, ctypes.byref(c), _ptr(Y), _dtype_code(Y),

@@ -217,3 +217,15 @@ def test_base3_gemm_and_forward_validation(lib):
     assert fwd(wsb=need - 1) == 7 and fwd(M=5) == 2 and fwd(K=32768) == 2 and fwd(K=8000) == 3
     assert fwd(X=None) == 1 and fwd(W=None) == 1 and fwd(c=None) == 1
     assert fwd(M=0, X=None, W=None) == 0
+
+
+def test_binding_checks_buffer_sizes():
+    """The binding checks every caller-provided buffer against the size its
+    shape needs (the C ABI cannot: it takes bare pointers)."""
+    import torch
+    hbl._fits(torch.empty(16, dtype=torch.uint8), 16, "x")
+    hbl._fits(None, 1 << 40, "x")
+    with pytest.raises(ValueError):
+        hbl._fits(torch.empty(15, dtype=torch.uint8), 16, "x")
+    with pytest.raises(ValueError):
+        hbl._fits(torch.empty(3, dtype=torch.float32), 16, "x")

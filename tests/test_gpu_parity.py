@@ -672,3 +672,26 @@ def test_backward_dx_only_and_empty():
     _sync()
     assert dW is None and np.array_equal(to_host(dX), to_host(dX2))
     assert e[0].shape == (0, K)
+
+
+def test_binding_rejects_small_buffers():
+    """Outputs and workspaces smaller than the call needs are refused before
+    anything is queued."""
+    import torch
+    rng = np.random.default_rng(2)
+    M, K, N = 8, 1024, 64
+    X = to_dev(rng.standard_normal((M, K)).astype(np.float32))
+    Wp, alpha = hbl.hbl_quantize_weights(to_dev(workloads.w_latent(rng, N, K)))
+    cfg = hbl.Config(act_bits=8)
+    small_y = torch.empty((M, N - 1), dtype=torch.float32, device="cuda:0")
+    with pytest.raises(ValueError):
+        hbl.hbl_forward(X, Wp, alpha, N, cfg, Y=small_y)
+    codes, xs, _, _ = hbl.hbl_quantize_activations(X, cfg)
+    with pytest.raises(ValueError):
+        hbl.hbl_gemm(codes, xs, 8, K, Wp[: N // 2], alpha, N)
+    with pytest.raises(ValueError):
+        hbl.hbl_backward(to_dev(rng.standard_normal((M, N)).astype(np.float32)), X, Wp, alpha, cfg,
+                         dX=torch.empty((M, K - 1), dtype=torch.float32, device="cuda:0"))
+    with pytest.raises(hbl.HblError):      # the workspace size is the C ABI's own check
+        hbl.hbl_forward(X, Wp, alpha, N, cfg, ws=torch.empty(16, dtype=torch.uint8, device="cuda:0"))
+    _sync()
