@@ -1,0 +1,82 @@
+"""Seeded random forward configurations through the C ABI, against the
+oracle: token counts from 1 to a few thousand (every dispatch path: the
+one-token fused kernel, the small-M GEMV, the decode tiles, 64-row and full
+GEMM tiles), every row length, INT4/INT8, with and without the Hadamard,
+each norm, gain or none, both input and output dtypes.  Up to 16 rows per
+case are checked against the oracle (the dense Hadamard costs K^2 per row)."""
+import numpy as np
+import pytest
+
+import bit_bitlinear_amd as hbl
+import oracle
+import workloads
+from parity import (check_codes_end_to_end, check_codes_given_inputs, check_y, check_z, to_dev, to_host,
+                    unpack_codes, y_to_f32)
+
+pytestmark = pytest.mark.gpu
+
+
+def _configs(n=24, seed=20261203):
+    rng = np.random.default_rng(seed)
+    Ms = [1, 2, 3, 4, 5, 9, 16, 17, 40, 63, 64, 65, 100, 129, 257, 700, 1500, 3000]
+    Ks = [256, 512, 1024, 2048, 4096, 8192, 16384]
+    out = []
+    for i in range(n):
+        K = int(rng.choice(Ks, p=[0.16, 0.16, 0.18, 0.18, 0.14, 0.1, 0.08]))
+        M = int(rng.choice(Ms))
+        if K == 16384:
+            M = min(M, 700)
+        N = int(rng.integers(1, 97)) * 16
+        out.append(dict(M=M, K=K, N=N, bits=int(rng.choice([4, 8])), had=bool(rng.random() < 0.7),
+                        norm=int(rng.choice([hbl.HBL_NORM_RMS, hbl.HBL_NORM_LN, hbl.HBL_NORM_NONE])),
+                        gain=bool(rng.random() < 0.5), xdt=str(rng.choice(["f32", "bf16"])),
+                        ydt=str(rng.choice(["f32", "bf16"])), big_ws=bool(rng.random() < 0.5), seed=i))
+    return out
+
+
+CONFIGS = _configs()
+
+
+@pytest.mark.parametrize("c", CONFIGS, ids=lambda c: "M%d-K%d-N%d-a%d-h%d-n%d-g%d-%s-%s" % (
+    c["M"], c["K"], c["N"], c["bits"], c["had"], c["norm"], c["gain"], c["xdt"], c["ydt"]))
+def test_forward_random_config(c):
+    import torch
+    M, K, N, bits, had, norm = c["M"], c["K"], c["N"], c["bits"], c["had"], c["norm"]
+    print("[case] random forward %s" % sorted(c.items()), flush=True)
+    rng = np.random.default_rng(1000 + c["seed"])
+    X, _ = workloads.x_outlier_gaussian(rng, M, K, 4, 30.0)
+    if norm == hbl.HBL_NORM_LN:
+        X = (X + np.float32(1.5)).astype(np.float32)
+    Xh = workloads.f32_to_bf16_bits(X) if c["xdt"] == "bf16" else X
+    W = workloads.w_latent(rng, N, K)
+    gain = (rng.standard_normal(K).astype(np.float32) * 0.5 + 1.0) if c["gain"] else None
+    cfg = hbl.Config(act_bits=bits, hadamard=had, norm=norm)
+    ydt = torch.float32 if c["ydt"] == "f32" else torch.bfloat16
+    Xd = to_dev(Xh)
+    gd = None if gain is None else to_dev(gain)
+    Wp, alpha = hbl.hbl_quantize_weights(to_dev(W))
+    ws_bytes = hbl.hbl_forward_workspace_bytes(M, K, N, cfg) if c["big_ws"] else hbl.hbl_workspace_bytes(M, K, cfg)
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device="cuda:0")
+    Y = hbl.hbl_forward(Xd, Wp, alpha, N, cfg, y_dtype=ydt, gain=gd, ws=ws)
+    codes, xs, z, s = hbl.hbl_quantize_activations(Xd, cfg, gain=gd, z_debug=True, s_debug=True)
+    torch.cuda.synchronize()
+    rows = workloads.sample_rows(M, 16)
+    a_gpu = to_host(alpha)[0]
+    assert abs(float(a_gpu) - float(oracle.weight_alpha(W))) <= 1e-6 * float(oracle.weight_alpha(W))
+    Wq = oracle.ternarize(W, a_gpu, 1e-5)
+    assert np.array_equal(to_host(Wp), oracle.pack_ternary(Wq))
+    q_gpu = unpack_codes(to_host(codes)[rows], K, bits)
+    z_gpu, s_gpu, d_gpu = to_host(z)[rows], to_host(s)[rows], to_host(xs)[rows]
+    ref = oracle.quantize_activations(Xh[rows], bits=bits, hadamard=had, gain=gain, norm=norm)
+    check_z(z_gpu, ref["z"], "z")
+    check_codes_given_inputs(z_gpu, s_gpu, d_gpu, q_gpu, bits, 0, 1e-5, "codes")
+    check_codes_end_to_end(q_gpu, ref["z"], ref["s"], ref["q"], "end-to-end codes")
+    # the forward's output is the oracle's product and rescale of the GPU's codes, bit for bit
+    y_exact = oracle.rescale(oracle.int_gemm(q_gpu, Wq), d_gpu, a_gpu)
+    got = to_host(Y)[rows]
+    assert np.array_equal(got, y_exact if c["ydt"] == "f32" else oracle.f32_to_bf16(y_exact))
+    # and, end to end, the oracle's own pipeline (boundary flips use the GPU's code)
+    flipped = np.any(q_gpu != ref["q"], axis=1)
+    q_cmp = np.where(flipped[:, None], q_gpu, ref["q"])
+    check_y(y_to_f32(got), oracle.rescale(oracle.int_gemm(q_cmp, Wq), ref["d"], a_gpu), "y",
+            bf16_out=c["ydt"] == "bf16")
