@@ -80,3 +80,57 @@ def test_forward_random_config(c):
     q_cmp = np.where(flipped[:, None], q_gpu, ref["q"])
     check_y(y_to_f32(got), oracle.rescale(oracle.int_gemm(q_cmp, Wq), ref["d"], a_gpu), "y",
             bf16_out=c["ydt"] == "bf16")
+
+
+def _bwd_configs(n=8, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        K = int(rng.choice([512, 1024, 2048, 4096, 8192]))
+        out.append(dict(M=int(rng.choice([1, 7, 64, 65, 300, 1100])), K=K, N=int(rng.integers(1, 65)) * 16,
+                        bits=int(rng.choice([4, 8])), had=bool(rng.random() < 0.7),
+                        norm=int(rng.choice([hbl.HBL_NORM_RMS, hbl.HBL_NORM_LN, hbl.HBL_NORM_NONE])),
+                        gain=bool(rng.random() < 0.5), dydt=str(rng.choice(["f32", "bf16"])),
+                        xdt=str(rng.choice(["f32", "bf16"])), seed=i))
+    return out
+
+
+@pytest.mark.parametrize("c", _bwd_configs(), ids=lambda c: "M%d-K%d-N%d-a%d-h%d-n%d-g%d-%s-%s" % (
+    c["M"], c["K"], c["N"], c["bits"], c["had"], c["norm"], c["gain"], c["dydt"], c["xdt"]))
+def test_backward_random_config(c):
+    """dX on up to 16 sampled rows and dW on 24 sampled columns against the
+    oracle (rowwise 2e-5 of the row's largest value)."""
+    import torch
+    M, K, N, bits, had, norm = c["M"], c["K"], c["N"], c["bits"], c["had"], c["norm"]
+    print("[case] random backward %s" % sorted(c.items()), flush=True)
+    rng = np.random.default_rng(5000 + c["seed"])
+    X, _ = workloads.x_outlier_gaussian(rng, M, K, 4, 30.0)
+    if norm == hbl.HBL_NORM_LN:
+        X = (X + np.float32(1.5)).astype(np.float32)
+    Xh = workloads.f32_to_bf16_bits(X) if c["xdt"] == "bf16" else X
+    dY = rng.standard_normal((M, N)).astype(np.float32)
+    dYh = workloads.f32_to_bf16_bits(dY) if c["dydt"] == "bf16" else dY
+    gain = (rng.standard_normal(K).astype(np.float32) * 0.5 + 1.0) if c["gain"] else None
+    cfg = hbl.Config(act_bits=bits, hadamard=had, norm=norm)
+    gd = None if gain is None else to_dev(gain)
+    Wp, alpha = hbl.hbl_quantize_weights(to_dev(workloads.w_latent(rng, N, K)))
+    dX, dW = hbl.hbl_backward(to_dev(dYh), to_dev(Xh), Wp, alpha, cfg, gain=gd)
+    codes, _, _, _ = hbl.hbl_quantize_activations(to_dev(Xh), cfg, gain=gd)
+    torch.cuda.synchronize()
+    a = to_host(alpha)[0]
+    Wq = oracle.unpack_ternary(to_host(Wp), K)
+    rows = workloads.sample_rows(M, 16)
+    dX_ref, _ = oracle.backward(dYh[rows], Xh[rows], Wq, a, bits=bits, hadamard=had, gain=gain, norm=norm,
+                                want_dW=False)
+    got = to_host(dX)[rows].astype(np.float64)
+    scale = np.maximum(np.max(np.abs(dX_ref), axis=1, keepdims=True), 1e-30)
+    assert np.all(np.abs(got - dX_ref) <= 2e-5 * scale)
+    cols = np.unique(np.concatenate([[0, K - 1], rng.choice(K, 22, replace=False)]))
+    ref = oracle.quantize_activations(Xh, bits=bits, hadamard=had, gain=gain, norm=norm)
+    q_gpu = unpack_codes(to_host(codes), K, bits)
+    check_codes_end_to_end(q_gpu, ref["z"], ref["s"], ref["q"], "backward codes")
+    q = np.where(q_gpu != ref["q"], q_gpu, ref["q"])
+    dW_ref = oracle.weight_grad(dYh, np.ascontiguousarray(q[:, cols]), ref["d"])
+    gotw = to_host(dW)[:, cols].astype(np.float64)
+    scale = np.maximum(np.max(np.abs(dW_ref), axis=1, keepdims=True), 1e-30)
+    assert np.all(np.abs(gotw - dW_ref) <= 2e-5 * scale)
