@@ -153,6 +153,7 @@ def main():
             hbl.hbl_quantize_weights(s0["W"], 1e-5, W_packed=s0["Wp"], alpha=s0["alpha"], ws=s0["wws"])
             hbl.hbl_quantize_activations(s0["X"], cfg, codes=s0["codes"], xscale=s0["xs"])
             hbl.hbl_gemm(s0["codes"], s0["xs"], bits, K, s0["Wp"], s0["alpha"], N, Y=s0["Y"])
+            hbl.hbl_forward(s0["X"], s0["Wp"], s0["alpha"], N, cfg, Y=s0["Y"], ws=s0["ws"])
         torch.cuda.synchronize()
         print("counter run done: %s" % layer.desc)
         return
