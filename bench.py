@@ -79,8 +79,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only (the H-BitLinear forward is measured on one "
-              "MI355X's share); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU only (each workload is one MI355X's share of a layer); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -101,7 +101,7 @@ const char* hbl_status_string(hbl_status s) {
         case HBL_ERR_DTYPE: return "unknown dtype";
         case HBL_ERR_BITS: return "unsupported act_bits, a4_mode, norm or hadamard flag";
         case HBL_ERR_WORKSPACE: return "workspace too small";
-        case HBL_ERR_UNSUPPORTED: return "request not supported by this build";
+        case HBL_ERR_UNSUPPORTED: return "request not supported by this library";
         case HBL_ERR_HIP: return "HIP error (see hbl_last_hip_error)";
     }
     return "unknown status";

@@ -51,7 +51,7 @@ typedef enum {
     HBL_ERR_DTYPE = 5,       /* unknown hbl_dtype */
     HBL_ERR_BITS = 6,        /* act_bits not 4 or 8, or unknown a4_mode / norm */
     HBL_ERR_WORKSPACE = 7,   /* workspace smaller than the *_workspace_bytes query */
-    HBL_ERR_UNSUPPORTED = 8, /* valid request this build does not implement */
+    HBL_ERR_UNSUPPORTED = 8, /* valid request this library does not implement */
     HBL_ERR_HIP = 9          /* a HIP call failed; see hbl_last_hip_error() */
 } hbl_status;
 
@@ -75,7 +75,7 @@ typedef struct {
     float quant_eps;   /* added to the per-token statistic in the quantiser divisor */
 } hbl_config;
 
-/* Limits of this build. */
+/* Limits of this library. */
 #define HBL_MAX_K 32768
 #define HBL_MIN_K 256
 
