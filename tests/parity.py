@@ -104,3 +104,19 @@ def check_y(y_gpu, y_ref, what="", bf16_out=False):
 
 def y_to_f32(y: np.ndarray) -> np.ndarray:
     return oracle.bf16_to_f32(y) if y.dtype == np.uint16 else y
+
+
+def check_dw(got, dY, q, d, dW_ref, what=""):
+    """Weight-gradient tolerance derived from the arithmetic: P = fp32(dY * d)
+    enters the products as a bf16 high part plus a bf16 remainder (unit
+    roundoff 2^-8 each, so P is carried to 2^-16 of itself) and the sums run
+    in fp32, so each element may differ from the exact sum by at most
+    2^-16 * sum_m |P_m q_mk| plus the fp32 accumulation error; the test
+    allows 2^-15 of that absolute sum.  (A bound relative to the row's largest
+    value is wrong when a few tokens' terms cancel.)"""
+    P = np.abs(oracle.as_f32(dY).astype(np.float64) * np.asarray(d, np.float64)[:, None])
+    absum = P.T @ np.abs(np.asarray(q, np.float64))
+    err = np.abs(np.asarray(got, np.float64) - dW_ref)
+    bad = err > 2.0 ** -15 * absum + 1e-30
+    assert not np.any(bad), "%s: %d elements beyond 2^-15 of sum|P q|, worst ratio %.3g" % (
+        what, int(bad.sum()), float(np.max(err / np.maximum(absum, 1e-30))))

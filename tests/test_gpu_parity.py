@@ -11,7 +11,7 @@ import pytest
 import bit_bitlinear_amd as hbl
 import oracle
 import workloads
-from parity import (check_codes_end_to_end, check_codes_given_inputs, check_y, check_z, to_dev, to_host,
+from parity import (check_codes_end_to_end, check_codes_given_inputs, check_dw, check_y, check_z, to_dev, to_host,
                     unpack_codes, y_to_f32)
 
 pytestmark = pytest.mark.gpu
@@ -616,7 +616,7 @@ def test_backward_parity(M, K, N, bits, had, norm, use_gain, dydt, xdt):
     assert _rowwise_close(to_host(dX).astype(np.float64), dX_ref, 2e-5)
     q, d = _backward_codes(Xh, to_host(codes), K, bits, had, gain, norm)
     dW_ref = oracle.weight_grad(dYh, q, d)
-    assert _rowwise_close(to_host(dW).astype(np.float64), dW_ref, 2e-5)
+    check_dw(to_host(dW), dYh, q, d, dW_ref, "dW")
 
 
 def _backward_codes(Xh, codes_gpu, K, bits, had, gain, norm):
@@ -652,8 +652,9 @@ def test_backward_large_sampled(M, K, N, bits):
     dX_ref, _ = oracle.backward(dY[rows], X[rows], Wq, a, bits=bits, want_dW=False)
     assert _rowwise_close(to_host(dX)[rows].astype(np.float64), dX_ref, 2e-5)
     q, d = _backward_codes(X, to_host(codes), K, bits, True, None, hbl.HBL_NORM_RMS)
-    dW_ref = oracle.weight_grad(dY, np.ascontiguousarray(q[:, cols]), d)
-    assert _rowwise_close(to_host(dW)[:, cols].astype(np.float64), dW_ref, 2e-5)
+    qc = np.ascontiguousarray(q[:, cols])
+    dW_ref = oracle.weight_grad(dY, qc, d)
+    check_dw(to_host(dW)[:, cols], dY, qc, d, dW_ref, "dW")
 
 
 def test_backward_dx_only_and_empty():
