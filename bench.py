@@ -15,8 +15,10 @@ sets (> 512 MiB) that the 256 MB last-level cache cannot hold them.
 
 Prints one JSON line.  Besides the throughput it reports, for the kernel that
 takes the most time per step, the algorithmic work per launch divided by its
-average launch time (HIP events on the launch stream) against the MI355X peak,
-and the CPU oracle timed on a bounded row sample on the host cores.
+average launch time (HIP events on the launch stream) against the MI355X
+peak and against the ceiling measured in the same process by the probe
+kernels of libhbl_peaks.so (an HBM copy and dense matrix-core loops), and the
+CPU oracle timed on a bounded row sample on the host cores.
 """
 from __future__ import annotations
 
@@ -35,6 +37,82 @@ PEAK_I8_TOPS = 5000.0          # MI355X dense INT8 MFMA, TOP/s
 PEAK_F6F4_TOPS = 10100.0       # MI355X dense FP6 / FP4 MFMA, TFLOP/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 ROTATE_BYTES = 576 << 20       # > 2 x 256 MB last-level cache
+
+_PEAKS = None
+
+
+def measured_peaks():
+    """Ceilings measured on this GPU by the probe kernels of libhbl_peaks.so
+    (built beside libhbl.so): a 512 MiB streaming copy (read + write bytes)
+    and loops of dense i8, FP6 x FP4 and bf16 matrix-core instructions on
+    register operands; each the best of 3 timed rounds after a warm-up, with
+    HIP events on the stream the probes run on.  Computed once per process."""
+    global _PEAKS
+    if _PEAKS is not None:
+        return _PEAKS
+    import ctypes
+
+    import torch
+    from bit_bitlinear_amd import build as hbl_build
+
+    if not os.path.exists(hbl_build.PEAKS_LIB):
+        raise RuntimeError("%s not found; build it with __graft_entry__.build()" % hbl_build.PEAKS_LIB)
+    lib = ctypes.CDLL(hbl_build.PEAKS_LIB)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.hbl_peak_copy.argtypes = [P, P, I64, P]
+    lib.hbl_peak_mfma.argtypes = [I32, P, I64, I32, I32, P]
+    lib.hbl_peak_mfma_ops.argtypes = [I32, I32, I32]
+    lib.hbl_peak_mfma_ops.restype = I64
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def best_us(launch, reps=5):
+        launch()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                launch()
+            e1.record(stream)
+            e1.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            best = us if best is None else min(best, us)
+        return best
+
+    nbytes = 512 << 20
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+
+    def copy():
+        if lib.hbl_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes, sp) != 0:
+            raise RuntimeError("hbl_peak_copy failed")
+
+    out = {"hbm_copy_GBps": round(2 * nbytes / (best_us(copy) * 1e-6) / 1e9, 1)}
+    del src, dst
+    blocks, iters = 2048, 2000
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    for kind, key in ((0, "mfma_i8_TOPS"), (1, "mfma_f6f4_TFLOPS"), (2, "mfma_bf16_TFLOPS")):
+        def run(kind=kind):
+            if lib.hbl_peak_mfma(kind, ctypes.c_void_p(sink.data_ptr()), sink.numel(), blocks, iters, sp) != 0:
+                raise RuntimeError("hbl_peak_mfma failed")
+        ops = lib.hbl_peak_mfma_ops(kind, blocks, iters)
+        out[key] = round(ops / (best_us(run, reps=2) * 1e-6) / 1e12, 1)
+    torch.cuda.synchronize()
+    out["method"] = ("512 MiB 16-byte streaming copy (2 x bytes); 2048 x 256-thread blocks each issuing 4 "
+                     "independent matrix-core instructions per round on register operands")
+    _PEAKS = out
+    return out
+
+
+def with_measured_peak(roof, key):
+    """Add the measured ceiling for this roofline's bound and the fraction of it."""
+    pk = measured_peaks()
+    roof["peak_measured"] = pk[key]
+    roof["frac_measured"] = round(roof["achieved"] / pk[key], 4)
+    return roof
 
 
 def parse():
@@ -266,6 +344,8 @@ def main():
     roofline = {"kernel": dom_name, "bound": dom["bound"], "achieved": round(dom["achieved"], 2),
                 "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4), "traffic": traffic,
                 "work_per_launch": dom["work"], "work_desc": dom["work_desc"], "us_per_launch": round(dom["us"], 3)}
+    with_measured_peak(roofline, "hbm_copy_GBps" if dom["unit"] == "GB/s" else
+                       "mfma_f6f4_TFLOPS" if dom["peak"] == PEAK_F6F4_TOPS else "mfma_i8_TOPS")
 
     # ----------------------------------------------------------- CPU baseline
     cpu = None
@@ -297,6 +377,7 @@ def main():
         "forward_us": round(t_fwd, 3),
         "forward_only_tokens_per_s": round(M / (t_fwd * 1e-6), 1),
         "roofline": roofline,
+        "box_peaks": measured_peaks(),
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "cpu_baseline": cpu,
@@ -413,12 +494,13 @@ def bench_backward(args):
         "data": "synthetic (the layer's seeded inputs; dY ~ N(0,1) in bf16)",
         "config": {"workload": "backward of %s" % layer.desc, "M": M, "K": K, "N": N,
                    "rotating_sets": R, "timing": "HIP graph replay of captured launches"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "roofline": with_measured_peak({"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "kernel": "gemm_bf16_dma_kernel (dZ, then dW with high part and remainder in one launch)", "us_per_step": round(us, 3),
                      "work_desc": "6 M N K flops of the three bf16 products over the whole step's time (the "
                                   "operand preparation and the row kernel included), a lower bound for the "
-                                  "products alone"},
+                                  "products alone"}, "mfma_bf16_TFLOPS"),
+        "box_peaks": measured_peaks(),
         "cpu_baseline": cpu,
     }))
 
@@ -490,10 +572,12 @@ def bench_heads(args):
         "data": "synthetic (seeded N(0,1) with a log-normal scale per token and head)",
         "config": {"workload": "%s: %d tokens x %d heads x %d, bf16 in, %d-bit codes" % (name, M, H, D, bits),
                    "rotating_sets": R, "timing": "HIP graph replay of captured launches"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "roofline": with_measured_peak({"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                      "kernel": "head_quant_kernel", "us_per_launch": round(us, 3),
                      "work_desc": "read X (bf16) + write codes + write scales, %d bytes per launch" % work},
+            "hbm_copy_GBps"),
+        "box_peaks": measured_peaks(),
         "cpu_baseline": cpu,
     }))
 
@@ -583,10 +667,12 @@ def bench_base3(args):
                    "rotating_sets": R, "timing": "HIP graph replay of captured launches"},
         "forward_us": round(fwd_us, 3), "forward_2bit_us": round(fwd2_us, 3),
         "gemv_us": round(gemv_us, 3), "gemv_2bit_us": round(gemv2_us, 3),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "roofline": with_measured_peak({"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                      "kernel": "gemv_base3_kernel", "us_per_launch": round(gemv_us, 3),
                      "work_desc": "base-3 weights + codes + scales + bf16 Y, %d bytes per launch" % work},
+            "hbm_copy_GBps"),
+        "box_peaks": measured_peaks(),
         "cpu_baseline": cpu,
     }))
     del g1, g2, g3, g4

@@ -10,6 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhbl.so")
+PEAKS_LIB = os.path.join(HERE, "libhbl_peaks.so")  # probe kernels for measured ceilings (benchmark only)
 SOURCES = ["api.hip", "weight_quant.hip", "act_quant.hip", "act_pack.hip", "gemm.hip", "forward_small.hip",
            "head_quant.hip", "backward.hip", "base3.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -35,19 +36,25 @@ def _compile(src: str, build_dir: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    build_dir = os.path.join(ROOT, "_build")
-    os.makedirs(build_dir, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, build_dir), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    build_dir = os.path.join(ROOT, "_build")
+    os.makedirs(build_dir, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        objs = list(ex.map(lambda s: _compile(s, build_dir), SOURCES + ["peaks.hip"]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PEAKS_LIB)
     if verbose:
         print("built", LIB)
+        print("built", PEAKS_LIB)
     return LIB
 
 

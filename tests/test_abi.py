@@ -229,3 +229,40 @@ def test_binding_checks_buffer_sizes():
         hbl._fits(torch.empty(15, dtype=torch.uint8), 16, "x")
     with pytest.raises(ValueError):
         hbl._fits(torch.empty(3, dtype=torch.float32), 16, "x")
+
+
+def _peaks_lib():
+    import ctypes
+    from bit_bitlinear_amd import build as hbl_build
+    lib = ctypes.CDLL(hbl_build.PEAKS_LIB)
+    lib.hbl_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.hbl_peak_mfma.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_void_p]
+    lib.hbl_peak_mfma_ops.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib.hbl_peak_mfma_ops.restype = ctypes.c_int64
+    return lib
+
+
+def test_peaks_library_exports_and_host_checks():
+    """The probe library the benchmark uses for measured ceilings: every
+    symbol include/hbl_peaks.h declares is exported, the op counts are the
+    instructions' dense work, and bad arguments are refused before any launch."""
+    import os
+    lib = _peaks_lib()
+    names = hbl.declared_symbols(os.path.join(os.path.dirname(hbl.HEADER_PATH), "hbl_peaks.h"))
+    assert names == ["hbl_peak_copy", "hbl_peak_mfma", "hbl_peak_mfma_ops"]
+    assert all(hasattr(lib, n) for n in names)
+    # 4 waves x 4 instructions per round: i8 32x32x32, FP6 x FP4 32x32x64, bf16 32x32x16
+    assert lib.hbl_peak_mfma_ops(0, 1, 1) == 16 * 2 * 32 * 32 * 32
+    assert lib.hbl_peak_mfma_ops(1, 3, 5) == 16 * 2 * 32 * 32 * 64 * 15
+    assert lib.hbl_peak_mfma_ops(2, 2048, 2000) == 16 * 2 * 32 * 32 * 16 * 2048 * 2000
+    for bad in ((3, 1, 1), (0, 0, 1), (0, 1, 0), (0, (1 << 20) + 1, 1), (0, 1, (1 << 24) + 1)):
+        assert lib.hbl_peak_mfma_ops(*bad) == -1
+    assert lib.hbl_peak_mfma(3, 16, 256, 1, 1, None) == 1            # unknown kind
+    assert lib.hbl_peak_mfma(0, 16, 255, 1, 1, None) == 1            # out too short
+    assert lib.hbl_peak_mfma(0, None, 256, 1, 1, None) == 1          # no output
+    assert lib.hbl_peak_copy(16, 4096, 17, None) == 1                # not a multiple of 16
+    assert lib.hbl_peak_copy(16, 32, 64, None) == 1                  # overlapping
+    assert lib.hbl_peak_copy(None, 4096, 16, None) == 1              # null
+    assert lib.hbl_peak_copy(24, 4096, 16, None) == 1                # misaligned
+    assert lib.hbl_peak_copy(16, 4096, 0, None) == 0                 # nothing to do
