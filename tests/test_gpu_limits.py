@@ -1,5 +1,6 @@
-"""The largest output width the C ABI admits, N = 2^20 columns, on every GEMM
-path: the one-token GEMV, the decode GEMM, the prefill GEMM (INT8 and INT4,
+"""Size limits of the C ABI.  The largest M the GEMM admits (2^23 rows) and
+an activation quantisation whose input passes 2^31 bytes.  The largest output
+width, N = 2^20 columns, on every GEMM path: the one-token GEMV, the decode GEMM, the prefill GEMM (INT8 and INT4,
 ragged M), the FP6 x FP4 GEMM inside hbl_forward, and base-3 packing and its
 GEMV.  At this width a
 128-row output tile spans 512 MiB (fp32), the edge of the kernels' 32-bit
@@ -97,3 +98,50 @@ def test_base3_max_width(M, K, bits):
     assert np.array_equal(to_host(W3.index_select(0, torch.from_numpy(cols).to(W3.device))), oracle.pack_base3(Wq))
     y_ref = oracle.rescale(oracle.int_gemm(q, Wq), d, alpha[0])
     assert np.array_equal(_sampled(Y, cols), oracle.f32_to_bf16(y_ref))
+
+
+def test_gemm_max_rows():
+    """hbl_gemm at M = 2^23 rows (the largest it admits; 1 GiB of INT8 codes),
+    bit for bit on sampled rows, the first and last 8 included.  The codes are
+    drawn on the GPU by a seeded generator; only the sampled rows come back."""
+    import torch
+    M, K, N = 1 << 23, 128, 16
+    print("[case] gemm M=2^23 K=%d N=%d a8" % (K, N), flush=True)
+    rng = np.random.default_rng(23)
+    gen = torch.Generator(device="cuda:0").manual_seed(23)
+    codes = torch.randint(-128, 128, (M, K), generator=gen, device="cuda:0", dtype=torch.int8)
+    xs = torch.rand(M, generator=gen, device="cuda:0", dtype=torch.float32) * 0.01 + 1e-3
+    Wp = _VALID[rng.integers(0, len(_VALID), size=(N, K // 4), dtype=np.uint8)]
+    alpha = np.array([0.0211], np.float32)
+    Y = hbl.hbl_gemm(codes, xs, 8, K, to_dev(Wp), to_dev(alpha), N, y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(8), M - 8 + np.arange(8), rng.choice(M, 48, replace=False)]))
+    ri = torch.from_numpy(rows).to("cuda:0")
+    q = to_host(codes.index_select(0, ri))
+    d = to_host(xs.index_select(0, ri))
+    y_ref = oracle.rescale(oracle.int_gemm(q, oracle.unpack_ternary(Wp, K)), d, alpha[0])
+    assert np.array_equal(to_host(Y.index_select(0, ri)), oracle.f32_to_bf16(y_ref))
+
+
+def test_quantize_activations_past_2gib():
+    """hbl_quantize_activations over 2^23 + 5 rows of K = 256 fp32 (8 GiB of
+    input, so row offsets pass 2^31 bytes): codes and scales of sampled rows,
+    the first and last 8 included, against the oracle (a code may differ only
+    at a rounding boundary, checked)."""
+    import torch
+    M, K = (1 << 23) + 5, 256
+    print("[case] quantize activations M=2^23+5 K=%d fp32" % K, flush=True)
+    rng = np.random.default_rng(5)
+    gen = torch.Generator(device="cuda:0").manual_seed(5)
+    X = torch.randn((M, K), generator=gen, device="cuda:0", dtype=torch.float32)
+    cfg = hbl.Config(act_bits=8)
+    codes, xs, _, _ = hbl.hbl_quantize_activations(X, cfg)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(8), M - 8 + np.arange(8), rng.choice(M, 48, replace=False)]))
+    ri = torch.from_numpy(rows).to("cuda:0")
+    Xs = to_host(X.index_select(0, ri))
+    ref = oracle.quantize_activations(Xs, bits=8, hadamard=cfg.hadamard)
+    from parity import check_codes_end_to_end
+    check_codes_end_to_end(unpack_codes(to_host(codes.index_select(0, ri)), K, 8), ref["z"], ref["s"], ref["q"],
+                           "codes past 2 GiB")
+    assert np.allclose(to_host(xs.index_select(0, ri)), ref["d"], rtol=1e-5, atol=0)
