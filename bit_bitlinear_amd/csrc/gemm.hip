@@ -441,8 +441,12 @@ hipError_t launch_gemv_small(const uint8_t* A, const float* xscale, int64_t M, i
     return hipGetLastError();
 }
 
-// Ring depth 3 (loads two K steps ahead); 2 and 4 measured within 3% of it.
+// Ring depth: 3 stages (loads two K steps ahead) for the 4-wave blocks, where
+// a fourth 24 KiB stage would leave room for one block per CU instead of two;
+// 4 stages for the 8-wave blocks, which run one block per CU (3-6% faster than
+// 3 stages at 4096 x 2048 x 2048 INT8 and INT4 and at 2048 x 4096 x 4096).
 constexpr int kDmaStages = 3;
+constexpr int kDmaStages8w = 4;
 
 bool gemv_small_shape(int64_t M, int64_t K) {
     return M <= kGvMaxM && K >= 1024 && K <= 16384 && (K & (K - 1)) == 0;
@@ -500,7 +504,7 @@ hipError_t launch_typed(const uint8_t* A, const float* xscale, int64_t M, int64_
         // (measured 3% faster at 4096 x 2048 x 2048)
         const int tiles_n = (int)((N + 255) / 256);
         const int tiles_total = tiles_n * (int)((M + 127) / 128);
-        hipLaunchKernelGGL((gemm_dma_kernel<BITS, YT, 2, 2, kDmaStages, 4>), dim3(tiles_total), dim3(512), 0, s, A,
+        hipLaunchKernelGGL((gemm_dma_kernel<BITS, YT, 2, 2, kDmaStages8w, 4>), dim3(tiles_total), dim3(512), 0, s, A,
                            xscale, M, K, Wp, alpha, N, Y, tiles_n, tiles_total);
     } else if constexpr (BITS == 8) {
         // fewer than 128 tiles of 128 x 256 (a few hundred tokens): 64-row
@@ -508,7 +512,7 @@ hipError_t launch_typed(const uint8_t* A, const float* xscale, int64_t M, int64_
         // many CUs take part (measured 256 x 4096 x 4096: 26.3 -> 18.6 us)
         const int tiles_n = (int)((N + 255) / 256);
         const int tiles_total = tiles_n * (int)((M + 63) / 64);
-        hipLaunchKernelGGL((gemm_dma_kernel<BITS, YT, 1, 2, kDmaStages, 4>), dim3(tiles_total), dim3(512), 0, s, A,
+        hipLaunchKernelGGL((gemm_dma_kernel<BITS, YT, 1, 2, kDmaStages8w, 4>), dim3(tiles_total), dim3(512), 0, s, A,
                            xscale, M, K, Wp, alpha, N, Y, tiles_n, tiles_total);
     } else {
         // the same for INT4 codes (64-byte rows: a 64-row code tile is too
