@@ -324,11 +324,12 @@ hbl_status hbl_forward_latent(const void* X, int32_t x_dtype, int64_t M, int64_t
     const bool tiled = hbl::gemm_uses_decode_kernel(M, K);
     const int layout = f6 ? hbl::kCodesFp6 : tiled ? hbl::kCodesDecTiled : hbl::kCodesRowMajor;
     if (K <= kFuseActPackMaxK) {
-        // short rows: the activation blocks and the packing blocks share one grid
-        e = hbl::launch_weight_partial(W, w_dtype, N * K, (double*)wws, n_partial, s);
+        // short rows: the activation rows share one grid with the partial |W|
+        // sums (neither needs the other), then the packing
+        e = hbl::launch_act_and_pack(X, x_dtype, M, K, gain, *cfg, codes, xscale, W, w_dtype, N * K, w_eps, nullptr,
+                                     (double*)wws, n_partial, W_packed, alpha, s, layout);
         if (e == hipSuccess)
-            e = hbl::launch_act_and_pack(X, x_dtype, M, K, gain, *cfg, codes, xscale, W, w_dtype, N * K, w_eps,
-                                         (const double*)wws, n_partial, W_packed, alpha, s, layout);
+            e = hbl::launch_weight_pack(W, w_dtype, N, K, w_eps, W_packed, alpha, (const double*)wws, n_partial, s);
     } else {
         e = hbl::launch_weight_quant(W, w_dtype, N, K, w_eps, W_packed, alpha, (double*)wws, n_partial, s);
         if (e == hipSuccess)

@@ -168,16 +168,24 @@ namespace hbl {
 hipError_t launch_weight_quant(const void* W, int w_dtype, int64_t N, int64_t K, float eps, uint8_t* W_packed,
                                float* alpha, double* partial, int n_partial, hipStream_t s);
 int weight_partial_count(int64_t count);
+// elements per partial-sum block (a multiple of 4096)
+int64_t weight_partial_slice(int64_t count);
+// the second of the two weight launches alone: alpha from the partial sums, then the 2-bit words
+hipError_t launch_weight_pack(const void* W, int w_dtype, int64_t N, int64_t K, float eps, uint8_t* W_packed,
+                              float* alpha, const double* partial, int n_partial, hipStream_t s);
 // the first of the two weight launches alone: partial |W| sums into `partial`
 hipError_t launch_weight_partial(const void* W, int w_dtype, int64_t count, double* partial, int n_partial,
                                  hipStream_t s);
 
-// Activation quantisation of M rows and the weight packing (after
-// launch_weight_partial) in one launch: blocks [0, M) quantise rows, the
-// rest pack weight groups.
+// Activation quantisation of M rows and one half of the weight
+// ternarisation in one launch: blocks [0, M) quantise rows, the rest either
+// write the n_partial partial |W| sums into partial_out (partial_out not
+// null; the packing follows with launch_weight_pack) or pack weight groups
+// from the partial sums of an earlier launch_weight_partial.
 hipError_t launch_act_and_pack(const void* X, int x_dtype, int64_t M, int64_t K, const float* gain,
                                const hbl_config& cfg, void* codes, float* xscale, const void* W, int w_dtype,
-                               int64_t NK, float w_eps, const double* partial, int n_partial, uint8_t* W_packed,
+                               int64_t NK, float w_eps, const double* partial, double* partial_out, int n_partial,
+                               uint8_t* W_packed,
                                float* alpha, hipStream_t s, int layout = kCodesRowMajor);  // K <= 2048
 
 // layout: kCodesRowMajor (the ABI's), kCodesDecTiled, or kCodesFp6 (INT4, K >= 512)

@@ -47,6 +47,71 @@ HBL_DEVINL void unpack16(const uint4 q, float (&v)[8]) {
     }
 }
 
+// Partial |W| sums.  Block blk sums |W| over elements [blk*per_block,
+// (blk+1)*per_block) in fp64 in one fixed order, the order of a block of
+// kPartialVThreads threads: in every round of kPartialRoundVecs*256 16-byte
+// vectors, virtual thread t adds the elements of vectors u*256 + t (u
+// ascending, elements in order), then each 64-thread virtual wave is summed
+// by wave_sum_f64 and the wave sums are added in wave order, as
+// block_sum_f64 does.  A block of NT real threads (NT a multiple of 64
+// dividing 256) plays 256/NT virtual threads per thread (virtual thread
+// h*NT + tid), so the result does not depend on NT: the standalone launch
+// (256 threads) and the 64-thread blocks that share a grid with the
+// activation rows write the same partial sums bit for bit.
+// red: kPartialVThreads/64 doubles of LDS.
+constexpr int kPartialVThreads = 256;
+constexpr int kPartialRoundVecs = 8;  // 16-byte loads per virtual thread and round
+
+template <typename T, int NT>
+HBL_DEVINL void wq_partial_block(const T* __restrict__ W, int64_t count, int64_t per_block,
+                                 double* __restrict__ partial, int64_t blk, double* red) {
+    static_assert(NT % kWave == 0 && kPartialVThreads % NT == 0, "thread count");
+    constexpr int V = Vec16<T>::n;
+    constexpr int VT = kPartialVThreads / NT;   // virtual threads per thread
+    constexpr int HB = VT >= 2 ? 2 : 1;         // virtual threads whose loads are issued together
+    const int64_t begin = blk * per_block;
+    const int64_t n = min(count, begin + per_block) - begin;
+    constexpr int64_t R = (int64_t)kPartialRoundVecs * kPartialVThreads * V;  // elements per round
+    double s[VT];
+#pragma unroll
+    for (int h = 0; h < VT; h++) s[h] = 0.0;
+    for (int64_t r0 = 0; r0 < n; r0 += R) {
+        // elements past this block's slice load as zeros, which add nothing
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + begin + r0, min(R, n - r0) * (int64_t)sizeof(T));
+#pragma unroll
+        for (int h0 = 0; h0 < VT; h0 += HB) {
+            uint4 q[HB][kPartialRoundVecs];
+#pragma unroll
+            for (int h = 0; h < HB; h++)
+#pragma unroll
+                for (int u = 0; u < kPartialRoundVecs; u++)
+                    q[h][u] = buf_load16(
+                        rs, (uint32_t)((u * kPartialVThreads + (h0 + h) * NT + (int)threadIdx.x) * 16));
+#pragma unroll
+            for (int h = 0; h < HB; h++)
+#pragma unroll
+                for (int u = 0; u < kPartialRoundVecs; u++) {
+                    float v[V];
+                    unpack16(q[h][u], v);
+#pragma unroll
+                    for (int j = 0; j < V; j++) s[h0 + h] += (double)fabsf(v[j]);
+                }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < VT; h++) {
+        const double w = wave_sum_f64(s[h]);
+        if ((threadIdx.x & (kWave - 1)) == 0) red[h * (NT / kWave) + threadIdx.x / kWave] = w;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double r = 0.0;
+#pragma unroll
+        for (int i = 0; i < kPartialVThreads / kWave; i++) r += red[i];
+        partial[blk] = r;
+    }
+}
+
 // 2-bit code of a ternary value: 0 -> 00, +1 -> 01, -1 -> 11.
 HBL_DEVINL uint32_t tern_code_div(float w, float den) {
     // correctly rounded fp32 division, then round half to even, then clamp

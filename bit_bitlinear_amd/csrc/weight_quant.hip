@@ -27,33 +27,12 @@ constexpr int kWqThreads = 256;
 constexpr int kMaxPartials = 512;
 // Elements per wq_partial block are a multiple of this (keeps 16-byte vectors aligned).
 constexpr int64_t kPartialQuantum = 4096;
-constexpr int kRoundVecs = 8;     // 16-byte loads per thread issued together in wq_partial
 
 template <typename T>
 __global__ __launch_bounds__(kWqThreads) void wq_partial(const T* __restrict__ W, int64_t count, int64_t per_block,
                                                          double* __restrict__ partial) {
-    __shared__ double red[kWqThreads / kWave];
-    constexpr int V = Vec16<T>::n;
-    const int64_t begin = (int64_t)blockIdx.x * per_block;
-    const int64_t n = min(count, begin + per_block) - begin;
-    constexpr int64_t R = (int64_t)kRoundVecs * kWqThreads * V;  // elements per round
-    double s = 0.0;
-    for (int64_t r0 = 0; r0 < n; r0 += R) {
-        // elements past this block's slice load as zeros, which add nothing
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(W + begin + r0, min(R, n - r0) * (int64_t)sizeof(T));
-        uint4 q[kRoundVecs];
-#pragma unroll
-        for (int u = 0; u < kRoundVecs; u++) q[u] = buf_load16(rs, (uint32_t)((u * kWqThreads + threadIdx.x) * 16));
-#pragma unroll
-        for (int u = 0; u < kRoundVecs; u++) {
-            float v[V];
-            unpack16(q[u], v);
-#pragma unroll
-            for (int j = 0; j < V; j++) s += (double)fabsf(v[j]);
-        }
-    }
-    s = block_sum_f64<kWqThreads>(s, red);
-    if (threadIdx.x == 0) partial[blockIdx.x] = s;
+    __shared__ double red[kPartialVThreads / kWave];
+    wq_partial_block<T, kWqThreads>(W, count, per_block, partial, blockIdx.x, red);
 }
 
 template <typename T>
@@ -72,6 +51,8 @@ int64_t partial_slice(int64_t count) {
 }
 }  // namespace
 
+int64_t weight_partial_slice(int64_t count) { return partial_slice(count); }
+
 int weight_partial_count(int64_t count) {
     const int64_t per = partial_slice(count);
     return (int)((count + per - 1) / per);
@@ -89,20 +70,25 @@ hipError_t launch_weight_partial(const void* W, int w_dtype, int64_t count, doub
     return hipGetLastError();
 }
 
-hipError_t launch_weight_quant(const void* W, int w_dtype, int64_t N, int64_t K, float eps, uint8_t* W_packed,
-                               float* alpha, double* partial, int n_partial, hipStream_t s) {
+hipError_t launch_weight_pack(const void* W, int w_dtype, int64_t N, int64_t K, float eps, uint8_t* W_packed,
+                              float* alpha, const double* partial, int n_partial, hipStream_t s) {
     const int64_t count = N * K;
     const int64_t n_groups = count / 16;
     const int64_t blocks = (n_groups + (int64_t)kWqThreads * kPackGroups - 1) / ((int64_t)kWqThreads * kPackGroups);
-    hipError_t e = launch_weight_partial(W, w_dtype, count, partial, n_partial, s);
-    if (e != hipSuccess) return e;
     if (w_dtype == HBL_F32)
         hipLaunchKernelGGL(wq_pack<float>, dim3((unsigned)blocks), dim3(kWqThreads), 0, s, (const float*)W, n_groups,
-                           count, eps, (const double*)partial, n_partial, (uint32_t*)W_packed, alpha);
+                           count, eps, partial, n_partial, (uint32_t*)W_packed, alpha);
     else
         hipLaunchKernelGGL(wq_pack<uint16_t>, dim3((unsigned)blocks), dim3(kWqThreads), 0, s, (const uint16_t*)W,
-                           n_groups, count, eps, (const double*)partial, n_partial, (uint32_t*)W_packed, alpha);
+                           n_groups, count, eps, partial, n_partial, (uint32_t*)W_packed, alpha);
     return hipGetLastError();
+}
+
+hipError_t launch_weight_quant(const void* W, int w_dtype, int64_t N, int64_t K, float eps, uint8_t* W_packed,
+                               float* alpha, double* partial, int n_partial, hipStream_t s) {
+    hipError_t e = launch_weight_partial(W, w_dtype, N * K, partial, n_partial, s);
+    if (e != hipSuccess) return e;
+    return launch_weight_pack(W, w_dtype, N, K, eps, W_packed, alpha, partial, n_partial, s);
 }
 
 }  // namespace hbl
