@@ -389,6 +389,13 @@ HBL_DEVINL void act_row_quantise(ActRegs<LK, NT, Tin>& v, const float* __restric
         s_mul = beta == 0.f ? 0.f : sqrt7_f32() / (beta + quant_eps);
         d_out = beta == 0.f ? 0.f : beta / sqrt7_f32();
     }
+    // With quant_eps = 0 a statistic below num / FLT_MAX (a row of magnitude
+    // about 1e-37 or less) overflows the multiplier to +inf; such a row is
+    // taken as a zero statistic (s = d = 0, codes 0), as the oracle reads it.
+    if (__builtin_isinf(s_mul)) {
+        s_mul = 0.f;
+        d_out = 0.f;
+    }
     if (tid == 0) {
         *xs_out = d_out;
         if (s_out) *s_out = s_mul;

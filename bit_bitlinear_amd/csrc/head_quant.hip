@@ -7,7 +7,8 @@
 // pages; the reading: a symmetric absmax quantiser whose signed code is
 // stored with the offset 2^(b-1):
 //   gamma = max|x|, Qp = 2^(b-1) - 1, s = Qp/(gamma+eps), d = gamma/Qp,
-//   u = clamp(rint(x*s), -Qp, Qp) + 2^(b-1)        (gamma = 0: s = d = 0)
+//   u = clamp(rint(x*s), -Qp, Qp) + 2^(b-1)        (gamma = 0: s = d = 0; so too
+//   when eps = 0 and Qp/gamma overflows fp32)
 //
 // HBM-bound streaming kernel.  Lane l of the grid takes the 8 consecutive
 // elements 8*(l % G) .. +7 of head vector l / G (G = D/8 lanes per vector,
@@ -57,8 +58,12 @@ __global__ __launch_bounds__(kHqThreads) void head_quant_kernel(const Tin* __res
     if (!live) return;
     constexpr int zp = 1 << (BITS - 1), qp = zp - 1;
     const float gamma = a;
-    const float s = gamma == 0.f ? 0.f : (float)qp / (gamma + eps);
-    if (j == 0) d_out[v] = gamma == 0.f ? 0.f : gamma / (float)qp;
+    float s = gamma == 0.f ? 0.f : (float)qp / (gamma + eps);
+    // eps = 0 and gamma below qp / FLT_MAX: the multiplier overflows; the
+    // vector is taken as gamma = 0 (every code at the zero point)
+    const bool zero = gamma == 0.f || __builtin_isinf(s);
+    if (zero) s = 0.f;
+    if (j == 0) d_out[v] = zero ? 0.f : gamma / (float)qp;
     uint32_t u[8];
 #pragma unroll
     for (int i = 0; i < 8; i++) u[i] = (uint32_t)((int)rintf(fminf(fmaxf(x[i] * s, (float)-qp), (float)qp)) + zp);

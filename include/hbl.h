@@ -137,7 +137,9 @@ hbl_status hbl_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, const hb
  *                          natural order, H[i][j] = (-1)^popcount(i&j)/sqrt(K),
  *                          computed by an in-register/LDS fast transform)
  *   s, d from z           INT8: gamma = max|z|, s = 127/(gamma+eps), d = gamma/127
- *                          INT4: see hbl_a4_mode.  A zero statistic gives s = d = 0.
+ *                          INT4: see hbl_a4_mode.  A zero statistic gives s = d = 0,
+ *                          and so does one whose s overflows fp32 (quant_eps = 0
+ *                          and a row below about 1e-37: reading of the lost formula).
  *   q = clip(rint(z*s))   INT8 [-128,127] -> codes int8 [M][K]
  *                          INT4 [-8,7]     -> codes uint8 [M][K/2] (packed)
  *   xscale[m] = d
@@ -205,7 +207,8 @@ hbl_status hbl_forward_latent(const void* X, int32_t x_dtype, int64_t M, int64_t
  * X [M][H][D] (fp32 or bf16; post-RoPE states; row-major, so also [M][H*D]):
  *   gamma = max_d |x|, Qp = 2^(bits-1) - 1, s = Qp/(gamma + eps) (fp32),
  *   d = gamma/Qp,  u = clamp(rint(x*s), -Qp, Qp) + 2^(bits-1)  in [1, 2^bits - 1]
- *   (round half to even; gamma == 0 gives d = 0 and every u = 2^(bits-1);
+ *   (round half to even; gamma == 0 gives d = 0 and every u = 2^(bits-1), as
+ *   does a gamma so small that s overflows fp32 when eps = 0;
  *   dequantised value (u - 2^(bits-1)) * d).  The formula is the reading of
  *   the page taken here: a symmetric absmax quantiser stored with an offset.
  * codes: uint8 [M][H][D*bits/8]: bits = 8 one byte per code; 4 two per byte,

@@ -239,7 +239,13 @@ int hbo_act_scale(const float* z, int64_t K, int bits, int a4_mode, float eps, f
     }
     if (stat == 0.0f) { *s_out = 0.0f; *d_out = 0.0f; return HBO_OK; }
     float den = stat + eps;
-    *s_out = num / den;
+    float s = num / den;
+    /* With eps = 0 a statistic below num / FLT_MAX (about 3.7e-37 for INT8)
+     * makes the multiplier overflow to +inf, and 0 * inf has no code.  The
+     * pages never reach this range; the reading taken: such a row is
+     * treated as a zero statistic (s = d = 0, all codes 0). */
+    if (isinf(s)) { *s_out = 0.0f; *d_out = 0.0f; return HBO_OK; }
+    *s_out = s;
     *d_out = stat / num;
     return HBO_OK;
 }
@@ -413,6 +419,18 @@ int hbo_quantize_heads(const float* X, int64_t M, int64_t H, int64_t D, int bits
         const float den = gamma + eps;
         const float s = gamma == 0.f ? 0.f : (float)qp / den;
         d_out[v] = gamma == 0.f ? 0.f : gamma / (float)qp;
+        if (isinf(s)) {
+            /* eps = 0 and gamma below qp / FLT_MAX: the multiplier overflows;
+             * the vector is treated as gamma == 0 (the reading of O7). */
+            d_out[v] = 0.f;
+            memset(codes + v * vb, 0, (size_t)vb);
+            for (int64_t j = 0; j < D; j++) {
+                if (bits == 8) codes[v * vb + j] = (uint8_t)zp;
+                else if (bits == 4) codes[v * vb + j / 2] |= (uint8_t)(zp << (4 * (j % 2)));
+                else codes[v * vb + (3 * j + 2) / 8] |= (uint8_t)(1u << ((3 * j + 2) % 8));
+            }
+            continue;
+        }
         uint8_t* out = codes + v * vb;
         memset(out, 0, (size_t)vb);
         for (int64_t j = 0; j < D; j++) {

@@ -75,6 +75,16 @@ MUTANTS = [
      "const int t = k < K ? Wq[n * K + k] : -1;"),
     ("base3_row_bytes_wrong", "return 16 * ((K + 79) / 80);", "return 16 * (K / 80 + 1);"),
     ("base3_unpack_sign_swapped", "const int t = v % 3 - 1;", "const int t = 1 - v % 3;"),
+    ("bf16_by_truncation", "out[i] = (uint16_t)((v.u + 0x7FFFu + lsb) >> 16);", "out[i] = (uint16_t)(v.u >> 16);"),
+    ("bf16_round_half_away", "out[i] = (uint16_t)((v.u + 0x7FFFu + lsb) >> 16);",
+     "out[i] = (uint16_t)((v.u + 0x8000u) >> 16);"),
+    ("rescale_factors_premultiplied",
+     "float t = (float)acc[m * N + n] * d[m];\n            y[m * N + n] = t * alpha;",
+     "float t = (float)acc[m * N + n] * (d[m] * alpha);\n            y[m * N + n] = t;"),
+    ("rescale_single_fp64_product",
+     "float t = (float)acc[m * N + n] * d[m];\n            y[m * N + n] = t * alpha;",
+     "double t = (double)acc[m * N + n] * (double)d[m];\n            y[m * N + n] = (float)(t * (double)alpha);"),
+    ("act_scale_overflow_kept", "if (isinf(s)) { *s_out = 0.0f; *d_out = 0.0f; return HBO_OK; }", ""),
 ]
 
 

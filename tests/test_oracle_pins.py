@@ -292,6 +292,140 @@ def test_rescale_hand():
     assert y.tolist() == [[0.375, -0.625, 0.0]]
 
 
+def _golden_rows(name):
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", name)
+    rows = []
+    with open(path) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+def _fp32_rne(x):
+    """Round a nonzero rational to the nearest fp32 (ties to even) with exact
+    integer arithmetic; normal range only.  Returns the bit pattern."""
+    from fractions import Fraction
+    neg = x < 0
+    x = abs(Fraction(x))
+    e = 0
+    while x >= Fraction(2 ** 24) * Fraction(2) ** e:
+        e += 1
+    while x < Fraction(2 ** 23) * Fraction(2) ** e:
+        e -= 1
+    m = x / Fraction(2) ** e
+    fl = m.numerator // m.denominator
+    r = m - fl
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and fl % 2):
+        fl += 1
+    if fl == 2 ** 24:
+        fl, e = 2 ** 23, e + 1
+    return (int(neg) << 31) | ((e + 23 + 127) << 23) | (fl - 2 ** 23)
+
+
+def test_rescale_rounding_order_golden():
+    """y = fp32(fp32(acc*d)*alpha), the factor d first: hand-derived cases
+    (tests/golden/rescale_order.txt) where acc*fp32(d*alpha) and the exact
+    triple product round to a neighbouring fp32; the expected bits are derived
+    again here from exact fractions."""
+    from fractions import Fraction
+    for acc, dh, ah, yh, other in _golden_rows("rescale_order.txt"):
+        acc = int(acc)
+        d = np.array([int(dh, 16)], np.uint32).view(np.float32)
+        a = np.array([int(ah, 16)], np.uint32).view(np.float32)[0]
+        y = oracle.rescale(np.array([[acc]], np.int32), d, a)
+        assert int(y.view(np.uint32)[0, 0]) == int(yh, 16)
+        t = _fp32_rne(acc * Fraction(float(d[0])))
+        t_val = Fraction(float(np.array([t], np.uint32).view(np.float32)[0]))
+        assert _fp32_rne(t_val * Fraction(float(a))) == int(yh, 16)
+        assert _fp32_rne(acc * Fraction(float(d[0])) * Fraction(float(a))) == int(other, 16) != int(yh, 16)
+
+
+def test_rescale_rounding_order_random():
+    """The same rounding order on 20000 random (acc, d, alpha), each checked
+    against the exact-fraction derivation of fp32(fp32(acc*d)*alpha)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(31)
+    acc = rng.integers(-2 ** 20, 2 ** 20, size=(200, 100)).astype(np.int32)
+    acc[acc == 0] = 1
+    d = rng.uniform(1e-3, 1.0, 200).astype(np.float32)
+    a = np.float32(rng.uniform(1e-3, 0.1))
+    y = oracle.rescale(acc, d, a).view(np.uint32)
+    fa = Fraction(float(a))
+    for m in range(200):
+        fd = Fraction(float(d[m]))
+        for n in range(0, 100, 7):
+            t = _fp32_rne(int(acc[m, n]) * fd)
+            tv = Fraction(float(np.array([t], np.uint32).view(np.float32)[0]))
+            assert int(y[m, n]) == _fp32_rne(tv * fa)
+
+
+def test_bf16_rounding_golden():
+    """fp32 -> bf16 of the bf16 output variant: hand-derived ties (both ways,
+    both signs), values just above and below a tie, subnormals, overflow of
+    the largest finite values to infinity (tests/golden/bf16_rne.txt)."""
+    rows = _golden_rows("bf16_rne.txt")
+    x = np.array([int(r[0], 16) for r in rows], np.uint32).view(np.float32)
+    want = [int(r[1], 16) for r in rows]
+    assert oracle.f32_to_bf16(x).tolist() == want
+
+
+def test_bf16_rounding_matches_torch():
+    """Against torch's fp32 -> bf16 conversion (a library routine, round to
+    nearest even) on 400k values: random bit patterns of every exponent
+    (NaN excluded, outside the contract), exact ties, and ties with the top
+    half odd and even."""
+    rng = np.random.default_rng(32)
+    bits = rng.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    bits = bits[(bits & 0x7F800000) != 0x7F800000]                 # no inf / NaN in the random part
+    ties = (rng.integers(0, 2 ** 16, size=100000, dtype=np.uint64).astype(np.uint32) << 16) | 0x8000
+    ties = ties[(ties & 0x7F800000) != 0x7F800000]
+    near = np.concatenate([ties - 1, ties + 1])
+    allb = np.concatenate([bits, ties, near]).astype(np.uint32)
+    x = allb.view(np.float32)
+    got = oracle.f32_to_bf16(x)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_act_scale_overflow_is_zero_statistic():
+    """eps = 0 and a statistic so small that s = num/stat overflows fp32: the
+    row is treated as a zero statistic (s = d = 0, codes 0).  127/1e-37 and
+    7/2e-38 exceed the largest fp32 (3.4028e38); 127/4e-37 = 3.175e38 does not,
+    so that row keeps its codes (the absmax element maps to 127)."""
+    z = np.array([[1e-37, 0.0, -5e-38, 0.0]], np.float32)
+    s, d = oracle.act_scale(z, 8, eps=0.0)
+    assert float(s) == 0.0 and float(d) == 0.0
+    assert oracle.act_codes(z, 8, float(s)).tolist() == [0, 0, 0, 0]
+    z2 = np.array([[2e-38, 0.0, -1.5e-38, 0.0]], np.float32)
+    s2, d2 = oracle.act_scale(z2, 4, a4_mode=oracle.A4_ABSMAX, eps=0.0)
+    assert float(s2) == 0.0 and float(d2) == 0.0
+    z3 = np.array([[4e-37, 0.0, -2e-37, 0.0]], np.float32)
+    s3, d3 = oracle.act_scale(z3, 8, eps=0.0)
+    assert np.isfinite(s3) and float(s3) > 3.0e38
+    assert oracle.act_codes(z3, 8, float(s3)).tolist() == [127, 0, -64, 0]
+    r = oracle.quantize_activations(np.array([[1e-37, 0, -5e-38, 0] * 64], np.float32), bits=8, hadamard=False,
+                                    norm=oracle.NORM_NONE, quant_eps=0.0)
+    assert not r["q"].any() and float(r["d"][0]) == 0.0
+
+
+def test_heads_scale_overflow_is_zero_vector():
+    """The head quantiser under the same reading: gamma with qp/gamma above the
+    largest fp32 (eps = 0) gives d = 0 and every code at the zero point."""
+    # qp / FLT_MAX: 8.8e-39 (3 bits, subnormal), 2.06e-38 (4 bits), 3.73e-37 (8 bits)
+    for bits, gamma in ((3, 8e-39), (4, 2e-38), (8, 1e-37)):
+        x = np.zeros((1, 2, 32), np.float32)
+        x[0, :, 3] = gamma
+        x[0, :, 5] = -gamma / 2
+        x[0, 1, 3] = gamma * 20          # qp / gamma finite: keeps its codes
+        codes, d = oracle.quantize_heads(x, bits, eps=0.0)
+        u = oracle.unpack_heads(codes, 32, bits)
+        assert float(d[0, 0]) == 0.0 and (u[0, 0] == 1 << (bits - 1)).all()
+        assert float(d[0, 1]) > 0.0 and int(u[0, 1, 3]) == (1 << bits) - 1
+
+
 # --------------------------------------------------------------- end to end
 @pytest.mark.parametrize("K", [256, 1024, 4096])
 def test_forward_closed_form_hadamard_column(K):
