@@ -1,24 +1,26 @@
 """Benchmark of the H-BitLinear forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layer NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-A step is one pass of the whole hot path over one batch of synthetic input:
-per-tensor absmean ternarisation of the latent weights and the layer forward
-(norm + Hadamard + per-token quantisation, then the integer GEMM with the
-rescale epilogue), run as hbl_forward_latent, which gives the results of
-hbl_quantize_weights followed by hbl_forward bit for bit in three launches
-(the same two calls are timed too, as ms_per_step_two_calls).  The default layer is the
-attention output projection Wo of a 1.3B-like model: 4096 tokens, K = N = 2048,
-bf16 activations, INT8 codes, bf16 output.  Inputs are seeded synthetic arrays
-already resident in HBM; the timed steps rotate over enough distinct buffer
-sets (> 512 MiB) that the 256 MB last-level cache cannot hold them.
+Default workload: the 3B-like layer chain at 8192 tokens, all INT4 activations
+(plain BitLinear QKV 4096 -> 12288 and gate/up 4096 -> 32768, H-BitLinear Wo
+4096 -> 4096 and Wdown 16384 -> 4096), bf16 in and out.  A step is one pass of
+the hot path over one batch: the forward of the four layers (norm, Hadamard
+where the layer has it, per-token INT4 quantisation, the integer product on the
+FP6 x FP4 matrix cores, the rescale) against weights that were ternarised and
+converted to FP4 once beforehand, as a deployment holds them.  The weight
+ternarisation and conversion are timed separately.  Inputs are seeded
+synthetic arrays already resident in HBM; the timed steps are replayed from
+HIP graphs, exactly --steps of them, rotating over enough distinct buffer
+sets (> 512 MiB) that the 256 MB last-level cache cannot hold a step's inputs.
 
-Prints one JSON line.  Besides the throughput it reports, for the kernel that
-takes the most time per step, the algorithmic work per launch divided by its
-average launch time (HIP events on the launch stream) against the MI355X
-peak and against the ceiling measured in the same process by the probe
-kernels of libhbl_peaks.so (an HBM copy and dense matrix-core loops), and the
-CPU oracle timed on a bounded row sample on the host cores.
+Prints one JSON line: tokens/s and TOPS of the step; for the kernel that takes
+the most time per step, the algorithmic work per launch over its average
+launch time (HIP events on the launch stream, recorded around each kernel
+inside eager steps) against the MI355X peak and against ceilings measured in
+the same process; the same figures for the other workloads (1.3B-like Wo with
+INT8 codes, 7B-like Wdown, decode at 1, 16 and 64 tokens); and the CPU oracle
+timed on a bounded row sample on the host cores.
 """
 from __future__ import annotations
 
@@ -32,21 +34,39 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+METRIC = "H-BitLinear tokens/s + TOPS (a4/a8 × ternary W) and % of HBM/MFMA roofline"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_I8_TOPS = 5000.0          # MI355X dense INT8 MFMA, TOP/s
 PEAK_F6F4_TOPS = 10100.0       # MI355X dense FP6 / FP4 MFMA, TFLOP/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 ROTATE_BYTES = 576 << 20       # > 2 x 256 MB last-level cache
+DECODE_W_BYTES = 8 << 20       # 2-bit weights of the 8192 x 4096 decode layer
 
 _PEAKS = None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def measured_peaks():
     """Ceilings measured on this GPU by the probe kernels of libhbl_peaks.so
-    (built beside libhbl.so): a 512 MiB streaming copy (read + write bytes)
-    and loops of dense i8, FP6 x FP4 and bf16 matrix-core instructions on
-    register operands; each the best of 3 timed rounds after a warm-up, with
-    HIP events on the stream the probes run on.  Computed once per process."""
+    (built beside libhbl.so), timed with HIP events on the stream they run on:
+      * a 512 MiB streaming copy (read + write bytes),
+      * streaming reads of 8 MiB (the decode layer's 2-bit weights) and of
+        64 MiB, each launch replayed from a HIP graph over buffers rotated
+        past the last-level cache,
+      * an empty 256-block kernel replayed from a graph (the launch floor),
+      * loops of dense i8, FP6 x FP4 and bf16 matrix-core instructions on
+        register operands.
+    Each figure is the best of 3 timed rounds after a warm-up.  Computed once."""
     global _PEAKS
     if _PEAKS is not None:
         return _PEAKS
@@ -60,6 +80,10 @@ def measured_peaks():
     lib = ctypes.CDLL(hbl_build.PEAKS_LIB)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.hbl_peak_copy.argtypes = [P, P, I64, P]
+    lib.hbl_peak_read.argtypes = [P, I64, P, I64, P]
+    lib.hbl_peak_read_sink_len.argtypes = [I64]
+    lib.hbl_peak_read_sink_len.restype = I64
+    lib.hbl_peak_empty.argtypes = [I32, P]
     lib.hbl_peak_mfma.argtypes = [I32, P, I64, I32, I32, P]
     lib.hbl_peak_mfma_ops.argtypes = [I32, I32, I32]
     lib.hbl_peak_mfma_ops.restype = I64
@@ -82,27 +106,58 @@ def measured_peaks():
             best = us if best is None else min(best, us)
         return best
 
+    def graph_best_us(launches):
+        """One graph holding every launch once; microseconds per launch."""
+        for f in launches:
+            f()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in launches:
+                f()
+        us = best_us(g.replay, reps=3) / len(launches)
+        del g
+        return us
+
+    def ok(rc, what):
+        if rc != 0:
+            raise RuntimeError("%s failed (%d)" % (what, rc))
+
     nbytes = 512 << 20
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
 
     def copy():
-        if lib.hbl_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes, sp) != 0:
-            raise RuntimeError("hbl_peak_copy failed")
+        ok(lib.hbl_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes, sp), "copy")
 
     out = {"hbm_copy_GBps": round(2 * nbytes / (best_us(copy) * 1e-6) / 1e9, 1)}
-    del src, dst
+    del dst
+    # streaming reads at the decode layer's weight size and at 64 MiB, over
+    # distinct slices of the 512 MiB buffer (every replay reads cold data)
+    for size, key in ((DECODE_W_BYTES, "hbm_read_8MiB_GBps"), (64 << 20, "hbm_read_64MiB_GBps")):
+        slices = nbytes // size
+        sink = torch.empty(lib.hbl_peak_read_sink_len(size), dtype=torch.int32, device=dev)
+        base = src.data_ptr()
+        launches = [lambda i=i: ok(lib.hbl_peak_read(ctypes.c_void_p(base + i * size), size,
+                                                    ctypes.c_void_p(sink.data_ptr()), sink.numel(), sp), "read")
+                    for i in range(slices)]
+        us = graph_best_us(launches)
+        out[key] = round(size / (us * 1e-6) / 1e9, 1)
+        out[key.replace("GBps", "us")] = round(us, 3)
+        del sink
+    del src
+    out["launch_floor_us"] = round(graph_best_us([lambda: ok(lib.hbl_peak_empty(256, sp), "empty")] * 64), 3)
     blocks, iters = 2048, 2000
     sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
     for kind, key in ((0, "mfma_i8_TOPS"), (1, "mfma_f6f4_TFLOPS"), (2, "mfma_bf16_TFLOPS")):
         def run(kind=kind):
-            if lib.hbl_peak_mfma(kind, ctypes.c_void_p(sink.data_ptr()), sink.numel(), blocks, iters, sp) != 0:
-                raise RuntimeError("hbl_peak_mfma failed")
+            ok(lib.hbl_peak_mfma(kind, ctypes.c_void_p(sink.data_ptr()), sink.numel(), blocks, iters, sp), "mfma")
         ops = lib.hbl_peak_mfma_ops(kind, blocks, iters)
         out[key] = round(ops / (best_us(run, reps=2) * 1e-6) / 1e12, 1)
     torch.cuda.synchronize()
-    out["method"] = ("512 MiB 16-byte streaming copy (2 x bytes); 2048 x 256-thread blocks each issuing 4 "
-                     "independent matrix-core instructions per round on register operands")
+    out["method"] = ("512 MiB 16-byte streaming copy (2 x bytes); 8 MiB and 64 MiB streaming reads and an empty "
+                     "256-block kernel, graph-replayed; 2048 x 256-thread blocks each issuing 4 independent "
+                     "matrix-core instructions per round on register operands")
     _PEAKS = out
     return out
 
@@ -111,6 +166,7 @@ def with_measured_peak(roof, key):
     """Add the measured ceiling for this roofline's bound and the fraction of it."""
     pk = measured_peaks()
     roof["peak_measured"] = pk[key]
+    roof["peak_measured_key"] = key
     roof["frac_measured"] = round(roof["achieved"] / pk[key], 4)
     return roof
 
@@ -118,18 +174,21 @@ def with_measured_peak(roof, key):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=400)
-    p.add_argument("--warmup", type=int, default=40)
-    p.add_argument("--layer", default="wo_1.3b")
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="chain_3b",
+                   help="chain_3b (default: the 3B-like four-layer chain) or one layer of workloads/")
+    p.add_argument("--layer", default=None, help="alias of --workload for one layer")
     p.add_argument("--op", choices=("layer", "heads", "backward", "base3"), default="layer",
-                   help="layer: the H-BitLinear step (default); heads: the low-bit attention-state quantiser "
+                   help="layer: the H-BitLinear forward (default); heads: the low-bit attention-state quantiser "
                         "(per-head absmax to a 3-bit KV cache) on the 3B-like KV shape; backward: the layer's "
-                        "straight-through backward (dX and dW) on --layer")
+                        "straight-through backward (dX and dW) on --layer; base3: decode with base-3 weights")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--kernel-iters", type=int, default=200)
+    p.add_argument("--no-subresults", action="store_true", help="skip the other workloads' figures")
+    p.add_argument("--kernel-iters", type=int, default=20)
     p.add_argument("--counter-run", action="store_true",
                    help="for rocprofv3 --pmc passes: a 256 MiB device copy (the counters' known-size reference), "
-                        "then each kernel of the layer 3 times; prints no JSON")
+                        "then each kernel of the workload 3 times; prints no JSON")
     return p.parse_args()
 
 
@@ -153,265 +212,497 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only (each workload is one MI355X's share of a layer); "
-              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
-        sys.exit(2)
+def committed_traffic(kernel, workload):
+    """HBM bytes per launch from committed counter passes (profiles/), only
+    while the kernel's sources are unchanged since the counters were taken."""
+    tfile = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (kernel, workload))
+    if not os.path.exists(tfile):
+        return None
+    t = read_kv(tfile)
+    if t.get("source_hash") != source_hash(t.get("sources", "").split()):
+        return None
+    return int(t["bytes_per_launch"])
 
+
+# ------------------------------------------------------------------ setup --
+def _to_dev(X):
     import numpy as np
+    import torch
+    if X.dtype == np.uint16:
+        return torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    return torch.from_numpy(X).to("cuda:0")
+
+
+def _use_fp4(layer):
+    """INT4 prefill layers run on the FP6 x FP4 matrix cores with FP4 weights."""
+    import bit_bitlinear_amd as hbl
+    cfg = hbl.Config(act_bits=layer.act_bits, hadamard=layer.hadamard)
+    return layer.act_bits == 4 and layer.M > 64 and layer.K >= 512 and \
+        hbl.hbl_forward_workspace_bytes(layer.M, layer.K, layer.N, cfg) > hbl.hbl_workspace_bytes(layer.M, layer.K, cfg)
+
+
+class Prepared:
+    """One layer's device buffers: R rotating sets of (X, weights, workspace, Y)."""
+
+    def __init__(self, layer, seed=0, rotate=True):
+        import torch
+
+        import bit_bitlinear_amd as hbl
+        import workloads
+        self.layer = L = layer
+        self.cfg = hbl.Config(act_bits=L.act_bits, hadamard=L.hadamard)
+        self.fp4 = _use_fp4(L)
+        self.X_host, self.W_host, _ = workloads.make_inputs(L, seed)
+        X = _to_dev(self.X_host)
+        Wd = torch.from_numpy(self.W_host).to("cuda:0")
+        self.ydt = torch.bfloat16 if L.y_dtype == "bf16" else torch.float32
+        # weights: ternarised once (S0), then converted to FP4 for the FP6 x FP4 path
+        self.wws = torch.empty(hbl.hbl_weight_workspace_bytes(L.N, L.K), dtype=torch.uint8, device="cuda:0")
+        self.Wlat = Wd
+        Wp, alpha = hbl.hbl_quantize_weights(Wd, 1e-5, ws=self.wws)
+        W4 = hbl.hbl_pack_fp4(Wp, L.K) if self.fp4 else None
+        self.alpha = alpha
+        ws_bytes = (hbl.hbl_forward_fp4_workspace_bytes(L.M, L.K, self.cfg) if self.fp4
+                    else hbl.hbl_workspace_bytes(L.M, L.K, self.cfg))
+        y_bytes = L.M * L.N * (2 if self.ydt == torch.bfloat16 else 4)
+        w_bytes = L.N * L.K // 2 if self.fp4 else L.N * L.K // 4
+        set_bytes = X.numel() * X.element_size() + w_bytes + ws_bytes + y_bytes
+        self.set_bytes = set_bytes
+        self.R = max(1, -(-ROTATE_BYTES // set_bytes)) if rotate else 1
+        self.sets = []
+        for r in range(self.R):
+            s = {"X": X if r == 0 else X.clone(),
+                 "Wp": Wp if r == 0 else Wp.clone(),
+                 "ws": torch.empty(max(1, ws_bytes), dtype=torch.uint8, device="cuda:0"),
+                 "Y": torch.empty((L.M, L.N), dtype=self.ydt, device="cuda:0")}
+            if self.fp4:
+                s["W4"] = W4 if r == 0 else W4.clone()
+            self.sets.append(s)
+        del Wd
+        torch.cuda.synchronize()
+
+    def forward(self, r):
+        import bit_bitlinear_amd as hbl
+        s, L = self.sets[r], self.layer
+        if self.fp4:
+            hbl.hbl_forward_fp4(s["X"], s["W4"], self.alpha, L.N, self.cfg, Y=s["Y"], ws=s["ws"])
+        else:
+            hbl.hbl_forward(s["X"], s["Wp"], self.alpha, L.N, self.cfg, Y=s["Y"], ws=s["ws"])
+
+    # the stage entry points, writing into the same workspace regions as the forward
+    def stage_views(self, r):
+        import torch
+        L, s = self.layer, self.sets[r]
+        if self.fp4:
+            cb = -(-(L.M * L.K * 3 // 4) // 256) * 256
+            codes = s["ws"][:L.M * L.K * 3 // 4].view(L.M, L.K * 3 // 4)
+        else:
+            cb = -(-(L.M * L.K * L.act_bits // 8) // 256) * 256
+            codes = s["ws"][:L.M * L.K * L.act_bits // 8].view(L.M, -1)
+            if L.act_bits == 8:
+                codes = codes.view(torch.int8)
+        xs = s["ws"][cb:cb + 4 * L.M].view(torch.float32)
+        return codes, xs
+
+    def act(self, r):
+        import bit_bitlinear_amd as hbl
+        codes, xs = self.stage_views(r)
+        if self.fp4:
+            hbl.hbl_quantize_activations_fp6(self.sets[r]["X"], self.cfg, codes6=codes, xscale=xs)
+        else:
+            hbl.hbl_quantize_activations(self.sets[r]["X"], self.cfg, codes=codes, xscale=xs)
+
+    def gemm(self, r):
+        import bit_bitlinear_amd as hbl
+        L, s = self.layer, self.sets[r]
+        codes, xs = self.stage_views(r)
+        if self.fp4:
+            hbl.hbl_gemm_fp6fp4(codes, xs, L.K, s["W4"], self.alpha, L.N, Y=s["Y"])
+        else:
+            hbl.hbl_gemm(codes, xs, L.act_bits, L.K, s["Wp"], self.alpha, L.N, Y=s["Y"])
+
+    def work(self):
+        """Algorithmic work per launch of each kernel (SURVEY-defined units)."""
+        L = self.layer
+        x_bytes = L.M * L.K * (2 if L.x_dtype == "bf16" else 4)
+        y_bytes = L.M * L.N * (2 if L.y_dtype == "bf16" else 4)
+        code_bytes = L.M * L.K * L.act_bits // 8
+        return {"act_bytes": x_bytes + code_bytes + 4 * L.M,
+                "gemm_ops": 2 * L.M * L.N * L.K,
+                "gemm_bytes": code_bytes + 4 * L.M + L.N * L.K // 4 + y_bytes,
+                "fwd_small_bytes": x_bytes + L.N * L.K // 4 + 4 + y_bytes}
+
+
+def capture(fns):
+    """One HIP graph per entry of fns (each a callable queueing launches)."""
+    import torch
+    graphs = []
+    for f in fns:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            f()
+        graphs.append(g)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    return graphs
+
+
+def replay_timed(graphs, n):
+    """Replay graphs[i % R] for i < n; returns (wall seconds, event ms), both
+    bracketed by synchronisations."""
+    import torch
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(n):
+        graphs[i % len(graphs)].replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, e0.elapsed_time(e1)
+
+
+def graph_us(fn, R, iters):
+    """Microseconds per call of fn(r): one HIP graph holding fn(0) .. fn(R-1)
+    (one call per buffer set, so short kernels run back to back without the
+    host in between), replayed ceil(iters / R) times; events on the launch
+    stream."""
+    graphs = capture([lambda: [fn(r) for r in range(R)]])
+    reps = max(1, -(-iters // R))
+    _, ms = replay_timed(graphs, reps)
+    del graphs
+    return ms * 1e3 / (reps * R)
+
+
+def roofline(kernel, bound, work, us, unit, peak, peak_key, traffic=None, desc=""):
+    per_s = work / (us * 1e-6)
+    achieved = per_s / 1e12 if unit == "TFLOP/s" else per_s / 1e9
+    r = {"kernel": kernel, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": traffic, "work_per_launch": work,
+         "us_per_launch": round(us, 3), "work_desc": desc}
+    return with_measured_peak(r, peak_key)
+
+
+# ------------------------------------------------------------- the chain --
+def bench_chain(args):
     import torch
 
     import bit_bitlinear_amd as hbl
     import workloads
 
-    if args.op == "heads":
-        return bench_heads(args)
-    if args.op == "backward":
-        return bench_backward(args)
-    if args.op == "base3":
-        return bench_base3(args)
-    layer = workloads.by_name(args.layer)
-    M, K, N, bits = layer.M, layer.K, layer.N, layer.act_bits
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+    torch.cuda.set_device(0)
     hbl.load_library()
+    layers = workloads.CHAIN_3B
+    M = layers[0].M
+    preps = [Prepared(L, seed=i, rotate=False) for i, L in enumerate(layers)]
+    assert all(p.fp4 for p in preps)
+    step_bytes = sum(p.set_bytes for p in preps)
+    R = max(1, -(-ROTATE_BYTES // step_bytes))
+    if R > 1:  # a small chain would need more sets; the 3B chain's step touches > 1 GiB
+        raise RuntimeError("chain smaller than the rotation size")
 
-    # ---------------------------------------------------------------- inputs
-    X, W, _ = workloads.make_inputs(layer, seed=0)
-    if layer.x_dtype == "bf16":
-        Xd = torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).to(dev)
-    else:
-        Xd = torch.from_numpy(X).to(dev)
-    Wd = torch.from_numpy(W).to(dev)
-    ydt = torch.bfloat16 if layer.y_dtype == "bf16" else torch.float32
-    cfg = hbl.Config(act_bits=bits, hadamard=layer.hadamard)
-    # the workspace that selects the fastest forward path (FP6 x FP4 matrix
-    # cores for INT4 prefill shapes, else the INT8 ones)
-    ws_bytes = hbl.hbl_forward_workspace_bytes(M, K, N, cfg)
-    f6f4 = ws_bytes > hbl.hbl_workspace_bytes(M, K, cfg)
-    wws_bytes = hbl.hbl_weight_workspace_bytes(N, K)
-    y_bytes = M * N * (2 if ydt == torch.bfloat16 else 4)
-    set_bytes = Xd.numel() * Xd.element_size() + Wd.numel() * 4 + N * K // 4 + ws_bytes + y_bytes
-    R = max(2, -(-ROTATE_BYTES // set_bytes))
-    sets = []
-    for r in range(R):
-        s = {
-            "X": Xd if r == 0 else Xd.clone(),
-            "W": Wd if r == 0 else Wd.clone(),
-            "Wp": torch.empty((N, K // 4), dtype=torch.uint8, device=dev),
-            "alpha": torch.empty(1, dtype=torch.float32, device=dev),
-            "wws": torch.empty(wws_bytes, dtype=torch.uint8, device=dev),
-            "ws": torch.empty(ws_bytes, dtype=torch.uint8, device=dev),
-            "Y": torch.empty((M, N), dtype=ydt, device=dev),
-            "codes": torch.empty((M, K if bits == 8 else K // 2), dtype=torch.int8 if bits == 8 else torch.uint8,
-                                 device=dev),
-            "xs": torch.empty(M, dtype=torch.float32, device=dev),
-        }
-        sets.append(s)
+    def step(r=0):
+        for p in preps:
+            p.forward(r)
+
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
+    graphs = capture([step])
+    wall, ev_ms = replay_timed(graphs, args.steps)
+    del graphs
+    ms_per_step = wall / args.steps * 1e3
+    ops_step = sum(2 * p.layer.M * p.layer.N * p.layer.K for p in preps)
 
-    def step(s):
-        hbl.hbl_forward_latent(s["X"], s["W"], cfg, 1e-5, W_packed=s["Wp"], alpha=s["alpha"], Y=s["Y"], ws=s["ws"],
-                               wws=s["wws"])
-
-    def step_two_calls(s):
-        hbl.hbl_quantize_weights(s["W"], 1e-5, W_packed=s["Wp"], alpha=s["alpha"], ws=s["wws"])
-        hbl.hbl_forward(s["X"], s["Wp"], s["alpha"], N, cfg, Y=s["Y"], ws=s["ws"])
-
-    if args.counter_run:
-        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)   # 256 MiB
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        s0 = sets[0]
-        for _ in range(3):
-            hbl.hbl_quantize_weights(s0["W"], 1e-5, W_packed=s0["Wp"], alpha=s0["alpha"], ws=s0["wws"])
-            hbl.hbl_quantize_activations(s0["X"], cfg, codes=s0["codes"], xscale=s0["xs"])
-            hbl.hbl_gemm(s0["codes"], s0["xs"], bits, K, s0["Wp"], s0["alpha"], N, Y=s0["Y"])
-            hbl.hbl_forward(s0["X"], s0["Wp"], s0["alpha"], N, cfg, Y=s0["Y"], ws=s0["ws"])
-        torch.cuda.synchronize()
-        print("counter run done: %s" % layer.desc)
-        return
-
-    # ---------------------------------------------------------------- steps
-    # Eager warmup (also initialises every kernel), then the timed work is
-    # captured once in HIP graphs (one launch per rotating buffer set) and the
-    # graphs are replayed, so the host's per-call overhead does not gate the
-    # GPU; the graph holds kernel launches only.
-    for i in range(args.warmup):
-        step(sets[i % R])
-    torch.cuda.synchronize()
-
-    def capture(fn):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for r in range(R):
-                fn(sets[r])
-        g.replay()
-        torch.cuda.synchronize()
-        return g
-
-    reps = max(1, -(-args.steps // R))
-    timed_steps = reps * R
-
-    def timed_replays(g):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            g.replay()
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0
-
-    wall = timed_replays(capture(step))
-    ms_per_step = wall / timed_steps * 1e3
-    tokens_per_s = M * timed_steps / wall
-    wall_two = timed_replays(capture(step_two_calls))
-
-    # ------------------------------------------------------ per-kernel timing
+    # per-kernel times inside eager steps: events around each stage launch
     stream = torch.cuda.current_stream()
+    n_it = max(3, args.kernel_iters)
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in preps] for _ in range(n_it)]
+    for i in range(n_it):
+        for j, p in enumerate(preps):
+            ev[i][j][0].record(stream)
+            p.act(0)
+            ev[i][j][1].record(stream)
+            p.gemm(0)
+            ev[i][j][2].record(stream)
+    torch.cuda.synchronize()
+    per_layer = []
+    for j, p in enumerate(preps):
+        t_act = sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(1, n_it)) / (n_it - 1) * 1e3
+        t_gemm = sum(ev[i][j][1].elapsed_time(ev[i][j][2]) for i in range(1, n_it)) / (n_it - 1) * 1e3
+        w = p.work()
+        L = p.layer
+        act6_bytes = L.M * L.K * 2 + L.M * L.K * 3 // 4 + 4 * L.M
+        per_layer.append({
+            "layer": L.desc, "act_us": round(t_act, 3), "gemm_us": round(t_gemm, 3),
+            "gemm_ops": w["gemm_ops"], "gemm_TOPS": round(w["gemm_ops"] / (t_gemm * 1e-6) / 1e12, 1),
+            "gemm_frac_f6f4_peak": round(w["gemm_ops"] / (t_gemm * 1e-6) / 1e12 / PEAK_F6F4_TOPS, 4),
+            "act_GBps": round(w["act_bytes"] / (t_act * 1e-6) / 1e9, 1),
+            "act_bytes_algorithmic": w["act_bytes"], "act_bytes_fp6": act6_bytes})
+    # weight preparation (S0 + FP4 conversion), once per weight, timed apart
+    wprep = []
+    for p in preps:
+        L = p.layer
+        t_wq = graph_us(lambda r, p=p: hbl.hbl_quantize_weights(p.Wlat, 1e-5, W_packed=p.sets[0]["Wp"],
+                                                                 alpha=p.alpha, ws=p.wws), 1, 3)
+        t_f4 = graph_us(lambda r, p=p: hbl.hbl_pack_fp4(p.sets[0]["Wp"], L.K, W4=p.sets[0]["W4"]), 1, 3)
+        wprep.append({"layer": L.name, "ternarise_us": round(t_wq, 2), "to_fp4_us": round(t_f4, 2),
+                      "ternarise_GBps": round((L.N * L.K * 4 + L.N * L.K // 4 + 4) / (t_wq * 1e-6) / 1e9, 1)})
+    tot_gemm_us = sum(x["gemm_us"] for x in per_layer)
+    tot_act_us = sum(x["act_us"] for x in per_layer)
+    n_l = len(preps)
+    # the dominant kernel: the FP6 x FP4 GEMM, one launch per layer; its
+    # average launch does (ops of the four layers) / 4 in (their time) / 4
+    traffic = committed_traffic("gemm_f6f4", "chain_3b")
+    roof = roofline("gemm_f6f4_kernel (hbl_gemm_fp6fp4; one launch per layer, averaged over the 4 layers)",
+                    "mfma", ops_step // n_l, tot_gemm_us / n_l, "TFLOP/s", PEAK_F6F4_TOPS, "mfma_f6f4_TFLOPS",
+                    traffic, "2*M*N*K ops of the 4 layers / 4 per launch; INT4 codes as FP6 E3M2 x ternary "
+                             "weights as FP4 E2M1, exact fp32 sums")
+    del preps
+    torch.cuda.empty_cache()
 
-    def time_launches(fn, iters):
-        g = capture(fn)
-        reps_k = max(1, -(-iters // R))
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for _ in range(reps_k):
-            g.replay()
-        ev1.record(stream)
-        ev1.synchronize()
-        return ev0.elapsed_time(ev1) / (reps_k * R) * 1e3   # microseconds per launch
-
-    it = args.kernel_iters
-    t_wq = time_launches(lambda s: hbl.hbl_quantize_weights(s["W"], 1e-5, W_packed=s["Wp"], alpha=s["alpha"],
-                                                            ws=s["wws"]), it)
-    t_act = time_launches(lambda s: hbl.hbl_quantize_activations(s["X"], cfg, codes=s["codes"], xscale=s["xs"]), it)
-    t_gemm = time_launches(lambda s: hbl.hbl_gemm(s["codes"], s["xs"], bits, K, s["Wp"], s["alpha"], N, Y=s["Y"]), it)
-    # one token with K a power of two in [1024, 16384]: hbl_forward is one fused launch
-    fused = M == 1 and 1024 <= K <= 16384 and (K & (K - 1)) == 0
-    # hbl_forward as a whole (up to 64 tokens its codes take the decode GEMM's tiled order)
-    t_fwd = time_launches(lambda s: hbl.hbl_forward(s["X"], s["Wp"], s["alpha"], N, cfg, Y=s["Y"], ws=s["ws"]), it)
-
-    x_bytes = M * K * (2 if layer.x_dtype == "bf16" else 4)
-    code_bytes = M * K * bits // 8
-    kernels = {
-        "weight_ternarise": {"us": t_wq, "bound": "hbm", "unit": "GB/s",
-                             "work": N * K * 4 + N * K // 4 + 4,
-                             "work_desc": "read latent W once (fp32) + write 2-bit W + alpha"},
-        "norm_fwht_quant": {"us": t_act, "bound": "hbm", "unit": "GB/s",
-                            "work": x_bytes + code_bytes + 4 * M,
-                            "work_desc": "read X + write codes + write xscale"},
-        "gemm_i8_mfma" if M > 64 else "gemv_decode": {
-            "us": t_gemm, "bound": "mfma" if M > 64 else "hbm", "unit": "TFLOP/s" if M > 64 else "GB/s",
-            "work": 2 * M * N * K if M > 64 else code_bytes + 4 * M + N * K // 4 + M * N * 2,
-            "work_desc": "2*M*N*K integer ops" if M > 64 else "read codes + xscale + 2-bit W, write Y"},
-    }
-    if f6f4:
-        # the FP6 x FP4 GEMM runs only inside hbl_forward (with the FP6
-        # activation kernel and the FP4 weight conversion): its ops over the
-        # whole forward's time, a lower bound for the GEMM alone
-        kernels["forward_fp6xfp4"] = {
-            "us": t_fwd, "bound": "mfma", "unit": "TFLOP/s", "work": 2 * M * N * K, "peak": PEAK_F6F4_TOPS,
-            "work_desc": "2*M*N*K ops over hbl_forward (FP6 activation codes, FP4 weights, FP6 x FP4 GEMM)"}
-    if fused:
-        kernels["forward_small_fused"] = {
-            "us": t_fwd, "bound": "hbm", "unit": "GB/s",
-            "work": x_bytes + N * K // 4 + 4 + M * N * (2 if ydt == torch.bfloat16 else 4),
-            "work_desc": "read X + 2-bit W + alpha, write Y (codes stay on chip)"}
-    for k, v in kernels.items():
-        per_s = v["work"] / (v["us"] * 1e-6)
-        v["achieved"] = per_s / 1e12 if v["unit"] == "TFLOP/s" else per_s / 1e9
-        v["peak"] = v.get("peak") or (PEAK_I8_TOPS if v["unit"] == "TFLOP/s" else PEAK_HBM_GBS)
-        v["frac"] = v["achieved"] / v["peak"]
-    # the dominant kernel of the step (for a fused forward or the FP6 x FP4
-    # path, the stage kernels it replaces are not in the step)
-    replaced = ("norm_fwht_quant", "gemv_decode") if fused else ("norm_fwht_quant", "gemm_i8_mfma") if f6f4 else ()
-    dom_name = max((k for k in kernels if k not in replaced), key=lambda k: kernels[k]["us"])
-    dom = kernels[dom_name]
-
-    # HBM bytes per launch from committed counter passes, only while the
-    # kernel's sources are unchanged since the counters were taken
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (dom_name, layer.name))
-    if os.path.exists(tfile):
-        t = read_kv(tfile)
-        if t.get("source_hash") == source_hash(t.get("sources", "").split()):
-            traffic = int(t["bytes_per_launch"])
-
-    roofline = {"kernel": dom_name, "bound": dom["bound"], "achieved": round(dom["achieved"], 2),
-                "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4), "traffic": traffic,
-                "work_per_launch": dom["work"], "work_desc": dom["work_desc"], "us_per_launch": round(dom["us"], 3)}
-    with_measured_peak(roofline, "hbm_copy_GBps" if dom["unit"] == "GB/s" else
-                       "mfma_f6f4_TFLOPS" if dom["peak"] == PEAK_F6F4_TOPS else "mfma_i8_TOPS")
-
-    # ----------------------------------------------------------- CPU baseline
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(layer, X, W)
-
+    subs = None if args.no_subresults else subresults(args)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_chain(layers)
     out = {
-        "metric": "H-BitLinear tokens/s + TOPS (a4/a8 x ternary W) and % of HBM/MFMA roofline",
-        "value": round(tokens_per_s, 1),
+        "metric": METRIC,
+        "value": round(M * args.steps / wall, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": timed_steps,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp6xfp4" if f6f4 else "i8",
-        "data": "synthetic (seeded; outlier-channel activations, N(0,0.02) latent weights)",
-        "config": {"workload": layer.desc, "M": M, "K": K, "N": N, "act_bits": bits,
-                   "hadamard": layer.hadamard, "x_dtype": layer.x_dtype, "y_dtype": layer.y_dtype,
-                   "step": "hbl_forward_latent (ternarise latent W + forward; = hbl_quantize_weights then "
-                           "hbl_forward, bit for bit)", "rotating_sets": R,
-                   "gemm": ("FP6 x FP4 matrix cores (INT4 codes as FP6 E3M2, ternary as FP4 E2M1, exact fp32 sums)"
-                            if f6f4 else "INT8 matrix cores (int32 sums)"),
-                   "timing": "HIP graph replay of captured launches"},
-        "tops": round(2.0 * M * N * K * timed_steps / wall / 1e12, 2),
-        "ms_per_step_two_calls": round(wall_two / timed_steps * 1e3, 5),
-        "forward_us": round(t_fwd, 3),
-        "forward_only_tokens_per_s": round(M / (t_fwd * 1e-6), 1),
-        "roofline": roofline,
+        "dtype": "fp6xfp4",
+        "data": "synthetic (seeded Gaussian, outlier-mixture and SwiGLU-like activations; N(0,0.02) latent "
+                "weights, ternarised once)",
+        "config": {"workload": "chain_3b: 3B-like layer chain at 8192 tokens, INT4 activations, bf16 in/out: "
+                               "QKV 4096->12288 and gate/up 4096->32768 (BitLinear), Wo 4096->4096 and Wdown "
+                               "16384->4096 (H-BitLinear)",
+                   "M": M, "layers": [p["layer"] for p in per_layer], "act_bits": 4,
+                   "step": "hbl_forward_fp4 on each of the 4 layers (norm [+ Hadamard] + INT4 codes as FP6, "
+                           "FP6 x FP4 GEMM + rescale) against weights ternarised and converted to FP4 once",
+                   "timing": "HIP graph replay, one graph per step, exactly --steps replays"},
+        "tops": round(ops_step * args.steps / wall / 1e12, 2),
+        "ms_per_step_events": round(ev_ms / args.steps, 5),
+        "kernel_us_per_step": {"gemm_f6f4": round(tot_gemm_us, 2), "act_fp6": round(tot_act_us, 2)},
+        "roofline": roof,
+        "layers": per_layer,
+        "weight_prep": wprep,
         "box_peaks": measured_peaks(),
-        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                    for k, v in kernels.items()},
+        "subresults": subs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(layer, X, W):
-    """The oracle as it stands, timed on the host cores on a bounded sample of
-    the same workload: weight quantisation of the full W once, then the
-    forward of the first S rows; tokens/s scales the row time to all M rows."""
-    import numpy as np
+def subresults(args):
+    """The other workloads, each measured the same way (graph replay over
+    rotating buffer sets): the forward, and its dominant kernel against its
+    roofline."""
+    import torch
 
+    import bit_bitlinear_amd as hbl
+    import workloads
+
+    out = {}
+    it = max(20, args.kernel_iters)
+    for layer in (workloads.WO_1P3B, workloads.WDOWN_7B) + workloads.DECODE:
+        p = Prepared(layer)
+        L, w = p.layer, p.work()
+        fwd = graph_us(p.forward, p.R, it)
+        r = {"workload": L.desc, "forward_us": round(fwd, 3), "tokens_per_s": round(L.M / (fwd * 1e-6), 1),
+             "forward_TOPS": round(w["gemm_ops"] / (fwd * 1e-6) / 1e12, 2),
+             "gemm": "FP6 x FP4 matrix cores" if p.fp4 else "INT8 matrix cores" if L.M > 64 else "decode GEMV"}
+        fused = L.M == 1 and 1024 <= L.K <= 16384
+        if fused:
+            # one launch (Kernel F): the forward is the kernel
+            r["roofline"] = roofline("forward_small_kernel (hbl_forward, one launch)", "hbm", w["fwd_small_bytes"],
+                                     fwd, "GB/s", PEAK_HBM_GBS, "hbm_read_8MiB_GBps", None,
+                                     "read X + 2-bit W + alpha, write Y")
+        else:
+            act = graph_us(p.act, p.R, it)
+            gemm = graph_us(p.gemm, p.R, it)
+            r["act_us"] = round(act, 3)
+            r["act_GBps"] = round(w["act_bytes"] / (act * 1e-6) / 1e9, 1)
+            r["gemm_us"] = round(gemm, 3)
+            if p.fp4:
+                r["roofline"] = roofline("gemm_f6f4_kernel (hbl_gemm_fp6fp4)", "mfma", w["gemm_ops"], gemm,
+                                         "TFLOP/s", PEAK_F6F4_TOPS, "mfma_f6f4_TFLOPS",
+                                         committed_traffic("gemm_f6f4", L.name), "2*M*N*K ops")
+            elif L.M > 64:
+                r["roofline"] = roofline("gemm_dma_kernel (hbl_gemm, INT8)", "mfma", w["gemm_ops"], gemm, "TFLOP/s",
+                                         PEAK_I8_TOPS, "mfma_i8_TOPS", committed_traffic("gemm_i8_mfma", L.name),
+                                         "2*M*N*K integer ops")
+            else:
+                r["roofline"] = roofline("decode GEMM (hbl_gemm, row-major codes)", "hbm", w["gemm_bytes"], gemm,
+                                         "GB/s", PEAK_HBM_GBS, "hbm_read_8MiB_GBps", None,
+                                         "read codes + xscale + 2-bit W, write Y")
+        out[L.name] = r
+        del p
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline_chain(layers):
+    """The oracle as it stands, timed on the host cores on a bounded sample of
+    the same workload: the forward of the first S rows of each of the four
+    layers (weights ternarised once beforehand, as on the GPU), scaled to
+    tokens/s = S / (time of the four layers)."""
     import oracle
 
-    Xs = X
-    t0 = time.perf_counter()
-    Wq, _, alpha = oracle.quantize_weights(W)
-    t_wq = time.perf_counter() - t0
-    # calibrate on 16 rows, then size the sample for about 2 s of wall time
-    t0 = time.perf_counter()
-    oracle.forward(Xs[:16], Wq, alpha, bits=layer.act_bits, hadamard=layer.hadamard)
-    per_row = (time.perf_counter() - t0) / 16
-    S = int(min(layer.M, max(64, round(2.0 / max(per_row, 1e-6)))))
-    S = max(16, S - S % 16)
-    t0 = time.perf_counter()
-    oracle.forward(Xs[:S], Wq, alpha, bits=layer.act_bits, hadamard=layer.hadamard)
-    t_rows = time.perf_counter() - t0
-    t_step = t_wq + t_rows * layer.M / S
     cores = oracle.num_threads()
-    return {"value": round(layer.M / t_step, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": "full weight ternarisation once (%.3f s) + forward of the first %d of %d rows (%.3f s), "
-                      "scaled to all rows; %d OpenMP threads" % (t_wq, S, layer.M, t_rows, cores),
-            "cpu_seconds": round((t_wq + t_rows) * cores, 1)}
+    Wq = []
+    t0 = time.perf_counter()
+    inputs = []
+    import workloads
+    for i, L in enumerate(layers):
+        X, W, _ = workloads.make_inputs(L, seed=i, M=64)
+        q, _, a = oracle.quantize_weights(W)
+        Wq.append((q, a))
+        inputs.append(X)
+    t_wq = time.perf_counter() - t0
+
+    def run(S):
+        t = time.perf_counter()
+        for L, X, (q, a) in zip(layers, inputs, Wq):
+            oracle.forward(X[:S], q, a, bits=L.act_bits, hadamard=L.hadamard)
+        return time.perf_counter() - t
+
+    per_row = run(cores) / cores
+    S = int(max(cores, min(64, round(2.0 / max(per_row, 1e-6)))))
+    S -= S % cores if S > cores else 0
+    t = run(S)
+    return {"value": round(S / t, 3), "unit": "tokens/s", "cores": cores, "cpu_model": cpu_model(),
+            "kind": "oracle",
+            "sample": "forward of the first %d of %d rows through the 4 chain layers (%.2f s wall on %d OpenMP "
+                      "threads; weights ternarised beforehand, %.1f s, not counted), scaled to tokens/s"
+                      % (S, layers[0].M, t, cores, t_wq),
+            "cpu_seconds": round(t * cores, 1)}
+
+
+# -------------------------------------------------------------- one layer --
+def bench_single(args, layer):
+    """One layer of workloads/ as the step (forward with weights prepared once),
+    for the profiles of that layer; the JSON line has the same fields."""
+    import torch
+
+    import bit_bitlinear_amd as hbl
+
+    torch.cuda.set_device(0)
+    hbl.load_library()
+    p = Prepared(layer)
+    L, w = p.layer, p.work()
+    for i in range(args.warmup):
+        p.forward(i % p.R)
+    torch.cuda.synchronize()
+    graphs = capture([lambda r=r: p.forward(r) for r in range(p.R)])
+    wall, ev_ms = replay_timed(graphs, args.steps)
+    del graphs
+    it = max(20, args.kernel_iters)
+    fused = L.M == 1 and 1024 <= L.K <= 16384
+    fwd = graph_us(p.forward, p.R, it)
+    if fused:
+        roof = roofline("forward_small_kernel (hbl_forward, one launch)", "hbm", w["fwd_small_bytes"], fwd, "GB/s",
+                        PEAK_HBM_GBS, "hbm_read_8MiB_GBps", None, "read X + 2-bit W + alpha, write Y")
+        kern = {}
+    else:
+        act = graph_us(p.act, p.R, it)
+        gemm = graph_us(p.gemm, p.R, it)
+        kern = {"act_us": round(act, 3), "gemm_us": round(gemm, 3),
+                "act_GBps": round(w["act_bytes"] / (act * 1e-6) / 1e9, 1)}
+        if p.fp4:
+            roof = roofline("gemm_f6f4_kernel (hbl_gemm_fp6fp4)", "mfma", w["gemm_ops"], gemm, "TFLOP/s",
+                            PEAK_F6F4_TOPS, "mfma_f6f4_TFLOPS", committed_traffic("gemm_f6f4", L.name),
+                            "2*M*N*K ops")
+        elif L.M > 64:
+            roof = roofline("gemm_dma_kernel (hbl_gemm, INT8)", "mfma", w["gemm_ops"], gemm, "TFLOP/s",
+                            PEAK_I8_TOPS, "mfma_i8_TOPS", committed_traffic("gemm_i8_mfma", L.name),
+                            "2*M*N*K integer ops")
+        else:
+            roof = roofline("decode GEMM (hbl_gemm, row-major codes)", "hbm", w["gemm_bytes"], gemm, "GB/s",
+                            PEAK_HBM_GBS, "hbm_read_8MiB_GBps", None, "read codes + xscale + 2-bit W, write Y")
+    # the same layer from latent weights (ternarised in every step), for training-time callers
+    lat = None
+    if not p.fp4:
+        lat = graph_us(lambda r: hbl.hbl_forward_latent(p.sets[r]["X"], p.Wlat, p.cfg, 1e-5,
+                                                        W_packed=p.sets[r]["Wp"], alpha=p.alpha, Y=p.sets[r]["Y"],
+                                                        ws=p.sets[r]["ws"], wws=p.wws), p.R, it)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_chain((L,))
+    print(json.dumps({
+        "metric": METRIC, "value": round(L.M * args.steps / wall, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp6xfp4" if p.fp4 else "i8",
+        "data": "synthetic (seeded; outlier-channel activations, N(0,0.02) latent weights, ternarised once)",
+        "config": {"workload": L.desc, "M": L.M, "K": L.K, "N": L.N, "act_bits": L.act_bits,
+                   "hadamard": L.hadamard, "rotating_sets": p.R,
+                   "step": "hbl_forward_fp4" if p.fp4 else "hbl_forward",
+                   "timing": "HIP graph replay, exactly --steps replays"},
+        "tops": round(w["gemm_ops"] * args.steps / wall / 1e12, 2),
+        "ms_per_step_events": round(ev_ms / args.steps, 5),
+        "forward_us": round(fwd, 3), "latent_step_us": None if lat is None else round(lat, 3),
+        "kernels": kern, "roofline": roof, "box_peaks": measured_peaks(), "cpu_baseline": cpu,
+    }), flush=True)
+
+
+def counter_run(name):
+    """For rocprofv3 --pmc passes: a 256 MiB device copy (the counters'
+    known-size reference), then each kernel of the workload 3 times."""
+    import torch
+
+    import bit_bitlinear_amd as hbl
+    import workloads
+
+    torch.cuda.set_device(0)
+    hbl.load_library()
+    layers = workloads.CHAIN_3B if name == "chain_3b" else (workloads.by_name(name),)
+    src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    del src, dst
+    for i, L in enumerate(layers):
+        p = Prepared(L, seed=i, rotate=False)
+        for _ in range(3):
+            p.act(0)
+            p.gemm(0)
+            p.forward(0)
+        torch.cuda.synchronize()
+        del p
+        torch.cuda.empty_cache()
+    print("counter run done: %s" % name, flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only (every workload is one MI355X's share of a layer, and this build "
+              "uses a single GPU); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if args.op == "heads":
+        return bench_heads(args)
+    if args.op == "backward":
+        if args.layer is None:
+            args.layer = "wo_1.3b"
+        return bench_backward(args)
+    if args.op == "base3":
+        if args.layer is None:
+            args.layer = "decode_m1"
+        return bench_base3(args)
+    name = args.layer or args.workload
+    if args.counter_run:
+        return counter_run(name)
+    if name == "chain_3b":
+        return bench_chain(args)
+    import workloads
+    return bench_single(args, workloads.by_name(name))
 
 
 def bench_backward(args):
@@ -483,7 +774,7 @@ def bench_backward(args):
         t0 = time.perf_counter()
         oracle.backward(dY[:S], X[:S], Wq, a, bits=bits, hadamard=layer.hadamard)
         t = time.perf_counter() - t0
-        cpu = {"value": round(S / t, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        cpu = {"value": round(S / t, 2), "unit": "tokens/s", "cores": 1, "cpu_model": cpu_model(), "kind": "oracle",
                "sample": "dX and dW of the first %d of %d rows (%.2f s, single-threaded C; dW of a row subset is "
                          "the same work per row)" % (S, M, t)}
     print(json.dumps({
@@ -562,7 +853,7 @@ def bench_heads(args):
         t0 = time.perf_counter()
         oracle.quantize_heads(Xb, bits, eps=1e-5)
         t = time.perf_counter() - t0
-        cpu = {"value": round(M / t, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        cpu = {"value": round(M / t, 2), "unit": "tokens/s", "cores": 1, "cpu_model": cpu_model(), "kind": "oracle",
                "sample": "the whole workload (%d x %d heads x %d), single-threaded C, %.3f s" % (M, H, D, t)}
     print(json.dumps({
         "metric": "low-bit attention-state quantisation tokens/s (per-head absmax to a 3-bit KV cache)",
@@ -655,7 +946,8 @@ def bench_base3(args):
         Wq = oracle.unpack_base3(W3.cpu().numpy(), K)
         oracle.forward(X, Wq, float(alpha.cpu().numpy()[0]), bits=bits, hadamard=layer.hadamard)
         t = time.perf_counter() - t0
-        cpu = {"value": round(M / t, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+        cpu = {"value": round(M / t, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "cpu_model": cpu_model(),
+               "kind": "oracle",
                "sample": "all %d tokens: base-3 unpack of the weights and the forward (%.2f s)" % (M, t)}
     print(json.dumps({
         "metric": "decode tokens/s with base-3 weights (five per byte)",
@@ -676,6 +968,7 @@ def bench_base3(args):
         "cpu_baseline": cpu,
     }))
     del g1, g2, g3, g4
+
 
 
 if __name__ == "__main__":

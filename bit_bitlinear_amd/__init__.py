@@ -19,7 +19,9 @@ __all__ = [
     "hbl_packed_weight_bytes", "hbl_weight_workspace_bytes", "hbl_quantize_weights",
     "hbl_workspace_bytes", "hbl_forward_workspace_bytes", "hbl_quantize_activations", "hbl_gemm", "hbl_forward", "hbl_forward_latent",
     "hbl_quantize_heads", "hbl_backward_workspace_bytes", "hbl_backward", "hbl_status_string",
-    "hbl_last_hip_error",
+    "hbl_last_hip_error", "hbl_base3_weight_bytes", "hbl_pack_base3", "hbl_gemm_base3", "hbl_forward_base3",
+    "hbl_fp4_weight_bytes", "hbl_pack_fp4", "hbl_fp6_codes_bytes", "hbl_quantize_activations_fp6",
+    "hbl_gemm_fp6fp4", "hbl_forward_fp4_workspace_bytes", "hbl_forward_fp4",
     "HBL_F32", "HBL_BF16", "HBL_NORM_RMS", "HBL_NORM_LN", "HBL_NORM_NONE",
     "HBL_A4_ABSMEAN_SQRT7", "HBL_A4_ABSMAX_7",
 ]
@@ -108,6 +110,13 @@ def load_library(path: str | None = None):
         "hbl_pack_base3": [P, I64, I64, P, P],
         "hbl_gemm_base3": [P, P, I32, I64, I64, P, P, I64, P, I32, P],
         "hbl_forward_base3": [P, I32, I64, I64, P, P, P, I64, PCFG, P, I32, P, SZ, P],
+        "hbl_fp4_weight_bytes": [I64, I64, PSZ],
+        "hbl_pack_fp4": [P, I64, I64, P, P],
+        "hbl_fp6_codes_bytes": [I64, I64, PSZ],
+        "hbl_quantize_activations_fp6": [P, I32, I64, I64, P, PCFG, P, P, P],
+        "hbl_gemm_fp6fp4": [P, P, I64, I64, P, P, I64, P, I32, P],
+        "hbl_forward_fp4_workspace_bytes": [I64, I64, PCFG, PSZ],
+        "hbl_forward_fp4": [P, I32, I64, I64, P, P, P, I64, PCFG, P, I32, P, SZ, P],
     }
     for name, argtypes in sigs.items():
         f = getattr(lib, name)
@@ -452,4 +461,91 @@ def hbl_forward_base3(X, W3, alpha, N: int, cfg: Config, y_dtype=None, gain=None
     _check("hbl_forward_base3", lib.hbl_forward_base3(_ptr(X), _dtype_code(X), M, K, _ptr(gain), _ptr(W3),
                                                       _ptr(alpha), N, ctypes.byref(c), _ptr(Y), _dtype_code(Y),
                                                       _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return Y
+
+
+# ------------------------------------------ FP4 weights and FP6 codes (INT4) --
+def hbl_fp4_weight_bytes(N: int, K: int) -> int:
+    return _size_out(load_library().hbl_fp4_weight_bytes, N, K)
+
+
+def hbl_fp6_codes_bytes(M: int, K: int) -> int:
+    return _size_out(load_library().hbl_fp6_codes_bytes, M, K)
+
+
+def hbl_forward_fp4_workspace_bytes(M: int, K: int, cfg: Config) -> int:
+    c = cfg.c()
+    return _size_out(load_library().hbl_forward_fp4_workspace_bytes, M, K, ctypes.byref(c))
+
+
+def hbl_pack_fp4(W_packed, K: int, W4=None, stream=None):
+    """2-bit packed ternary weights [N][K/4] -> FP4 E2M1 weights uint8 [N][K/2]."""
+    torch = _torch()
+    lib = load_library()
+    _dev(W_packed, "W_packed")
+    N = W_packed.shape[0]
+    if W4 is None:
+        W4 = torch.empty((N, K // 2), dtype=torch.uint8, device=W_packed.device)
+    _dev(W4, "W4")
+    _fits(W_packed, N * K // 4, "W_packed"); _fits(W4, N * K // 2, "W4")
+    _check("hbl_pack_fp4", lib.hbl_pack_fp4(_ptr(W_packed), N, K, _ptr(W4), _stream(stream)))
+    return W4
+
+
+def hbl_quantize_activations_fp6(X, cfg: Config, gain=None, codes6=None, xscale=None, stream=None):
+    """INT4 activation codes of X [M][K] as FP6 (the FP6 x FP4 GEMM's operand
+    order).  Returns (codes6 uint8 [M][K*3/4], xscale float32 [M])."""
+    torch = _torch()
+    lib = load_library()
+    _dev(X, "X"); _dev(gain, "gain")
+    M, K = X.shape
+    if codes6 is None:
+        codes6 = torch.empty((M, K * 3 // 4), dtype=torch.uint8, device=X.device)
+    if xscale is None:
+        xscale = torch.empty(M, dtype=torch.float32, device=X.device)
+    _dev(codes6, "codes6"); _dev(xscale, "xscale")
+    _fits(codes6, M * K * 3 // 4, "codes6"); _fits(xscale, 4 * M, "xscale"); _fits(gain, 4 * K, "gain")
+    c = cfg.c()
+    _check("hbl_quantize_activations_fp6",
+           lib.hbl_quantize_activations_fp6(_ptr(X), _dtype_code(X), M, K, _ptr(gain), ctypes.byref(c), _ptr(codes6),
+                                            _ptr(xscale), _stream(stream)))
+    return codes6, xscale
+
+
+def hbl_gemm_fp6fp4(codes6, xscale, K: int, W4, alpha, N: int, y_dtype=None, Y=None, stream=None):
+    """FP6 codes x FP4 weights on the FP6 x FP4 matrix cores with the rescale
+    epilogue.  Returns Y [M][N]."""
+    torch = _torch()
+    lib = load_library()
+    for t, n in ((codes6, "codes6"), (xscale, "xscale"), (W4, "W4"), (alpha, "alpha")):
+        _dev(t, n)
+    M = codes6.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=y_dtype or torch.float32, device=codes6.device)
+    _dev(Y, "Y")
+    _fits(codes6, M * K * 3 // 4, "codes6"); _fits(xscale, 4 * M, "xscale")
+    _fits(W4, N * K // 2, "W4"); _fits(alpha, 4, "alpha"); _fits(Y, M * N * _esize(Y), "Y")
+    _check("hbl_gemm_fp6fp4", lib.hbl_gemm_fp6fp4(_ptr(codes6), _ptr(xscale), M, K, _ptr(W4), _ptr(alpha), N,
+                                                  _ptr(Y), _dtype_code(Y), _stream(stream)))
+    return Y
+
+
+def hbl_forward_fp4(X, W4, alpha, N: int, cfg: Config, y_dtype=None, gain=None, Y=None, ws=None, stream=None):
+    """The INT4 forward of X [M][K] against FP4 weights (FP6 x FP4 matrix
+    cores).  Bit for bit hbl_forward on the same ternary values.  Returns Y."""
+    torch = _torch()
+    lib = load_library()
+    _dev(X, "X"); _dev(W4, "W4"); _dev(alpha, "alpha"); _dev(gain, "gain")
+    M, K = X.shape
+    if Y is None:
+        Y = torch.empty((M, N), dtype=y_dtype or X.dtype, device=X.device)
+    if ws is None:
+        ws = torch.empty(max(1, hbl_forward_fp4_workspace_bytes(M, K, cfg)), dtype=torch.uint8, device=X.device)
+    _dev(Y, "Y"); _dev(ws, "ws")
+    _fits(W4, N * K // 2, "W4"); _fits(alpha, 4, "alpha"); _fits(gain, 4 * K, "gain")
+    _fits(Y, M * N * _esize(Y), "Y")
+    c = cfg.c()
+    _check("hbl_forward_fp4", lib.hbl_forward_fp4(_ptr(X), _dtype_code(X), M, K, _ptr(gain), _ptr(W4), _ptr(alpha),
+                                                  N, ctypes.byref(c), _ptr(Y), _dtype_code(Y), _ptr(ws),
+                                                  ws.numel() * ws.element_size(), _stream(stream)))
     return Y

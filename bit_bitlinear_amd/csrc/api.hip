@@ -345,6 +345,110 @@ hbl_status hbl_forward_latent(const void* X, int32_t x_dtype, int64_t M, int64_t
     return e == hipSuccess ? HBL_OK : hip_fail(e);
 }
 
+// ------------------------------------------------ FP4 weights, FP6 codes --
+// The INT4 prefill path on the FP6 x FP4 matrix cores with the weights
+// converted to FP4 once, ahead of the forward passes.
+
+static hbl_status check_fp6_act(int64_t M, int64_t K, const hbl_config* cfg) {
+    hbl_status st = check_config(cfg);
+    if (st != HBL_OK) return st;
+    if (cfg->act_bits != 4) return HBL_ERR_BITS;
+    if ((st = check_act_shape(M, K)) != HBL_OK) return st;
+    if (K < 512) return HBL_ERR_SHAPE;  // whole FP6 operand pieces per row
+    return HBL_OK;
+}
+
+static hbl_status check_fp6_gemm(int64_t M, int64_t K, int64_t N) {
+    hbl_status st = check_gemm_shape(M, K, N);
+    if (st != HBL_OK) return st;
+    if (K < 512) return HBL_ERR_SHAPE;
+    return HBL_OK;
+}
+
+static size_t fp6_codes_bytes(int64_t M, int64_t K) { return (size_t)M * (size_t)K * 3 / 4; }
+
+hbl_status hbl_fp4_weight_bytes(int64_t N, int64_t K, size_t* bytes) {
+    if (!bytes) return HBL_ERR_NULL;
+    const hbl_status st = check_weight_shape(N, K);
+    if (st != HBL_OK) return st;
+    *bytes = (size_t)N * (size_t)(K / 2);
+    return HBL_OK;
+}
+
+hbl_status hbl_pack_fp4(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W4, void* stream) {
+    const hbl_status st = check_weight_shape(N, K);
+    if (st != HBL_OK) return st;
+    if (!W_packed || !W4) return HBL_ERR_NULL;
+    if (!aligned16(W_packed) || !aligned16(W4)) return HBL_ERR_ALIGN;
+    const hipError_t e = hbl::launch_weights_to_fp4(W_packed, N, K, W4, (hipStream_t)stream);
+    return e == hipSuccess ? HBL_OK : hip_fail(e);
+}
+
+hbl_status hbl_fp6_codes_bytes(int64_t M, int64_t K, size_t* bytes) {
+    if (!bytes) return HBL_ERR_NULL;
+    if (M < 0 || M > kMaxRows || K < 512 || K > HBL_MAX_K) return HBL_ERR_SHAPE;
+    if (K % 128) return HBL_ERR_ALIGN;
+    *bytes = fp6_codes_bytes(M, K);
+    return HBL_OK;
+}
+
+hbl_status hbl_quantize_activations_fp6(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
+                                        const hbl_config* cfg, uint8_t* codes6, float* xscale, void* stream) {
+    hbl_status st = check_fp6_act(M, K, cfg);
+    if (st != HBL_OK) return st;
+    if (!dtype_ok(x_dtype)) return HBL_ERR_DTYPE;
+    if (M == 0) return HBL_OK;
+    if (!X || !codes6 || !xscale) return HBL_ERR_NULL;
+    if (!aligned16(X) || !aligned16(codes6) || !aligned(xscale, 4) || !aligned(gain, 4)) return HBL_ERR_ALIGN;
+    const hipError_t e = hbl::launch_act_quant(X, x_dtype, M, K, gain, *cfg, codes6, xscale, nullptr, nullptr,
+                                               (hipStream_t)stream, hbl::kCodesFp6);
+    return e == hipSuccess ? HBL_OK : hip_fail(e);
+}
+
+hbl_status hbl_gemm_fp6fp4(const uint8_t* codes6, const float* xscale, int64_t M, int64_t K, const uint8_t* W4,
+                           const float* alpha, int64_t N, void* Y, int32_t y_dtype, void* stream) {
+    if (!dtype_ok(y_dtype)) return HBL_ERR_DTYPE;
+    const hbl_status st = check_fp6_gemm(M, K, N);
+    if (st != HBL_OK) return st;
+    if (M == 0) return HBL_OK;
+    if (!codes6 || !xscale || !W4 || !alpha || !Y) return HBL_ERR_NULL;
+    if (!aligned16(codes6) || !aligned(xscale, 4) || !aligned16(W4) || !aligned(alpha, 4) || !aligned16(Y))
+        return HBL_ERR_ALIGN;
+    const hipError_t e = hbl::launch_gemm_f6f4(codes6, xscale, M, K, W4, alpha, N, Y, y_dtype, (hipStream_t)stream);
+    return e == hipSuccess ? HBL_OK : hip_fail(e);
+}
+
+hbl_status hbl_forward_fp4_workspace_bytes(int64_t M, int64_t K, const hbl_config* cfg, size_t* bytes) {
+    if (!bytes) return HBL_ERR_NULL;
+    const hbl_status st = check_fp6_act(M, K, cfg);
+    if (st != HBL_OK) return st;
+    *bytes = round_up(fp6_codes_bytes(M, K), 256) + round_up((size_t)M * sizeof(float), 256);
+    return HBL_OK;
+}
+
+hbl_status hbl_forward_fp4(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
+                           const uint8_t* W4, const float* alpha, int64_t N, const hbl_config* cfg, void* Y,
+                           int32_t y_dtype, void* ws, size_t ws_bytes, void* stream) {
+    hbl_status st = check_fp6_act(M, K, cfg);
+    if (st != HBL_OK) return st;
+    if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return HBL_ERR_DTYPE;
+    if ((st = check_fp6_gemm(M, K, N)) != HBL_OK) return st;
+    if (M == 0) return HBL_OK;
+    if (!X || !W4 || !alpha || !Y || !ws) return HBL_ERR_NULL;
+    if (!aligned16(X) || !aligned16(W4) || !aligned(alpha, 4) || !aligned16(Y) || !aligned16(ws) ||
+        !aligned(gain, 4))
+        return HBL_ERR_ALIGN;
+    const size_t cb = round_up(fp6_codes_bytes(M, K), 256);
+    if (ws_bytes < cb + round_up((size_t)M * sizeof(float), 256)) return HBL_ERR_WORKSPACE;
+    const hipStream_t s = (hipStream_t)stream;
+    uint8_t* codes6 = (uint8_t*)ws;
+    float* xs = (float*)(codes6 + cb);
+    hipError_t e = hbl::launch_act_quant(X, x_dtype, M, K, gain, *cfg, codes6, xs, nullptr, nullptr, s,
+                                         hbl::kCodesFp6);
+    if (e == hipSuccess) e = hbl::launch_gemm_f6f4(codes6, xs, M, K, W4, alpha, N, Y, y_dtype, s);
+    return e == hipSuccess ? HBL_OK : hip_fail(e);
+}
+
 hbl_status hbl_base3_weight_bytes(int64_t N, int64_t K, size_t* bytes) {
     if (!bytes) return HBL_ERR_NULL;
     const hbl_status st = check_weight_shape(N, K);

@@ -200,6 +200,48 @@ hbl_status hbl_forward_latent(const void* X, int32_t x_dtype, int64_t M, int64_t
                               size_t ws_bytes, void* wws, size_t wws_bytes, void* stream);
 
 /*
+ * INT4 prefill on the gfx950 FP6 x FP4 matrix cores with the weights held in
+ * FP4 (the hardware-format reading of the pages' remark that 4-bit
+ * activations suit native low-bit compute for batched inference, "新智元: 微软
+ * BitNet v2" repost, section "原生4比特盘算").  Every INT4 code [-8, 7] is exact
+ * in FP6 E3M2 and every ternary weight in FP4 E2M1; |acc| <= 8*K <= 2^18, so
+ * the fp32 sums are exact integers and Y is the same bit for bit as
+ * hbl_forward's with INT4 codes.
+ *
+ * FP4 weight format (library definition): W4 uint8 [N][K/2]; weight k of row n
+ * sits in byte k/2, low nibble for even k, as E2M1: 0 -> 0x0, +1 -> 0x2,
+ * -1 -> 0xA.  hbl_fp4_weight_bytes: N*K/2 (constraints as
+ * hbl_packed_weight_bytes).  hbl_pack_fp4: W_packed (the 2-bit layout of
+ * hbl_quantize_weights) -> W4, the same ternary values; a deployment converts
+ * once per weight.  Both buffers 16-byte aligned.
+ *
+ * FP6 codes: uint8 [M][K*3/4] (hbl_fp6_codes_bytes), the INT4 codes of
+ * hbl_quantize_activations as E3M2 fields in the operand order of the
+ * FP6 x FP4 GEMM; the order inside a row is private to this library and read
+ * only by hbl_gemm_fp6fp4.  hbl_quantize_activations_fp6 writes them (same
+ * computation and xscale as hbl_quantize_activations with cfg->act_bits = 4,
+ * which it requires; K a power of two in [512, 32768]).
+ * hbl_gemm_fp6fp4: Y = fp32(fp32(acc * xscale[m]) * alpha), fp32 or bf16, from
+ * FP6 codes and FP4 weights; K in [512, 32768], K % 128 == 0, N in [16, 2^20],
+ * N % 16 == 0, 0 <= M <= 2^23 (M == 0 queues nothing).
+ * hbl_forward_fp4: hbl_quantize_activations_fp6 into the workspace
+ * (hbl_forward_fp4_workspace_bytes: the FP6 codes, then xscale, each region
+ * 256-byte aligned), then hbl_gemm_fp6fp4; bit for bit hbl_forward with the
+ * same config on the same ternary values.  Constraints: those of both.
+ */
+hbl_status hbl_fp4_weight_bytes(int64_t N, int64_t K, size_t* bytes);
+hbl_status hbl_pack_fp4(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W4, void* stream);
+hbl_status hbl_fp6_codes_bytes(int64_t M, int64_t K, size_t* bytes);
+hbl_status hbl_quantize_activations_fp6(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
+                                        const hbl_config* cfg, uint8_t* codes6, float* xscale, void* stream);
+hbl_status hbl_gemm_fp6fp4(const uint8_t* codes6, const float* xscale, int64_t M, int64_t K, const uint8_t* W4,
+                           const float* alpha, int64_t N, void* Y, int32_t y_dtype, void* stream);
+hbl_status hbl_forward_fp4_workspace_bytes(int64_t M, int64_t K, const hbl_config* cfg, size_t* bytes);
+hbl_status hbl_forward_fp4(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
+                           const uint8_t* W4, const float* alpha, int64_t N, const hbl_config* cfg, void* Y,
+                           int32_t y_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Low-bit attention states, beside the layer ("新智元: 微软 BitNet v2" repost,
  * section "实验结果": after RoPE the Q, K and V heads are quantised directly to
  * unsigned integers by absmax, with no calibration; a 3-bit KV cache keeps

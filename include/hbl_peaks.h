@@ -31,6 +31,18 @@ enum {
  * of HBM traffic (read + write). */
 int hbl_peak_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
+/* Streaming read of `bytes` (a multiple of 16, > 0) from src (16-byte
+ * aligned), 16 bytes per lane and load, four loads per thread; nothing is
+ * written unless the data's folded words hit a fixed value, so the traffic
+ * is the read alone.  sink (device, sink_len 32-bit words) must hold
+ * hbl_peak_read_sink_len(bytes) words. */
+int hbl_peak_read(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_len, void* stream);
+int64_t hbl_peak_read_sink_len(int64_t bytes);
+
+/* An empty kernel of `blocks` workgroups of 256 threads (blocks in
+ * [1, 2^20]): the fixed cost of one launch. */
+int hbl_peak_empty(int blocks, void* stream);
+
 /* `blocks` workgroups of 256 threads (4 waves); every wave issues `iters`
  * rounds of four independent instructions of kind `kind` on register
  * operands, then writes one 32-bit value per thread to out[0 .. blocks*256)

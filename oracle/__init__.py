@@ -99,6 +99,8 @@ def _load():
     lib.hbo_pack_base3.restype = I
     lib.hbo_unpack_base3.argtypes = [P, I64, I64, P]
     lib.hbo_unpack_base3.restype = I
+    lib.hbo_pack_fp4.argtypes = [P, I64, I64, P]
+    lib.hbo_pack_fp4.restype = I
     _lib = lib
     return lib
 
@@ -382,4 +384,14 @@ def unpack_base3(W3: np.ndarray, K: int) -> np.ndarray:
         raise ValueError("row length does not match K")
     out = np.empty((N, K), np.int8)
     _check(_load().hbo_unpack_base3(_ptr(W3), N, K, _ptr(out)), "unpack_base3")
+    return out
+
+
+# ---------------------------------------------------------------- O14 ------
+def pack_fp4(Wq: np.ndarray) -> np.ndarray:
+    """O14: ternary int8 [N][K] -> FP4 E2M1 weights uint8 [N][K/2] (low nibble = even k)."""
+    Wq = _c(Wq, np.int8)
+    N, K = Wq.shape
+    out = np.empty((N, K // 2), np.uint8)
+    _check(_load().hbo_pack_fp4(_ptr(Wq), N, K, _ptr(out)), "pack_fp4")
     return out

@@ -31,6 +31,8 @@
  *               to unsigned b-bit integers (b = 3, 4, 8)   ([XZY] 实验结果)
  *   O12 the layer's straight-through backward: dX through H and the norm, dW
  *   O13 base-3 weight storage: five ternary weights per byte   ([CSDN] 掩码存储)
+ *   O14 FP4 weight storage: one ternary weight per 4-bit E2M1 code (the
+ *       format of the FP6 x FP4 prefill path; [XZY] 原生4比特盘算)
  *
  * Rounding is round-half-to-even (rint under the default FP environment)
  * everywhere.  No step is fused, blocked or reordered beyond these definitions.
@@ -606,6 +608,33 @@ int hbo_unpack_base3(const uint8_t* in, int64_t N, int64_t K, int8_t* Wq) {
                 if (k < K) Wq[n * K + k] = (int8_t)t;
                 else if (t != 0) return HBO_ERR;
             }
+        }
+    return HBO_OK;
+}
+
+/* --------------------------------------------------------------- O14 ---- */
+/* FP4 weight storage for the INT4 prefill path on FP6 x FP4 matrix hardware
+ * ([XZY] "原生4比特盘算": 4-bit activations suit native low-bit compute; the
+ * format is the library's own).  W4 [N][K/2]: weight k of row n in byte k/2,
+ * the low nibble for even k.  The nibble is the E2M1 encoding of the ternary
+ * value: sign in bit 3, a 2-bit exponent with bias 1 in bits 2..1, one
+ * mantissa bit in bit 0; so 0 -> 0000, +1.0 -> 0010 (exponent 1, mantissa
+ * 0), -1.0 -> 1010.  Requires K even. */
+int hbo_pack_fp4(const int8_t* Wq, int64_t N, int64_t K, uint8_t* W4) {
+    if (N < 0 || K < 2 || K % 2) return HBO_ERR;
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k += 2) {
+            uint8_t b = 0;
+            for (int h = 0; h < 2; h++) {
+                const int t = Wq[n * K + k + h];
+                uint8_t code;
+                if (t == 0) code = 0x0;
+                else if (t == 1) code = 0x2;
+                else if (t == -1) code = 0xA;
+                else return HBO_ERR;
+                b |= (uint8_t)(code << (4 * h));
+            }
+            W4[n * (K / 2) + k / 2] = b;
         }
     return HBO_OK;
 }

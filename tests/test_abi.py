@@ -20,7 +20,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = hbl.declared_symbols()
-    assert len(names) == 18
+    assert len(names) == 25
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
 
@@ -240,6 +240,10 @@ def _peaks_lib():
                                   ctypes.c_void_p]
     lib.hbl_peak_mfma_ops.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     lib.hbl_peak_mfma_ops.restype = ctypes.c_int64
+    lib.hbl_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.hbl_peak_read_sink_len.argtypes = [ctypes.c_int64]
+    lib.hbl_peak_read_sink_len.restype = ctypes.c_int64
+    lib.hbl_peak_empty.argtypes = [ctypes.c_int32, ctypes.c_void_p]
     return lib
 
 
@@ -250,7 +254,8 @@ def test_peaks_library_exports_and_host_checks():
     import os
     lib = _peaks_lib()
     names = hbl.declared_symbols(os.path.join(os.path.dirname(hbl.HEADER_PATH), "hbl_peaks.h"))
-    assert names == ["hbl_peak_copy", "hbl_peak_mfma", "hbl_peak_mfma_ops"]
+    assert names == ["hbl_peak_copy", "hbl_peak_empty", "hbl_peak_mfma", "hbl_peak_mfma_ops", "hbl_peak_read",
+                     "hbl_peak_read_sink_len"]
     assert all(hasattr(lib, n) for n in names)
     # 4 waves x 4 instructions per round: i8 32x32x32, FP6 x FP4 32x32x64, bf16 32x32x16
     assert lib.hbl_peak_mfma_ops(0, 1, 1) == 16 * 2 * 32 * 32 * 32
@@ -266,3 +271,50 @@ def test_peaks_library_exports_and_host_checks():
     assert lib.hbl_peak_copy(None, 4096, 16, None) == 1              # null
     assert lib.hbl_peak_copy(24, 4096, 16, None) == 1                # misaligned
     assert lib.hbl_peak_copy(16, 4096, 0, None) == 0                 # nothing to do
+    assert lib.hbl_peak_read_sink_len(8 << 20) == (8 << 20) // 16 // 1024 * 256
+    assert lib.hbl_peak_read_sink_len(17) == -1
+    assert lib.hbl_peak_read(16, 4096, 32, 255, None) == 1           # sink too short (one block of 256)
+    assert lib.hbl_peak_read(24, 4096, 32, 256, None) == 1           # misaligned
+    assert lib.hbl_peak_read(16, 0, 32, 256, None) == 1              # nothing to read
+    assert lib.hbl_peak_empty(0, None) == 1 and lib.hbl_peak_empty((1 << 20) + 1, None) == 1
+
+
+def test_fp4_fp6_validation(lib):
+    """The FP4-weight INT4 path: size queries, weight conversion, FP6 codes,
+    the FP6 x FP4 GEMM and the forward reject bad arguments on the host."""
+    c4, c8 = hbl.Config(act_bits=4), hbl.Config(act_bits=8)
+    assert hbl.hbl_fp4_weight_bytes(4096, 16384) == 4096 * 8192
+    assert hbl.hbl_fp6_codes_bytes(8192, 16384) == 8192 * 12288
+    assert hbl.hbl_forward_fp4_workspace_bytes(8192, 16384, c4) >= 8192 * 12288 + 8192 * 4
+    with pytest.raises(hbl.HblError) as e:
+        hbl.hbl_forward_fp4_workspace_bytes(8192, 16384, c8)           # INT8 codes have no FP6 form
+    assert e.value.status == 6
+    with pytest.raises(hbl.HblError) as e:
+        hbl.hbl_forward_fp4_workspace_bytes(8, 256, c4)                # K < 512
+    assert e.value.status == 2
+    with pytest.raises(hbl.HblError) as e:
+        hbl.hbl_fp6_codes_bytes(8, 576)                                # K % 128
+    assert e.value.status == 4
+    assert lib.hbl_pack_fp4(None, 16, 64, A16b, None) == 1
+    assert lib.hbl_pack_fp4(A16, 16, 40, A16b, None) == 4
+    assert lib.hbl_pack_fp4(MIS, 16, 64, A16b, None) == 4
+    cc4, cc8 = c4.c(), c8.c()
+    q6 = lib.hbl_quantize_activations_fp6
+    assert q6(A16, 0, 8, 1024, None, ctypes.byref(cc8), A16b, A16b, None) == 6
+    assert q6(A16, 0, 8, 256, None, ctypes.byref(cc4), A16b, A16b, None) == 2
+    assert q6(A16, 0, 8, 1536, None, ctypes.byref(cc4), A16b, A16b, None) == 3
+    assert q6(A16, 3, 8, 1024, None, ctypes.byref(cc4), A16b, A16b, None) == 5
+    assert q6(None, 0, 8, 1024, None, ctypes.byref(cc4), A16b, A16b, None) == 1
+    assert q6(A16, 0, 0, 1024, None, ctypes.byref(cc4), None, None, None) == 0   # M = 0 queues nothing
+    g = lib.hbl_gemm_fp6fp4
+    assert g(A16, A16b, 8, 384, A16b, A16b, 64, A16b, 0, None) == 2              # K < 512
+    assert g(A16, A16b, 8, 576, A16b, A16b, 64, A16b, 0, None) == 4              # K % 128
+    assert g(A16, A16b, 8, 1024, A16b, A16b, 40, A16b, 0, None) == 4             # N % 16
+    assert g(A16, A16b, 8, 1024, A16b, A16b, 64, A16b, 9, None) == 5
+    assert g(A16, A16b, 8, 1024, MIS, A16b, 64, A16b, 0, None) == 4
+    assert g(None, A16b, 8, 1024, A16b, A16b, 64, A16b, 0, None) == 1
+    f = lib.hbl_forward_fp4
+    assert f(A16, 0, 8, 1024, None, A16b, A16b, 64, ctypes.byref(cc4), A16b, 0, A16b, 16, None) == 7
+    assert f(A16, 0, 8, 1024, None, A16b, A16b, 64, ctypes.byref(cc8), A16b, 0, A16b, 1 << 20, None) == 6
+    assert f(A16, 0, 8, 1024, None, None, A16b, 64, ctypes.byref(cc4), A16b, 0, A16b, 1 << 20, None) == 1
+    assert f(A16, 0, 8, 1024, None, A16b, A16b, 72, ctypes.byref(cc4), A16b, 0, A16b, 1 << 20, None) == 4

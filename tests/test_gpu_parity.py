@@ -477,6 +477,7 @@ def test_forward_latent_f6f4_matches_two_calls(M, K, N, xdt, wdt):
 # alpha must equal hbl_quantize_weights + hbl_forward bit for bit.
 LATENT_CASES = [
     # (M, K, N, bits, hadamard, x dtype, W dtype, y dtype)
+    (4096, 2048, 2048, 8, True, "bf16", "f32", "bf16"),   # the 1.3B Wo shape: shared grid, 8-wave GEMM
     (300, 2048, 2048, 8, True, "bf16", "f32", "bf16"),
     (37, 256, 272, 4, True, "f32", "f32", "f32"),
     (16, 8192, 4096, 4, True, "f32", "f32", "bf16"),
@@ -655,6 +656,42 @@ def test_backward_large_sampled(M, K, N, bits):
     qc = np.ascontiguousarray(q[:, cols])
     dW_ref = oracle.weight_grad(dY, qc, d)
     check_dw(to_host(dW)[:, cols], dY, qc, d, dW_ref, "dW")
+
+
+def test_backward_wdown_7b_sampled():
+    """The 7B Wdown backward shape the benchmark times (8192 x 16384 -> 4096,
+    INT4, bf16 dY): 24 sampled rows of dX against the oracle, 32 sampled
+    columns of dW against the oracle's weight gradient on the GPU's own codes
+    and factors (identical quantiser inputs; those codes are themselves
+    checked against the oracle on the sampled rows), with the M-dependent
+    bound of parity.dw_tolerance (8192 tokens: about 5 * 2^-16)."""
+    layer = workloads.WDOWN_7B
+    M, K, N, bits = layer.M, layer.K, layer.N, layer.act_bits
+    _announce("backward wdown_7b M=%d K=%d N=%d a%d" % (M, K, N, bits))
+    X, W, _ = workloads.make_inputs(layer, 0)
+    rng = np.random.default_rng(11)
+    dY = workloads.f32_to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    cfg = hbl.Config(act_bits=bits, hadamard=layer.hadamard)
+    Wp, alpha = hbl.hbl_quantize_weights(to_dev(W))
+    Xd = to_dev(X)
+    dX, dW = hbl.hbl_backward(to_dev(dY), Xd, Wp, alpha, cfg)
+    codes, xs, _, _ = hbl.hbl_quantize_activations(Xd, cfg)
+    _sync()
+    rows = workloads.sample_rows(M, 24)
+    cols = np.unique(np.concatenate([np.arange(4), K - 4 + np.arange(4), rng.choice(K, 24, replace=False)]))
+    a = to_host(alpha)[0]
+    Wq = oracle.unpack_ternary(to_host(Wp), K)
+    dX_rows = to_host(dX)[rows].astype(np.float64)
+    dW_cols = np.ascontiguousarray(to_host(dW)[:, cols])
+    q_gpu = unpack_codes(to_host(codes), K, bits)
+    d_gpu = to_host(xs)
+    del dX, dW, Xd
+    dX_ref, _ = oracle.backward(dY[rows], X[rows], Wq, a, bits=bits, hadamard=layer.hadamard, want_dW=False)
+    assert _rowwise_close(dX_rows, dX_ref, 2e-5)
+    ref = oracle.quantize_activations(X[rows], bits=bits, hadamard=layer.hadamard)
+    check_codes_end_to_end(q_gpu[rows], ref["z"], ref["s"], ref["q"], "backward codes")
+    qc = np.ascontiguousarray(q_gpu[:, cols])
+    check_dw(dW_cols, dY, qc, d_gpu, oracle.weight_grad(dY, qc, d_gpu), "dW 7B")
 
 
 def test_backward_dx_only_and_empty():

@@ -84,6 +84,8 @@ MUTANTS = [
     ("rescale_single_fp64_product",
      "float t = (float)acc[m * N + n] * d[m];\n            y[m * N + n] = t * alpha;",
      "double t = (double)acc[m * N + n] * (double)d[m];\n            y[m * N + n] = (float)(t * (double)alpha);"),
+    ("fp4_nibbles_swapped", "b |= (uint8_t)(code << (4 * h));", "b |= (uint8_t)(code << (4 * (1 - h)));"),
+    ("fp4_minus_one_code", "else if (t == -1) code = 0xA;", "else if (t == -1) code = 0x6;"),
     ("act_scale_overflow_kept", "if (isinf(s)) { *s_out = 0.0f; *d_out = 0.0f; return HBO_OK; }", ""),
 ]
 

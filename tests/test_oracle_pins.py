@@ -657,3 +657,38 @@ def test_base3_rejects_bad_input():
     bad[0, 3] = 124        # digits 1,2,1,1,1: k = 15 is 0, the padding weight k = 16 is +1
     with pytest.raises(ValueError):
         oracle.unpack_base3(bad, 16)
+
+
+# ------------------------------------------------------------- FP4 (O14) ----
+def _e2m1_value(nib):
+    """Value of a 4-bit E2M1 code from the format's definition (sign bit 3,
+    exponent bits 2..1 with bias 1, mantissa bit 0; exponent 0 is subnormal)."""
+    sign = -1.0 if nib & 8 else 1.0
+    e, m = (nib >> 1) & 3, nib & 1
+    return sign * (0.5 * m if e == 0 else 2.0 ** (e - 1) * (1 + 0.5 * m))
+
+
+def test_pack_fp4_golden():
+    path = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden", "pack_fp4_k8.txt")
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if "=" in line:
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.split()
+    wq = np.array([[int(t) for t in vals["weights"]]], np.int8)
+    assert oracle.pack_fp4(wq).tolist() == [[int(b, 16) for b in vals["bytes"]]]
+
+
+def test_pack_fp4_decodes_to_the_ternary_values():
+    """Every nibble decodes (E2M1 definition) to its weight, at every position,
+    and the low nibble holds the even k."""
+    rng = np.random.default_rng(41)
+    wq = rng.integers(-1, 2, size=(7, 96)).astype(np.int8)
+    p = oracle.pack_fp4(wq)
+    dec = np.array([[_e2m1_value((p[n, k // 2] >> (4 * (k % 2))) & 15) for k in range(96)] for n in range(7)])
+    assert np.array_equal(dec, wq.astype(np.float64))
+    one = np.zeros((1, 16), np.int8)
+    one[0, 5] = -1
+    assert oracle.pack_fp4(one)[0].tolist() == [0, 0, 0xA0, 0, 0, 0, 0, 0]
