@@ -45,6 +45,11 @@ DECODE_W_BYTES = 8 << 20       # 2-bit weights of the 8192 x 4096 decode layer
 _PEAKS = None
 
 
+def log(msg):
+    """Progress of the run on stderr (stdout carries only the JSON line)."""
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -90,6 +95,9 @@ def measured_peaks():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def cur():
+        return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
     def best_us(launch, reps=5):
         launch()
@@ -138,15 +146,16 @@ def measured_peaks():
         slices = nbytes // size
         sink = torch.empty(lib.hbl_peak_read_sink_len(size), dtype=torch.int32, device=dev)
         base = src.data_ptr()
+        # the stream is read at call time: inside a graph capture it is the capture stream
         launches = [lambda i=i: ok(lib.hbl_peak_read(ctypes.c_void_p(base + i * size), size,
-                                                    ctypes.c_void_p(sink.data_ptr()), sink.numel(), sp), "read")
+                                                    ctypes.c_void_p(sink.data_ptr()), sink.numel(), cur()), "read")
                     for i in range(slices)]
         us = graph_best_us(launches)
         out[key] = round(size / (us * 1e-6) / 1e9, 1)
         out[key.replace("GBps", "us")] = round(us, 3)
         del sink
     del src
-    out["launch_floor_us"] = round(graph_best_us([lambda: ok(lib.hbl_peak_empty(256, sp), "empty")] * 64), 3)
+    out["launch_floor_us"] = round(graph_best_us([lambda: ok(lib.hbl_peak_empty(256, cur()), "empty")] * 64), 3)
     blocks, iters = 2048, 2000
     sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
     for kind, key in ((0, "mfma_i8_TOPS"), (1, "mfma_f6f4_TFLOPS"), (2, "mfma_bf16_TFLOPS")):
@@ -159,6 +168,7 @@ def measured_peaks():
                      "256-block kernel, graph-replayed; 2048 x 256-thread blocks each issuing 4 independent "
                      "matrix-core instructions per round on register operands")
     _PEAKS = out
+    log("measured peaks done")
     return out
 
 
@@ -262,8 +272,10 @@ class Prepared:
         Wp, alpha = hbl.hbl_quantize_weights(Wd, 1e-5, ws=self.wws)
         W4 = hbl.hbl_pack_fp4(Wp, L.K) if self.fp4 else None
         self.alpha = alpha
+        # the workspace of the fastest forward path (for 5 to 64 tokens it holds
+        # the K-split decode GEMM's partial sums)
         ws_bytes = (hbl.hbl_forward_fp4_workspace_bytes(L.M, L.K, self.cfg) if self.fp4
-                    else hbl.hbl_workspace_bytes(L.M, L.K, self.cfg))
+                    else hbl.hbl_forward_workspace_bytes(L.M, L.K, L.N, self.cfg))
         y_bytes = L.M * L.N * (2 if self.ydt == torch.bfloat16 else 4)
         w_bytes = L.N * L.K // 2 if self.fp4 else L.N * L.K // 4
         set_bytes = X.numel() * X.element_size() + w_bytes + ws_bytes + y_bytes
@@ -396,7 +408,10 @@ def bench_chain(args):
     hbl.load_library()
     layers = workloads.CHAIN_3B
     M = layers[0].M
-    preps = [Prepared(L, seed=i, rotate=False) for i, L in enumerate(layers)]
+    preps = []
+    for i, L in enumerate(layers):
+        preps.append(Prepared(L, seed=i, rotate=False))
+        log("inputs ready: %s" % L.desc)
     assert all(p.fp4 for p in preps)
     step_bytes = sum(p.set_bytes for p in preps)
     R = max(1, -(-ROTATE_BYTES // step_bytes))
@@ -414,6 +429,7 @@ def bench_chain(args):
     wall, ev_ms = replay_timed(graphs, args.steps)
     del graphs
     ms_per_step = wall / args.steps * 1e3
+    log("chain: %d steps timed, %.3f ms per step" % (args.steps, ms_per_step))
     ops_step = sum(2 * p.layer.M * p.layer.N * p.layer.K for p in preps)
 
     # per-kernel times inside eager steps: events around each stage launch
@@ -463,8 +479,11 @@ def bench_chain(args):
     del preps
     torch.cuda.empty_cache()
 
+    log("chain: per-kernel times and weight preparation done")
     subs = None if args.no_subresults else subresults(args)
     cpu = None if args.no_cpu_baseline else cpu_baseline_chain(layers)
+    if cpu:
+        log("cpu baseline done")
     out = {
         "metric": METRIC,
         "value": round(M * args.steps / wall, 1),
@@ -538,10 +557,15 @@ def subresults(args):
                                          PEAK_I8_TOPS, "mfma_i8_TOPS", committed_traffic("gemm_i8_mfma", L.name),
                                          "2*M*N*K integer ops")
             else:
-                r["roofline"] = roofline("decode GEMM (hbl_gemm, row-major codes)", "hbm", w["gemm_bytes"], gemm,
-                                         "GB/s", PEAK_HBM_GBS, "hbm_read_8MiB_GBps", None,
-                                         "read codes + xscale + 2-bit W, write Y")
+                # decode: hbl_forward = activation kernel, K-split GEMM, exact
+                # reduction; the bytes the forward must move against its time
+                r["roofline"] = roofline("hbl_forward (activation kernel + K-split GEMM + reduction)", "hbm",
+                                         w["fwd_small_bytes"], fwd, "GB/s", PEAK_HBM_GBS, "hbm_read_8MiB_GBps", None,
+                                         "read X + 2-bit W + alpha, write Y (codes and partial sums are "
+                                         "intermediate)")
+                r["gemm_single_pass_us"] = r.pop("gemm_us")
         out[L.name] = r
+        log("subresult %s: forward %.3f us" % (L.name, fwd))
         del p
         torch.cuda.empty_cache()
     return out
@@ -623,8 +647,10 @@ def bench_single(args, layer):
                             PEAK_I8_TOPS, "mfma_i8_TOPS", committed_traffic("gemm_i8_mfma", L.name),
                             "2*M*N*K integer ops")
         else:
-            roof = roofline("decode GEMM (hbl_gemm, row-major codes)", "hbm", w["gemm_bytes"], gemm, "GB/s",
-                            PEAK_HBM_GBS, "hbm_read_8MiB_GBps", None, "read codes + xscale + 2-bit W, write Y")
+            roof = roofline("hbl_forward (activation kernel + K-split GEMM + reduction)", "hbm",
+                            w["fwd_small_bytes"], fwd, "GB/s", PEAK_HBM_GBS, "hbm_read_8MiB_GBps", None,
+                            "read X + 2-bit W + alpha, write Y (codes and partial sums are intermediate)")
+            kern["gemm_single_pass_us"] = kern.pop("gemm_us")
     # the same layer from latent weights (ternarised in every step), for training-time callers
     lat = None
     if not p.fp4:
