@@ -272,8 +272,7 @@ class Prepared:
         Wp, alpha = hbl.hbl_quantize_weights(Wd, 1e-5, ws=self.wws)
         W4 = hbl.hbl_pack_fp4(Wp, L.K) if self.fp4 else None
         self.alpha = alpha
-        # the workspace of the fastest forward path (for 5 to 64 tokens it holds
-        # the K-split decode GEMM's partial sums)
+        # the workspace of the fastest forward path
         ws_bytes = (hbl.hbl_forward_fp4_workspace_bytes(L.M, L.K, self.cfg) if self.fp4
                     else hbl.hbl_forward_workspace_bytes(L.M, L.K, L.N, self.cfg))
         y_bytes = L.M * L.N * (2 if self.ydt == torch.bfloat16 else 4)
@@ -557,12 +556,12 @@ def subresults(args):
                                          PEAK_I8_TOPS, "mfma_i8_TOPS", committed_traffic("gemm_i8_mfma", L.name),
                                          "2*M*N*K integer ops")
             else:
-                # decode: hbl_forward = activation kernel, K-split GEMM, exact
-                # reduction; the bytes the forward must move against its time
-                r["roofline"] = roofline("hbl_forward (activation kernel + K-split GEMM + reduction)", "hbm",
+                # decode: hbl_forward = activation kernel (codes in the decode
+                # tile layout) + decode GEMM; the bytes the forward must move
+                # against its time
+                r["roofline"] = roofline("hbl_forward (activation kernel + decode GEMM)", "hbm",
                                          w["fwd_small_bytes"], fwd, "GB/s", PEAK_HBM_GBS, "hbm_read_8MiB_GBps", None,
-                                         "read X + 2-bit W + alpha, write Y (codes and partial sums are "
-                                         "intermediate)")
+                                         "read X + 2-bit W + alpha, write Y (the codes are intermediate)")
                 r["gemm_single_pass_us"] = r.pop("gemm_us")
         out[L.name] = r
         log("subresult %s: forward %.3f us" % (L.name, fwd))
@@ -647,9 +646,9 @@ def bench_single(args, layer):
                             PEAK_I8_TOPS, "mfma_i8_TOPS", committed_traffic("gemm_i8_mfma", L.name),
                             "2*M*N*K integer ops")
         else:
-            roof = roofline("hbl_forward (activation kernel + K-split GEMM + reduction)", "hbm",
+            roof = roofline("hbl_forward (activation kernel + decode GEMM)", "hbm",
                             w["fwd_small_bytes"], fwd, "GB/s", PEAK_HBM_GBS, "hbm_read_8MiB_GBps", None,
-                            "read X + 2-bit W + alpha, write Y (codes and partial sums are intermediate)")
+                            "read X + 2-bit W + alpha, write Y (the codes are intermediate)")
             kern["gemm_single_pass_us"] = kern.pop("gemm_us")
     # the same layer from latent weights (ternarised in every step), for training-time callers
     lat = None

@@ -87,16 +87,6 @@ size_t ws_codes_bytes(int64_t M, int64_t K, int32_t bits) {
     return round_up(codes_bytes(M <= 64 ? (M + 15) / 16 * 16 : M, K, bits), 256);
 }
 
-// Decode shapes (5 to 64 tokens) whose forward runs the K-split GEMM when the
-// workspace also holds its int32 partial sums (after the codes and scales).
-bool use_ksplit_shape(int64_t M, int64_t K, int64_t N, const hbl_config* cfg) {
-    return !hbl::forward_small_eligible(M, K) && hbl::gemm_ksplit_eligible(M, K, N, cfg->act_bits);
-}
-size_t ksplit_ws_bytes(int64_t M, int64_t K, int64_t N, int32_t bits) {
-    return ws_codes_bytes(M, K, bits) + round_up((size_t)M * sizeof(float), 256) +
-           round_up(hbl::ksplit_part_bytes(M, K, N, bits), 256);
-}
-
 }  // namespace
 
 extern "C" {
@@ -168,7 +158,6 @@ hbl_status hbl_forward_workspace_bytes(int64_t M, int64_t K, int64_t N, const hb
         const size_t f = f6f4_ws_bytes(M, K, N);
         if (f > *bytes) *bytes = f;
     }
-    if (use_ksplit_shape(M, K, N, cfg)) *bytes = ksplit_ws_bytes(M, K, N, cfg->act_bits);
     return HBL_OK;
 }
 
@@ -291,13 +280,6 @@ hbl_status hbl_forward(const void* X, int32_t x_dtype, int64_t M, int64_t K, con
     }
     void* codes = ws;
     float* xscale = (float*)((uint8_t*)ws + cb);
-    if (use_ksplit_shape(M, K, N, cfg) && ws_bytes >= ksplit_ws_bytes(M, K, N, cfg->act_bits)) {
-        int32_t* part = (int32_t*)((uint8_t*)xscale + round_up((size_t)M * sizeof(float), 256));
-        hipError_t e = hbl::launch_act_quant(X, x_dtype, M, K, gain, *cfg, codes, xscale, nullptr, nullptr, s);
-        if (e == hipSuccess)
-            e = hbl::launch_gemm_ksplit(codes, xscale, cfg->act_bits, M, K, W_packed, alpha, N, Y, y_dtype, part, s);
-        return e == hipSuccess ? HBL_OK : hip_fail(e);
-    }
     // codes that only the decode GEMM reads go out in its tile layout
     const bool tiled = hbl::gemm_uses_decode_kernel(M, K);
     hipError_t e = hbl::launch_act_quant(X, x_dtype, M, K, gain, *cfg, codes, xscale, nullptr, nullptr, s,

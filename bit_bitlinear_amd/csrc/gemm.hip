@@ -12,7 +12,6 @@
 // operands hold the same k set, so the k order inside an operand does not
 // matter to the result.
 #include "int_dot.h"
-#include "lds_attr.h"
 #include "lds_dma.h"
 
 namespace hbl {
@@ -406,143 +405,6 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_kernel(const uint8_t*
             const int64_t m = t * 16 + 4 * g + r;
             if (m < M && n < N) store_y<YT>(Y + m * N + n, rescale(sum >> Shift<BITS>::value, xscale[m], alpha));
         }
-    }
-}
-
-// ================================================= K-split decode GEMM ==
-// 5 to 64 tokens with a workspace for partial sums (hbl_forward with the
-// larger workspace).  The decode GEMM above gives every block 16 columns and
-// all of K, so every block re-reads all the codes from L2 (64 MiB of L2 reads
-// for 64 tokens x 8192 INT4 codes against 4096 columns).  Here a block takes
-// 64 columns and one of KS slices of K: it copies the codes of its slice
-// (Mp rows x K/KS codes) into LDS once (LDS-direct loads, 1 KiB per wave
-// instruction), streams its 64 weight rows of the slice into registers, and
-// four waves of 16 columns each run v_mfma_i32_16x16x64_i8 over all row
-// tiles.  The exact int32 partial sums go to the workspace; a second launch
-// adds the KS partials of each output in a fixed order (integer, exact),
-// then applies the rescale.  Code bytes read from L2 drop by 4x per column
-// (64 instead of 16 columns per block), against KS * M * N * 4 bytes of
-// partials written and read back.
-//
-// Per 256-k super-step ss and 64-k MFMA step d, lane (r = lane % 16,
-// g = lane / 16) supplies k in [256 ss + 64 g + 16 d, +16) for both operands
-// (any consistent assignment of k to the MFMA's slots gives the same sum):
-// its weight bytes for a super-step are one 16-byte load, and its codes 32
-// (INT4) or 64 (INT8) consecutive bytes.  LDS rows hold the codes of one token
-// row; 16-byte chunk c of row r is stored at chunk c ^ (r % 16), so the 16
-// rows of a row tile read at one logical chunk hit 16 different bank groups.
-constexpr int kKsCols = 64, kKsThreads = 256, kKsMaxLds = 128 * 1024;
-
-template <int BITS, int MT>
-__global__ __launch_bounds__(kKsThreads) void gemm_ksplit_kernel(const uint8_t* __restrict__ A, int64_t M, int64_t K,
-                                                                 const uint8_t* __restrict__ Wp, int64_t N,
-                                                                 int32_t* __restrict__ part, int KSL) {
-    extern __shared__ __attribute__((aligned(1024))) uint8_t lds_codes[];
-    constexpr int Mp = 16 * MT;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, g = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * kKsCols;
-    const int ks = blockIdx.y;
-    const int64_t k0 = (int64_t)ks * KSL;
-    const int64_t a_ld = K * BITS / 8;
-    const int RB = KSL * BITS / 8;  // code bytes of one row in this slice (>= 256)
-    const int cpr = RB / 16;        // 16-byte chunks per row
-    const int n_sup = KSL / 256;    // super-steps in the slice (<= 16)
-
-    // 1. codes of the slice -> LDS (rows past M load zeros)
-    const v4u a_desc = rsrc_words(A, M * a_ld);
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_codes;
-    const int n_inst = Mp * cpr / 64;  // 1 KiB wave instructions for the whole tile
-    for (int i = wave; i < n_inst; i += kKsThreads / 64) {
-        const int c_lin = i * 64 + lane;  // physical chunk index in LDS
-        const int row = c_lin / cpr, c = c_lin % cpr;
-        const uint32_t goff = (uint32_t)(row * a_ld + k0 * BITS / 8 + ((c ^ (row & 15)) * 16));
-        lds_dma16(a_desc, __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)(i * 1024)), goff);
-    }
-    // 2. this wave's 16 weight rows of the slice -> registers (one 16-byte vector per super-step)
-    const int64_t n = n0 + wave * 16 + l16;
-    const __amdgpu_buffer_rsrc_t w_rsrc = make_rsrc(Wp + n0 * (K / 4), (N - n0) * (K / 4));
-    uint4 wv[16];
-    const uint32_t w_lane = (uint32_t)((wave * 16 + l16) * (K / 4) + k0 / 4 + g * 16);
-#pragma unroll
-    for (int u = 0; u < 16; u++)
-        if (u < n_sup) wv[u] = buf_load16(w_rsrc, w_lane + (uint32_t)u * 64);
-    wait_vmcnt<0>();  // the codes have landed (and the weights: n_sup is not a compile-time count)
-    __syncthreads();
-
-    v4i acc[MT];
-#pragma unroll
-    for (int t = 0; t < MT; t++) acc[t] = v4i{0, 0, 0, 0};
-    constexpr int kAB = BITS == 8 ? 64 : 32;  // code bytes per lane and super-step
-#pragma unroll
-    for (int u = 0; u < 16; u++) {
-        if (u < n_sup) {
-            uint4 aq[MT][kAB / 16];
-#pragma unroll
-            for (int t = 0; t < MT; t++) {
-                const int row = 16 * t + l16;
-#pragma unroll
-                for (int v = 0; v < kAB / 16; v++) {
-                    const int c = (u * 256 * BITS / 8 + g * kAB) / 16 + v;  // logical chunk
-                    aq[t][v] = *reinterpret_cast<const uint4*>(lds_codes + row * RB + ((c ^ (row & 15)) * 16));
-                }
-            }
-#pragma unroll
-            for (int d = 0; d < 4; d++) {
-                const uint4 q = wv[u];
-                const v4i bw = unpack_w(d == 0 ? q.x : d == 1 ? q.y : d == 2 ? q.z : q.w);
-#pragma unroll
-                for (int t = 0; t < MT; t++) {
-                    v4i a;
-                    if constexpr (BITS == 8) {
-                        const uint4 x = aq[t][d];
-                        a = v4i{(int)x.x, (int)x.y, (int)x.z, (int)x.w};
-                    } else {
-                        const uint4 x = aq[t][d >> 1];
-                        a = (d & 1) ? unpack_a4(x.z, x.w) : unpack_a4(x.x, x.y);
-                    }
-                    acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bw, acc[t], 0, 0, 0);
-                }
-            }
-        }
-    }
-    // 3. partial sums (lane: column l16, rows 4 g + r of each row tile), rows < M only
-    if (n < N) {
-        int32_t* pp = part + (int64_t)ks * M * N + n;
-#pragma unroll
-        for (int t = 0; t < MT; t++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int64_t m = 16 * t + 4 * g + r;
-                if (m < M) pp[m * N] = acc[t][r];
-            }
-    }
-}
-
-// Adds the KS partials of 4 consecutive outputs (fixed order, exact), undoes
-// the operand scaling and applies the rescale.
-template <int BITS, typename YT>
-__global__ __launch_bounds__(256) void ksplit_reduce_kernel(const int32_t* __restrict__ part, int KS, int64_t M,
-                                                            int64_t N, const float* __restrict__ xscale,
-                                                            const float* __restrict__ alpha_p, YT* __restrict__ Y) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // group of 4 outputs
-    if (i >= M * N / 4) return;
-    const int64_t m = (4 * i) / N;
-    int4 s = *reinterpret_cast<const int4*>(part + 4 * i);
-    for (int k = 1; k < KS; k++) {
-        const int4 v = *reinterpret_cast<const int4*>(part + (int64_t)k * M * N + 4 * i);
-        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-    }
-    const float d = xscale[m], alpha = *alpha_p;
-    constexpr int sh = Shift<BITS>::value;
-    const float y0 = rescale(s.x >> sh, d, alpha), y1 = rescale(s.y >> sh, d, alpha);
-    const float y2 = rescale(s.z >> sh, d, alpha), y3 = rescale(s.w >> sh, d, alpha);
-    if constexpr (sizeof(YT) == 4) {
-        *reinterpret_cast<float4*>(Y + 4 * i) = make_float4(y0, y1, y2, y3);
-    } else {
-        const v2bf h01 = __builtin_convertvector((v2f){y0, y1}, v2bf);
-        const v2bf h23 = __builtin_convertvector((v2f){y2, y3}, v2bf);
-        *reinterpret_cast<uint2*>(Y + 4 * i) = make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
     }
 }
 
@@ -1000,67 +862,6 @@ hipError_t launch_weights_to_fp4(const uint8_t* W_packed, int64_t N, int64_t K, 
     hipLaunchKernelGGL(weights_to_fp4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint32_t*)W_packed,
                        n_words, (uint2*)W4);
     return hipGetLastError();
-}
-
-// K-split decode GEMM: slices of K/KS with KS the smallest power of two >= 4
-// that keeps a slice's codes (16-row-padded) within 128 KiB of LDS and each
-// slice a whole number of 256-k super-steps (at most 16 of them).
-static int ksplit_count(int64_t M, int64_t K, int act_bits) {
-    const int64_t Mp = (M + 15) / 16 * 16;
-    for (int ks = 4; ks <= 64; ks *= 2) {
-        if (K % ((int64_t)ks * 256) != 0) return 0;
-        const int64_t ksl = K / ks;
-        if (ksl / 256 <= 16 && Mp * ksl * act_bits / 8 <= kKsMaxLds && ksl * act_bits / 8 >= 256) return ks;
-    }
-    return 0;
-}
-
-bool gemm_ksplit_eligible(int64_t M, int64_t K, int64_t N, int act_bits) {
-    return M >= 5 && M <= 64 && N % 4 == 0 && K > 0 && (K & (K - 1)) == 0 && ksplit_count(M, K, act_bits) > 0;
-}
-
-size_t ksplit_part_bytes(int64_t M, int64_t K, int64_t N, int act_bits) {
-    return (size_t)ksplit_count(M, K, act_bits) * (size_t)M * (size_t)N * 4;
-}
-
-template <int BITS>
-static hipError_t launch_ksplit_typed(const uint8_t* A, const float* xscale, int64_t M, int64_t K, const uint8_t* Wp,
-                               const float* alpha, int64_t N, void* Y, int y_dtype, int32_t* part, hipStream_t s) {
-    const int KS = ksplit_count(M, K, BITS);
-    const int KSL = (int)(K / KS);
-    const int mt = (int)((M + 15) / 16);
-    const size_t lds = (size_t)mt * 16 * KSL * BITS / 8;
-    const dim3 grid((unsigned)((N + kKsCols - 1) / kKsCols), (unsigned)KS);
-    // the kernel's dynamic LDS limit is raised to kKsMaxLds once per device
-    static std::atomic<uint32_t> lds_set[4] = {{0}, {0}, {0}, {0}};
-    auto go = [&](auto kern, int i) -> hipError_t {
-        if (hipError_t e = set_dynamic_lds(kern, kKsMaxLds, lds_set[i]); e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, grid, dim3(kKsThreads), lds, s, A, M, K, Wp, N, part, KSL);
-        return hipGetLastError();
-    };
-    hipError_t e = mt == 1 ? go(gemm_ksplit_kernel<BITS, 1>, 0)
-                 : mt == 2 ? go(gemm_ksplit_kernel<BITS, 2>, 1)
-                 : mt == 3 ? go(gemm_ksplit_kernel<BITS, 3>, 2)
-                           : go(gemm_ksplit_kernel<BITS, 4>, 3);
-    if (e != hipSuccess) return e;
-    const dim3 rgrid((unsigned)((M * N / 4 + 255) / 256));
-    if (y_dtype == HBL_F32)
-        hipLaunchKernelGGL((ksplit_reduce_kernel<BITS, float>), rgrid, dim3(256), 0, s, part, KS, M, N, xscale, alpha,
-                           (float*)Y);
-    else
-        hipLaunchKernelGGL((ksplit_reduce_kernel<BITS, uint16_t>), rgrid, dim3(256), 0, s, part, KS, M, N, xscale,
-                           alpha, (uint16_t*)Y);
-    return hipGetLastError();
-}
-
-hipError_t launch_gemm_ksplit(const void* codes, const float* xscale, int act_bits, int64_t M, int64_t K,
-                              const uint8_t* W_packed, const float* alpha, int64_t N, void* Y, int y_dtype,
-                              int32_t* part, hipStream_t s) {
-    if (!gemm_ksplit_eligible(M, K, N, act_bits)) return hipErrorInvalidValue;
-    return act_bits == 8 ? launch_ksplit_typed<8>((const uint8_t*)codes, xscale, M, K, W_packed, alpha, N, Y, y_dtype,
-                                                  part, s)
-                         : launch_ksplit_typed<4>((const uint8_t*)codes, xscale, M, K, W_packed, alpha, N, Y, y_dtype,
-                                                  part, s);
 }
 
 bool gemm_uses_decode_kernel(int64_t M, int64_t K) {

@@ -220,14 +220,6 @@ int64_t base3_row_bytes(int64_t K);
 hipError_t launch_pack_base3(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W3, hipStream_t s);
 hipError_t launch_gemv_base3(const void* codes, const float* xscale, int act_bits, int64_t M, int64_t K,
                              const uint8_t* W3, const float* alpha, int64_t N, void* Y, int y_dtype, hipStream_t s);
-// K-split decode GEMM for 5 to 64 tokens (row-major codes): int32 partial
-// sums of K/KS slices in `part` (ksplit_part_bytes), then an exact reduction
-// with the rescale.  Same results as launch_gemm, bit for bit.
-bool gemm_ksplit_eligible(int64_t M, int64_t K, int64_t N, int act_bits);
-size_t ksplit_part_bytes(int64_t M, int64_t K, int64_t N, int act_bits);
-hipError_t launch_gemm_ksplit(const void* codes, const float* xscale, int act_bits, int64_t M, int64_t K,
-                              const uint8_t* W_packed, const float* alpha, int64_t N, void* Y, int y_dtype,
-                              int32_t* part, hipStream_t s);
 // true when launch_gemm runs the decode GEMM for this shape; the codes may
 // then be in the decode tile layout (rows padded to a multiple of 16)
 bool gemm_uses_decode_kernel(int64_t M, int64_t K);

@@ -118,10 +118,6 @@ hbl_status hbl_workspace_bytes(int64_t M, int64_t K, const hbl_config* cfg, size
 /*
  * Workspace with which hbl_forward and hbl_forward_latent take their fastest
  * path for an M x K by N x K layer: >= hbl_workspace_bytes(M, K, cfg).  For
- * 5 to 64 tokens (K a power of two, N % 4 == 0) it adds room for int32
- * partial sums, and hbl_forward then splits K over several blocks per output
- * column and adds the partials exactly in a second launch (same Y bit for
- * bit; hbl_forward_latent keeps its single-pass decode GEMM).  For
  * INT4 activations at prefill sizes (M > 64, K >= 512, at least 128 output
  * tiles of 256 x 256) it adds room for the codes as FP6 and the weights as
  * FP4, and a workspace of this size lets the forward multiply them on the

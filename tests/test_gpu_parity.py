@@ -472,52 +472,6 @@ def test_forward_latent_f6f4_matches_two_calls(M, K, N, xdt, wdt):
     assert np.array_equal(to_host(Y), to_host(Y2))
 
 
-# 5 to 64 tokens with the larger workspace (hbl_forward_workspace_bytes): the
-# K-split decode GEMM (int32 partials of K slices, then an exact reduction).
-# Y must equal the single-pass decode GEMM (the smaller workspace) and the
-# stage entry points bit for bit, and the oracle's arithmetic on the GPU's
-# codes.  Ragged M and N, INT8 and INT4, 1 to 4 row tiles, 4 and 8 slices.
-KSPLIT_CASES = [
-    # (M, K, N, bits, x dtype, y dtype)
-    (5, 8192, 4096, 4, "f32", "bf16"),
-    (16, 8192, 4096, 4, "f32", "bf16"),
-    (64, 8192, 4096, 4, "f32", "bf16"),
-    (64, 8192, 4096, 8, "bf16", "f32"),
-    (33, 2048, 1008, 4, "bf16", "bf16"),
-    (17, 32768, 256, 8, "bf16", "bf16"),
-    (48, 16384, 528, 4, "f32", "f32"),
-    (8, 1024, 64, 8, "f32", "f32"),
-]
-
-
-@pytest.mark.parametrize("M,K,N,bits,xdt,ydt", KSPLIT_CASES)
-def test_forward_ksplit_decode_matches_single_pass(M, K, N, bits, xdt, ydt):
-    import torch
-    _announce("forward ksplit M=%d K=%d N=%d a%d %s->%s" % (M, K, N, bits, xdt, ydt))
-    rng = np.random.default_rng(M * 5 + K + N + bits)
-    X, _ = workloads.x_outlier_gaussian(rng, M, K, 4, 30.0)
-    W = workloads.w_latent(rng, N, K)
-    Xd = to_dev(workloads.f32_to_bf16_bits(X) if xdt == "bf16" else X)
-    cfg = hbl.Config(act_bits=bits)
-    small = hbl.hbl_workspace_bytes(M, K, cfg)
-    big = hbl.hbl_forward_workspace_bytes(M, K, N, cfg)
-    assert big >= small + M * N * 4 * 4  # room for at least four slices of partial sums
-    Wp, alpha = hbl.hbl_quantize_weights(to_dev(W))
-    yt = torch.float32 if ydt == "f32" else torch.bfloat16
-    Yk = hbl.hbl_forward(Xd, Wp, alpha, N, cfg, y_dtype=yt, ws=torch.empty(big, dtype=torch.uint8, device="cuda:0"))
-    Y1 = hbl.hbl_forward(Xd, Wp, alpha, N, cfg, y_dtype=yt, ws=torch.empty(small, dtype=torch.uint8, device="cuda:0"))
-    codes, xs, _, _ = hbl.hbl_quantize_activations(Xd, cfg)
-    Y2 = hbl.hbl_gemm(codes, xs, bits, K, Wp, alpha, N, y_dtype=yt)
-    _sync()
-    got = to_host(Yk)
-    assert np.array_equal(got, to_host(Y1))
-    assert np.array_equal(got, to_host(Y2))
-    q = unpack_codes(to_host(codes), K, bits)
-    a = to_host(alpha)[0]
-    y_exact = oracle.rescale(oracle.int_gemm(q, oracle.unpack_ternary(to_host(Wp), K)), to_host(xs), a)
-    assert np.array_equal(got, y_exact if ydt == "f32" else oracle.f32_to_bf16(y_exact))
-
-
 # hbl_forward_latent: weights ternarised and the forward run in three launches
 # (activation quantisation and weight packing share a grid); Y, W_packed and
 # alpha must equal hbl_quantize_weights + hbl_forward bit for bit.
