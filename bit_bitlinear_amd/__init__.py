@@ -21,7 +21,8 @@ __all__ = [
     "hbl_quantize_heads", "hbl_backward_workspace_bytes", "hbl_backward", "hbl_status_string",
     "hbl_last_hip_error", "hbl_base3_weight_bytes", "hbl_pack_base3", "hbl_gemm_base3", "hbl_forward_base3",
     "hbl_fp4_weight_bytes", "hbl_pack_fp4", "hbl_fp6_codes_bytes", "hbl_quantize_activations_fp6",
-    "hbl_gemm_fp6fp4", "hbl_forward_fp4_workspace_bytes", "hbl_forward_fp4",
+    "hbl_gemm_fp6fp4", "hbl_forward_fp4_workspace_bytes", "hbl_forward_fp4", "hbl_forward_noalloc",
+    "HBL_NOALLOC_SCRATCH_BYTES",
     "HBL_F32", "HBL_BF16", "HBL_NORM_RMS", "HBL_NORM_LN", "HBL_NORM_NONE",
     "HBL_A4_ABSMEAN_SQRT7", "HBL_A4_ABSMAX_7",
 ]
@@ -34,6 +35,7 @@ HBL_F32, HBL_BF16 = 0, 1
 HBL_NORM_RMS, HBL_NORM_LN, HBL_NORM_NONE = 0, 1, 2
 HBL_A4_ABSMEAN_SQRT7, HBL_A4_ABSMAX_7 = 0, 1
 HBL_OK = 0
+HBL_NOALLOC_SCRATCH_BYTES = 32 << 20   # the static workspace of hbl_forward_noalloc
 
 _STATUS_NAMES = {0: "HBL_OK", 1: "HBL_ERR_NULL", 2: "HBL_ERR_SHAPE", 3: "HBL_ERR_NOT_POW2", 4: "HBL_ERR_ALIGN",
                  5: "HBL_ERR_DTYPE", 6: "HBL_ERR_BITS", 7: "HBL_ERR_WORKSPACE", 8: "HBL_ERR_UNSUPPORTED",
@@ -117,6 +119,7 @@ def load_library(path: str | None = None):
         "hbl_gemm_fp6fp4": [P, P, I64, I64, P, P, I64, P, I32, P],
         "hbl_forward_fp4_workspace_bytes": [I64, I64, PCFG, PSZ],
         "hbl_forward_fp4": [P, I32, I64, I64, P, P, P, I64, PCFG, P, I32, P, SZ, P],
+        "hbl_forward_noalloc": [P, I32, I64, I64, P, P, P, I64, PCFG, P, I32, P],
     }
     for name, argtypes in sigs.items():
         f = getattr(lib, name)
@@ -548,4 +551,24 @@ def hbl_forward_fp4(X, W4, alpha, N: int, cfg: Config, y_dtype=None, gain=None, 
     _check("hbl_forward_fp4", lib.hbl_forward_fp4(_ptr(X), _dtype_code(X), M, K, _ptr(gain), _ptr(W4), _ptr(alpha),
                                                   N, ctypes.byref(c), _ptr(Y), _dtype_code(Y), _ptr(ws),
                                                   ws.numel() * ws.element_size(), _stream(stream)))
+    return Y
+
+
+def hbl_forward_noalloc(X, W_packed, alpha, N: int, cfg: Config, y_dtype=None, gain=None, Y=None, stream=None):
+    """hbl_forward with the workspace in the library's static device array
+    (no allocation by the library; Y is allocated here only when not given).
+    Returns Y [M][N]."""
+    torch = _torch()
+    lib = load_library()
+    _dev(X, "X"); _dev(W_packed, "W_packed"); _dev(alpha, "alpha"); _dev(gain, "gain")
+    M, K = X.shape
+    if Y is None:
+        Y = torch.empty((M, N), dtype=y_dtype or X.dtype, device=X.device)
+    _dev(Y, "Y")
+    _fits(W_packed, N * K // 4, "W_packed"); _fits(alpha, 4, "alpha"); _fits(gain, 4 * K, "gain")
+    _fits(Y, M * N * _esize(Y), "Y")
+    c = cfg.c()
+    _check("hbl_forward_noalloc", lib.hbl_forward_noalloc(_ptr(X), _dtype_code(X), M, K, _ptr(gain), _ptr(W_packed),
+                                                          _ptr(alpha), N, ctypes.byref(c), _ptr(Y), _dtype_code(Y),
+                                                          _stream(stream)))
     return Y

@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhbl.so")
 PEAKS_LIB = os.path.join(HERE, "libhbl_peaks.so")  # probe kernels for measured ceilings (benchmark only)
 SOURCES = ["api.hip", "weight_quant.hip", "act_quant.hip", "act_pack.hip", "gemm.hip", "forward_small.hip",
-           "head_quant.hip", "backward.hip", "base3.hip"]
+           "head_quant.hip", "backward.hip", "base3.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -89,6 +89,25 @@ size_t ws_codes_bytes(int64_t M, int64_t K, int32_t bits) {
 
 }  // namespace
 
+namespace hbl {
+void record_hip_error(hipError_t e) { g_last_hip_error = (int32_t)e; }
+
+hbl_status check_forward_args(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
+                              const uint8_t* W_packed, const float* alpha, int64_t N, const hbl_config* cfg,
+                              const void* Y, int32_t y_dtype) {
+    hbl_status st = check_config(cfg);
+    if (st != HBL_OK) return st;
+    if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return HBL_ERR_DTYPE;
+    if ((st = check_act_shape(M, K)) != HBL_OK) return st;
+    if ((st = check_gemm_shape(M, K, N)) != HBL_OK) return st;
+    if (M == 0) return HBL_OK;
+    if (!X || !W_packed || !alpha || !Y) return HBL_ERR_NULL;
+    if (!aligned16(X) || !aligned16(W_packed) || !aligned(alpha, 4) || !aligned16(Y) || !aligned(gain, 4))
+        return HBL_ERR_ALIGN;
+    return HBL_OK;
+}
+}  // namespace hbl
+
 extern "C" {
 
 const char* hbl_status_string(hbl_status s) {
@@ -247,18 +266,10 @@ hbl_status hbl_gemm(const void* codes, const float* xscale, int32_t act_bits, in
 hbl_status hbl_forward(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
                        const uint8_t* W_packed, const float* alpha, int64_t N, const hbl_config* cfg, void* Y,
                        int32_t y_dtype, void* ws, size_t ws_bytes, void* stream) {
-    hbl_status st = check_config(cfg);
-    if (st != HBL_OK) return st;
-    if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype)) return HBL_ERR_DTYPE;
-    st = check_act_shape(M, K);
-    if (st != HBL_OK) return st;
-    st = check_gemm_shape(M, K, N);
-    if (st != HBL_OK) return st;
-    if (M == 0) return HBL_OK;
-    if (!X || !W_packed || !alpha || !Y || !ws) return HBL_ERR_NULL;
-    if (!aligned16(X) || !aligned16(W_packed) || !aligned(alpha, 4) || !aligned16(Y) || !aligned16(ws) ||
-        !aligned(gain, 4))
-        return HBL_ERR_ALIGN;
+    hbl_status st = hbl::check_forward_args(X, x_dtype, M, K, gain, W_packed, alpha, N, cfg, Y, y_dtype);
+    if (st != HBL_OK || M == 0) return st;
+    if (!ws) return HBL_ERR_NULL;
+    if (!aligned16(ws)) return HBL_ERR_ALIGN;
     const size_t cb = ws_codes_bytes(M, K, cfg->act_bits);
     const size_t need = cb + round_up((size_t)M * sizeof(float), 256);
     if (ws_bytes < need) return HBL_ERR_WORKSPACE;

@@ -224,6 +224,14 @@ hipError_t launch_gemv_base3(const void* codes, const float* xscale, int act_bit
 // then be in the decode tile layout (rows padded to a multiple of 16)
 bool gemm_uses_decode_kernel(int64_t M, int64_t K);
 
+// Sets the HIP error that hbl_last_hip_error() reports on this thread.
+void record_hip_error(hipError_t e);
+// Every check hbl_forward makes on its arguments except the workspace's
+// (HBL_OK also for M == 0, which queues nothing).
+hbl_status check_forward_args(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
+                              const uint8_t* W_packed, const float* alpha, int64_t N, const hbl_config* cfg,
+                              const void* Y, int32_t y_dtype);
+
 // The whole forward for M = kForwardSmallMaxM = 1 token and K a power of two
 // in [1024, 16384], in one launch (codes and scale stay on chip).
 constexpr int kForwardSmallMaxM = 1;

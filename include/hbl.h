@@ -329,6 +329,23 @@ hbl_status hbl_forward_base3(const void* X, int32_t x_dtype, int64_t M, int64_t 
                              const uint8_t* W3, const float* alpha, int64_t N, const hbl_config* cfg, void* Y,
                              int32_t y_dtype, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * hbl_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation and result, bit for bit, with the workspace taken from a
+ * static device array of HBL_NOALLOC_SCRATCH_BYTES inside the library (each
+ * GPU it runs on holds one until the process ends).  The caller still passes
+ * X, the weights, alpha and Y.  Returns HBL_ERR_WORKSPACE when the shape's
+ * hbl_workspace_bytes(M, K, cfg) exceeds HBL_NOALLOC_SCRATCH_BYTES; otherwise
+ * the errors and constraints of hbl_forward.  The call allocates nothing.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (other streams, or unordered host threads) race.
+ */
+#define HBL_NOALLOC_SCRATCH_BYTES (32u << 20)
+hbl_status hbl_forward_noalloc(const void* X, int32_t x_dtype, int64_t M, int64_t K, const float* gain,
+                               const uint8_t* W_packed, const float* alpha, int64_t N, const hbl_config* cfg,
+                               void* Y, int32_t y_dtype, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* hbl_status_string(hbl_status status);
 

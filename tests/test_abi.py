@@ -20,7 +20,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = hbl.declared_symbols()
-    assert len(names) == 25
+    assert len(names) == 26
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
 
@@ -318,3 +318,19 @@ def test_fp4_fp6_validation(lib):
     assert f(A16, 0, 8, 1024, None, A16b, A16b, 64, ctypes.byref(cc8), A16b, 0, A16b, 1 << 20, None) == 6
     assert f(A16, 0, 8, 1024, None, None, A16b, 64, ctypes.byref(cc4), A16b, 0, A16b, 1 << 20, None) == 1
     assert f(A16, 0, 8, 1024, None, A16b, A16b, 72, ctypes.byref(cc4), A16b, 0, A16b, 1 << 20, None) == 4
+
+
+def test_forward_noalloc_host_checks(lib):
+    """The no-allocation forward rejects on the host, before any HIP call:
+    shapes whose workspace exceeds the static scratch, and bad arguments."""
+    c8 = hbl.Config(act_bits=8).c()
+    f = lib.hbl_forward_noalloc
+    # 8192 x 8192 INT8 codes need 64 MiB > HBL_NOALLOC_SCRATCH_BYTES
+    assert f(A16, 0, 8192, 8192, None, A16b, A16b, 256, ctypes.byref(c8), A16b, 0, None) == 7
+    assert f(A16, 0, 8, 300, None, A16b, A16b, 256, ctypes.byref(c8), A16b, 0, None) == 3   # K not a power of two
+    assert f(None, 0, 8, 256, None, A16b, A16b, 256, ctypes.byref(c8), A16b, 0, None) == 1
+    assert f(MIS, 0, 8, 256, None, A16b, A16b, 256, ctypes.byref(c8), A16b, 0, None) == 4
+    assert f(None, 0, 0, 256, None, None, None, 256, ctypes.byref(c8), None, 0, None) == 0   # M = 0: nothing
+    bad = hbl.Config(act_bits=5).c()
+    assert f(A16, 0, 8, 256, None, A16b, A16b, 256, ctypes.byref(bad), A16b, 0, None) == 6
+    assert hbl.HBL_NOALLOC_SCRATCH_BYTES == 32 << 20
