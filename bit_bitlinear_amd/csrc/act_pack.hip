@@ -68,9 +68,9 @@ hipError_t launch_ap(const Tin* X, int64_t M, const float* gain, const hbl_confi
                      const TW* W, int64_t NK, float w_eps, const double* partial, double* partial_out, int n_partial, uint8_t* Wp,
                      float* alpha, hipStream_t s) {
     constexpr int NT = threads_for(LK);
-    // the Hadamard's fp32 row; the FP6 layout stages its K*3/4 code bytes there too
+    // the Hadamard's fp32 row; the FP6 layout stages one dword per four codes there too
     const size_t row_bytes = HAD ? (size_t)ActShape<LK, NT, Tin>::lds_floats * sizeof(float) : 0;
-    const size_t lds_bytes = LAYOUT == kCodesFp6 && row_bytes < (size_t)(3 << LK) / 4 ? (size_t)(3 << LK) / 4 : row_bytes;
+    const size_t lds_bytes = LAYOUT == kCodesFp6 && row_bytes < (size_t)(1 << LK) ? (size_t)(1 << LK) : row_bytes;
     auto kern = act_pack_kernel<LK, NT, Tin, BITS, HAD, TW, LAYOUT>;
     static std::atomic<uint32_t> lds_set{0};  // devices with the LDS limit raised for this kernel
     if (hipError_t e = set_dynamic_lds(kern, lds_bytes, lds_set); e != hipSuccess) return e;

@@ -32,9 +32,9 @@ template <int LK, typename Tin, int BITS, bool HAD, int LAYOUT>
 hipError_t launch_one(const Tin* X, int64_t M, const float* gain, const hbl_config& cfg, void* codes, float* xscale,
                       float* z_debug, float* s_debug, hipStream_t s) {
     constexpr int NT = threads_for(LK);
-    // the Hadamard's fp32 row; the FP6 layout stages its K*3/4 code bytes there too
+    // the Hadamard's fp32 row; the FP6 layout stages one dword per four codes there too
     const size_t row_bytes = HAD ? (size_t)ActShape<LK, NT, Tin>::lds_floats * sizeof(float) : 0;
-    const size_t lds_bytes = LAYOUT == kCodesFp6 && row_bytes < (size_t)(3 << LK) / 4 ? (size_t)(3 << LK) / 4 : row_bytes;
+    const size_t lds_bytes = LAYOUT == kCodesFp6 && row_bytes < (size_t)(1 << LK) ? (size_t)(1 << LK) : row_bytes;
     auto kern = act_quant_kernel<LK, NT, Tin, BITS, HAD, LAYOUT>;
     static std::atomic<uint32_t> lds_set{0};  // devices with the LDS limit raised for this kernel
     if (hipError_t e = set_dynamic_lds(kern, lds_bytes, lds_set); e != hipSuccess) return e;

@@ -433,15 +433,9 @@ HBL_DEVINL void act_row_quantise(ActRegs<LK, NT, Tin>& v, const float* __restric
         }
         if constexpr (LAYOUT == kCodesFp6) {
             static_assert(BITS == 4 && VW == 4, "FP6 codes: INT4 values, four per vector");
-            // four 6-bit fields = 3 whole bytes at natural byte nb = 3*e0/4,
-            // staged in LDS (free since the statistic's barrier) in their
-            // final order; one 16-byte piece and one 8-byte piece per operand
-            const uint32_t f = fp6_e3m2_x4(b[0], b[1], b[2], b[3]);
-            const int nb = 3 * e0 / 4, o = nb % 96, op = o / 24, ob = o % 24;
-            const int base16 = nb - o + op * 16, base8 = nb - o + (4 + (op & 1)) * 16 + 8 * (op >> 1) - 16;
-            uint8_t* const st = reinterpret_cast<uint8_t*>(lds);
-#pragma unroll
-            for (int x2 = 0; x2 < 3; x2++) st[(ob + x2 < 16 ? base16 : base8) + ob + x2] = (uint8_t)(f >> (8 * x2));
+            // the vector's four 6-bit fields (24 bits) as one dword at dword
+            // e0/4 of LDS (free since the statistic's barrier), natural order
+            reinterpret_cast<uint32_t*>(lds)[e0 / 4] = fp6_e3m2_x4(b[0], b[1], b[2], b[3]);
             continue;
         }
         // a vector's 2 or 4 code bytes never cross a 16-byte chunk of the tile layout
@@ -467,10 +461,28 @@ HBL_DEVINL void act_row_quantise(ActRegs<LK, NT, Tin>& v, const float* __restric
         }
     }
     if constexpr (LAYOUT == kCodesFp6) {
-        // the staged FP6 row (K*3/4 bytes) leaves in 16-byte stores
+        // Each group of 16 codes (four staged dwords) becomes the 12 bytes of
+        // its natural FP6 bit string and goes straight to its place in the
+        // GEMM layout: per K step of 128 codes (8 groups, 96 bytes) operand
+        // op = group/2 keeps its first 16 bytes at 16 op and its last 8 at
+        // 16 (4 + op % 2) + 8 (op / 2); an even group fills bytes 0..11 of
+        // the operand, an odd one bytes 12..23 (4 in the first piece, 8 in
+        // the second).  All stores 4-byte aligned.
         __syncthreads();
         const uint4* src = reinterpret_cast<const uint4*>(lds);
-        for (int c = tid; c < K * 3 / 64; c += NT) reinterpret_cast<uint4*>(crow)[c] = src[c];
+        for (int q = tid; q < K / 16; q += NT) {
+            const uint4 d = src[q];
+            const uint32_t w0 = d.x | (d.y << 24), w1 = (d.y >> 8) | (d.z << 16), w2 = (d.z >> 16) | (d.w << 8);
+            const int j = q & 7, op = j >> 1;
+            uint8_t* const step = crow + 96 * (q >> 3);
+            if ((j & 1) == 0) {
+                uint32_t* p = reinterpret_cast<uint32_t*>(step + 16 * op);
+                p[0] = w0; p[1] = w1; p[2] = w2;
+            } else {
+                *reinterpret_cast<uint32_t*>(step + 16 * op + 12) = w0;
+                *reinterpret_cast<uint2*>(step + 16 * (4 + (op & 1)) + 8 * (op >> 1)) = make_uint2(w1, w2);
+            }
+        }
     }
 }
 
