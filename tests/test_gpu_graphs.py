@@ -120,3 +120,53 @@ def test_heads_and_base3_graph_replays():
 
     g = _replay_and_compare(run, [codes, scales, W3, Y], _eager_noise)
     del g
+
+
+def test_fp4_fp6_graph_replays():
+    """The FP6 x FP4 path: weight conversion, FP6 activation codes, the GEMM
+    and the forward, all in one graph, against the eager results."""
+    import torch
+    M, K, N = 1000, 4096, 2048  # ragged M: a partial last tile row
+    _announce("graph fp4/fp6 M=%d K=%d N=%d" % (M, K, N))
+    rng = np.random.default_rng(9)
+    Xd = to_dev(workloads.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32)))
+    Wp, alpha = hbl.hbl_quantize_weights(to_dev(workloads.w_latent(rng, N, K)))
+    cfg = hbl.Config(act_bits=4, hadamard=True)
+    W4 = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda:0")
+    codes6 = torch.empty((M, K * 3 // 4), dtype=torch.uint8, device="cuda:0")
+    xs = torch.empty((M,), dtype=torch.float32, device="cuda:0")
+    Y1 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    Y2 = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(hbl.hbl_forward_fp4_workspace_bytes(M, K, cfg), dtype=torch.uint8, device="cuda:0")
+
+    def run():
+        hbl.hbl_pack_fp4(Wp, K, W4=W4)
+        hbl.hbl_quantize_activations_fp6(Xd, cfg, codes6=codes6, xscale=xs)
+        hbl.hbl_gemm_fp6fp4(codes6, xs, K, W4, alpha, N, Y=Y1)
+        hbl.hbl_forward_fp4(Xd, W4, alpha, N, cfg, Y=Y2, ws=ws)
+
+    g = _replay_and_compare(run, [W4, codes6, xs, Y1, Y2], _eager_noise)
+    del g
+
+
+def test_forward_noalloc_graph_replays():
+    """The no-allocation forward is meant for graph capture: replays of the
+    captured call reproduce hbl_forward's eager result bit for bit."""
+    import torch
+    layer = workloads.by_name("wo_1.3b")
+    M, K, N = layer.M, layer.K, layer.N
+    _announce("graph forward_noalloc %s" % layer.desc)
+    X, W, _ = workloads.make_inputs(layer, 0)
+    Xd = to_dev(X)
+    Wp, alpha = hbl.hbl_quantize_weights(to_dev(W))
+    cfg = hbl.Config(act_bits=layer.act_bits, hadamard=layer.hadamard)
+    Y_ref = hbl.hbl_forward(Xd, Wp, alpha, N, cfg, y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+
+    def run():
+        hbl.hbl_forward_noalloc(Xd, Wp, alpha, N, cfg, Y=Y)
+
+    g = _replay_and_compare(run, [Y], _eager_noise)
+    assert np.array_equal(to_host(Y), to_host(Y_ref)), "no-alloc forward differs from hbl_forward"
+    del g

@@ -132,3 +132,58 @@ def test_backward_random_config(c):
     qc = np.ascontiguousarray(np.where(q_gpu != ref["q"], q_gpu, ref["q"])[:, cols])
     dW_ref = oracle.weight_grad(dYh, qc, ref["d"])
     check_dw(to_host(dW)[:, cols], dYh, qc, ref["d"], dW_ref, "dW")
+
+
+def _fp4_configs(n=12, seed=20261204):
+    rng = np.random.default_rng(seed)
+    Ms = [65, 100, 257, 700, 1500, 3000]
+    Ks = [512, 1024, 2048, 4096, 8192, 16384]
+    out = []
+    for i in range(n):
+        K = int(rng.choice(Ks))
+        M = int(rng.choice(Ms)) if K < 16384 else int(rng.choice(Ms[:4]))
+        N = int(rng.integers(1, 97)) * 16
+        out.append(dict(M=M, K=K, N=N, had=bool(rng.random() < 0.7),
+                        norm=int(rng.choice([hbl.HBL_NORM_RMS, hbl.HBL_NORM_LN, hbl.HBL_NORM_NONE])),
+                        gain=bool(rng.random() < 0.5), xdt=str(rng.choice(["f32", "bf16"])),
+                        ydt=str(rng.choice(["f32", "bf16"])), seed=i))
+    return out
+
+
+@pytest.mark.parametrize("c", _fp4_configs(), ids=lambda c: "M%d-K%d-N%d-h%d-n%d-g%d-%s-%s" % (
+    c["M"], c["K"], c["N"], c["had"], c["norm"], c["gain"], c["xdt"], c["ydt"]))
+def test_forward_fp4_random_config(c):
+    """hbl_forward_fp4 (FP4 weights, FP6 codes) on random INT4 configurations:
+    the FP4 bytes against the oracle, Y bit for bit equal to hbl_forward (INT8
+    matrix-core path) and, on sampled rows, to the oracle's product and
+    rescale of the GPU's codes."""
+    import torch
+    M, K, N, had, norm = c["M"], c["K"], c["N"], c["had"], c["norm"]
+    print("[case] random forward_fp4 %s" % sorted(c.items()), flush=True)
+    rng = np.random.default_rng(2000 + c["seed"])
+    X, _ = workloads.x_outlier_gaussian(rng, M, K, 4, 30.0)
+    if norm == hbl.HBL_NORM_LN:
+        X = (X + np.float32(1.5)).astype(np.float32)
+    Xh = workloads.f32_to_bf16_bits(X) if c["xdt"] == "bf16" else X
+    W = workloads.w_latent(rng, N, K)
+    gain = (rng.standard_normal(K).astype(np.float32) * 0.5 + 1.0) if c["gain"] else None
+    cfg = hbl.Config(act_bits=4, hadamard=had, norm=norm)
+    ydt = torch.float32 if c["ydt"] == "f32" else torch.bfloat16
+    Xd = to_dev(Xh)
+    gd = None if gain is None else to_dev(gain)
+    Wp, alpha = hbl.hbl_quantize_weights(to_dev(W))
+    W4 = hbl.hbl_pack_fp4(Wp, K)
+    Y4 = hbl.hbl_forward_fp4(Xd, W4, alpha, N, cfg, y_dtype=ydt, gain=gd)
+    ws = torch.empty(max(1, hbl.hbl_workspace_bytes(M, K, cfg)), dtype=torch.uint8, device="cuda:0")
+    Y8 = hbl.hbl_forward(Xd, Wp, alpha, N, cfg, y_dtype=ydt, gain=gd, ws=ws)
+    codes, xs, _, _ = hbl.hbl_quantize_activations(Xd, cfg, gain=gd)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(W4), oracle.pack_fp4(oracle.unpack_ternary(to_host(Wp), K)))
+    assert np.array_equal(to_host(Y4), to_host(Y8)), "FP6 x FP4 forward differs from the INT8 path"
+    rows = workloads.sample_rows(M, 16)
+    a_gpu = to_host(alpha)[0]
+    Wq = oracle.ternarize(W, a_gpu, 1e-5)
+    q_gpu = unpack_codes(to_host(codes)[rows], K, 4)
+    y_exact = oracle.rescale(oracle.int_gemm(q_gpu, Wq), to_host(xs)[rows], a_gpu)
+    got = to_host(Y4)[rows]
+    assert np.array_equal(got, y_exact if c["ydt"] == "f32" else oracle.f32_to_bf16(y_exact))
