@@ -105,22 +105,33 @@ HBL_DEVINL int lds_off(int e) {
 // register j = (g*2^R + f)*VW + v holds element base(g, f) + v with
 //   gamma = g*NT + tid, low part -> bits [VB, LO), high part -> bits [LO+R, LK),
 //   f -> bits [LO, LO+R), v -> bits [0, VB).
+// phase_elem gives base(g, f) for thread t.  With gamma = g*NT + t (t < NT) every
+// bit of the result comes from either g, f or t, so base = elem(g, f, 0) |
+// elem(0, 0, t) with disjoint bits, both multiples of VW, and lds_off splits
+// the same way: the thread's part is computed once per phase and the (g, f)
+// part is a constant of the unrolled loops (an immediate offset of the LDS
+// access), not an address computation per access.
 template <int NT, int VB, int LO, int R>
-HBL_DEVINL int phase_base(int g, int f) {
-    const int gam = g * NT + (int)threadIdx.x;
+HBL_DEVINL int phase_elem(int g, int f, int t) {
+    const int gam = g * NT + t;
     const int low = gam & ((1 << (LO - VB)) - 1);
     const int high = gam >> (LO - VB);
     return (low << VB) | (f << LO) | (high << (LO + R));
+}
+template <int NT, int VB, int LO, int R>
+HBL_DEVINL int phase_base(int g, int f) {
+    return phase_elem<NT, VB, LO, R>(0, 0, (int)threadIdx.x) + phase_elem<NT, VB, LO, R>(g, f, 0);
 }
 
 template <int NT, int E, int VB, int LO, int R>
 HBL_DEVINL void phase_read(const float* lds, float* v) {
     constexpr int VW = 1 << VB, G = E >> (VB + R), S = 1 << R;
+    const float* const base = lds + lds_off<VW>(phase_elem<NT, VB, LO, R>(0, 0, (int)threadIdx.x));
 #pragma unroll
     for (int g = 0; g < G; g++)
 #pragma unroll
         for (int f = 0; f < S; f++) {
-            const float* p = lds + lds_off<VW>(phase_base<NT, VB, LO, R>(g, f));
+            const float* p = base + lds_off<VW>(phase_elem<NT, VB, LO, R>(g, f, 0));
             float* d = v + (g * S + f) * VW;
             if constexpr (VW == 4) {
                 const float4 q = *reinterpret_cast<const float4*>(p);
@@ -135,11 +146,12 @@ HBL_DEVINL void phase_read(const float* lds, float* v) {
 template <int NT, int E, int VB, int LO, int R>
 HBL_DEVINL void phase_write(float* lds, const float* v) {
     constexpr int VW = 1 << VB, G = E >> (VB + R), S = 1 << R;
+    float* const base = lds + lds_off<VW>(phase_elem<NT, VB, LO, R>(0, 0, (int)threadIdx.x));
 #pragma unroll
     for (int g = 0; g < G; g++)
 #pragma unroll
         for (int f = 0; f < S; f++) {
-            float* p = lds + lds_off<VW>(phase_base<NT, VB, LO, R>(g, f));
+            float* p = base + lds_off<VW>(phase_elem<NT, VB, LO, R>(g, f, 0));
             const float* s = v + (g * S + f) * VW;
             if constexpr (VW == 4) *reinterpret_cast<float4*>(p) = make_float4(s[0], s[1], s[2], s[3]);
             else *reinterpret_cast<float2*>(p) = make_float2(s[0], s[1]);
@@ -317,11 +329,12 @@ HBL_DEVINL void act_row_quantise(ActRegs<LK, NT, Tin>& v, const float* __restric
     // ---- 2. Hadamard: register bits now, thread bits through LDS
     if constexpr (HAD) {
         reg_fwht<E>(v);
+        float* const base = lds + lds_off<VW>(tid * V);  // the thread's part of the offsets (see phase_elem)
 #pragma unroll
         for (int c = 0; c < C; c++)
 #pragma unroll
             for (int j = 0; j < V; j += VW) {
-                float* p = lds + lds_off<VW>((c * NT + tid) * V + j);
+                float* p = base + lds_off<VW>(c * NT * V + j);
                 if constexpr (VW == 4) *reinterpret_cast<float4*>(p) = make_float4(v[c * V + j], v[c * V + j + 1],
                                                                                    v[c * V + j + 2], v[c * V + j + 3]);
                 else *reinterpret_cast<float2*>(p) = make_float2(v[c * V + j], v[c * V + j + 1]);

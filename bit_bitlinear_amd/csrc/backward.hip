@@ -339,11 +339,12 @@ __global__ __launch_bounds__(NT) void bwd_rows_kernel(float* __restrict__ dzx, c
     act_row_load<LK, NT, float>(drow, v);
     if constexpr (HAD) {
         reg_fwht<E>(v);
+        float* const base = lds + lds_off<VW>(tid * V);  // the thread's part of the offsets (see phase_elem)
 #pragma unroll
         for (int c = 0; c < S::C; c++)
 #pragma unroll
             for (int j = 0; j < V; j += VW) {
-                float* p = lds + lds_off<VW>((c * NT + tid) * V + j);
+                float* p = base + lds_off<VW>(c * NT * V + j);
                 *reinterpret_cast<float4*>(p) = make_float4(v[c * V + j], v[c * V + j + 1], v[c * V + j + 2], v[c * V + j + 3]);
             }
         __syncthreads();
