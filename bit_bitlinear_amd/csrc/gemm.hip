@@ -610,8 +610,19 @@ template <typename YT, int BM, int BN, int WGM, int WGN, int S>
 __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_f6f4_kernel(
     const uint8_t* __restrict__ A6, const float* __restrict__ xscale, int64_t M, int64_t K,
     const uint8_t* __restrict__ W4, const float* __restrict__ alpha_p, int64_t N, YT* __restrict__ Y, int tiles_n,
-    int tiles_total) {
+    int tiles_total, int stagger) {
     using T = F6Tile<BM, BN, WGM, WGN, S>;
+    // De-phasing: every block of one wave of tiles reaches its epilogue at
+    // the same moment and the output write then runs alone at HBM write
+    // speed.  With many waves of tiles the first wave's blocks start
+    // staggered by XCD, `stagger` x 64 cycles apart; the later blocks inherit
+    // the offsets, so one XCD's epilogue overlaps the others' main loops
+    // (3-5% on the 3B-like gate/up shape, 16 waves of tiles; nothing gained
+    // with 6 or fewer, so the launcher passes 0 there).
+    if (stagger > 0 && (int)blockIdx.x < 256) {
+        const int n = (int)(blockIdx.x & 7) * stagger;
+        for (int i = 0; i < n; i += 16) __builtin_amdgcn_s_sleep(16);
+    }
     constexpr int TA = T::TA, TB = T::TB;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[T::lds_bytes];
     float* const xs_tile = reinterpret_cast<float*>(smem + (T::xs_in_ring ? 0 : S * T::stage));
@@ -846,12 +857,14 @@ hipError_t launch_gemm_f6f4(const uint8_t* codes6, const float* xscale, int64_t 
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
     const int tt = (int)tiles;
     constexpr int NT = 64 * kF6WGM * kF6WGN;
+    // at least 10 waves of tiles over the 256 CUs (one block each): XCDs start 128 x 64 cycles apart
+    const int stagger = tt >= 10 * 256 ? 128 : 0;
     if (y_dtype == HBL_F32)
         hipLaunchKernelGGL((gemm_f6f4_kernel<float, kF6BM, kF6BN, kF6WGM, kF6WGN, kF6Stages>), dim3(tt), dim3(NT), 0,
-                           s, codes6, xscale, M, K, W4, alpha, N, (float*)Y, tiles_n, tt);
+                           s, codes6, xscale, M, K, W4, alpha, N, (float*)Y, tiles_n, tt, stagger);
     else
         hipLaunchKernelGGL((gemm_f6f4_kernel<uint16_t, kF6BM, kF6BN, kF6WGM, kF6WGN, kF6Stages>), dim3(tt), dim3(NT),
-                           0, s, codes6, xscale, M, K, W4, alpha, N, (uint16_t*)Y, tiles_n, tt);
+                           0, s, codes6, xscale, M, K, W4, alpha, N, (uint16_t*)Y, tiles_n, tt, stagger);
     return hipGetLastError();
 }
 
