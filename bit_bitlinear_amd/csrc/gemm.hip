@@ -654,17 +654,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_f6f4_kernel(
         w_off[u] = (uint32_t)(row * w_ld + f6_w_chunk(p, row) * 16);
     }
     const uint32_t smem_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+    // the K step's byte offset inside a row (below one row) rides in soffset;
+    // the LDS destinations are wave-uniform, computed in scalar registers
+    const uint32_t wave_s = __builtin_amdgcn_readfirstlane((uint32_t)wave);
+    const uint32_t a_dst = __builtin_amdgcn_readfirstlane(smem_addr) + wave_s * (uint32_t)(T::a_inst * 1024);
+    const uint32_t w_dst = __builtin_amdgcn_readfirstlane(smem_addr) + (uint32_t)T::a_bytes +
+                           wave_s * (uint32_t)(T::w_inst * 1024);
     auto issue = [&](int kt, int st) {
-        const uint32_t base = smem_addr + (uint32_t)(st * T::stage);
+        const uint32_t st_off = (uint32_t)(st * T::stage);
+        const uint32_t a_k = (uint32_t)(kt * kF6ARow), w_k = (uint32_t)(kt * kF6WRow);
 #pragma unroll
-        for (int u = 0; u < T::a_inst; u++)
-            lds_dma16(a_desc, __builtin_amdgcn_readfirstlane(base + (uint32_t)((wave * T::a_inst + u) * 1024)),
-                      a_off[u] + (uint32_t)(kt * kF6ARow));
+        for (int u = 0; u < T::a_inst; u++) lds_dma16_so(a_desc, a_dst + st_off + (uint32_t)(u * 1024), a_off[u], a_k);
 #pragma unroll
-        for (int u = 0; u < T::w_inst; u++)
-            lds_dma16(w_desc,
-                      __builtin_amdgcn_readfirstlane(base + (uint32_t)(T::a_bytes + (wave * T::w_inst + u) * 1024)),
-                      w_off[u] + (uint32_t)(kt * kF6WRow));
+        for (int u = 0; u < T::w_inst; u++) lds_dma16_so(w_desc, w_dst + st_off + (uint32_t)(u * 1024), w_off[u], w_k);
     };
 
     v16f acc[TA][TB];
@@ -679,30 +681,29 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_f6f4_kernel(
     // lr of each 32-wide MFMA tile, k 32*lh .. +31 of each 64-k MFMA step
     const int lr = lane & 31;
     const int lh = lane >> 5;
-    int a_o16[TA][2], a_o8[TA], w_o[TB][2];
+    // The code swizzle of row r = wm*32*TA + i*32 + lr depends only on bit 3
+    // of lr, and the weight swizzle of column c = wn*32*TB + j*32 + lr only on
+    // bits 2-3 of lr, so every fragment offset is a per-lane base plus a
+    // constant: codes a_lane + i*32 rows + 32 bytes per k-step (+64 for the
+    // 8-byte pieces), weights w_lane[k-step] + j*32 rows.  The LDS reads then
+    // take the constants as immediate offsets instead of an address add each.
+    const int a_lane = (wm * 32 * TA + lr) * kF6ARow + 16 * (lh ^ ((lr >> 3) & 1));
+    int w_lane[2];
 #pragma unroll
-    for (int i = 0; i < TA; i++) {
-        const int row = wm * 32 * TA + i * 32 + lr;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; s2++) a_o16[i][s2] = row * kF6ARow + f6_a_chunk(2 * s2 + lh, row) * 16;
-        a_o8[i] = row * kF6ARow + f6_a_chunk(4 + lh, row) * 16;
-    }
-#pragma unroll
-    for (int j = 0; j < TB; j++) {
-        const int col = wn * 32 * TB + j * 32 + lr;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; s2++) w_o[j][s2] = T::a_bytes + col * kF6WRow + f6_w_chunk(2 * s2 + lh, col) * 16;
-    }
+    for (int s2 = 0; s2 < 2; s2++)
+        w_lane[s2] = T::a_bytes + (wn * 32 * TB + lr) * kF6WRow + (((2 * s2 + lh) ^ ((lr >> 2) & 3)) * 16);
     // fragments of the two k-steps of a K step (fa0/fw0: k-step 0, fa1/fw1:
     // k-step 1) and the code tails of two consecutive K steps
     uint4 fa0[TA], fw0[TB], fa1[TA], fw1[TB], ta[TA], tb[TA];
 #define HBL_F6_READ(FA, FW, ST, S2)                                                                          \
     {                                                                                                        \
-        _Pragma("unroll") for (int i = 0; i < TA; i++) FA[i] = *reinterpret_cast<const uint4*>((ST) + a_o16[i][S2]); \
-        _Pragma("unroll") for (int j = 0; j < TB; j++) FW[j] = *reinterpret_cast<const uint4*>((ST) + w_o[j][S2]);   \
+        _Pragma("unroll") for (int i = 0; i < TA; i++)                                                      \
+            FA[i] = *reinterpret_cast<const uint4*>((ST) + a_lane + (i * 32 * kF6ARow + 32 * (S2)));          \
+        _Pragma("unroll") for (int j = 0; j < TB; j++)                                                      \
+            FW[j] = *reinterpret_cast<const uint4*>((ST) + w_lane[S2] + j * 32 * kF6WRow);                    \
     }
 #define HBL_F6_TAIL(TL, ST) \
-    { _Pragma("unroll") for (int i = 0; i < TA; i++) TL[i] = *reinterpret_cast<const uint4*>((ST) + a_o8[i]); }
+    { _Pragma("unroll") for (int i = 0; i < TA; i++) TL[i] = *reinterpret_cast<const uint4*>((ST) + a_lane + (i * 32 * kF6ARow + 64)); }
     // formats: 3 = FP6 E3M2 (codes), 4 = FP4 E2M1 (weights); unscaled
 #define HBL_F6_MFMA(FA, FW, TL, S2)                                                                          \
     {                                                                                                        \
