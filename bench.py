@@ -11,8 +11,10 @@ FP6 x FP4 matrix cores, the rescale) against weights that were ternarised and
 converted to FP4 once beforehand, as a deployment holds them.  The weight
 ternarisation and conversion are timed separately.  Inputs are seeded
 synthetic arrays already resident in HBM; the timed steps are replayed from
-HIP graphs, exactly --steps of them, rotating over enough distinct buffer
-sets (> 512 MiB) that the 256 MB last-level cache cannot hold a step's inputs.
+HIP graphs, exactly --steps of them.  The chain's four layers together hold
+about 1.6 GB of inputs, weights, codes and outputs, far more than the 256 MB
+last-level cache; the single-layer workloads rotate over enough distinct
+buffer sets (> 512 MiB) that the cache cannot hold a step's inputs.
 
 Prints one JSON line: tokens/s and TOPS of the step; for the kernel that takes
 the most time per step, the algorithmic work per launch over its average
