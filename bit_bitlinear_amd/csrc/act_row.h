@@ -36,6 +36,8 @@ namespace hbl {
 namespace {
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+typedef float v16f_cvt __attribute__((ext_vector_type(16)));    // operand of the BF6 conversion
+typedef unsigned v6u_cvt __attribute__((ext_vector_type(6)));   // its 32 packed 6-bit fields
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
@@ -420,6 +422,11 @@ HBL_DEVINL void act_row_quantise(ActRegs<LK, NT, Tin>& v, const float* __restric
     constexpr int SLO = HAD ? Ph::LAST_LO : 0;
     constexpr int SR = HAD ? Ph::LAST_R : 0;
     constexpr int NVEC = E / VW;
+    // FP6: the rounded codes as floats and each vector's element index, for
+    // the conversion after the loop
+    constexpr bool kFp6 = LAYOUT == kCodesFp6;
+    float rq[kFp6 ? E : 1];
+    int e0s[kFp6 ? NVEC : 1];
 #pragma unroll
     for (int u = 0; u < NVEC; u++) {
         int e0;  // element index of vector u
@@ -435,6 +442,19 @@ HBL_DEVINL void act_row_quantise(ActRegs<LK, NT, Tin>& v, const float* __restric
             if constexpr (VW == 4) *reinterpret_cast<float4*>(zd) = make_float4(z[0], z[1], z[2], z[3]);
             else *reinterpret_cast<float2*>(zd) = make_float2(z[0], z[1]);
         }
+        if constexpr (kFp6) {
+            static_assert(BITS == 4 && VW == 4, "FP6 codes: INT4 values, four per vector");
+            // the same decision as code_bits: one rounded fp32 product, the
+            // clamp, round half to even; the integer stays a float (+0 turns
+            // a rounded -0 into +0, so code 0 is always the all-zero field)
+#pragma unroll
+            for (int x2 = 0; x2 < VW; x2++) {
+                const float t = z[x2] * s_mul;
+                rq[u * VW + x2] = __builtin_rintf(fminf(fmaxf(t, lo), hi)) + 0.0f;
+            }
+            e0s[u] = e0;
+            continue;
+        }
         uint32_t b[VW];
 #pragma unroll
         for (int x2 = 0; x2 < VW; x2++) {
@@ -443,13 +463,6 @@ HBL_DEVINL void act_row_quantise(ActRegs<LK, NT, Tin>& v, const float* __restric
             // clamp cannot bind and is skipped
             if constexpr (BITS == 8) b[x2] = code_bits_unclamped(z[x2], s_mul);
             else b[x2] = code_bits(z[x2], s_mul, lo, hi);
-        }
-        if constexpr (LAYOUT == kCodesFp6) {
-            static_assert(BITS == 4 && VW == 4, "FP6 codes: INT4 values, four per vector");
-            // the vector's four 6-bit fields (24 bits) as one dword at dword
-            // e0/4 of LDS (free since the statistic's barrier), natural order
-            reinterpret_cast<uint32_t*>(lds)[e0 / 4] = fp6_e3m2_x4(b[0], b[1], b[2], b[3]);
-            continue;
         }
         // a vector's 2 or 4 code bytes never cross a 16-byte chunk of the tile layout
         const int kb = BITS == 8 ? e0 : e0 / 2;
@@ -473,7 +486,37 @@ HBL_DEVINL void act_row_quantise(ActRegs<LK, NT, Tin>& v, const float* __restric
             }
         }
     }
-    if constexpr (LAYOUT == kCodesFp6) {
+    if constexpr (kFp6) {
+        // The hardware conversion turns 32 floats into their BF6 (E3M2)
+        // fields, field 2k from the first operand's element k and field
+        // 2k + 1 from the second's; every code in [-8, 7] is exact and the
+        // scale is 1.  Fed the even and the odd codes, it returns this
+        // thread's 32 codes as one natural-order bit string of six dwords, in
+        // which vector u's four fields are bits 24u .. 24u + 23.  Each
+        // vector's 24 bits go to LDS as one dword at dword e0/4 (LDS is free
+        // since the statistic's barrier), natural order.
+        constexpr int NG = (E + 31) / 32;
+#pragma unroll
+        for (int g = 0; g < NG; g++) {
+            v16f_cvt ev, od;
+#pragma unroll
+            for (int k = 0; k < 16; k++) {
+                ev[k] = 32 * g + 2 * k < E ? rq[32 * g + 2 * k] : 0.f;
+                od[k] = 32 * g + 2 * k + 1 < E ? rq[32 * g + 2 * k + 1] : 0.f;
+            }
+            const v6u_cvt f = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(ev, od, 1.0f);
+#pragma unroll
+            for (int uu = 0; uu < 8; uu++) {
+                const int u = 8 * g + uu;
+                if (u >= NVEC) break;
+                const int bit = 24 * uu, d = bit >> 5, sh = bit & 31;
+                uint32_t w;
+                if (sh == 0) w = f[d];
+                else if (d == 5) w = f[d] >> sh;
+                else w = __builtin_amdgcn_alignbit(f[d + 1], f[d], sh);
+                reinterpret_cast<uint32_t*>(lds)[e0s[u] / 4] = w & 0xFFFFFFu;
+            }
+        }
         // Each group of 16 codes (four staged dwords) becomes the 12 bytes of
         // its natural FP6 bit string and goes straight to its place in the
         // GEMM layout: per K step of 128 codes (8 groups, 96 bytes) operand

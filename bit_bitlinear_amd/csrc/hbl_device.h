@@ -72,35 +72,6 @@ HBL_DEVINL int dec_tile_offset(int kb) {  // kb: byte index of the code inside i
 // one 8-byte piece.  A row is K*3/4 bytes.
 enum { kCodesRowMajor = 0, kCodesDecTiled = 1, kCodesFp6 = 2 };
 
-// Position of byte nb of a row's natural FP6 bit string in the layout above.
-HBL_DEVINL int fp6_byte_offset(int nb) {
-    const int o = nb % 96, op = o / 24, ob = o % 24, s = op >> 1, h = op & 1;
-    return nb - o + (ob < 16 ? (2 * s + h) * 16 + ob : (4 + h) * 16 + 8 * s + (ob - 16));
-}
-
-// FP6 E3M2 encoding of an integer v in [-8, 8]: magnitudes 0..8 map to
-// 0, 12, 16, 18, 20, 21, 22, 23, 24 (exponent field e, mantissa m: (1 + m/4) * 2^(e-3)).
-HBL_DEVINL uint32_t fp6_e3m2(int v) {
-    const uint32_t a = (uint32_t)(v < 0 ? -v : v);
-    const uint32_t mag = a >= 8 ? 24u : (__builtin_amdgcn_perm(0x17161514u, 0x12100C00u, a) & 0xFFu);
-    return mag | (v < 0 ? 32u : 0u);
-}
-
-// Four INT4 codes (two's complement in the low 4 bits of c0..c3) -> their
-// FP6 E3M2 fields packed at bits 0, 6, 12, 18: a 16-entry byte table looked
-// up with two byte permutes (codes 0..7 and -8..-1), the same values as
-// fp6_e3m2.
-HBL_DEVINL uint32_t fp6_e3m2_x4(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3) {
-    const uint32_t idx = (__builtin_amdgcn_perm(c1, c0, 0x0c0c0400u) | __builtin_amdgcn_perm(c3, c2, 0x04000c0cu)) &
-                         0x0F0F0F0Fu;  // one code per byte
-    const uint32_t i7 = idx & 0x07070707u;
-    const uint32_t pos = __builtin_amdgcn_perm(0x17161514u, 0x12100C00u, i7);  // 0..7: 0 12 16 18 20 21 22 23
-    const uint32_t neg = __builtin_amdgcn_perm(0x2C303234u, 0x35363738u, i7);  // -8..-1: 56 55 54 53 52 50 48 44
-    const uint32_t m = ((idx >> 3) & 0x01010101u) * 0xFFu;                      // bytes holding a negative code
-    const uint32_t y = (neg & m) | (pos & ~m);
-    return (y & 0x3Fu) | ((y >> 2) & 0xFC0u) | ((y >> 4) & 0x3F000u) | ((y >> 6) & 0xFC0000u);
-}
-
 // ---- wave / block reductions (fixed butterfly order: deterministic) ----
 HBL_DEVINL float wave_sum_f32(float v) {
 #pragma unroll
