@@ -10,16 +10,17 @@ where the layer has it, per-token INT4 quantisation, the integer product on the
 FP6 x FP4 matrix cores, the rescale) against weights that were ternarised and
 converted to FP4 once beforehand, as a deployment holds them.  The weight
 ternarisation and conversion are timed separately.  Inputs are seeded
-synthetic arrays already resident in HBM; the timed steps are replayed from
-HIP graphs, exactly --steps of them.  The chain's four layers together hold
+synthetic arrays already resident in HBM; exactly --steps steps are timed,
+launched back to back with HIP events around every kernel (the same steps
+replayed from a HIP graph are reported beside them).  The chain's four layers together hold
 about 1.6 GB of inputs, weights, codes and outputs, far more than the 256 MB
 last-level cache; the single-layer workloads rotate over enough distinct
 buffer sets (> 512 MiB) that the cache cannot hold a step's inputs.
 
 Prints one JSON line: tokens/s and TOPS of the step; for the kernel that takes
 the most time per step, the algorithmic work per launch over its average
-launch time (HIP events on the launch stream, recorded around each kernel
-inside eager steps) against the MI355X peak and against ceilings measured in
+launch time (HIP events on the launch stream, recorded around each kernel of
+the timed steps) against the MI355X peak and against ceilings measured in
 the same process; the same figures for the other workloads (1.3B-like Wo with
 INT8 codes, 7B-like Wdown, decode at 1, 16 and 64 tokens); and the CPU oracle
 timed on a bounded row sample on the host cores.
@@ -419,36 +420,51 @@ def bench_chain(args):
     if R > 1:  # a small chain would need more sets; the 3B chain's step touches > 1 GiB
         raise RuntimeError("chain smaller than the rotation size")
 
-    def step(r=0):
-        for p in preps:
-            p.forward(r)
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        # one forward of each layer: its two launches (the activation kernel,
+        # then the GEMM: exactly the launches of hbl_forward_fp4), with HIP
+        # events on the launch stream around each when evs is given
+        for j, p in enumerate(preps):
+            if evs is not None:
+                evs[j][0].record(stream)
+            p.act(0)
+            if evs is not None:
+                evs[j][1].record(stream)
+            p.gemm(0)
+            if evs is not None:
+                evs[j][2].record(stream)
 
     for _ in range(args.warmup):
         step()
+    # the timed region: exactly --steps steps, launched back to back (the host
+    # enqueues a step in well under the GPU's time for it), every kernel
+    # bracketed by events, so the per-kernel averages come from these steps
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in preps] for _ in range(args.steps)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    graphs = capture([step])
-    wall, ev_ms = replay_timed(graphs, args.steps)
-    del graphs
+    t0 = time.perf_counter()
+    e_start.record(stream)
+    for i in range(args.steps):
+        step(ev[i])
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = e_start.elapsed_time(e_end)
     ms_per_step = wall / args.steps * 1e3
     log("chain: %d steps timed, %.3f ms per step" % (args.steps, ms_per_step))
     ops_step = sum(2 * p.layer.M * p.layer.N * p.layer.K for p in preps)
+    # cross-check: the same steps through hbl_forward_fp4, replayed from a HIP graph
+    graphs = capture([lambda r=0: [p.forward(0) for p in preps]])
+    wall_g, _ = replay_timed(graphs, args.steps)
+    del graphs
 
-    # per-kernel times inside eager steps: events around each stage launch
-    stream = torch.cuda.current_stream()
-    n_it = max(3, args.kernel_iters)
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in preps] for _ in range(n_it)]
-    for i in range(n_it):
-        for j, p in enumerate(preps):
-            ev[i][j][0].record(stream)
-            p.act(0)
-            ev[i][j][1].record(stream)
-            p.gemm(0)
-            ev[i][j][2].record(stream)
-    torch.cuda.synchronize()
     per_layer = []
+    n_it = args.steps
     for j, p in enumerate(preps):
-        t_act = sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(1, n_it)) / (n_it - 1) * 1e3
-        t_gemm = sum(ev[i][j][1].elapsed_time(ev[i][j][2]) for i in range(1, n_it)) / (n_it - 1) * 1e3
+        t_act = sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(n_it)) / n_it * 1e3
+        t_gemm = sum(ev[i][j][1].elapsed_time(ev[i][j][2]) for i in range(n_it)) / n_it * 1e3
         w = p.work()
         L = p.layer
         act6_bytes = L.M * L.K * 2 + L.M * L.K * 3 // 4 + 4 * L.M
@@ -503,11 +519,14 @@ def bench_chain(args):
                                "QKV 4096->12288 and gate/up 4096->32768 (BitLinear), Wo 4096->4096 and Wdown "
                                "16384->4096 (H-BitLinear)",
                    "M": M, "layers": [p["layer"] for p in per_layer], "act_bits": 4,
-                   "step": "hbl_forward_fp4 on each of the 4 layers (norm [+ Hadamard] + INT4 codes as FP6, "
-                           "FP6 x FP4 GEMM + rescale) against weights ternarised and converted to FP4 once",
-                   "timing": "HIP graph replay, one graph per step, exactly --steps replays"},
+                   "step": "the forward of each of the 4 layers (hbl_quantize_activations_fp6: norm [+ Hadamard] "
+                           "+ INT4 codes as FP6; hbl_gemm_fp6fp4: FP6 x FP4 GEMM + rescale; the two launches of "
+                           "hbl_forward_fp4) against weights ternarised and converted to FP4 once",
+                   "timing": "exactly --steps steps launched back to back, HIP events around every kernel on the "
+                             "launch stream; the roofline's kernel times are averages over these steps"},
         "tops": round(ops_step * args.steps / wall / 1e12, 2),
         "ms_per_step_events": round(ev_ms / args.steps, 5),
+        "ms_per_step_graph": round(wall_g / args.steps * 1e3, 5),
         "kernel_us_per_step": {"gemm_f6f4": round(tot_gemm_us, 2), "act_fp6": round(tot_act_us, 2)},
         "roofline": roof,
         "layers": per_layer,
