@@ -73,7 +73,10 @@ def measured_peaks():
         past the last-level cache,
       * an empty 256-block kernel replayed from a graph (the launch floor),
       * loops of dense i8, FP6 x FP4 and bf16 matrix-core instructions on
-        register operands.
+        register operands,
+      * the data path of one compute unit: LDS reads, LDS-direct loads, and
+        both mixed with FP6 x FP4 instructions in the proportions of one K
+        step of the FP6 x FP4 GEMM tile (with and without its barrier).
     Each figure is the best of 3 timed rounds after a warm-up.  Computed once."""
     global _PEAKS
     if _PEAKS is not None:
@@ -166,10 +169,39 @@ def measured_peaks():
             ok(lib.hbl_peak_mfma(kind, ctypes.c_void_p(sink.data_ptr()), sink.numel(), blocks, iters, sp), "mfma")
         ops = lib.hbl_peak_mfma_ops(kind, blocks, iters)
         out[key] = round(ops / (best_us(run, reps=2) * 1e-6) / 1e12, 1)
+    del sink
+    # the data path of one compute unit: one 8-wave workgroup per compute unit, a 2 MiB source that the L2
+    # caches hold; cycles from the shader clock the probe reads (s_memtime against the 100 MHz counter)
+    lib.hbl_peak_lds.argtypes = [I32, P, I64, I32, I32, P, I64, P, I64, P]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    lsrc = torch.ones((2 << 20) // 4, dtype=torch.int32, device=dev)
+    clk = torch.zeros(2 * cus, dtype=torch.int64, device=dev)
+    lsink = torch.zeros(cus, dtype=torch.int32, device=dev)
+    rounds = 2000
+    for kind, key in ((0, "lds_read"), (1, "lds_direct"), (2, "fp6_kstep"), (3, "fp6_kstep_nobarrier")):
+        def run(kind=kind):
+            ok(lib.hbl_peak_lds(kind, ctypes.c_void_p(lsrc.data_ptr()), lsrc.numel() * 4, cus, rounds,
+                                ctypes.c_void_p(clk.data_ptr()), clk.numel(), ctypes.c_void_p(lsink.data_ptr()),
+                                lsink.numel(), sp), "lds")
+        us = best_us(run, reps=1)
+        c = clk.view(cus, 2).double().cpu()
+        ghz = float(c[:, 0].median() / (c[:, 1].median() / 100e6) / 1e9)
+        cyc = us * 1e3 * ghz / rounds  # shader cycles per round
+        if kind == 0:
+            out["lds_read_B_per_clk_cu"] = round(8 * 14 * 1024 / cyc, 1)
+        elif kind == 1:
+            out["lds_direct_load_B_per_clk_cu"] = round(8 * 5 * 1024 / cyc, 1)
+        else:  # per SIMD and round: 2 waves x 16 instructions at 32 cycles each at the dense rate
+            out[key + "_mfma_util"] = round(2 * 16 * 32 / cyc, 4)
+            out[key + "_clock_GHz"] = round(ghz, 3)
+    del lsrc, clk, lsink
     torch.cuda.synchronize()
     out["method"] = ("512 MiB 16-byte streaming copy (2 x bytes); 8 MiB and 64 MiB streaming reads and an empty "
                      "256-block kernel, graph-replayed; 2048 x 256-thread blocks each issuing 4 independent "
-                     "matrix-core instructions per round on register operands")
+                     "matrix-core instructions per round on register operands; one 8-wave workgroup per compute "
+                     "unit for the LDS data path: per wave and round 14 LDS reads of 16 B (lds_read), 5 LDS-direct "
+                     "loads of 1 KiB from a 2 MiB source (lds_direct), and both with 16 FP6 x FP4 instructions "
+                     "and a barrier (fp6_kstep: one K step of the 256 x 256 FP6 x FP4 tile; _nobarrier without it)")
     _PEAKS = out
     log("measured peaks done")
     return out

@@ -1,8 +1,10 @@
 // peaks.hip -- probe kernels that measure the ceilings of one gfx950 GPU: a
-// streaming 16-byte copy (HBM) and loops of dense matrix-core instructions
-// (i8, FP6 x FP4, bf16) on register operands.  The benchmark times them and
-// reports its own kernels against the measured figures beside the published
-// peaks.  Not part of the H-BitLinear layer.
+// streaming 16-byte copy (HBM), loops of dense matrix-core instructions
+// (i8, FP6 x FP4, bf16) on register operands, and the data path of one
+// compute unit (LDS reads, LDS-direct loads, and the two mixed with
+// matrix-core work in the proportions of one FP6 x FP4 GEMM K step).  The
+// benchmark times them and reports its own kernels against the measured
+// figures beside the published peaks.  Not part of the H-BitLinear layer.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -109,6 +111,121 @@ __global__ __launch_bounds__(256) void peak_mfma_kernel(int32_t* __restrict__ ou
     out[(int64_t)blockIdx.x * 256 + t] = res;
 }
 
+// ---- data path of one compute unit
+constexpr int kLdsThreads = 512;             // 8 waves, two per SIMD
+constexpr int kLdsBytes = 96 * 1024;         // > 80 KiB: one workgroup per compute unit
+constexpr int kLdsWaveSpan = 10 * 1024;      // LDS-direct ring of a wave: 2 rounds x 5 KiB
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// One LDS-direct load: lane l's 16 bytes at voff of the resource land at LDS
+// byte lds_addr + 16*l (M0 holds lds_addr and is restored); no register result.
+__device__ __forceinline__ void peak_lds_direct16(v4u desc, uint32_t lds_addr, uint32_t voff) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_addr), "v"(voff), "s"(desc)
+        : "memory");
+}
+
+// s_waitcnt on the vector-memory counter alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void peak_wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kLdsThreads, 1) void peak_lds_kernel(const uint8_t* __restrict__ src, uint32_t src_mask,
+                                                                 int iters, int64_t* __restrict__ clk,
+                                                                 uint32_t* __restrict__ sink) {
+    constexpr bool kLoads = KIND != HBL_PEAK_LDS_READ;
+    constexpr bool kReads = KIND != HBL_PEAK_LDS_DIRECT;
+    constexpr bool kMfma = KIND == HBL_PEAK_LDS_KSTEP || KIND == HBL_PEAK_LDS_KSTEP_NOBAR;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < kLdsBytes / 16; i += kLdsThreads)
+        reinterpret_cast<uint4*>(lds)[i] = make_uint4(i, 3 * i + 1, 5 * i + 2, 7 * i + 3);
+    __syncthreads();
+    const uint64_t a = (uint64_t)src;
+    const v4u desc = {(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, src_mask + 1u, 0x00020000u};
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+    const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr + (uint32_t)(wave * kLdsWaveSpan));
+    const uint32_t first = (uint32_t)((blockIdx.x * 8 + wave) * 5) * 1024u + (uint32_t)lane * 16u;
+    auto issue = [&](int it) {
+        if constexpr (kLoads) {
+#pragma unroll
+            for (int u = 0; u < 5; u++)
+                peak_lds_direct16(desc, ring + (uint32_t)((it & 1) * 5120 + u * 1024),
+                                  (first + (uint32_t)u * 1024u + (uint32_t)it * 40960u) & src_mask);
+        }
+    };
+    long long t0 = 0, r0 = 0;
+    if (tid == 0) {
+        t0 = (long long)__builtin_amdgcn_s_memtime();
+        r0 = (long long)__builtin_amdgcn_s_memrealtime();
+    }
+    uint4 x = make_uint4(0, 0, 0, 0);
+    v16f acc[8] = {};
+    v8i fa = {lane, 1, 2, 3, 4, 5, 0, 0};
+    const v8i fb = {lane ^ 5, 3, 2, 1, 0, 0, 0, 0};
+    issue(0);
+    issue(1);
+    for (int it = 0; it < iters; it++) {
+        if constexpr (kLoads) peak_wait_vmcnt<5>();  // this round's loads have landed
+        if constexpr (KIND == HBL_PEAK_LDS_KSTEP) asm volatile("s_barrier" ::: "memory");
+        issue(it + 2 < iters ? it + 2 : iters - 1);
+        if constexpr (kReads) {
+            // a wave reads its own ring and the next wave's: offsets below 86 KiB
+            const uint8_t* rd = lds + wave * kLdsWaveSpan + lane * 16 + (it & 3) * 64;
+            uint4 f[14];
+#pragma unroll
+            for (int q = 0; q < 14; q++) f[q] = *reinterpret_cast<const uint4*>(rd + q * 1024);
+            if constexpr (kMfma) {
+#pragma unroll
+                for (int m = 0; m < 16; m++) {  // one LDS read between consecutive instructions
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    acc[m & 7] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, acc[m & 7], 3, 4, 0, 0, 0, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 14; q += 2) {
+                x.x ^= f[q].x ^ f[q + 1].x;
+                x.y ^= f[q].y ^ f[q + 1].y;
+                x.z ^= f[q].z ^ f[q + 1].z;
+                x.w ^= f[q].w ^ f[q + 1].w;
+            }
+            if constexpr (kMfma) fa[0] ^= (int)(x.x & 1u);  // the next round's instructions use this round's reads
+        }
+    }
+    peak_wait_vmcnt<0>();  // no LDS-direct load may be in flight when the workgroup ends
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) s += acc[j][r];
+    const uint32_t v = x.x ^ x.y ^ x.z ^ x.w ^ __float_as_uint(s);
+    if (v == 0x9E3779B9u) sink[blockIdx.x] = v;
+    if (tid == 0) {
+        clk[2 * (int64_t)blockIdx.x] = (long long)__builtin_amdgcn_s_memtime() - t0;
+        clk[2 * (int64_t)blockIdx.x + 1] = (long long)__builtin_amdgcn_s_memrealtime() - r0;
+    }
+}
+
+template <int KIND>
+int launch_peak_lds(const void* src, uint32_t mask, int blocks, int iters, int64_t* clk, uint32_t* sink,
+                    hipStream_t s) {
+    auto k = peak_lds_kernel<KIND>;
+    if (hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess)
+        return 2;
+    hipLaunchKernelGGL(k, dim3(blocks), dim3(kLdsThreads), kLdsBytes, s, (const uint8_t*)src, mask, iters, clk, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
 int64_t ops_per_instruction(int kind) {
     switch (kind) {
         case HBL_PEAK_MFMA_I8: return 2LL * 32 * 32 * 32;
@@ -180,4 +297,24 @@ extern "C" int hbl_peak_empty(int blocks, void* stream) {
     if (blocks < 1 || blocks > (1 << 20)) return 1;
     hipLaunchKernelGGL(peak_empty_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream);
     return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+extern "C" int hbl_peak_lds(int kind, const void* src, int64_t src_bytes, int blocks, int iters, int64_t* clk,
+                            int64_t clk_len, uint32_t* sink, int64_t sink_len, void* stream) {
+    if (kind < HBL_PEAK_LDS_READ || kind > HBL_PEAK_LDS_KSTEP_NOBAR) return 1;
+    if (blocks < 1 || blocks > (1 << 20) || iters < 2 || iters > (1 << 24)) return 1;
+    if (!clk || clk_len < 2 * (int64_t)blocks || !sink || sink_len < blocks) return 1;
+    uint32_t mask = 0;
+    if (kind != HBL_PEAK_LDS_READ) {
+        if (!src || (uintptr_t)src % 16) return 1;
+        if (src_bytes < (1 << 16) || src_bytes > (1 << 30) || (src_bytes & (src_bytes - 1)) != 0) return 1;
+        mask = (uint32_t)(src_bytes - 1);
+    }
+    const hipStream_t s = (hipStream_t)stream;
+    switch (kind) {
+        case HBL_PEAK_LDS_READ: return launch_peak_lds<HBL_PEAK_LDS_READ>(src, mask, blocks, iters, clk, sink, s);
+        case HBL_PEAK_LDS_DIRECT: return launch_peak_lds<HBL_PEAK_LDS_DIRECT>(src, mask, blocks, iters, clk, sink, s);
+        case HBL_PEAK_LDS_KSTEP: return launch_peak_lds<HBL_PEAK_LDS_KSTEP>(src, mask, blocks, iters, clk, sink, s);
+        default: return launch_peak_lds<HBL_PEAK_LDS_KSTEP_NOBAR>(src, mask, blocks, iters, clk, sink, s);
+    }
 }

@@ -54,6 +54,31 @@ int hbl_peak_mfma(int kind, int32_t* out, int64_t out_len, int blocks, int iters
  * or -1 for an invalid argument. */
 int64_t hbl_peak_mfma_ops(int kind, int blocks, int iters);
 
+/* Data-path probe of hbl_peak_lds: the work of one wave in one round. */
+enum {
+    HBL_PEAK_LDS_READ = 0,      /* 14 LDS reads of 16 bytes per lane (14 KiB per wave) */
+    HBL_PEAK_LDS_DIRECT = 1,    /* 5 LDS-direct loads (buffer_load ... lds) of 1 KiB from src */
+    HBL_PEAK_LDS_KSTEP = 2,     /* 5 LDS-direct loads, 14 LDS reads, 16 FP6 x FP4 32x32x64
+                                   matrix-core instructions, one workgroup barrier: the per-wave
+                                   work of one 128-deep K step of a 256 x 256 FP6 x FP4 tile */
+    HBL_PEAK_LDS_KSTEP_NOBAR = 3 /* the same without the barrier */
+};
+
+/* `blocks` workgroups of 8 waves, each holding 96 KiB of LDS so that no two
+ * share a compute unit (launch one per compute unit); every wave runs `iters`
+ * rounds of the work of `kind`, with its LDS-direct loads two rounds ahead.
+ * src (device, 16-byte aligned) holds src_bytes, a power of two in
+ * [64 KiB, 1 GiB]; the loads walk it round robin (a small src stays in the
+ * L2 caches).  Kind HBL_PEAK_LDS_READ ignores src (it may be NULL).
+ * clk (device, clk_len >= 2 * blocks 64-bit words) receives, per workgroup,
+ * the shader-clock cycles (s_memtime) and the 100 MHz real-time ticks
+ * (s_memrealtime) that its first wave spent in the loop: their ratio is the
+ * shader clock.  sink (device, sink_len >= blocks words) is written only if
+ * the folded data hit a fixed value, so nothing can be discarded.
+ * blocks in [1, 2^20], iters in [2, 2^24]. */
+int hbl_peak_lds(int kind, const void* src, int64_t src_bytes, int blocks, int iters, int64_t* clk,
+                 int64_t clk_len, uint32_t* sink, int64_t sink_len, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -244,6 +244,8 @@ def _peaks_lib():
     lib.hbl_peak_read_sink_len.argtypes = [ctypes.c_int64]
     lib.hbl_peak_read_sink_len.restype = ctypes.c_int64
     lib.hbl_peak_empty.argtypes = [ctypes.c_int32, ctypes.c_void_p]
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.hbl_peak_lds.argtypes = [I32, P, I64, I32, I32, P, I64, P, I64, P]
     return lib
 
 
@@ -254,8 +256,8 @@ def test_peaks_library_exports_and_host_checks():
     import os
     lib = _peaks_lib()
     names = hbl.declared_symbols(os.path.join(os.path.dirname(hbl.HEADER_PATH), "hbl_peaks.h"))
-    assert names == ["hbl_peak_copy", "hbl_peak_empty", "hbl_peak_mfma", "hbl_peak_mfma_ops", "hbl_peak_read",
-                     "hbl_peak_read_sink_len"]
+    assert names == ["hbl_peak_copy", "hbl_peak_empty", "hbl_peak_lds", "hbl_peak_mfma", "hbl_peak_mfma_ops",
+                     "hbl_peak_read", "hbl_peak_read_sink_len"]
     assert all(hasattr(lib, n) for n in names)
     # 4 waves x 4 instructions per round: i8 32x32x32, FP6 x FP4 32x32x64, bf16 32x32x16
     assert lib.hbl_peak_mfma_ops(0, 1, 1) == 16 * 2 * 32 * 32 * 32
@@ -277,6 +279,20 @@ def test_peaks_library_exports_and_host_checks():
     assert lib.hbl_peak_read(24, 4096, 32, 256, None) == 1           # misaligned
     assert lib.hbl_peak_read(16, 0, 32, 256, None) == 1              # nothing to read
     assert lib.hbl_peak_empty(0, None) == 1 and lib.hbl_peak_empty((1 << 20) + 1, None) == 1
+    # data-path probe: kind, source size (a power of two in [64 KiB, 1 GiB]), counts and buffer lengths
+    good = (1, 4096, 1 << 21, 4, 10, 64, 8, 128, 4, None)
+    def lds(**kw):
+        a = list(good)
+        for k, v in kw.items():
+            a[["kind", "src", "bytes", "blocks", "iters", "clk", "clk_len", "sink", "sink_len", "s"].index(k)] = v
+        return lib.hbl_peak_lds(*a)
+    assert lds(kind=4) == 1 and lds(kind=-1) == 1
+    assert lds(bytes=(1 << 21) + 16) == 1 and lds(bytes=1 << 15) == 1 and lds(bytes=1 << 31) == 1
+    assert lds(src=None) == 1 and lds(src=4104) == 1
+    assert lds(blocks=0) == 1 and lds(blocks=(1 << 20) + 1) == 1
+    assert lds(iters=1) == 1 and lds(iters=(1 << 24) + 1) == 1
+    assert lds(clk_len=7) == 1 and lds(clk=None) == 1
+    assert lds(sink_len=3) == 1 and lds(sink=None) == 1
 
 
 def test_fp4_fp6_validation(lib):
