@@ -67,7 +67,8 @@ def cpu_model() -> str:
 def measured_peaks():
     """Ceilings measured on this GPU by the probe kernels of libhbl_peaks.so
     (built beside libhbl.so), timed with HIP events on the stream they run on:
-      * a 512 MiB streaming copy (read + write bytes),
+      * a 512 MiB streaming copy (read + write bytes), and a 32 MiB streaming
+        write (the output burst of one wave of FP6 x FP4 GEMM tiles),
       * streaming reads of 8 MiB (the decode layer's 2-bit weights) and of
         64 MiB, each launch replayed from a HIP graph over buffers rotated
         past the last-level cache,
@@ -145,6 +146,16 @@ def measured_peaks():
         ok(lib.hbl_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes, sp), "copy")
 
     out = {"hbm_copy_GBps": round(2 * nbytes / (best_us(copy) * 1e-6) / 1e9, 1)}
+    # a 32 MiB streaming write (the output of one wave of 256 x 256 bf16 GEMM tiles on 256 compute units)
+    # over distinct slices of the 512 MiB buffer, graph-replayed
+    wsize = 32 << 20
+    lib.hbl_peak_write.argtypes = [P, I64, P]
+    wbase = dst.data_ptr()
+    launches = [lambda i=i: ok(lib.hbl_peak_write(ctypes.c_void_p(wbase + i * wsize), wsize, cur()), "write")
+                for i in range(nbytes // wsize)]
+    us = graph_best_us(launches)
+    out["hbm_write_32MiB_GBps"] = round(wsize / (us * 1e-6) / 1e9, 1)
+    out["hbm_write_32MiB_us"] = round(us, 3)
     del dst
     # streaming reads at the decode layer's weight size and at 64 MiB, over
     # distinct slices of the 512 MiB buffer (every replay reads cold data)
@@ -178,7 +189,8 @@ def measured_peaks():
     clk = torch.zeros(2 * cus, dtype=torch.int64, device=dev)
     lsink = torch.zeros(cus, dtype=torch.int32, device=dev)
     rounds = 2000
-    for kind, key in ((0, "lds_read"), (1, "lds_direct"), (2, "fp6_kstep"), (3, "fp6_kstep_nobarrier")):
+    for kind, key in ((0, "lds_read"), (1, "lds_direct"), (2, "fp6_kstep"), (3, "fp6_kstep_nobarrier"),
+                      (4, "fp6_kstep_noload")):
         def run(kind=kind):
             ok(lib.hbl_peak_lds(kind, ctypes.c_void_p(lsrc.data_ptr()), lsrc.numel() * 4, cus, rounds,
                                 ctypes.c_void_p(clk.data_ptr()), clk.numel(), ctypes.c_void_p(lsink.data_ptr()),
@@ -201,7 +213,8 @@ def measured_peaks():
                      "matrix-core instructions per round on register operands; one 8-wave workgroup per compute "
                      "unit for the LDS data path: per wave and round 14 LDS reads of 16 B (lds_read), 5 LDS-direct "
                      "loads of 1 KiB from a 2 MiB source (lds_direct), and both with 16 FP6 x FP4 instructions "
-                     "and a barrier (fp6_kstep: one K step of the 256 x 256 FP6 x FP4 tile; _nobarrier without it)")
+                     "and a barrier (fp6_kstep: one K step of the 256 x 256 FP6 x FP4 tile; _nobarrier without the "
+                     "barrier, _noload without the loads); a 32 MiB streaming write, graph-replayed")
     _PEAKS = out
     log("measured peaks done")
     return out

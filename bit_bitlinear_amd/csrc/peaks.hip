@@ -57,6 +57,18 @@ __global__ __launch_bounds__(kCopyThreads) void peak_read_kernel(const uint4* __
     if (x == 0x9E3779B9u) sink[(int64_t)blockIdx.x * kCopyThreads + threadIdx.x] = x;
 }
 
+// Streaming write: each thread stores kCopyUnroll 16-byte vectors spaced one
+// block apart; nothing is read.
+__global__ __launch_bounds__(kCopyThreads) void peak_write_kernel(uint4* __restrict__ dst, int64_t n) {
+    const int64_t base = (int64_t)blockIdx.x * (kCopyThreads * kCopyUnroll) + threadIdx.x;
+    const uint4 v = make_uint4((uint32_t)base, (uint32_t)blockIdx.x, 0x5A5A5A5Au, 0u);
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; u++) {
+        const int64_t i = base + (int64_t)u * kCopyThreads;
+        if (i < n) dst[i] = v;
+    }
+}
+
 // An empty kernel: the per-launch floor of a grid of the given size.
 __global__ __launch_bounds__(256) void peak_empty_kernel() {}
 
@@ -142,9 +154,10 @@ template <int KIND>
 __global__ __launch_bounds__(kLdsThreads, 1) void peak_lds_kernel(const uint8_t* __restrict__ src, uint32_t src_mask,
                                                                  int iters, int64_t* __restrict__ clk,
                                                                  uint32_t* __restrict__ sink) {
-    constexpr bool kLoads = KIND != HBL_PEAK_LDS_READ;
+    constexpr bool kLoads = KIND != HBL_PEAK_LDS_READ && KIND != HBL_PEAK_LDS_KSTEP_NOLOAD;
     constexpr bool kReads = KIND != HBL_PEAK_LDS_DIRECT;
-    constexpr bool kMfma = KIND == HBL_PEAK_LDS_KSTEP || KIND == HBL_PEAK_LDS_KSTEP_NOBAR;
+    constexpr bool kMfma = KIND == HBL_PEAK_LDS_KSTEP || KIND == HBL_PEAK_LDS_KSTEP_NOBAR ||
+                           KIND == HBL_PEAK_LDS_KSTEP_NOLOAD;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int i = tid; i < kLdsBytes / 16; i += kLdsThreads)
@@ -176,7 +189,8 @@ __global__ __launch_bounds__(kLdsThreads, 1) void peak_lds_kernel(const uint8_t*
     issue(1);
     for (int it = 0; it < iters; it++) {
         if constexpr (kLoads) peak_wait_vmcnt<5>();  // this round's loads have landed
-        if constexpr (KIND == HBL_PEAK_LDS_KSTEP) asm volatile("s_barrier" ::: "memory");
+        if constexpr (KIND == HBL_PEAK_LDS_KSTEP || KIND == HBL_PEAK_LDS_KSTEP_NOLOAD)
+            asm volatile("s_barrier" ::: "memory");
         issue(it + 2 < iters ? it + 2 : iters - 1);
         if constexpr (kReads) {
             // a wave reads its own ring and the next wave's: offsets below 86 KiB
@@ -287,6 +301,19 @@ extern "C" int hbl_peak_read(const void* src, int64_t bytes, uint32_t* sink, int
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
+extern "C" int hbl_peak_write(void* dst, int64_t bytes, void* stream) {
+    if (bytes < 0 || bytes % 16) return 1;
+    if (bytes == 0) return 0;
+    if (!dst || (uintptr_t)dst % 16) return 1;
+    const int64_t n = bytes / 16;
+    const int64_t per_block = kCopyThreads * kCopyUnroll;
+    const int64_t blocks = (n + per_block - 1) / per_block;
+    if (blocks > 0x7FFFFFFF) return 1;
+    hipLaunchKernelGGL(peak_write_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0, (hipStream_t)stream,
+                       (uint4*)dst, n);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
 extern "C" int64_t hbl_peak_read_sink_len(int64_t bytes) {
     if (bytes <= 0 || bytes % 16) return -1;
     const int64_t per_block = kCopyThreads * kCopyUnroll;
@@ -301,11 +328,11 @@ extern "C" int hbl_peak_empty(int blocks, void* stream) {
 
 extern "C" int hbl_peak_lds(int kind, const void* src, int64_t src_bytes, int blocks, int iters, int64_t* clk,
                             int64_t clk_len, uint32_t* sink, int64_t sink_len, void* stream) {
-    if (kind < HBL_PEAK_LDS_READ || kind > HBL_PEAK_LDS_KSTEP_NOBAR) return 1;
+    if (kind < HBL_PEAK_LDS_READ || kind > HBL_PEAK_LDS_KSTEP_NOLOAD) return 1;
     if (blocks < 1 || blocks > (1 << 20) || iters < 2 || iters > (1 << 24)) return 1;
     if (!clk || clk_len < 2 * (int64_t)blocks || !sink || sink_len < blocks) return 1;
     uint32_t mask = 0;
-    if (kind != HBL_PEAK_LDS_READ) {
+    if (kind != HBL_PEAK_LDS_READ && kind != HBL_PEAK_LDS_KSTEP_NOLOAD) {
         if (!src || (uintptr_t)src % 16) return 1;
         if (src_bytes < (1 << 16) || src_bytes > (1 << 30) || (src_bytes & (src_bytes - 1)) != 0) return 1;
         mask = (uint32_t)(src_bytes - 1);
@@ -315,6 +342,8 @@ extern "C" int hbl_peak_lds(int kind, const void* src, int64_t src_bytes, int bl
         case HBL_PEAK_LDS_READ: return launch_peak_lds<HBL_PEAK_LDS_READ>(src, mask, blocks, iters, clk, sink, s);
         case HBL_PEAK_LDS_DIRECT: return launch_peak_lds<HBL_PEAK_LDS_DIRECT>(src, mask, blocks, iters, clk, sink, s);
         case HBL_PEAK_LDS_KSTEP: return launch_peak_lds<HBL_PEAK_LDS_KSTEP>(src, mask, blocks, iters, clk, sink, s);
-        default: return launch_peak_lds<HBL_PEAK_LDS_KSTEP_NOBAR>(src, mask, blocks, iters, clk, sink, s);
+        case HBL_PEAK_LDS_KSTEP_NOBAR:
+            return launch_peak_lds<HBL_PEAK_LDS_KSTEP_NOBAR>(src, mask, blocks, iters, clk, sink, s);
+        default: return launch_peak_lds<HBL_PEAK_LDS_KSTEP_NOLOAD>(src, mask, blocks, iters, clk, sink, s);
     }
 }

@@ -31,6 +31,11 @@ enum {
  * of HBM traffic (read + write). */
 int hbl_peak_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
+/* Streaming write of `bytes` (a multiple of 16, >= 0) to dst (16-byte
+ * aligned), 16 bytes per lane and store, four stores per thread, nothing
+ * read: the burst of output one wave of GEMM tiles leaves behind. */
+int hbl_peak_write(void* dst, int64_t bytes, void* stream);
+
 /* Streaming read of `bytes` (a multiple of 16, > 0) from src (16-byte
  * aligned), 16 bytes per lane and load, four loads per thread; nothing is
  * written unless the data's folded words hit a fixed value, so the traffic
@@ -61,7 +66,8 @@ enum {
     HBL_PEAK_LDS_KSTEP = 2,     /* 5 LDS-direct loads, 14 LDS reads, 16 FP6 x FP4 32x32x64
                                    matrix-core instructions, one workgroup barrier: the per-wave
                                    work of one 128-deep K step of a 256 x 256 FP6 x FP4 tile */
-    HBL_PEAK_LDS_KSTEP_NOBAR = 3 /* the same without the barrier */
+    HBL_PEAK_LDS_KSTEP_NOBAR = 3, /* the same without the barrier */
+    HBL_PEAK_LDS_KSTEP_NOLOAD = 4 /* HBL_PEAK_LDS_KSTEP without the LDS-direct loads */
 };
 
 /* `blocks` workgroups of 8 waves, each holding 96 KiB of LDS so that no two
@@ -69,7 +75,8 @@ enum {
  * rounds of the work of `kind`, with its LDS-direct loads two rounds ahead.
  * src (device, 16-byte aligned) holds src_bytes, a power of two in
  * [64 KiB, 1 GiB]; the loads walk it round robin (a small src stays in the
- * L2 caches).  Kind HBL_PEAK_LDS_READ ignores src (it may be NULL).
+ * L2 caches).  Kinds HBL_PEAK_LDS_READ and HBL_PEAK_LDS_KSTEP_NOLOAD ignore
+ * src (it may be NULL).
  * clk (device, clk_len >= 2 * blocks 64-bit words) receives, per workgroup,
  * the shader-clock cycles (s_memtime) and the 100 MHz real-time ticks
  * (s_memrealtime) that its first wave spent in the loop: their ratio is the

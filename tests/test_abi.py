@@ -257,7 +257,7 @@ def test_peaks_library_exports_and_host_checks():
     lib = _peaks_lib()
     names = hbl.declared_symbols(os.path.join(os.path.dirname(hbl.HEADER_PATH), "hbl_peaks.h"))
     assert names == ["hbl_peak_copy", "hbl_peak_empty", "hbl_peak_lds", "hbl_peak_mfma", "hbl_peak_mfma_ops",
-                     "hbl_peak_read", "hbl_peak_read_sink_len"]
+                     "hbl_peak_read", "hbl_peak_read_sink_len", "hbl_peak_write"]
     assert all(hasattr(lib, n) for n in names)
     # 4 waves x 4 instructions per round: i8 32x32x32, FP6 x FP4 32x32x64, bf16 32x32x16
     assert lib.hbl_peak_mfma_ops(0, 1, 1) == 16 * 2 * 32 * 32 * 32
@@ -286,13 +286,18 @@ def test_peaks_library_exports_and_host_checks():
         for k, v in kw.items():
             a[["kind", "src", "bytes", "blocks", "iters", "clk", "clk_len", "sink", "sink_len", "s"].index(k)] = v
         return lib.hbl_peak_lds(*a)
-    assert lds(kind=4) == 1 and lds(kind=-1) == 1
+    assert lds(kind=5) == 1 and lds(kind=-1) == 1
     assert lds(bytes=(1 << 21) + 16) == 1 and lds(bytes=1 << 15) == 1 and lds(bytes=1 << 31) == 1
     assert lds(src=None) == 1 and lds(src=4104) == 1
     assert lds(blocks=0) == 1 and lds(blocks=(1 << 20) + 1) == 1
     assert lds(iters=1) == 1 and lds(iters=(1 << 24) + 1) == 1
     assert lds(clk_len=7) == 1 and lds(clk=None) == 1
     assert lds(sink_len=3) == 1 and lds(sink=None) == 1
+    lib.hbl_peak_write.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    assert lib.hbl_peak_write(4096, 17, None) == 1                  # not a multiple of 16
+    assert lib.hbl_peak_write(None, 16, None) == 1                  # null
+    assert lib.hbl_peak_write(4104, 16, None) == 1                  # misaligned
+    assert lib.hbl_peak_write(4096, 0, None) == 0                   # nothing to do
 
 
 def test_fp4_fp6_validation(lib):
