@@ -381,7 +381,9 @@ class Prepared:
             hbl.hbl_gemm(codes, xs, L.act_bits, L.K, s["Wp"], self.alpha, L.N, Y=s["Y"])
 
     def work(self):
-        """Algorithmic work per launch of each kernel (SURVEY-defined units)."""
+        """Algorithmic work per launch of each kernel: bytes that must cross HBM
+        (input rows, INT8/INT4-equivalent codes, scales, 2-bit weights, output)
+        and 2*M*N*K integer ops for the product."""
         L = self.layer
         x_bytes = L.M * L.K * (2 if L.x_dtype == "bf16" else 4)
         y_bytes = L.M * L.N * (2 if L.y_dtype == "bf16" else 4)
