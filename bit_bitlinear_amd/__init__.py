@@ -497,7 +497,8 @@ def hbl_pack_fp4(W_packed, K: int, W4=None, stream=None):
 
 def hbl_quantize_activations_fp6(X, cfg: Config, gain=None, codes6=None, xscale=None, stream=None):
     """INT4 activation codes of X [M][K] as FP6 (the FP6 x FP4 GEMM's operand
-    order).  Returns (codes6 uint8 [M][K*3/4], xscale float32 [M])."""
+    order, private to the library, for these M and K).  Returns (codes6 uint8
+    [M][K*3/4] as storage, xscale float32 [M])."""
     torch = _torch()
     lib = load_library()
     _dev(X, "X"); _dev(gain, "gain")

@@ -52,9 +52,13 @@ __global__ __launch_bounds__(NT) void act_pack_kernel(const Tin* __restrict__ X,
         const int64_t row = b - p_lo;
         ActRegs<LK, NT, Tin> v;
         act_row_load<LK, NT, Tin>(X + row * S::K, v);
-        uint8_t* const crow = codes + (LAYOUT == kCodesDecTiled ? dec_tile_row_base<BITS>(row, S::K) : row * (LAYOUT == kCodesFp6 ? S::K * 3 / 4 : S::K * BITS / 8));
+        const Fp6RowPlace f6 = LAYOUT == kCodesFp6 ? fp6_row_place(row, M, S::K) : Fp6RowPlace{0, 96, 0};
+        uint8_t* const crow = codes + (LAYOUT == kCodesDecTiled ? dec_tile_row_base<BITS>(row, S::K)
+                                       : LAYOUT == kCodesFp6    ? f6.base
+                                                                : row * (S::K * BITS / 8));
         act_row_quantise<LK, NT, Tin, BITS, HAD, LAYOUT>(v, gain, norm, norm_eps, quant_eps, a4_mode, lds, partf,
-                                                        partd, crow, xscale + row, nullptr, nullptr);
+                                                        partd, crow, xscale + row, nullptr, nullptr, f6.stride,
+                                                        f6.swz);
     } else if (partial_out) {
         __shared__ double red[kPartialVThreads / kWave];
         wq_partial_block<TW, NT>(W, count, per_block, partial_out, p_lo, red);

@@ -16,27 +16,35 @@ namespace {
 // statistic and the pointers at run time (3B-like layer shapes, K = 2048 to
 // 16384).
 template <int LK, int NT, typename Tin, int BITS, bool HAD, int LAYOUT, bool PLAIN>
-__global__ __launch_bounds__(NT) void act_quant_kernel(const Tin* __restrict__ X, const float* __restrict__ gain,
-                                                       int norm, float norm_eps, float quant_eps, int a4_mode,
-                                                       uint8_t* __restrict__ codes, float* __restrict__ xscale,
-                                                       float* __restrict__ z_debug, float* __restrict__ s_debug) {
+__global__ __launch_bounds__(NT) void act_quant_kernel(const Tin* __restrict__ X, int64_t M,
+                                                       const float* __restrict__ gain, int norm, float norm_eps,
+                                                       float quant_eps, int a4_mode, uint8_t* __restrict__ codes,
+                                                       float* __restrict__ xscale, float* __restrict__ z_debug,
+                                                       float* __restrict__ s_debug) {
     using S = ActShape<LK, NT, Tin>;
     extern __shared__ __attribute__((aligned(16))) float lds[];  // float4 accesses
     __shared__ ActPartF<LK, NT, Tin> partf;
     __shared__ ActPartD<LK, NT, Tin> partd;
-    const int64_t row = blockIdx.x;
+    // FP6 codes: rows are dealt to the XCDs in contiguous ranges (block b runs
+    // on XCD b % 8), so that the 96-byte pieces of neighbouring rows, which
+    // share cache lines in the FP6 layout, meet in one L2
+    const int64_t b = blockIdx.x;
+    const int64_t row = LAYOUT == kCodesFp6 && M % 8 == 0 ? (b % 8) * (M / 8) + b / 8 : b;
     ActRegs<LK, NT, Tin> v;
     act_row_load<LK, NT, Tin>(X + row * S::K, v);
-    uint8_t* const crow = codes + (LAYOUT == kCodesDecTiled ? dec_tile_row_base<BITS>(row, S::K) : row * (LAYOUT == kCodesFp6 ? S::K * 3 / 4 : S::K * BITS / 8));
+    const Fp6RowPlace f6 = LAYOUT == kCodesFp6 ? fp6_row_place(row, M, S::K) : Fp6RowPlace{0, 96, 0};
+    uint8_t* const crow = codes + (LAYOUT == kCodesDecTiled ? dec_tile_row_base<BITS>(row, S::K)
+                                   : LAYOUT == kCodesFp6    ? f6.base
+                                                            : row * (S::K * BITS / 8));
     if constexpr (PLAIN)
         act_row_quantise<LK, NT, Tin, BITS, HAD, LAYOUT>(v, nullptr, (int)HBL_NORM_RMS, norm_eps, quant_eps,
                                                         (int)HBL_A4_ABSMEAN_SQRT7, lds, partf, partd, crow,
-                                                        xscale + row, nullptr, nullptr);
+                                                        xscale + row, nullptr, nullptr, f6.stride, f6.swz);
     else
         act_row_quantise<LK, NT, Tin, BITS, HAD, LAYOUT>(v, gain, norm, norm_eps, quant_eps, a4_mode, lds, partf,
                                                         partd, crow, xscale + row,
                                                         z_debug ? z_debug + row * S::K : nullptr,
-                                                        s_debug ? s_debug + row : nullptr);
+                                                        s_debug ? s_debug + row : nullptr, f6.stride, f6.swz);
 }
 
 template <int LK, typename Tin, int BITS, bool HAD, int LAYOUT, bool PLAIN>
@@ -50,7 +58,7 @@ hipError_t launch_one_as(const Tin* X, int64_t M, const float* gain, const hbl_c
     static std::atomic<uint32_t> lds_set{0};  // devices with the LDS limit raised for this kernel
     if (hipError_t e = set_dynamic_lds(kern, lds_bytes, lds_set); e != hipSuccess) return e;
     // one workgroup per row; gridDim.x is limited to 2^31-1
-    hipLaunchKernelGGL(kern, dim3((unsigned)M), dim3(NT), lds_bytes, s, X, gain, cfg.norm, cfg.norm_eps,
+    hipLaunchKernelGGL(kern, dim3((unsigned)M), dim3(NT), lds_bytes, s, X, M, gain, cfg.norm, cfg.norm_eps,
                        cfg.quant_eps, cfg.a4_mode, (uint8_t*)codes, xscale, z_debug, s_debug);
     return hipGetLastError();
 }

@@ -269,12 +269,13 @@ HBL_DEVINL void act_row_load(const Tin* __restrict__ x, ActRegs<LK, NT, Tin>& v)
 // kCodesDecTiled: crow is the row's base in the decode tile layout
 // (dec_tile_row_base) and byte kb goes to crow + dec_tile_offset(kb).
 // kCodesFp6 (INT4 only, four values per vector): the codes go out as FP6 E3M2
-// in the FP6 GEMM layout (fp6_byte_offset), crow at the row's K*3/4 bytes.
+// in the FP6 GEMM layout (hbl_device.h): crow at the row's 96 bytes of K step
+// 0, fp6_stride bytes between K steps, fp6_swz = the row's chunk swap.
 template <int LK, int NT, typename Tin, int BITS, bool HAD, int LAYOUT = kCodesRowMajor>
 HBL_DEVINL void act_row_quantise(ActRegs<LK, NT, Tin>& v, const float* __restrict__ gain, int norm, float norm_eps,
                                  float quant_eps, int a4_mode, float* lds, ActPartF<LK, NT, Tin>& partf,
                                  ActPartD<LK, NT, Tin>& partd, uint8_t* crow, float* xs_out, float* z_row,
-                                 float* s_out) {
+                                 float* s_out, int64_t fp6_stride = 96, int fp6_swz = 0) {
     using S = ActShape<LK, NT, Tin>;
     constexpr int K = S::K, LT = S::LT, E = S::E, V = S::V, LV = S::LV, C = S::C, VB = S::VB, VW = S::VW;
     constexpr int FREE = S::FREE, NW = S::NW;
@@ -520,23 +521,25 @@ HBL_DEVINL void act_row_quantise(ActRegs<LK, NT, Tin>& v, const float* __restric
         // Each group of 16 codes (four staged dwords) becomes the 12 bytes of
         // its natural FP6 bit string and goes straight to its place in the
         // GEMM layout: per K step of 128 codes (8 groups, 96 bytes) operand
-        // op = group/2 keeps its first 16 bytes at 16 op and its last 8 at
-        // 16 (4 + op % 2) + 8 (op / 2); an even group fills bytes 0..11 of
-        // the operand, an odd one bytes 12..23 (4 in the first piece, 8 in
-        // the second).  All stores 4-byte aligned.
+        // op = group/2 keeps its first 16 bytes in chunk op and its last 8 in
+        // half op / 2 of chunk 4 + op % 2 (chunks swapped as fp6_swz says);
+        // an even group fills bytes 0..11 of the operand, an odd one bytes
+        // 12..23 (4 in the first piece, 8 in the second).  All stores 4-byte
+        // aligned.
         __syncthreads();
         const uint4* src = reinterpret_cast<const uint4*>(lds);
         for (int q = tid; q < K / 16; q += NT) {
             const uint4 d = src[q];
             const uint32_t w0 = d.x | (d.y << 24), w1 = (d.y >> 8) | (d.z << 16), w2 = (d.z >> 16) | (d.w << 8);
             const int j = q & 7, op = j >> 1;
-            uint8_t* const step = crow + 96 * (q >> 3);
+            uint8_t* const step = crow + fp6_stride * (q >> 3);
+            uint8_t* const c16 = step + 16 * (op ^ fp6_swz);
             if ((j & 1) == 0) {
-                uint32_t* p = reinterpret_cast<uint32_t*>(step + 16 * op);
+                uint32_t* p = reinterpret_cast<uint32_t*>(c16);
                 p[0] = w0; p[1] = w1; p[2] = w2;
             } else {
-                *reinterpret_cast<uint32_t*>(step + 16 * op + 12) = w0;
-                *reinterpret_cast<uint2*>(step + 16 * (4 + (op & 1)) + 8 * (op >> 1)) = make_uint2(w1, w2);
+                *reinterpret_cast<uint32_t*>(c16 + 12) = w0;
+                *reinterpret_cast<uint2*>(step + 16 * (4 + ((op & 1) ^ fp6_swz)) + 8 * (op >> 1)) = make_uint2(w1, w2);
             }
         }
     }

@@ -70,7 +70,28 @@ HBL_DEVINL int dec_tile_offset(int kb) {  // kb: byte index of the code inside i
 // first 16 bytes are stored as 16-byte chunk 2s + h of the step and its last
 // 8 bytes as half s of chunk 4 + h, so that every lane reads one 16-byte and
 // one 8-byte piece.  A row is K*3/4 bytes.
+// Across rows the codes are grouped in bands of kF6Band rows (the GEMM's
+// block height).  In a band of R rows (R = kF6Band except in the last band),
+// K step s of all R rows is one block of R*96 bytes, row r of the band at
+// byte 96r, so that every LDS-direct load of the GEMM reads 1 KiB of
+// consecutive bytes.  Inside a row's 96 bytes the 16-byte chunks are stored
+// in the GEMM's LDS order (bank-conflict-free reads): in rows with bit 3 of
+// the row index set, chunk L sits at L ^ 1 (chunks 0..3) or 4 + ((L - 4) ^ 1)
+// (chunks 4, 5).  The M*K*3/4 bytes are private to the FP6 x FP4 GEMM.
 enum { kCodesRowMajor = 0, kCodesDecTiled = 1, kCodesFp6 = 2 };
+constexpr int kF6Band = 256;
+// Where row `row` of an M x K FP6 code matrix goes: its 96 bytes of K step s
+// start at base + s * stride; swz = 1 where the chunks are swapped.
+struct Fp6RowPlace {
+    int64_t base;
+    int64_t stride;
+    int swz;
+};
+HBL_DEVINL Fp6RowPlace fp6_row_place(int64_t row, int64_t M, int64_t K) {
+    const int64_t m0 = row - row % kF6Band;
+    const int64_t R = M - m0 < kF6Band ? M - m0 : kF6Band;
+    return Fp6RowPlace{m0 * (K * 3 / 4) + (row - m0) * 96, R * 96, (int)((row >> 3) & 1)};
+}
 
 // ---- wave / block reductions (fixed butterfly order: deterministic) ----
 HBL_DEVINL float wave_sum_f32(float v) {

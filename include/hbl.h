@@ -215,10 +215,11 @@ hbl_status hbl_forward_latent(const void* X, int32_t x_dtype, int64_t M, int64_t
  * hbl_quantize_weights) -> W4, the same ternary values; a deployment converts
  * once per weight.  Both buffers 16-byte aligned.
  *
- * FP6 codes: uint8 [M][K*3/4] (hbl_fp6_codes_bytes), the INT4 codes of
+ * FP6 codes: M*K*3/4 bytes (hbl_fp6_codes_bytes), the INT4 codes of
  * hbl_quantize_activations as E3M2 fields in the operand order of the
- * FP6 x FP4 GEMM; the order inside a row is private to this library and read
- * only by hbl_gemm_fp6fp4.  hbl_quantize_activations_fp6 writes them (same
+ * FP6 x FP4 GEMM (blocks of one K step of 256 rows); the order is private to
+ * this library, made for M and K together, and read only by hbl_gemm_fp6fp4
+ * with the same M and K.  hbl_quantize_activations_fp6 writes them (same
  * computation and xscale as hbl_quantize_activations with cfg->act_bits = 4,
  * which it requires; K a power of two in [512, 32768]).
  * hbl_gemm_fp6fp4: Y = fp32(fp32(acc * xscale[m]) * alpha), fp32 or bf16, from
