@@ -482,7 +482,8 @@ def hbl_forward_fp4_workspace_bytes(M: int, K: int, cfg: Config) -> int:
 
 
 def hbl_pack_fp4(W_packed, K: int, W4=None, stream=None):
-    """2-bit packed ternary weights [N][K/4] -> FP4 E2M1 weights uint8 [N][K/2]."""
+    """2-bit packed ternary weights [N][K/4] -> FP4 E2M1 weights, N*K/2 bytes
+    (held as uint8 [N][K/2]) in the library's W4 order; K % 128 == 0."""
     torch = _torch()
     lib = load_library()
     _dev(W_packed, "W_packed")

@@ -378,16 +378,23 @@ static hbl_status check_fp6_gemm(int64_t M, int64_t K, int64_t N) {
 
 static size_t fp6_codes_bytes(int64_t M, int64_t K) { return (size_t)M * (size_t)K * 3 / 4; }
 
+// The FP4 weight format holds whole GEMM K steps of 128 weights.
+static hbl_status check_fp4_shape(int64_t N, int64_t K) {
+    const hbl_status st = check_weight_shape(N, K);
+    if (st != HBL_OK) return st;
+    return K % 128 ? HBL_ERR_ALIGN : HBL_OK;
+}
+
 hbl_status hbl_fp4_weight_bytes(int64_t N, int64_t K, size_t* bytes) {
     if (!bytes) return HBL_ERR_NULL;
-    const hbl_status st = check_weight_shape(N, K);
+    const hbl_status st = check_fp4_shape(N, K);
     if (st != HBL_OK) return st;
     *bytes = (size_t)N * (size_t)(K / 2);
     return HBL_OK;
 }
 
 hbl_status hbl_pack_fp4(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W4, void* stream) {
-    const hbl_status st = check_weight_shape(N, K);
+    const hbl_status st = check_fp4_shape(N, K);
     if (st != HBL_OK) return st;
     if (!W_packed || !W4) return HBL_ERR_NULL;
     if (!aligned16(W_packed) || !aligned16(W4)) return HBL_ERR_ALIGN;

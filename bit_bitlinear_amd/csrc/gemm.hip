@@ -552,10 +552,11 @@ hipError_t launch_typed(const uint8_t* A, const float* xscale, int64_t M, int64_
 //   weights (chunks 0..3):               L ^ ((r >> 2) & 3)
 // Both maps are their own inverse.  The activation kernel stores the codes
 // already in this order, in blocks of one K step of a 256-row band (the FP6
-// layout of hbl_device.h), so every code load copies 1 KiB of consecutive
-// bytes; against rows of 96 bytes at the row stride of a row-major layout
-// this made the GEMM 9-11% faster on the 3B-like shapes.  The weight map is
-// applied on the global side.
+// layout of hbl_device.h), and the FP4 weight format stores the weights the
+// same way, so every load instruction copies 1 KiB of consecutive bytes.
+// Against rows of 96 (64) bytes at the row stride of row-major layouts this
+// made the GEMM 9-11% faster on the 3B-like shapes for the codes, and about
+// 3% more for the weights.
 //
 // Main loop, software-pipelined: the LDS fragments of the next MFMA k-step
 // are read while the current k-step's MFMAs run (scheduling barriers keep the
@@ -575,7 +576,6 @@ constexpr int kF6ARow = 96, kF6WRow = 64;  // bytes per row and K step
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-HBL_DEVINL int f6_w_chunk(int L, int r) { return L ^ ((r >> 2) & 3); }
 
 // Block BM x BN, WGM x WGN waves of (BM/WGM) x (BN/WGN), S-stage ring.
 template <int BM, int BN, int WGM, int WGN, int S>
@@ -647,16 +647,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_f6f4_kernel(
     static_assert(BM == kF6Band, "the FP6 code bands are the block height");
     const int rows_a = (int)min<int64_t>(BM, M - m0);
     const v4u a_desc = rsrc_words(A6 + m0 * a_ld, (int64_t)rows_a * a_ld);
-    const v4u w_desc = rsrc_words(W4 + n0 * w_ld, (N - n0) * w_ld);
+    // weights: the same for the FP4 layout's 256-row bands (blocks of one K
+    // step, rows_w * 64 bytes, in LDS order)
+    static_assert(BN == kF4Band, "the FP4 weight bands are the block width");
+    const int rows_w = (int)min<int64_t>(BN, N - n0);
+    const v4u w_desc = rsrc_words(W4 + n0 * w_ld, (int64_t)rows_w * w_ld);
     uint32_t a_off[T::a_inst], w_off[T::w_inst];
 #pragma unroll
     for (int u = 0; u < T::a_inst; u++) a_off[u] = (uint32_t)(((wave * T::a_inst + u) * 64 + lane) * 16);
 #pragma unroll
-    for (int u = 0; u < T::w_inst; u++) {
-        const int c = (wave * T::w_inst + u) * 64 + lane;
-        const int row = c / 4, p = c % 4;
-        w_off[u] = (uint32_t)(row * w_ld + f6_w_chunk(p, row) * 16);
-    }
+    for (int u = 0; u < T::w_inst; u++) w_off[u] = (uint32_t)(((wave * T::w_inst + u) * 64 + lane) * 16);
     const uint32_t smem_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
     // the K step's byte offset inside a row (below one row) rides in soffset;
     // the LDS destinations are wave-uniform, computed in scalar registers
@@ -666,7 +666,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_f6f4_kernel(
                            wave_s * (uint32_t)(T::w_inst * 1024);
     auto issue = [&](int kt, int st) {
         const uint32_t st_off = (uint32_t)(st * T::stage);
-        const uint32_t a_k = (uint32_t)(kt * rows_a * kF6ARow), w_k = (uint32_t)(kt * kF6WRow);
+        const uint32_t a_k = (uint32_t)(kt * rows_a * kF6ARow), w_k = (uint32_t)(kt * rows_w * kF6WRow);
 #pragma unroll
         for (int u = 0; u < T::a_inst; u++) lds_dma16_so(a_desc, a_dst + st_off + (uint32_t)(u * 1024), a_off[u], a_k);
 #pragma unroll
@@ -823,11 +823,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_f6f4_kernel(
 constexpr int kF6BM = 256, kF6BN = 256, kF6WGM = 4, kF6WGN = 2, kF6Stages = 4;
 
 // 2-bit packed weights -> FP4 E2M1: one 32-bit word (16 weights; weight e of
-// the group at bits 8*(e%4) + 2*(e/4)) -> 8 bytes (weight e at nibble e).
+// the group at bits 8*(e%4) + 2*(e/4)) -> 8 bytes (weight e at nibble e), put
+// at its place in the FP4 layout (fp4_byte_offset).
 // The 2-bit code c (00 = 0, 01 = +1, 11 = -1) becomes (c & 1) << 1 | (c & 2) << 2:
 // 0000 = 0, 0010 = +1.0, 1010 = -1.0.
 __global__ __launch_bounds__(256) void weights_to_fp4_kernel(const uint32_t* __restrict__ Wp, int64_t n_words,
-                                                             uint2* __restrict__ W4) {
+                                                             int64_t N, int64_t K, uint8_t* __restrict__ W4) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n_words) return;
     const uint32_t w = Wp[i];
@@ -842,7 +843,9 @@ __global__ __launch_bounds__(256) void weights_to_fp4_kernel(const uint32_t* __r
         const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
         o[half] = __builtin_amdgcn_perm(hi | (hi >> 4), lo | (lo >> 4), 0x06040200u);
     }
-    W4[i] = make_uint2(o[0], o[1]);
+    const int64_t words_per_row = K / 16;
+    const int64_t n = i / words_per_row;
+    *reinterpret_cast<uint2*>(W4 + fp4_byte_offset(n, 16 * (i - n * words_per_row), N, K)) = make_uint2(o[0], o[1]);
 }
 
 }  // namespace
@@ -878,7 +881,7 @@ hipError_t launch_weights_to_fp4(const uint8_t* W_packed, int64_t N, int64_t K, 
     const int64_t blocks = (n_words + 255) / 256;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL(weights_to_fp4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint32_t*)W_packed,
-                       n_words, (uint2*)W4);
+                       n_words, N, K, W4);
     return hipGetLastError();
 }
 

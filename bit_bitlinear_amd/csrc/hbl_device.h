@@ -80,6 +80,21 @@ HBL_DEVINL int dec_tile_offset(int kb) {  // kb: byte index of the code inside i
 // (chunks 4, 5).  The M*K*3/4 bytes are private to the FP6 x FP4 GEMM.
 enum { kCodesRowMajor = 0, kCodesDecTiled = 1, kCodesFp6 = 2 };
 constexpr int kF6Band = 256;
+
+// ---- FP4 E2M1 weights (the library's W4 format, include/hbl.h) ----
+// Weight rows in bands of kF4Band (the FP6 x FP4 GEMM's block width); in a
+// band of R rows, K step s (128 weights, 64 bytes per row) of all R rows is
+// one block of R*64 bytes, row r at byte 64r; inside a row's 64 bytes the
+// 16-byte chunk c (weights 32c .. 32c+31) sits at c ^ ((r >> 2) & 3), the
+// GEMM's LDS order; weight k at nibble k, low nibble first.  K % 128 == 0.
+constexpr int kF4Band = 256;
+// byte offset of the 8 bytes holding weights k .. k+15 (k % 16 == 0) of row n
+HBL_DEVINL int64_t fp4_byte_offset(int64_t n, int64_t k, int64_t N, int64_t K) {
+    const int64_t n0 = n - n % kF4Band;
+    const int64_t R = N - n0 < kF4Band ? N - n0 : kF4Band;
+    const int64_t r = n - n0, s = k / 128, c = (k % 128) / 32, h = (k % 32) / 16;
+    return n0 * (K / 2) + (s * R + r) * 64 + ((c ^ ((r >> 2) & 3)) * 16) + 8 * h;
+}
 // Where row `row` of an M x K FP6 code matrix goes: its 96 bytes of K step s
 // start at base + s * stride; swz = 1 where the chunks are swapped.
 struct Fp6RowPlace {
@@ -189,12 +204,12 @@ hipError_t launch_gemm(const void* codes, const float* xscale, int act_bits, int
                        const uint8_t* W_packed, const float* alpha, int64_t N, void* Y, int y_dtype,
                        hipStream_t s, bool dec_tiled = false);
 // FP6 x FP4 prefill GEMM (INT4 activation codes only): codes in the FP6
-// layout above, weights as FP4 E2M1 nibbles (W4: N rows of K/2 bytes, code k
-// at nibble k, low nibble first).  Same results as launch_gemm, bit for bit.
+// layout above, weights as FP4 E2M1 nibbles in the FP4 layout above.  Same
+// results as launch_gemm, bit for bit.
 bool gemm_f6f4_eligible(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemm_f6f4(const uint8_t* codes6, const float* xscale, int64_t M, int64_t K, const uint8_t* W4,
                             const float* alpha, int64_t N, void* Y, int y_dtype, hipStream_t s);
-// 2-bit packed ternary weights -> FP4 E2M1 nibbles (W4 as above)
+// 2-bit packed ternary weights -> FP4 E2M1 nibbles (W4 as above; K % 128 == 0)
 hipError_t launch_weights_to_fp4(const uint8_t* W_packed, int64_t N, int64_t K, uint8_t* W4, hipStream_t s);
 // The layer's straight-through backward: dX (fp32 [M][K]) and, when dW is not
 // null, dW (fp32 [N][K]); K a power of two in [512, 32768]; ws holds

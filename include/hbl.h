@@ -208,10 +208,16 @@ hbl_status hbl_forward_latent(const void* X, int32_t x_dtype, int64_t M, int64_t
  * the fp32 sums are exact integers and Y is the same bit for bit as
  * hbl_forward's with INT4 codes.
  *
- * FP4 weight format (library definition): W4 uint8 [N][K/2]; weight k of row n
- * sits in byte k/2, low nibble for even k, as E2M1: 0 -> 0x0, +1 -> 0x2,
- * -1 -> 0xA.  hbl_fp4_weight_bytes: N*K/2 (constraints as
- * hbl_packed_weight_bytes).  hbl_pack_fp4: W_packed (the 2-bit layout of
+ * FP4 weight format (library definition): W4, N*K/2 bytes, each ternary
+ * weight one E2M1 nibble: 0 -> 0x0, +1 -> 0x2, -1 -> 0xA.  The order suits
+ * the GEMM's loads: rows in bands of 256 (band b: rows 256b .. 256b+R-1, R =
+ * min(256, N - 256b)); in a band, K step s (weights 128s .. 128s+127, 64
+ * bytes per row) of all R rows is one block of R*64 bytes at byte
+ * 256b*K/2 + 64*s*R, row r of the band at +64r; inside those 64 bytes the
+ * 16 bytes of weights 32c .. 32c+31 sit at +16*(c ^ ((r >> 2) & 3)), weight k
+ * at nibble k % 32 (low nibble first).  hbl_fp4_weight_bytes: N*K/2
+ * (constraints as hbl_packed_weight_bytes, and K % 128 == 0, else
+ * HBL_ERR_ALIGN).  hbl_pack_fp4: W_packed (the 2-bit layout of
  * hbl_quantize_weights) -> W4, the same ternary values; a deployment converts
  * once per weight.  Both buffers 16-byte aligned.
  *

@@ -46,6 +46,26 @@ def unpack_codes(codes: np.ndarray, K: int, bits: int) -> np.ndarray:
     return codes.astype(np.int8) if bits == 8 else oracle.unpack_int4(codes, K)
 
 
+def fp4_library_order(w4_rows: np.ndarray) -> np.ndarray:
+    """Row-major FP4 bytes [N][K/2] (the oracle's O14 order: weight k of row n
+    in byte k/2, low nibble for even k) rearranged into the library's W4 byte
+    order as include/hbl.h defines it: bands of 256 rows; in a band of R rows
+    the 64 bytes of K step s of every row form one block of R*64 bytes, row r
+    at 64r, and the 16 bytes of weights 32c .. 32c+31 sit at 16*(c ^ ((r >> 2)
+    & 3)).  Returns the N*K/2 bytes, flat."""
+    N, KB = w4_rows.shape
+    S = KB // 64
+    out = np.empty(N * KB, dtype=np.uint8)
+    for b0 in range(0, N, 256):
+        R = min(256, N - b0)
+        blk = w4_rows[b0:b0 + R].reshape(R, S, 4, 16)          # [r][s][chunk c][byte]
+        r = np.arange(R)
+        src = np.arange(4)[None, :] ^ ((r[:, None] >> 2) & 3)  # position p holds chunk p ^ f(r)
+        phys = blk[r[:, None], :, src]                          # [r][p][s][byte]
+        out[b0 * KB:(b0 + R) * KB] = phys.transpose(2, 0, 1, 3).reshape(-1)
+    return out
+
+
 def check_z(z_gpu: np.ndarray, z_ref: np.ndarray, what=""):
     for m in range(z_ref.shape[0]):
         scale = float(np.max(np.abs(z_ref[m])))

@@ -316,9 +316,13 @@ def test_fp4_fp6_validation(lib):
     with pytest.raises(hbl.HblError) as e:
         hbl.hbl_fp6_codes_bytes(8, 576)                                # K % 128
     assert e.value.status == 4
-    assert lib.hbl_pack_fp4(None, 16, 64, A16b, None) == 1
+    with pytest.raises(hbl.HblError) as e:
+        hbl.hbl_fp4_weight_bytes(16, 64)                               # the FP4 format holds whole K steps of 128
+    assert e.value.status == 4
+    assert lib.hbl_pack_fp4(None, 16, 128, A16b, None) == 1
     assert lib.hbl_pack_fp4(A16, 16, 40, A16b, None) == 4
-    assert lib.hbl_pack_fp4(MIS, 16, 64, A16b, None) == 4
+    assert lib.hbl_pack_fp4(A16, 16, 64, A16b, None) == 4              # K % 128
+    assert lib.hbl_pack_fp4(MIS, 16, 128, A16b, None) == 4
     cc4, cc8 = c4.c(), c8.c()
     q6 = lib.hbl_quantize_activations_fp6
     assert q6(A16, 0, 8, 1024, None, ctypes.byref(cc8), A16b, A16b, None) == 6

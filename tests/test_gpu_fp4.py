@@ -13,7 +13,7 @@ import pytest
 import bit_bitlinear_amd as hbl
 import oracle
 import workloads
-from parity import to_dev, to_host, unpack_codes
+from parity import fp4_library_order, to_dev, to_host, unpack_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -27,7 +27,7 @@ def _sync():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("N,K", [(16, 16), (48, 80), (272, 512), (4096, 16384), (12288, 4096)])
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 640), (272, 512), (300, 1024), (4096, 16384), (12288, 4096)])
 def test_pack_fp4_matches_oracle(N, K):
     _announce("pack_fp4 N=%d K=%d" % (N, K))
     rng = np.random.default_rng(N + K)
@@ -36,7 +36,7 @@ def test_pack_fp4_matches_oracle(N, K):
     W4 = hbl.hbl_pack_fp4(Wp, K)
     _sync()
     Wq = oracle.unpack_ternary(to_host(Wp), K)
-    assert np.array_equal(to_host(W4), oracle.pack_fp4(Wq))
+    assert np.array_equal(to_host(W4).reshape(-1), fp4_library_order(oracle.pack_fp4(Wq)))
 
 
 FP4_CASES = [

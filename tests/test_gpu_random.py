@@ -10,8 +10,8 @@ import pytest
 import bit_bitlinear_amd as hbl
 import oracle
 import workloads
-from parity import (check_codes_end_to_end, check_codes_given_inputs, check_dw, check_y, check_z, to_dev, to_host,
-                    unpack_codes, y_to_f32)
+from parity import (check_codes_end_to_end, check_codes_given_inputs, check_dw, check_y, check_z, fp4_library_order,
+                    to_dev, to_host, unpack_codes, y_to_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -178,7 +178,7 @@ def test_forward_fp4_random_config(c):
     Y8 = hbl.hbl_forward(Xd, Wp, alpha, N, cfg, y_dtype=ydt, gain=gd, ws=ws)
     codes, xs, _, _ = hbl.hbl_quantize_activations(Xd, cfg, gain=gd)
     torch.cuda.synchronize()
-    assert np.array_equal(to_host(W4), oracle.pack_fp4(oracle.unpack_ternary(to_host(Wp), K)))
+    assert np.array_equal(to_host(W4).reshape(-1), fp4_library_order(oracle.pack_fp4(oracle.unpack_ternary(to_host(Wp), K))))
     assert np.array_equal(to_host(Y4), to_host(Y8)), "FP6 x FP4 forward differs from the INT8 path"
     rows = workloads.sample_rows(M, 16)
     a_gpu = to_host(alpha)[0]
