@@ -695,6 +695,7 @@ def bench_single(args, layer):
         p.forward(i % p.R)
     torch.cuda.synchronize()
     graphs = capture([lambda r=r: p.forward(r) for r in range(p.R)])
+    replay_timed(graphs, max(2, args.warmup))  # untimed replays first (see graph_us)
     wall, ev_ms = replay_timed(graphs, args.steps)
     del graphs
     it = max(20, args.kernel_iters)
