@@ -54,14 +54,23 @@ def log(msg):
 
 
 def cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it, with its family and model
+    numbers (a virtualised host may report only a generic model name)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" in line:
+                    k, v = (x.strip() for x in line.split(":", 1))
+                    if k in ("model name", "cpu family", "model", "stepping") and k not in fields:
+                        fields[k] = v
+                if not line.strip() and fields:
+                    break  # the first processor's block is enough
     except OSError:
         pass
-    return "unknown"
+    name = fields.get("model name", "unknown")
+    nums = ", ".join("%s %s" % (k, fields[k]) for k in ("cpu family", "model", "stepping") if k in fields)
+    return "%s (%s)" % (name, nums) if nums else name
 
 
 def measured_peaks():
