@@ -641,36 +641,44 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void gemm_f6f4_kernel(
 
     // codes: the tile's band of rows_a rows holds K step kt as one block of
     // rows_a * 96 bytes, already in LDS order (hbl_device.h), so each load
-    // instruction copies 1 KiB of consecutive bytes; in a band of fewer than
-    // BM rows the chunks past its end fetch the next step's bytes (or zeros
-    // past the band), which only feed output rows that are not stored
+    // instruction copies 1 KiB of consecutive bytes.  Every K step's loads
+    // get a buffer resource covering exactly that block: in a band of fewer
+    // than BM rows the lanes past the block read zeros (they feed only output
+    // rows that are not stored), and no load leaves the block.  (The scalar
+    // soffset of a buffer load is not part of its range check, so the step
+    // may not ride there: with the banded layout it is far larger than the
+    // block, and a short last band would read past the end of its buffer.)
     static_assert(BM == kF6Band, "the FP6 code bands are the block height");
     const int rows_a = (int)min<int64_t>(BM, M - m0);
-    const v4u a_desc = rsrc_words(A6 + m0 * a_ld, (int64_t)rows_a * a_ld);
+    const uint8_t* const a_band = A6 + m0 * a_ld;
+    const int64_t a_blk = (int64_t)rows_a * kF6ARow;  // bytes of one K step's block
     // weights: the same for the FP4 layout's 256-row bands (blocks of one K
     // step, rows_w * 64 bytes, in LDS order)
     static_assert(BN == kF4Band, "the FP4 weight bands are the block width");
     const int rows_w = (int)min<int64_t>(BN, N - n0);
-    const v4u w_desc = rsrc_words(W4 + n0 * w_ld, (int64_t)rows_w * w_ld);
+    const uint8_t* const w_band = W4 + n0 * w_ld;
+    const int64_t w_blk = (int64_t)rows_w * kF6WRow;
     uint32_t a_off[T::a_inst], w_off[T::w_inst];
 #pragma unroll
     for (int u = 0; u < T::a_inst; u++) a_off[u] = (uint32_t)(((wave * T::a_inst + u) * 64 + lane) * 16);
 #pragma unroll
     for (int u = 0; u < T::w_inst; u++) w_off[u] = (uint32_t)(((wave * T::w_inst + u) * 64 + lane) * 16);
     const uint32_t smem_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-    // the K step's byte offset inside a row (below one row) rides in soffset;
-    // the LDS destinations are wave-uniform, computed in scalar registers
+    // the K step moves the resources' (scalar) base; the per-lane offsets
+    // stay fixed, and the LDS destinations are wave-uniform, computed in
+    // scalar registers
     const uint32_t wave_s = __builtin_amdgcn_readfirstlane((uint32_t)wave);
     const uint32_t a_dst = __builtin_amdgcn_readfirstlane(smem_addr) + wave_s * (uint32_t)(T::a_inst * 1024);
     const uint32_t w_dst = __builtin_amdgcn_readfirstlane(smem_addr) + (uint32_t)T::a_bytes +
                            wave_s * (uint32_t)(T::w_inst * 1024);
     auto issue = [&](int kt, int st) {
         const uint32_t st_off = (uint32_t)(st * T::stage);
-        const uint32_t a_k = (uint32_t)(kt * rows_a * kF6ARow), w_k = (uint32_t)(kt * rows_w * kF6WRow);
+        const v4u a_desc = rsrc_words(a_band + kt * a_blk, a_blk);
+        const v4u w_desc = rsrc_words(w_band + kt * w_blk, w_blk);
 #pragma unroll
-        for (int u = 0; u < T::a_inst; u++) lds_dma16_so(a_desc, a_dst + st_off + (uint32_t)(u * 1024), a_off[u], a_k);
+        for (int u = 0; u < T::a_inst; u++) lds_dma16(a_desc, a_dst + st_off + (uint32_t)(u * 1024), a_off[u]);
 #pragma unroll
-        for (int u = 0; u < T::w_inst; u++) lds_dma16_so(w_desc, w_dst + st_off + (uint32_t)(u * 1024), w_off[u], w_k);
+        for (int u = 0; u < T::w_inst; u++) lds_dma16(w_desc, w_dst + st_off + (uint32_t)(u * 1024), w_off[u]);
     };
 
     v16f acc[TA][TB];

@@ -35,22 +35,6 @@ HBL_DEVINL void lds_dma16(v4u desc, uint32_t lds_addr, uint32_t voff) {
         : "memory");
 }
 
-// The same with a wave-uniform byte offset in the scalar soffset field, so a
-// loop-varying offset costs no per-lane add.  Rows past the resource's range
-// still read zeros: every caller keeps soff below one row, so the lane offset
-// alone is out of range exactly when the row is.
-HBL_DEVINL void lds_dma16_so(v4u desc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(lds_addr), "v"(voff), "s"(desc), "s"(soff)
-        : "memory");
-}
-
 // s_waitcnt that waits for the vector-memory counter only (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
 template <int N>
